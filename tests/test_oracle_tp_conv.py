@@ -1,0 +1,307 @@
+"""Pins for the oracle's tensor product, convolution, adjoints, second
+derivatives, forces and CSR construction."""
+import numpy as np
+import pytest
+import scipy.sparse
+import torch
+
+import oracle
+from clebsch_gordan_tensor_cg_amd import workloads as W
+from tests.dense_ref import DenseTP
+from tests.test_oracle_cg_sh import random_rotation, wigner_d
+
+rng = np.random.default_rng(99)
+
+
+def small_problems():
+    return [
+        oracle.Problem("3x0e+2x1o", "1x0e+1x1o+1x2e", "3x0e+2x1o+3x1o+2x2e", "uvu"),
+        oracle.Problem("2x0e+2x1o+2x2e", "2x0e+1x1o", "2x0e+2x1o+2x2e+2x3o", "uvu"),
+        oracle.Problem("2x0+3x1", "1x0+1x1+1x2", "3x0+2x1+1x2", "uvw"),
+        oracle.Problem("2x1e+1x2o", "2x1o+1x0e", "2x0o+3x1o+2x2o", "uvw", shared_weights=True),
+    ]
+
+
+def c1_problem():
+    cfg = W.config("c1")
+    return oracle.Problem(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.mode)
+
+
+def test_path_counts_of_the_workloads():
+    expect = {"c1": 7, "c2": 10, "c3": 17, "c5": 44}
+    for name, n in expect.items():
+        cfg = W.config(name)
+        p = oracle.Problem(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.mode, cfg.paths,
+                           cfg.shared_weights)
+        assert len(p.paths) == n, name
+    p = c1_problem()
+    assert (p.dim1, p.dim2, p.dim3, p.weight_numel) == (32, 9, 72, 56)
+    cfg = W.config("c2")
+    p2 = oracle.Problem(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, "uvu", cfg.paths)
+    assert (p2.dim1, p2.dim2, p2.dim3, p2.weight_numel) == (512, 16, 5120, 1280)
+    cfg = W.config("c3")
+    p3 = oracle.Problem(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, "uvu", cfg.paths)
+    assert (p3.dim1, p3.dim3, p3.weight_numel) == (1152, 9088, 2176)
+
+
+def _inputs(p, B):
+    x = rng.standard_normal((B, p.dim1))
+    y = rng.standard_normal((B, p.dim2))
+    w = rng.standard_normal(p.weight_numel if p.shared_weights else (B, p.weight_numel))
+    return x, y, w
+
+
+@pytest.mark.parametrize("k", range(4))
+def test_tp_forward_brute_force(k):
+    p = small_problems()[k]
+    x, y, w = _inputs(p, 7)
+    ref = DenseTP(p).forward(*(torch.from_numpy(a) for a in (x, y, w))).numpy()
+    np.testing.assert_allclose(p.tp_forward(x, y, w), ref, atol=1e-12)
+
+
+def test_tp_equivariance_and_parity():
+    p = c1_problem()
+    rs = np.random.default_rng(3)
+    Rot = random_rotation(rs)
+    D = wigner_d(3, Rot)
+    B = 5
+    x = rs.standard_normal((B, p.dim1))
+    r = rs.standard_normal((B, 3))
+    y = oracle.spherical_harmonics(2, r)
+    w = rs.standard_normal((B, p.weight_numel))
+
+    def rot(v, irreps):
+        v = v.copy()
+        o = 0
+        for ir in irreps:
+            blk = v[:, o:o + ir.mul * ir.dim].reshape(B, ir.mul, ir.dim)
+            v[:, o:o + ir.mul * ir.dim] = (blk @ D[ir.l].T).reshape(B, -1)
+            o += ir.mul * ir.dim
+        return v
+
+    def par(v, irreps):
+        v = v.copy()
+        o = 0
+        for ir in irreps:
+            v[:, o:o + ir.mul * ir.dim] *= ir.p
+            o += ir.mul * ir.dim
+        return v
+
+    y_rot = oracle.spherical_harmonics(2, r @ Rot.T)
+    np.testing.assert_allclose(y_rot, rot(y, p.in2), atol=1e-10)
+    np.testing.assert_allclose(p.tp_forward(rot(x, p.in1), y_rot, w),
+                               rot(p.tp_forward(x, y, w), p.out), atol=1e-9)
+    # inversion r -> -r: the SH pick up (-1)^l, matching their parity labels
+    y_inv = oracle.spherical_harmonics(2, -r)
+    np.testing.assert_allclose(y_inv, par(y, p.in2), atol=1e-12)
+    np.testing.assert_allclose(p.tp_forward(par(x, p.in1), y_inv, w),
+                               par(p.tp_forward(x, y, w), p.out), atol=1e-12)
+
+
+def _tiny_graph(n=9, e=30, seed=5):
+    rs = np.random.default_rng(seed)
+    src = rs.integers(0, n, e).astype(np.int32)
+    dst = rs.integers(0, n, e).astype(np.int32)
+    dst[0] = src[0]  # a self loop is legal input for the convolution itself
+    return n, src, dst
+
+
+@pytest.mark.parametrize("k", range(4))
+def test_conv_equals_unfused_gather_tp_scatter(k):
+    p = small_problems()[k]
+    n, src, dst = _tiny_graph()
+    x = rng.standard_normal((n, p.dim1))
+    y = rng.standard_normal((len(src), p.dim2))
+    w = rng.standard_normal(p.weight_numel if p.shared_weights else (len(src), p.weight_numel))
+    msgs = p.tp_forward(x[src], y, w if not p.shared_weights else w)
+    ref = np.zeros((n, p.dim3))
+    np.add.at(ref, dst, msgs)
+    out = p.conv_forward(x, y, w, src, dst, n)
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+    # any edge order gives the same sums
+    perm = rng.permutation(len(src))
+    w_p = w if p.shared_weights else w[perm]
+    np.testing.assert_allclose(p.conv_forward(x, y[perm], w_p, src[perm], dst[perm], n), out,
+                               atol=1e-12)
+
+
+def test_conv_scalar_path_is_spmv():
+    p = oracle.Problem("4x0e", "1x0e", "4x0e", "uvu")
+    n, src, dst = _tiny_graph(12, 60, 8)
+    x = rng.standard_normal((n, 4))
+    y = rng.standard_normal((len(src), 1))
+    w = rng.standard_normal((len(src), 4))
+    out = p.conv_forward(x, y, w, src, dst, n)
+    for u in range(4):
+        A = scipy.sparse.csr_matrix((y[:, 0] * w[:, u], (dst, src)), shape=(n, n))
+        np.testing.assert_allclose(out[:, u], A @ x[:, u], atol=1e-12)
+
+
+def test_conv_node_without_edges_is_zero():
+    p = c1_problem()
+    x = rng.standard_normal((4, p.dim1))
+    y = rng.standard_normal((2, p.dim2))
+    w = rng.standard_normal((2, p.weight_numel))
+    out = p.conv_forward(x, y, w, np.array([0, 1]), np.array([2, 2]), 4)
+    assert np.all(out[[0, 1, 3]] == 0.0)
+
+
+@pytest.mark.parametrize("k", range(4))
+def test_backward_adjoint_and_autograd(k):
+    p = small_problems()[k]
+    n, src, dst = _tiny_graph()
+    x = rng.standard_normal((n, p.dim1))
+    y = rng.standard_normal((len(src), p.dim2))
+    w = rng.standard_normal(p.weight_numel if p.shared_weights else (len(src), p.weight_numel))
+    g = rng.standard_normal((n, p.dim3))
+    gx, gy, gw = p.conv_backward(x, y, w, src, dst, g)
+    f = p.conv_forward(x, y, w, src, dst, n)
+    # trilinearity: <g, f> = <g_x, x> = <g_y, y> = <g_w, w>
+    s = (g * f).sum()
+    for a, b in ((gx, x), (gy, y), (gw, w)):
+        assert abs((a * b).sum() - s) < 1e-10 * (1 + abs(s))
+    # torch CPU autograd of the dense formulation
+    xt, yt, wt = (torch.from_numpy(a).requires_grad_() for a in (x, y, w))
+    out = DenseTP(p).conv(xt, yt, wt, src, dst, n)
+    ax, ay, aw = torch.autograd.grad(out, (xt, yt, wt), torch.from_numpy(g))
+    np.testing.assert_allclose(gx, ax.numpy(), atol=1e-11)
+    np.testing.assert_allclose(gy, ay.numpy(), atol=1e-11)
+    np.testing.assert_allclose(gw, aw.numpy(), atol=1e-11)
+
+
+def test_backward_finite_difference():
+    p = small_problems()[1]
+    n, src, dst = _tiny_graph()
+    x = rng.standard_normal((n, p.dim1))
+    y = rng.standard_normal((len(src), p.dim2))
+    w = rng.standard_normal((len(src), p.weight_numel))
+    g = rng.standard_normal((n, p.dim3))
+    gx, gy, gw = p.conv_backward(x, y, w, src, dst, g)
+    L = lambda x_, y_, w_: (g * p.conv_forward(x_, y_, w_, src, dst, n)).sum()
+    h = 1e-6
+    for (arr, grad, which) in ((x, gx, 0), (y, gy, 1), (w, gw, 2)):
+        for _ in range(5):
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            d = np.zeros_like(arr)
+            d[idx] = h
+            args_p = [x, y, w]
+            args_m = [x, y, w]
+            args_p[which] = arr + d
+            args_m[which] = arr - d
+            fd = (L(*args_p) - L(*args_m)) / (2 * h)
+            assert abs(fd - grad[idx]) < 1e-6 * (1 + abs(fd))
+
+
+@pytest.mark.parametrize("k", [0, 2, 3])
+def test_double_backward_matches_autograd(k):
+    p = small_problems()[k]
+    n, src, dst = _tiny_graph()
+    x = rng.standard_normal((n, p.dim1))
+    y = rng.standard_normal((len(src), p.dim2))
+    w = rng.standard_normal(p.weight_numel if p.shared_weights else (len(src), p.weight_numel))
+    g = rng.standard_normal((n, p.dim3))
+    ax, ay, aw = (rng.standard_normal(a.shape) for a in (x, y, w))
+    dg, dx, dy, dw = p.conv_double_backward(x, y, w, src, dst, g, ax, ay, aw)
+    xt, yt, wt, gt = (torch.from_numpy(a).requires_grad_() for a in (x, y, w, g))
+    out = DenseTP(p).conv(xt, yt, wt, src, dst, n)
+    gx, gy, gw = torch.autograd.grad(out, (xt, yt, wt), gt, create_graph=True)
+    S = (gx * torch.from_numpy(ax)).sum() + (gy * torch.from_numpy(ay)).sum() + \
+        (gw * torch.from_numpy(aw)).sum()
+    tg, tx, ty, tw = torch.autograd.grad(S, (gt, xt, yt, wt))
+    for a, b in ((dg, tg), (dx, tx), (dy, ty), (dw, tw)):
+        np.testing.assert_allclose(a, b.numpy(), atol=1e-10)
+    # absent cotangents are zero
+    dg1, dx1, dy1, dw1 = p.conv_double_backward(x, y, w, src, dst, g, None, ay, None)
+    assert np.abs(dy1).max() == 0.0
+
+
+# --------------------------------------------------------------------------
+# Forces on a small periodic box
+# --------------------------------------------------------------------------
+
+def _force_setup(n_atoms=40, seed=2):
+    out, paths = W.one_block_per_path("4x0e+4x1o", W.sh_irreps(3), ["0e", "1o", "2e", "3o"])
+    p = oracle.Problem("4x0e+4x1o", W.sh_irreps(3), out, "uvu", paths)
+    g = W.periodic_graph(n_atoms, density=0.1, cutoff=3.5, seed=seed)
+    rs = np.random.default_rng(seed)
+    x = rs.standard_normal((n_atoms, p.dim1))
+    w = rs.standard_normal((g.n_edges, p.weight_numel))
+    mask = np.zeros(p.dim3)
+    for ir, o in zip(p.out, oracle.irreps_offsets(p.out)):
+        if ir.l == 0 and ir.p == 1:
+            mask[o:o + ir.mul] = 1.0
+    return p, g, x, w, mask
+
+
+def _energy(p, g, x, w, mask, vec):
+    sh = oracle.spherical_harmonics(3, vec)
+    out = p.conv_forward(x, sh, w, g.src, g.dst, g.n_nodes)
+    return (out * mask).sum()
+
+
+def test_forces_finite_difference_and_translation():
+    p, g, x, w, mask = _force_setup()
+    sh = oracle.spherical_harmonics(3, g.vec)
+    G = np.broadcast_to(mask, (g.n_nodes, p.dim3))
+    _, g_sh, _ = p.conv_backward(x, sh, w, g.src, g.dst, G, need=("sh",))
+    F = oracle.forces(3, g.n_nodes, g.src, g.dst, g.vec, g_sh)
+    np.testing.assert_allclose(F.sum(0), 0.0, atol=1e-10)
+    h = 1e-5
+    for a in (0, 7, 23):
+        for c in range(3):
+            # moving atom a changes r_e = pos[dst]-pos[src] on its edges
+            d = np.zeros(3)
+            d[c] = h
+            sgn = (g.dst == a).astype(float) - (g.src == a).astype(float)
+            Ep = _energy(p, g, x, w, mask, g.vec + sgn[:, None] * d)
+            Em = _energy(p, g, x, w, mask, g.vec - sgn[:, None] * d)
+            fd = -(Ep - Em) / (2 * h)
+            assert abs(fd - F[a, c]) < 1e-6 * (1 + abs(fd)), (a, c, fd, F[a, c])
+
+
+def test_forces_rotate_with_the_frame():
+    p, g, x, w, mask = _force_setup()
+    rs = np.random.default_rng(4)
+    Rot = random_rotation(rs)
+    D = wigner_d(3, Rot)
+
+    def F_of(vec, xx):
+        sh = oracle.spherical_harmonics(3, vec)
+        G = np.broadcast_to(mask, (g.n_nodes, p.dim3))
+        _, g_sh, _ = p.conv_backward(xx, sh, w, g.src, g.dst, G, need=("sh",))
+        return oracle.forces(3, g.n_nodes, g.src, g.dst, vec, g_sh)
+
+    xr = x.copy()
+    o = 0
+    for ir in p.in1:
+        blk = xr[:, o:o + ir.mul * ir.dim].reshape(-1, ir.mul, ir.dim)
+        xr[:, o:o + ir.mul * ir.dim] = (blk @ D[ir.l].T).reshape(len(x), -1)
+        o += ir.mul * ir.dim
+    np.testing.assert_allclose(F_of(g.vec @ Rot.T, xr), F_of(g.vec, x) @ Rot.T, atol=1e-9)
+
+
+def test_force_loss_cotangent_finite_difference():
+    """gg_sh = dL/dg_sh for L = 1/2 sum |F|^2, F linear in g_sh."""
+    p, g, x, w, mask = _force_setup()
+    rs = np.random.default_rng(6)
+    g_sh = rs.standard_normal((g.n_edges, 16))
+    F = oracle.forces(3, g.n_nodes, g.src, g.dst, g.vec, g_sh)
+    gg = oracle.force_loss_cotangent(3, g.n_nodes, g.src, g.dst, g.vec, F)
+    h = 1e-6
+    for _ in range(6):
+        e, k = rs.integers(0, g.n_edges), rs.integers(0, 16)
+        d = np.zeros_like(g_sh)
+        d[e, k] = h
+        Lp = 0.5 * (oracle.forces(3, g.n_nodes, g.src, g.dst, g.vec, g_sh + d) ** 2).sum()
+        Lm = 0.5 * (oracle.forces(3, g.n_nodes, g.src, g.dst, g.vec, g_sh - d) ** 2).sum()
+        assert abs((Lp - Lm) / (2 * h) - gg[e, k]) < 1e-6 * (1 + abs(gg[e, k]))
+
+
+def test_csr_matches_stable_argsort():
+    for seed in range(3):
+        rs = np.random.default_rng(seed)
+        n = int(rs.integers(1, 50))
+        key = rs.integers(0, n, int(rs.integers(0, 400))).astype(np.int32)
+        perm, row_ptr = oracle.csr(key, n)
+        np.testing.assert_array_equal(perm, np.argsort(key, kind="stable"))
+        np.testing.assert_array_equal(row_ptr, np.concatenate([[0], np.cumsum(np.bincount(key, minlength=n))]))
