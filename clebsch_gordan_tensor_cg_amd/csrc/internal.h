@@ -1,0 +1,108 @@
+// Internal declarations of the cgtp library (planner, code generator,
+// runtime compiler and launchers).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/cgtp.h"
+
+namespace cgtp {
+
+constexpr int kMaxL = 6;
+
+struct Irrep {
+    int mul = 0;
+    int l = 0;
+    int parity = 0;  // +1 even, -1 odd, 0 unlabelled
+    int dim() const { return 2 * l + 1; }
+};
+
+// One nonzero of a real coupling tensor: R[i][j][k] = c.
+struct Nonzero {
+    int i, j, k;
+    double c;
+};
+
+struct Path {
+    int i1, i2, i3;
+    int l1, l2, l3;
+    int mul1, mul2, mul3;
+    int64_t off1, off2, off3;  // element offsets of the blocks in their rows
+    int64_t woff;              // offset of the path's weights in a weight row
+    int64_t wnum;              // number of weights of the path
+    std::vector<double> R;     // dense [d1][d2][d3]
+    std::vector<Nonzero> nz;   // nonzeros of R (|c| > 1e-14), i-major order
+};
+
+// A kernel "unit": the paths one wavefront evaluates for one item, and the
+// channel slice it covers.  Units of a group share code.
+struct Group {
+    std::vector<int> paths;     // indices into Plan::paths
+    std::vector<int> in1_blocks;
+    std::vector<int> out_blocks;
+    int max_mul = 0;            // channel range the group covers
+    int cpl = 1;                // channels per lane
+    int slices = 1;             // ceil(max_mul / (lanes_per_item * cpl))
+};
+
+struct KernelShape {
+    int lanes_per_item = 64;    // LPI: lanes that share one item
+    int items_per_wave = 1;     // 64 / LPI
+    std::vector<Group> groups;
+    int n_units = 0;            // sum of slices over groups
+};
+
+struct Plan {
+    std::vector<Irrep> in1, in2, out;
+    std::vector<int64_t> off1, off2, off3;
+    cgtp_mode mode = CGTP_UVU;
+    cgtp_dtype dtype = CGTP_F32;
+    uint32_t flags = 0;
+    int64_t dim1 = 0, dim2 = 0, dim3 = 0, wnumel = 0;
+    int lmax2 = 0;
+    std::vector<Path> paths;
+
+    KernelShape fwd, bwd;
+    std::string source;
+    std::string cache_key;
+    bool cached = false;
+    bool loaded = false;
+    int n_kernels = 0;
+
+    hipModule_t module = nullptr;
+    hipFunction_t k_fwd = nullptr;
+    hipFunction_t k_bwd = nullptr;
+    int device = -1;
+};
+
+// planner
+int parse_irreps(const char *s, std::vector<Irrep> &out, std::string &err);
+int real_coupling(int l1, int l2, int l3, std::vector<double> &R, std::string &err);
+void choose_shapes(Plan &p);
+
+// code generation
+std::string generate_source(const Plan &p);
+
+// runtime compilation and cache
+int compile_and_load(Plan &p, bool load, std::string &err);
+
+// error state
+int set_error(int code, const std::string &msg);
+void clear_error();
+
+// launch helpers for the fixed kernels (kernels.hip)
+int launch_segment_sum_rows(cgtp_dtype dt, const void *rows, const int32_t *row_ptr,
+                            const int32_t *perm, int64_t n_seg, int64_t width, void *out,
+                            int accumulate, hipStream_t s);
+int launch_sum_parts(cgtp_dtype dt, const void *parts, int n_parts, int64_t n, void *out,
+                     int accumulate, hipStream_t s);
+
+}  // namespace cgtp
+
+struct cgtp_plan_s {
+    cgtp::Plan p;
+};

@@ -1,0 +1,576 @@
+// Fixed HIP kernels for gfx950 and their C ABI entry points: CSR build
+// (counting sort with a per-segment rank so the order is exactly the stable
+// order), CSR validation, real spherical harmonics of edge vectors, the
+// force reduction and the force-loss cotangent, segment sums of rows and
+// sums of partial buffers.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "internal.h"
+
+namespace cgtp {
+namespace {
+
+constexpr int kBlock = 256;
+
+inline unsigned grid_for(int64_t n, int per_block = kBlock) {
+    int64_t g = (n + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > 0x7fffffff) g = 0x7fffffff;
+    return (unsigned)g;
+}
+
+int hip_check(hipError_t e, const char *what) {
+    if (e == hipSuccess) return CGTP_OK;
+    return set_error(CGTP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// Generic fills, row segment sums, part sums
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ void k_fill(T *p, int64_t n, T v) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// out[s][c] (=|+=) sum_{k in [row_ptr[s], row_ptr[s+1])} rows[perm[k]][c]
+template <class T>
+__global__ void k_segment_sum_rows(const T *__restrict__ rows, const int32_t *__restrict__ row_ptr,
+                                   const int32_t *__restrict__ perm, int64_t width, T *__restrict__ out,
+                                   int accumulate) {
+    const int64_t s = blockIdx.x;
+    const int beg = row_ptr[s], end = row_ptr[s + 1];
+    for (int64_t c = blockIdx.y * (int64_t)blockDim.x + threadIdx.x; c < width;
+         c += (int64_t)gridDim.y * blockDim.x) {
+        T acc = 0;
+        for (int k = beg; k < end; ++k) {
+            const int64_t r = perm ? perm[k] : k;
+            acc += rows[r * width + c];
+        }
+        T *o = out + s * width + c;
+        *o = accumulate ? *o + acc : acc;
+    }
+}
+
+template <class T>
+__global__ void k_sum_parts(const T *__restrict__ parts, int n_parts, int64_t n, T *__restrict__ out,
+                            int accumulate) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        T acc = 0;
+        for (int p = 0; p < n_parts; ++p) acc += parts[p * n + i];
+        out[i] = accumulate ? out[i] + acc : acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// CSR build
+// ---------------------------------------------------------------------------
+__global__ void k_count(const int32_t *__restrict__ key, int64_t n, int32_t *__restrict__ cnt) {
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
+         e += (int64_t)gridDim.x * blockDim.x)
+        atomicAdd(&cnt[key[e]], 1);
+}
+
+// Exclusive scan of cnt[0..n) into row_ptr[0..n], one workgroup of 1024.
+__global__ void __launch_bounds__(1024) k_scan(const int32_t *__restrict__ cnt, int64_t n,
+                                                int32_t *__restrict__ row_ptr) {
+    __shared__ int32_t part[1024];
+    __shared__ int32_t carry;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < n; base += 1024) {
+        const int64_t i = base + threadIdx.x;
+        int32_t v = i < n ? cnt[i] : 0;
+        part[threadIdx.x] = v;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            int32_t t = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+            __syncthreads();
+            part[threadIdx.x] += t;
+            __syncthreads();
+        }
+        if (i < n) row_ptr[i] = carry + part[threadIdx.x] - v;
+        __syncthreads();
+        if (threadIdx.x == 1023) carry += part[1023];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) row_ptr[n] = carry;
+}
+
+__global__ void k_scatter(const int32_t *__restrict__ key, int64_t n, const int32_t *__restrict__ row_ptr,
+                          int32_t *__restrict__ cursor, int32_t *__restrict__ tmp) {
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int k = key[e];
+        const int pos = atomicAdd(&cursor[k], 1);
+        tmp[row_ptr[k] + pos] = (int32_t)e;
+    }
+}
+
+// One wavefront per segment: each element's final slot is the number of
+// smaller edge ids in its segment, which reproduces the stable order no
+// matter in which order the scatter's atomics landed.
+__global__ void __launch_bounds__(64) k_rank_segments(const int32_t *__restrict__ row_ptr, int64_t n_keys,
+                                                      const int32_t *__restrict__ tmp,
+                                                      const int32_t *__restrict__ key,
+                                                      const int32_t *__restrict__ val,
+                                                      int32_t *__restrict__ perm,
+                                                      int32_t *__restrict__ sorted_key,
+                                                      int32_t *__restrict__ sorted_val) {
+    const int64_t s = blockIdx.x;
+    if (s >= n_keys) return;
+    const int beg = row_ptr[s], end = row_ptr[s + 1];
+    for (int i = beg + threadIdx.x; i < end; i += 64) {
+        const int32_t me = tmp[i];
+        int rank = 0;
+        for (int j = beg; j < end; ++j) rank += tmp[j] < me;
+        perm[beg + rank] = me;
+        if (sorted_key) sorted_key[beg + rank] = key[me];
+        if (sorted_val) sorted_val[beg + rank] = val[me];
+    }
+}
+
+__global__ void k_validate(const int32_t *__restrict__ row_ptr, int64_t n_rows, int64_t n_edges,
+                           const int32_t *__restrict__ idx, int64_t range, int32_t *__restrict__ bad) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t t0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    for (int64_t r = t0; r < n_rows; r += stride)
+        if (row_ptr[r] > row_ptr[r + 1]) bad[0] = 1;
+    if (t0 == 0 && (row_ptr[0] != 0 || row_ptr[n_rows] != n_edges)) bad[0] = 1;
+    if (idx)
+        for (int64_t e = t0; e < n_edges; e += stride)
+            if (idx[e] < 0 || idx[e] >= range) bad[0] = 1;
+}
+
+// ---------------------------------------------------------------------------
+// Real spherical harmonics, component normalisation.
+// On the unit sphere, with u = r/|r| and (u_x + i u_y)^m = A_m + i B_m:
+//   Y_{l,0}  = N_l0 Q_l^0(u_z)
+//   Y_{l,m}  = N_lm Q_l^m(u_z) A_m,  Y_{l,-m} = N_lm Q_l^m(u_z) B_m  (m > 0)
+// where Q_l^m = d^m P_l / dz^m obeys the associated-Legendre recurrence
+// (Q_m^m = (2m-1)!!, Q_{m+1}^m = (2m+1) z Q_m^m, then the three-term rule),
+// N_l0 = sqrt(2l+1), N_lm = sqrt(2(2l+1)(l-m)!/(l+m)!).
+// These polynomials extend Y off the sphere; the gradient with respect to r
+// is (I - u u^T) grad_u / |r|, independent of the extension, with
+// dQ_l^m/dz = Q_l^{m+1}, d(A_m,B_m)/dx = m (A_{m-1}, B_{m-1}),
+// d(A_m,B_m)/dy = m (-B_{m-1}, A_{m-1}).
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr double fact_d(int n) { return n <= 1 ? 1.0 : n * fact_d(n - 1); }
+
+template <int L>
+struct ShNorm {
+    double v[(L + 1) * (L + 1)];
+    constexpr ShNorm() : v() {
+        for (int l = 0; l <= L; ++l)
+            for (int m = 0; m <= l; ++m) {
+                double s = (2.0 * l + 1.0) * (m == 0 ? 1.0 : 2.0 * fact_d(l - m) / fact_d(l + m));
+                // constexpr square root by Newton's method
+                double r = s > 1 ? s : 1.0;
+                for (int it = 0; it < 64; ++it) r = 0.5 * (r + s / r);
+                v[l * l + l + m] = r;
+            }
+    }
+};
+
+template <class T, int L>
+struct ShPoly {
+    T Q[L + 2][L + 2];  // Q[l][m], with Q[l][l+1] = 0
+    T A[L + 1], B[L + 1];
+    __device__ void eval(T ux, T uy, T uz) {
+        for (int l = 0; l <= L; ++l)
+            for (int m = 0; m <= L + 1; ++m) Q[l][m] = 0;
+        T dfm = 1;  // (2m-1)!!
+        for (int m = 0; m <= L; ++m) {
+            if (m > 0) dfm *= (T)(2 * m - 1);
+            Q[m][m] = dfm;
+            if (m + 1 <= L) Q[m + 1][m] = (T)(2 * m + 1) * uz * dfm;
+            for (int l = m + 2; l <= L; ++l)
+                Q[l][m] = ((T)(2 * l - 1) * uz * Q[l - 1][m] - (T)(l + m - 1) * Q[l - 2][m]) / (T)(l - m);
+        }
+        A[0] = 1;
+        B[0] = 0;
+        for (int m = 1; m <= L; ++m) {
+            A[m] = ux * A[m - 1] - uy * B[m - 1];
+            B[m] = ux * B[m - 1] + uy * A[m - 1];
+        }
+    }
+};
+
+template <class T>
+__device__ inline void store_sh(T *p, T v) { *p = v; }
+__device__ inline void store_sh(uint16_t *p, float v) {
+    // round to nearest even bf16
+    uint32_t u = __float_as_uint(v);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    *p = (uint16_t)(u >> 16);
+}
+
+template <class T, class S, int L>
+__global__ void k_sh(const T *__restrict__ vec, const int32_t *__restrict__ perm, int64_t n,
+                     S *__restrict__ sh) {
+    constexpr ShNorm<L> N{};
+    constexpr int NS = (L + 1) * (L + 1);
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = perm ? perm[t] : t;
+        T rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
+        const T inv = (T)1 / sqrt(rx * rx + ry * ry + rz * rz);
+        ShPoly<T, L> P;
+        P.eval(rx * inv, ry * inv, rz * inv);
+        S *o = sh + t * NS;
+#pragma unroll
+        for (int l = 0; l <= L; ++l) {
+            store_sh(o + l * l + l, (T)N.v[l * l + l] * P.Q[l][0]);
+#pragma unroll
+            for (int m = 1; m <= l; ++m) {
+                const T nq = (T)N.v[l * l + l + m] * P.Q[l][m];
+                store_sh(o + l * l + l + m, nq * P.A[m]);
+                store_sh(o + l * l + l - m, nq * P.B[m]);
+            }
+        }
+    }
+}
+
+// grad_u of every Y_k contracted with a per-k weight: G = sum_k c_k grad_u Y_k
+template <class T, int L>
+__device__ inline void sh_grad_contract(const ShPoly<T, L> &P, const T *c, T G[3]) {
+    constexpr ShNorm<L> N{};
+    G[0] = G[1] = G[2] = 0;
+#pragma unroll
+    for (int l = 0; l <= L; ++l) {
+        // m = 0
+        G[2] += c[l * l + l] * (T)N.v[l * l + l] * P.Q[l][1];
+#pragma unroll
+        for (int m = 1; m <= l; ++m) {
+            const T nm = (T)N.v[l * l + l + m];
+            const T cp = c[l * l + l + m], cn = c[l * l + l - m];
+            const T q = P.Q[l][m], dq = P.Q[l][m + 1];
+            // Y+ = nm q A_m ; Y- = nm q B_m
+            G[0] += nm * q * (T)m * (cp * P.A[m - 1] + cn * P.B[m - 1]);
+            G[1] += nm * q * (T)m * (-cp * P.B[m - 1] + cn * P.A[m - 1]);
+            G[2] += nm * dq * (cp * P.A[m] + cn * P.B[m]);
+        }
+    }
+}
+
+// per-edge force vector v_t = J_t^T g_t = (I - u u^T) G / |r|
+template <class T, int L>
+__global__ void k_edge_force(const T *__restrict__ vec, const int32_t *__restrict__ perm,
+                             const T *__restrict__ g_sh, int64_t n, T *__restrict__ v) {
+    constexpr int NS = (L + 1) * (L + 1);
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = perm ? perm[t] : t;
+        T rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
+        const T rn = sqrt(rx * rx + ry * ry + rz * rz), inv = (T)1 / rn;
+        const T u[3] = {rx * inv, ry * inv, rz * inv};
+        ShPoly<T, L> P;
+        P.eval(u[0], u[1], u[2]);
+        T c[NS];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) c[k] = g_sh[t * NS + k];
+        T G[3];
+        sh_grad_contract<T, L>(P, c, G);
+        const T ug = u[0] * G[0] + u[1] * G[1] + u[2] * G[2];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) v[3 * t + a] = (G[a] - u[a] * ug) * inv;
+    }
+}
+
+// F[a] = -sum_{t in dst seg a} v_t + sum_{k in src seg a} v_{src_perm[k]}
+template <class T>
+__global__ void k_node_force(const T *__restrict__ v, const int32_t *__restrict__ dst_row_ptr,
+                             const int32_t *__restrict__ src_row_ptr, const int32_t *__restrict__ src_perm,
+                             int64_t n_nodes, T *__restrict__ F) {
+    for (int64_t a = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; a < n_nodes;
+         a += (int64_t)gridDim.x * blockDim.x) {
+        T f0 = 0, f1 = 0, f2 = 0;
+        for (int t = dst_row_ptr[a]; t < dst_row_ptr[a + 1]; ++t) {
+            f0 -= v[3 * t];
+            f1 -= v[3 * t + 1];
+            f2 -= v[3 * t + 2];
+        }
+        for (int k = src_row_ptr[a]; k < src_row_ptr[a + 1]; ++k) {
+            const int64_t t = src_perm[k];
+            f0 += v[3 * t];
+            f1 += v[3 * t + 1];
+            f2 += v[3 * t + 2];
+        }
+        F[3 * a] = f0;
+        F[3 * a + 1] = f1;
+        F[3 * a + 2] = f2;
+    }
+}
+
+// gg_sh[t] = -J_t d,  d = F[dst t] - F[src t];  J_t d = grad_u Y . d_perp / |r|
+template <class T, int L>
+__global__ void k_force_cotangent(const T *__restrict__ vec, const int32_t *__restrict__ perm,
+                                  const int32_t *__restrict__ src, const int32_t *__restrict__ dst,
+                                  const T *__restrict__ F, int64_t n, T *__restrict__ gg) {
+    constexpr ShNorm<L> N{};
+    constexpr int NS = (L + 1) * (L + 1);
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = perm ? perm[t] : t;
+        T rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
+        const T rn = sqrt(rx * rx + ry * ry + rz * rz), inv = (T)1 / rn;
+        const T u[3] = {rx * inv, ry * inv, rz * inv};
+        const int64_t a = dst[t], b = src[t];
+        T d[3] = {F[3 * a] - F[3 * b], F[3 * a + 1] - F[3 * b + 1], F[3 * a + 2] - F[3 * b + 2]};
+        const T ud = u[0] * d[0] + u[1] * d[1] + u[2] * d[2];
+#pragma unroll
+        for (int c = 0; c < 3; ++c) d[c] = (d[c] - u[c] * ud) * inv;
+        ShPoly<T, L> P;
+        P.eval(u[0], u[1], u[2]);
+        T *o = gg + t * NS;
+#pragma unroll
+        for (int l = 0; l <= L; ++l) {
+            o[l * l + l] = -(T)N.v[l * l + l] * P.Q[l][1] * d[2];
+#pragma unroll
+            for (int m = 1; m <= l; ++m) {
+                const T nm = (T)N.v[l * l + l + m];
+                const T q = P.Q[l][m], dq = P.Q[l][m + 1];
+                const T gp0 = nm * q * (T)m * P.A[m - 1], gp1 = -nm * q * (T)m * P.B[m - 1], gp2 = nm * dq * P.A[m];
+                const T gn0 = nm * q * (T)m * P.B[m - 1], gn1 = nm * q * (T)m * P.A[m - 1], gn2 = nm * dq * P.B[m];
+                o[l * l + l + m] = -(gp0 * d[0] + gp1 * d[1] + gp2 * d[2]);
+                o[l * l + l - m] = -(gn0 * d[0] + gn1 * d[1] + gn2 * d[2]);
+            }
+        }
+    }
+}
+
+template <template <int> class F, class... A>
+int dispatch_l(int lmax, A... a) {
+    switch (lmax) {
+        case 0: return F<0>::run(a...);
+        case 1: return F<1>::run(a...);
+        case 2: return F<2>::run(a...);
+        case 3: return F<3>::run(a...);
+        case 4: return F<4>::run(a...);
+        case 5: return F<5>::run(a...);
+        case 6: return F<6>::run(a...);
+    }
+    return set_error(CGTP_ERR_UNSUPPORTED, "lmax must be in [0, 6]");
+}
+
+template <int L>
+struct ShLaunch {
+    static int run(cgtp_dtype dt, const void *vec, const int32_t *perm, int64_t n, void *sh, hipStream_t s) {
+        unsigned g = grid_for(n);
+        if (dt == CGTP_F32)
+            hipLaunchKernelGGL((k_sh<float, float, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm, n, (float *)sh);
+        else if (dt == CGTP_F64)
+            hipLaunchKernelGGL((k_sh<double, double, L>), dim3(g), dim3(kBlock), 0, s, (const double *)vec, perm, n, (double *)sh);
+        else
+            hipLaunchKernelGGL((k_sh<float, uint16_t, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm, n, (uint16_t *)sh);
+        return hip_check(hipGetLastError(), "spherical harmonics launch");
+    }
+};
+
+template <int L>
+struct ForceLaunch {
+    static int run(cgtp_dtype dt, const void *vec, const int32_t *perm, const void *g_sh, int64_t n, void *v,
+                   hipStream_t s) {
+        unsigned g = grid_for(n);
+        if (dt == CGTP_F32)
+            hipLaunchKernelGGL((k_edge_force<float, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm,
+                               (const float *)g_sh, n, (float *)v);
+        else
+            hipLaunchKernelGGL((k_edge_force<double, L>), dim3(g), dim3(kBlock), 0, s, (const double *)vec, perm,
+                               (const double *)g_sh, n, (double *)v);
+        return hip_check(hipGetLastError(), "edge force launch");
+    }
+};
+
+template <int L>
+struct CotLaunch {
+    static int run(cgtp_dtype dt, const void *vec, const int32_t *perm, const int32_t *src, const int32_t *dst,
+                   const void *F, int64_t n, void *gg, hipStream_t s) {
+        unsigned g = grid_for(n);
+        if (dt == CGTP_F32)
+            hipLaunchKernelGGL((k_force_cotangent<float, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm,
+                               src, dst, (const float *)F, n, (float *)gg);
+        else
+            hipLaunchKernelGGL((k_force_cotangent<double, L>), dim3(g), dim3(kBlock), 0, s, (const double *)vec,
+                               perm, src, dst, (const double *)F, n, (double *)gg);
+        return hip_check(hipGetLastError(), "force cotangent launch");
+    }
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// internal launchers used by the generated-kernel paths
+// ---------------------------------------------------------------------------
+int launch_segment_sum_rows(cgtp_dtype dt, const void *rows, const int32_t *row_ptr, const int32_t *perm,
+                            int64_t n_seg, int64_t width, void *out, int accumulate, hipStream_t s) {
+    if (n_seg <= 0 || width <= 0) return CGTP_OK;
+    int64_t gy = (width + kBlock - 1) / kBlock;
+    if (gy > 65535) gy = 65535;
+    dim3 grid((unsigned)n_seg, (unsigned)gy);
+    if (dt == CGTP_F64)
+        hipLaunchKernelGGL(k_segment_sum_rows<double>, grid, dim3(kBlock), 0, s, (const double *)rows, row_ptr, perm,
+                           width, (double *)out, accumulate);
+    else
+        hipLaunchKernelGGL(k_segment_sum_rows<float>, grid, dim3(kBlock), 0, s, (const float *)rows, row_ptr, perm,
+                           width, (float *)out, accumulate);
+    return hip_check(hipGetLastError(), "segment sum launch");
+}
+
+int launch_sum_parts(cgtp_dtype dt, const void *parts, int n_parts, int64_t n, void *out, int accumulate,
+                     hipStream_t s) {
+    if (n <= 0) return CGTP_OK;
+    unsigned g = grid_for(n);
+    if (g > 65536) g = 65536;
+    if (dt == CGTP_F64)
+        hipLaunchKernelGGL(k_sum_parts<double>, dim3(g), dim3(kBlock), 0, s, (const double *)parts, n_parts, n,
+                           (double *)out, accumulate);
+    else
+        hipLaunchKernelGGL(k_sum_parts<float>, dim3(g), dim3(kBlock), 0, s, (const float *)parts, n_parts, n,
+                           (float *)out, accumulate);
+    return hip_check(hipGetLastError(), "part sum launch");
+}
+
+int launch_zero(cgtp_dtype dt, void *p, int64_t n, hipStream_t s) {
+    if (n <= 0) return CGTP_OK;
+    unsigned g = grid_for(n);
+    if (g > 65536) g = 65536;
+    if (dt == CGTP_F64)
+        hipLaunchKernelGGL(k_fill<double>, dim3(g), dim3(kBlock), 0, s, (double *)p, n, 0.0);
+    else
+        hipLaunchKernelGGL(k_fill<float>, dim3(g), dim3(kBlock), 0, s, (float *)p, n, 0.0f);
+    return hip_check(hipGetLastError(), "fill launch");
+}
+
+}  // namespace cgtp
+
+using namespace cgtp;
+
+extern "C" {
+
+int cgtp_csr_workspace_bytes(int64_t n_edges, int64_t n_keys, size_t *bytes) {
+    clear_error();
+    if (!bytes || n_edges < 0 || n_keys < 0)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_csr_workspace_bytes: bad argument");
+    *bytes = align256(sizeof(int32_t) * (size_t)(n_keys + 1)) * 2 + align256(sizeof(int32_t) * (size_t)(n_edges + 1));
+    return CGTP_OK;
+}
+
+int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int64_t n_keys, int32_t *perm,
+                   int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val, void *workspace,
+                   size_t workspace_bytes, cgtp_stream_t stream) {
+    clear_error();
+    hipStream_t s = (hipStream_t)stream;
+    size_t need = 0;
+    cgtp_csr_workspace_bytes(n_edges, n_keys, &need);
+    if (n_edges < 0 || n_keys < 0 || n_edges > 0x7fffffff || n_keys > 0x7ffffffe)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_build_csr: sizes out of range");
+    if (!row_ptr || (n_edges > 0 && (!key || !perm || (sorted_val && !val))) || !workspace ||
+        workspace_bytes < need)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_build_csr: NULL pointer or workspace too small");
+    char *ws = (char *)workspace;
+    int32_t *cnt = (int32_t *)ws;
+    int32_t *cursor = (int32_t *)(ws + align256(sizeof(int32_t) * (size_t)(n_keys + 1)));
+    int32_t *tmp = (int32_t *)(ws + 2 * align256(sizeof(int32_t) * (size_t)(n_keys + 1)));
+    unsigned gk = grid_for(n_keys + 1);
+    hipLaunchKernelGGL(k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, cnt, n_keys + 1, 0);
+    hipLaunchKernelGGL(k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, cursor, n_keys + 1, 0);
+    if (n_edges > 0) {
+        unsigned ge = grid_for(n_edges);
+        if (ge > 65536) ge = 65536;
+        hipLaunchKernelGGL(k_count, dim3(ge), dim3(kBlock), 0, s, key, n_edges, cnt);
+        hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, cnt, n_keys, row_ptr);
+        hipLaunchKernelGGL(k_scatter, dim3(ge), dim3(kBlock), 0, s, key, n_edges, row_ptr, cursor, tmp);
+        if (n_keys > 0)
+            hipLaunchKernelGGL(k_rank_segments, dim3((unsigned)n_keys), dim3(64), 0, s, row_ptr, n_keys, tmp, key,
+                               val, perm, sorted_key, sorted_val);
+    } else {
+        hipLaunchKernelGGL(k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, row_ptr, n_keys + 1, 0);
+    }
+    return hip_check(hipGetLastError(), "cgtp_build_csr launch");
+}
+
+int cgtp_validate_csr(const int32_t *row_ptr, int64_t n_rows, int64_t n_edges, const int32_t *idx,
+                      int64_t n_idx_range, void *workspace, cgtp_stream_t stream) {
+    clear_error();
+    hipStream_t s = (hipStream_t)stream;
+    if (!row_ptr || !workspace || n_rows < 0 || n_edges < 0)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_validate_csr: bad argument");
+    int32_t *bad = (int32_t *)workspace;
+    hipLaunchKernelGGL(k_fill<int32_t>, dim3(1), dim3(64), 0, s, bad, 1, 0);
+    unsigned g = grid_for(std::max(n_rows, n_edges));
+    if (g > 4096) g = 4096;
+    hipLaunchKernelGGL(k_validate, dim3(g), dim3(kBlock), 0, s, row_ptr, n_rows, n_edges, idx, n_idx_range, bad);
+    int32_t h = 0;
+    int rc = hip_check(hipMemcpyAsync(&h, bad, sizeof h, hipMemcpyDeviceToHost, s), "validate copy");
+    if (rc) return rc;
+    rc = hip_check(hipStreamSynchronize(s), "validate sync");
+    if (rc) return rc;
+    if (h) return set_error(CGTP_ERR_GRAPH, "CSR validation failed: row_ptr not monotone, wrong ends, or index out of range");
+    return CGTP_OK;
+}
+
+int cgtp_spherical_harmonics(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm, int64_t n,
+                             void *sh, cgtp_stream_t stream) {
+    clear_error();
+    if (n < 0 || (n > 0 && (!vec || !sh)))
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_spherical_harmonics: bad argument");
+    if (dtype != CGTP_F32 && dtype != CGTP_F64 && dtype != CGTP_BF16_F32ACC)
+        return set_error(CGTP_ERR_UNSUPPORTED, "cgtp_spherical_harmonics: dtype");
+    if (n == 0) return CGTP_OK;
+    return dispatch_l<ShLaunch>(lmax, dtype, vec, perm, n, sh, (hipStream_t)stream);
+}
+
+int cgtp_forces_workspace_bytes(int64_t n_edges, cgtp_dtype dtype, size_t *bytes) {
+    clear_error();
+    if (!bytes || n_edges < 0) return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_forces_workspace_bytes");
+    *bytes = align256((size_t)n_edges * 3 * (dtype == CGTP_F64 ? 8 : 4));
+    return CGTP_OK;
+}
+
+int cgtp_sh_forces(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm, const void *g_sh,
+                   const int32_t *dst_row_ptr, const int32_t *src_row_ptr, const int32_t *src_perm, int64_t n_nodes,
+                   int64_t n_edges, void *F, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
+    clear_error();
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype != CGTP_F32 && dtype != CGTP_F64) return set_error(CGTP_ERR_UNSUPPORTED, "cgtp_sh_forces: dtype");
+    size_t need = 0;
+    cgtp_forces_workspace_bytes(n_edges, dtype, &need);
+    if (n_nodes < 0 || n_edges < 0 || (n_nodes > 0 && (!F || !dst_row_ptr || !src_row_ptr)) ||
+        (n_edges > 0 && (!vec || !g_sh || !src_perm || !workspace)) || workspace_bytes < need)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sh_forces: bad argument");
+    if (n_edges > 0) {
+        int rc = dispatch_l<ForceLaunch>(lmax, dtype, vec, perm, g_sh, n_edges, workspace, s);
+        if (rc) return rc;
+    }
+    if (n_nodes == 0) return CGTP_OK;
+    unsigned g = grid_for(n_nodes);
+    if (dtype == CGTP_F32)
+        hipLaunchKernelGGL(k_node_force<float>, dim3(g), dim3(kBlock), 0, s, (const float *)workspace, dst_row_ptr,
+                           src_row_ptr, src_perm, n_nodes, (float *)F);
+    else
+        hipLaunchKernelGGL(k_node_force<double>, dim3(g), dim3(kBlock), 0, s, (const double *)workspace, dst_row_ptr,
+                           src_row_ptr, src_perm, n_nodes, (double *)F);
+    return hip_check(hipGetLastError(), "node force launch");
+}
+
+int cgtp_force_loss_sh_cotangent(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm,
+                                 const int32_t *src, const int32_t *dst, const void *F, int64_t n_edges,
+                                 void *gg_sh, cgtp_stream_t stream) {
+    clear_error();
+    if (dtype != CGTP_F32 && dtype != CGTP_F64)
+        return set_error(CGTP_ERR_UNSUPPORTED, "cgtp_force_loss_sh_cotangent: dtype");
+    if (n_edges < 0 || (n_edges > 0 && (!vec || !src || !dst || !F || !gg_sh)))
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_force_loss_sh_cotangent: bad argument");
+    if (n_edges == 0) return CGTP_OK;
+    return dispatch_l<CotLaunch>(lmax, dtype, vec, perm, src, dst, F, n_edges, gg_sh, (hipStream_t)stream);
+}
+
+}  // extern "C"

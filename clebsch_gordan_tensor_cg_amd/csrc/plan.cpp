@@ -1,0 +1,262 @@
+// Planner: irreps parsing, path enumeration and validation, real coupling
+// tensors, and the split of the work into wavefront units.
+//
+// "An Efficient Sparse Kernel Generator for O(3)-Equivariant Deep
+// Networks" (abstract) does the tensor product's analysis once, at model
+// compile time, and emits kernels specialised to it; this file is that
+// analysis.  The coupling tensors follow the textbook construction
+// (Clebsch-Gordan coefficients by the Racah formula, then a change of every
+// index to the real spherical-harmonic basis).
+#include <cmath>
+#include <complex>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <algorithm>
+#include <functional>
+#include <numeric>
+#include <string>
+
+#include "internal.h"
+
+namespace cgtp {
+
+// ---------------------------------------------------------------------------
+// Irreps grammar: term ('+' term)*, term = MUL 'x' L [e|o]
+// ---------------------------------------------------------------------------
+int parse_irreps(const char *s, std::vector<Irrep> &out, std::string &err) {
+    out.clear();
+    if (!s) {
+        err = "irreps string is NULL";
+        return CGTP_ERR_INVALID_ARGUMENT;
+    }
+    const char *c = s;
+    auto skip = [&]() {
+        while (*c == ' ' || *c == '\t') ++c;
+    };
+    auto number = [&](long &v) -> bool {
+        skip();
+        if (*c < '0' || *c > '9') return false;
+        v = 0;
+        while (*c >= '0' && *c <= '9') {
+            v = v * 10 + (*c - '0');
+            if (v > (1L << 30)) return false;
+            ++c;
+        }
+        return true;
+    };
+    int labelled = -1;
+    for (;;) {
+        Irrep ir;
+        long mul, l;
+        if (!number(mul)) break;
+        skip();
+        if (*c != 'x') break;
+        ++c;
+        if (!number(l)) break;
+        skip();
+        int par = 0;
+        if (*c == 'e') par = 1, ++c;
+        else if (*c == 'o') par = -1, ++c;
+        int lab = par != 0;
+        if (labelled >= 0 && lab != labelled) {
+            err = std::string("mixed parity-labelled and unlabelled irreps in '") + s + "'";
+            return CGTP_ERR_INVALID_ARGUMENT;
+        }
+        labelled = lab;
+        if (mul <= 0) {
+            err = std::string("multiplicity must be positive in '") + s + "'";
+            return CGTP_ERR_INVALID_ARGUMENT;
+        }
+        ir.mul = (int)mul;
+        ir.l = (int)l;
+        ir.parity = par;
+        out.push_back(ir);
+        skip();
+        if (*c == '+') {
+            ++c;
+            continue;
+        }
+        if (*c == 0) return CGTP_OK;
+        break;
+    }
+    err = std::string("cannot parse irreps '") + s + "' near offset " + std::to_string(c - s);
+    return CGTP_ERR_INVALID_ARGUMENT;
+}
+
+// ---------------------------------------------------------------------------
+// Real coupling tensors
+// ---------------------------------------------------------------------------
+namespace {
+
+using cld = std::complex<long double>;
+
+long double factorial_ld(int n) {
+    static long double tab[64];
+    static std::once_flag once;
+    std::call_once(once, [] {
+        tab[0] = 1.0L;
+        for (int i = 1; i < 64; ++i) tab[i] = tab[i - 1] * (long double)i;
+    });
+    return tab[n];
+}
+
+// <l1 m1 l2 m2 | l3 m3>, Condon-Shortley convention (Racah's closed form).
+long double clebsch_gordan(int l1, int m1, int l2, int m2, int l3, int m3) {
+    if (m1 + m2 != m3) return 0.0L;
+    if (std::abs(m1) > l1 || std::abs(m2) > l2 || std::abs(m3) > l3) return 0.0L;
+    if (l3 < std::abs(l1 - l2) || l3 > l1 + l2) return 0.0L;
+    const long double tri = factorial_ld(l1 + l2 - l3) * factorial_ld(l1 - l2 + l3) *
+                            factorial_ld(-l1 + l2 + l3) / factorial_ld(l1 + l2 + l3 + 1);
+    const long double mfac = factorial_ld(l1 + m1) * factorial_ld(l1 - m1) *
+                             factorial_ld(l2 + m2) * factorial_ld(l2 - m2) *
+                             factorial_ld(l3 + m3) * factorial_ld(l3 - m3);
+    // summation index z runs where every factorial argument is >= 0
+    const int zmin = std::max({0, l2 - l3 - m1, l1 - l3 + m2});
+    const int zmax = std::min({l1 + l2 - l3, l1 - m1, l2 + m2});
+    long double sum = 0.0L;
+    for (int z = zmin; z <= zmax; ++z) {
+        long double den = factorial_ld(z) * factorial_ld(l1 + l2 - l3 - z) *
+                          factorial_ld(l1 - m1 - z) * factorial_ld(l2 + m2 - z) *
+                          factorial_ld(l3 - l2 + m1 + z) * factorial_ld(l3 - l1 - m2 + z);
+        sum += ((z & 1) ? -1.0L : 1.0L) / den;
+    }
+    return std::sqrt((2.0L * l3 + 1.0L) * tri * mfac) * sum;
+}
+
+// Real harmonic of order m (degree l) as a combination of complex ones:
+// up to two (mu, coefficient) terms.
+struct Term {
+    int mu;
+    cld a;
+};
+int real_from_complex(int m, Term out[2]) {
+    const long double h = 1.0L / std::sqrt(2.0L);
+    const long double sgn = (std::abs(m) & 1) ? -1.0L : 1.0L;
+    if (m == 0) {
+        out[0] = {0, cld(1.0L, 0.0L)};
+        return 1;
+    }
+    if (m > 0) {
+        out[0] = {-m, cld(h, 0.0L)};
+        out[1] = {m, cld(sgn * h, 0.0L)};
+        return 2;
+    }
+    out[0] = {m, cld(0.0L, h)};
+    out[1] = {-m, cld(0.0L, -sgn * h)};
+    return 2;
+}
+
+}  // namespace
+
+int real_coupling(int l1, int l2, int l3, std::vector<double> &R, std::string &err) {
+    if (l1 < 0 || l2 < 0 || l3 < 0 || l1 > kMaxL || l2 > kMaxL || l3 > kMaxL) {
+        err = "degree above 6 is not supported";
+        return CGTP_ERR_UNSUPPORTED;
+    }
+    if (l3 < std::abs(l1 - l2) || l3 > l1 + l2) {
+        err = "degrees violate the triangle rule";
+        return CGTP_ERR_INVALID_ARGUMENT;
+    }
+    const int d1 = 2 * l1 + 1, d2 = 2 * l2 + 1, d3 = 2 * l3 + 1;
+    const bool odd = ((l1 + l2 + l3) & 1) != 0;
+    R.assign((size_t)d1 * d2 * d3, 0.0);
+    for (int m1 = -l1; m1 <= l1; ++m1) {
+        Term t1[2];
+        const int n1 = real_from_complex(m1, t1);
+        for (int m2 = -l2; m2 <= l2; ++m2) {
+            Term t2[2];
+            const int n2 = real_from_complex(m2, t2);
+            for (int m3 = -l3; m3 <= l3; ++m3) {
+                Term t3[2];
+                const int n3 = real_from_complex(m3, t3);
+                cld acc(0.0L, 0.0L);
+                for (int a = 0; a < n1; ++a)
+                    for (int b = 0; b < n2; ++b)
+                        for (int c = 0; c < n3; ++c) {
+                            if (t1[a].mu + t2[b].mu != t3[c].mu) continue;
+                            const long double cg =
+                                clebsch_gordan(l1, t1[a].mu, l2, t2[b].mu, l3, t3[c].mu);
+                            acc += t3[c].a * std::conj(t1[a].a) * std::conj(t2[b].a) * cg;
+                        }
+                R[((size_t)(m1 + l1) * d2 + (m2 + l2)) * d3 + (m3 + l3)] =
+                    (double)(odd ? acc.imag() : acc.real());
+            }
+        }
+    }
+    return CGTP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Work split.  Each wavefront evaluates one group of paths for one item
+// (node or sample) over a slice of channels.  Groups are the connected
+// components of "shares an input-1 block or an output block", so every
+// output block and every input-1 block is owned by exactly one group: the
+// forward writes each output block once, and the backward's per-edge
+// input-1 messages are written by exactly one wavefront.
+// ---------------------------------------------------------------------------
+namespace {
+
+int next_pow2(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+void split(Plan &p, KernelShape &ks, bool backward) {
+    const int np = (int)p.paths.size();
+    std::vector<int> parent(np);
+    std::iota(parent.begin(), parent.end(), 0);
+    std::function<int(int)> find = [&](int a) { return parent[a] == a ? a : parent[a] = find(parent[a]); };
+    for (int a = 0; a < np; ++a)
+        for (int b = a + 1; b < np; ++b)
+            if (p.paths[a].i1 == p.paths[b].i1 || p.paths[a].i3 == p.paths[b].i3)
+                parent[find(a)] = find(b);
+    ks.groups.clear();
+    std::vector<int> gid(np, -1);
+    for (int a = 0; a < np; ++a) {
+        int r = find(a);
+        if (gid[r] < 0) {
+            gid[r] = (int)ks.groups.size();
+            ks.groups.emplace_back();
+        }
+        Group &g = ks.groups[gid[r]];
+        g.paths.push_back(a);
+        auto add = [](std::vector<int> &v, int x) {
+            for (int y : v)
+                if (y == x) return;
+            v.push_back(x);
+        };
+        add(g.in1_blocks, p.paths[a].i1);
+        add(g.out_blocks, p.paths[a].i3);
+        g.max_mul = std::max(g.max_mul, std::max(p.paths[a].mul1, p.paths[a].mul3));
+    }
+    int max_mul = 0;
+    for (auto &g : ks.groups) max_mul = std::max(max_mul, g.max_mul);
+    ks.lanes_per_item = max_mul >= 64 ? 64 : next_pow2(std::max(1, max_mul));
+    ks.items_per_wave = 64 / ks.lanes_per_item;
+    const int wide = (p.dtype == CGTP_F64) ? 2 : 1;
+    ks.n_units = 0;
+    for (auto &g : ks.groups) {
+        // registers per channel held across the edge loop
+        int acc = 0, xin = 0, wts = 0;
+        for (int b : g.out_blocks) acc += p.out[b].dim();
+        for (int b : g.in1_blocks) xin += p.in1[b].dim();
+        for (int a : g.paths) wts += p.paths[a].mul2;
+        int per_ch = (acc + xin + wts) * wide;
+        if (backward) per_ch += xin * wide;  // message accumulators
+        g.cpl = 1;
+        if (ks.lanes_per_item == 64 && g.max_mul > 64 && per_ch * 2 <= 96) g.cpl = 2;
+        g.slices = (g.max_mul + ks.lanes_per_item * g.cpl - 1) / (ks.lanes_per_item * g.cpl);
+        ks.n_units += g.slices;
+    }
+}
+
+}  // namespace
+
+void choose_shapes(Plan &p) {
+    split(p, p.fwd, false);
+    split(p, p.bwd, true);
+}
+
+}  // namespace cgtp

@@ -1,0 +1,271 @@
+/*
+ * cgtp.h -- C ABI of the MI355X (gfx950) Clebsch-Gordan tensor-product
+ * library: the CG tensor product of irrep feature vectors, fused with the
+ * graph convolution that follows it, its gradient and its second
+ * derivatives, plus the CSR, spherical-harmonic and force helpers the
+ * convolution needs.
+ *
+ * Sources of the operations (the pages give no formulas; the plain
+ * mathematical definitions are used, see each call):
+ *   [KG]  "An Efficient Sparse Kernel Generator for O(3)-Equivariant Deep
+ *         Networks", abstract: the CG tensor product contracts two dense
+ *         feature vectors with a structured sparse tensor; it is fused with
+ *         the following graph convolution; kernels for its gradient and for
+ *         the higher partial derivatives needed for interatomic forces;
+ *         static analysis at model compile time.
+ *   [SE3] "Faster training and inference with NVIDIA's open-source
+ *         SE(3)-Transformer" (TFN section): a degree-d feature has 2d+1
+ *         components; pairwise products between degrees are summed per
+ *         output degree; fused key/value channels; basis precomputation.
+ *   [MACE] "Speeding Up MACE: Low-Precision Tricks for Equivariant Force
+ *         Fields", abstract: FP64 / FP32 / BF16-with-FP32-accumulation
+ *         policies; mismatched module layouts give wrong results, so the
+ *         layout below is fixed and documented.
+ *
+ * Conventions (fixed; every call uses them):
+ *   - Irreps strings: "MULxLp" terms joined by '+', p in {e,o} or absent
+ *     (no parity label; labelled and unlabelled terms may not be mixed).
+ *     Block b of a row holds MUL*(2L+1) entries, element (u, m) at
+ *     offset_b + u*(2L+1) + (m+L), m = -L..L.  Blocks are kept in string
+ *     order; nothing is sorted or merged.
+ *   - Real spherical-harmonic basis, component normalisation
+ *     (sum_m Y_lm^2 = 2l+1), l=1 ordered (y, z, x).
+ *   - Real coupling tensor of path (l1,l2,l3): the complex CG tensor
+ *     (Condon-Shortley phase) changed to the real basis; the real part is
+ *     used when l1+l2+l3 is even, the imaginary part when odd.  This gives
+ *     1x1->0 = -delta/sqrt(3) and 1x1->1 = +epsilon/sqrt(2).
+ *   - No path or irrep normalisation factors; convolution sums are plain.
+ *   - Weights, per path in path order: uvu -> [mul1][mul2]; uvw ->
+ *     [mul1][mul2][mul_out].  Per-item weights are rows of weight_numel
+ *     entries; CGTP_SHARED_WEIGHTS means one row shared by all items.
+ *   - Graph arrays: edges are given in destination-sorted (CSR) order;
+ *     edge t carries sh[t], w[t] and src[t]; the edges of node n are
+ *     t in [dst_row_ptr[n], dst_row_ptr[n+1]).  Indices are int32.
+ *
+ * Ownership and execution: the caller owns every device buffer; calls are
+ * asynchronous on the caller's stream (NULL = default stream); buffers must
+ * stay alive until the stream has completed.  Execution calls allocate no
+ * device memory: scratch space is passed in as `workspace`.  Outputs are
+ * overwritten (rows of nodes with no edges are written as zero) unless a
+ * call says otherwise.  A plan is immutable after creation and may be used
+ * from several threads and streams at once.
+ *
+ * Errors: every call returns CGTP_OK (0) or a negative cgtp_status; a
+ * description of the last error on the calling thread is returned by
+ * cgtp_last_error().  No C++ exception crosses this boundary.
+ */
+#ifndef CGTP_H
+#define CGTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *cgtp_stream_t; /* same handle as hipStream_t */
+typedef struct cgtp_plan_s *cgtp_plan_t;
+
+typedef enum {
+    CGTP_OK = 0,
+    CGTP_ERR_INVALID_ARGUMENT = -1, /* grammar, NULL, size, forbidden path, uvu mul mismatch */
+    CGTP_ERR_UNSUPPORTED = -2,      /* l > 6, unsupported dtype/mode/flag combination */
+    CGTP_ERR_COMPILE = -3,          /* kernel generation or compilation failed (log in last_error) */
+    CGTP_ERR_HIP = -4,              /* HIP runtime error */
+    CGTP_ERR_GRAPH = -5             /* malformed CSR input found by cgtp_validate_csr */
+} cgtp_status;
+
+typedef enum { CGTP_UVU = 0, CGTP_UVW = 1 } cgtp_mode;
+
+typedef enum {
+    CGTP_F32 = 0,         /* float inputs, float arithmetic and outputs */
+    CGTP_F64 = 1,         /* double everywhere */
+    CGTP_BF16_F32ACC = 2  /* bf16 x, sh, w; float accumulation; float outputs */
+} cgtp_dtype;
+
+enum {
+    CGTP_SHARED_WEIGHTS = 1u << 0, /* one weight row for all items (uvw layers) */
+    CGTP_PLAN_NO_LOAD = 1u << 1    /* generate and compile into the on-disk cache only;
+                                      no device contact; execution calls then fail */
+};
+
+/* A path couples block i_in1 of input 1 with block i_in2 of input 2 into
+ * block i_out of the output. */
+typedef struct {
+    int32_t i_in1, i_in2, i_out;
+} cgtp_path;
+
+typedef struct {
+    int64_t dim_in1, dim_in2, dim_out; /* row lengths in elements */
+    int64_t weight_numel;              /* weights per item (or shared) */
+    int32_t n_paths;
+    int32_t lmax_in2;  /* largest degree in input 2 (the SH degree in conv use) */
+    int32_t n_kernels; /* generated kernels in the plan's code object */
+    int32_t cached;    /* 1 if the code object came from the on-disk cache */
+} cgtp_plan_dims;
+
+/* ---------------------------------------------------------------------- */
+/* Planning ("static analysis at model compile-time", [KG]).               */
+/* ---------------------------------------------------------------------- */
+
+/* Parses the irreps, validates `paths` (n_paths > 0) or enumerates every
+ * allowed path (n_paths == 0: |l1-l2| <= l3 <= l1+l2, parity p1*p2 == p3
+ * when labelled, uvu needs mul_out == mul_in1; order i_in1, then i_in2,
+ * then i_out), computes each path's real coupling tensor in FP64, keeps
+ * its nonzeros, decides the kernels' work split from the register and LDS
+ * budget, emits HIP source for gfx950 with the nonzeros as constants, and
+ * compiles it (hipRTC) or loads it from the code-object cache
+ * ($CGTP_CACHE_DIR, default "_kcache" beside the library).  Degrees are
+ * limited to l <= 6.  Errors: INVALID_ARGUMENT, UNSUPPORTED, COMPILE, HIP.
+ * On success *out owns the plan; release it with cgtp_plan_destroy. */
+int cgtp_plan(const char *irreps_in1, const char *irreps_in2, const char *irreps_out,
+              const cgtp_path *paths, int32_t n_paths, cgtp_mode mode, cgtp_dtype dtype,
+              uint32_t flags, cgtp_plan_t *out);
+
+int cgtp_plan_info(cgtp_plan_t plan, cgtp_plan_dims *dims);
+
+/* Copies min(cap, n_paths) paths of the plan (after enumeration). */
+int cgtp_plan_paths(cgtp_plan_t plan, cgtp_path *paths, int32_t cap);
+
+/* Host copy of path p's real coupling tensor R[i][j][k] as used by the
+ * kernels ((2l1+1)*(2l2+1)*(2l3+1) doubles; cap = capacity in doubles). */
+int cgtp_plan_coupling(cgtp_plan_t plan, int32_t p, double *R, int64_t cap);
+
+/* Generated HIP source (NUL-terminated; truncated to cap bytes).  Returns
+ * the full length (excluding NUL) through *len when len != NULL. */
+int cgtp_plan_source(cgtp_plan_t plan, char *buf, int64_t cap, int64_t *len);
+
+void cgtp_plan_destroy(cgtp_plan_t plan);
+
+/* ---------------------------------------------------------------------- */
+/* Tensor product on independent items ([KG]: the CG tensor product).      */
+/*   out[b] = sum_paths W . CG(x[b], y[b])                                 */
+/* x [batch][dim_in1], y [batch][dim_in2], w [batch][weight_numel] (or     */
+/* [weight_numel] shared), out [batch][dim_out]; element type per dtype.    */
+/* ---------------------------------------------------------------------- */
+int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, int64_t batch,
+                 void *out, cgtp_stream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Fused graph convolution ([KG]: TP fused with the graph convolution).    */
+/*   out[n] = sum_{t in [row_ptr[n], row_ptr[n+1])} TP(x[src[t]], sh[t], w[t])
+ * x [n_nodes][dim_in1]; sh [n_edges][dim_in2]; w [n_edges][weight_numel]   */
+/* (or shared); src [n_edges]; dst_row_ptr [n_nodes+1]; out [n_nodes][dim_out].
+ * Each destination row is reduced by one workgroup and written once; no   */
+/* atomics.  src values must lie in [0, n_nodes) and row_ptr must be a      */
+/* monotone CSR with row_ptr[0] = 0, row_ptr[n_nodes] = n_edges; check     */
+/* untrusted input with cgtp_validate_csr first.                            */
+/* ---------------------------------------------------------------------- */
+int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
+                      const int32_t *src, const int32_t *dst_row_ptr, int64_t n_nodes,
+                      int64_t n_edges, void *out, cgtp_stream_t stream);
+
+/* Workspace needed by cgtp_conv_backward / cgtp_conv_double_backward for a
+ * graph with n_edges edges (bytes; 256-byte aligned pointer required). */
+int cgtp_conv_workspace_bytes(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges,
+                              size_t *bytes);
+
+/* Gradient of the convolution ([KG]: gradient kernels) for the output
+ * cotangent g_out [n_nodes][dim_out]:
+ *   g_x[s]  = sum over edges leaving s of d<g_out, out>/dx   [n_nodes][dim_in1]
+ *   g_sh[t] = d<g_out, out>/dsh[t]                            [n_edges][dim_in2]
+ *   g_w[t]  = d<g_out, out>/dw[t]            [n_edges][weight_numel] (or shared sum)
+ * Edge arrays in dst-sorted order as in cgtp_conv_forward; dst [n_edges] is
+ * the destination of each edge in that order; src_row_ptr [n_nodes+1] and
+ * src_perm [n_edges] give, for each source node s, the positions (into the
+ * dst-sorted arrays) of its edges: src_perm[src_row_ptr[s] ..
+ * src_row_ptr[s+1]).  g_x is reduced per source node without atomics.
+ * Any of g_x, g_sh, g_w may be NULL (not computed).  Shared-weight plans
+ * are not supported here (UNSUPPORTED). */
+int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
+                       const int32_t *src, const int32_t *dst, const int32_t *dst_row_ptr,
+                       const int32_t *src_row_ptr, const int32_t *src_perm, const void *g_out,
+                       int64_t n_nodes, int64_t n_edges, void *g_x, void *g_sh, void *g_w,
+                       void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
+/* Second derivatives ([KG]: higher partial derivatives for forces).  The
+ * convolution f(x, sh, w) is trilinear, so for cotangents (gg_x, gg_sh,
+ * gg_w) on the backward's outputs the derivatives of
+ *   S = <gg_x, g_x> + <gg_sh, g_sh> + <gg_w, g_w>
+ * are forward and backward calls with substituted arguments:
+ *   d_g_out = f(gg_x, sh, w) + f(x, gg_sh, w) + f(x, sh, gg_w)
+ *   d_x     = fx*(g_out; gg_sh, w) + fx*(g_out; sh, gg_w)
+ *   d_sh    = fsh*(g_out; gg_x, w) + fsh*(g_out; x, gg_w)
+ *   d_w     = fw*(g_out; gg_x, sh) + fw*(g_out; x, gg_sh)
+ * NULL cotangents are zero; NULL outputs are skipped.  Shapes as in
+ * cgtp_conv_backward (d_g_out has the shape of g_out). */
+int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
+                              const int32_t *src, const int32_t *dst,
+                              const int32_t *dst_row_ptr, const int32_t *src_row_ptr,
+                              const int32_t *src_perm, const void *g_out, const void *gg_x,
+                              const void *gg_sh, const void *gg_w, int64_t n_nodes,
+                              int64_t n_edges, void *d_g_out, void *d_x, void *d_sh, void *d_w,
+                              void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Helpers                                                                  */
+/* ---------------------------------------------------------------------- */
+
+/* Stable sort of edge ids by key (key[e] in [0, n_keys)):
+ *   perm[t] = t-th edge id in (key, edge id) order; row_ptr[n] = #edges with
+ *   key < n (n_keys+1 entries); sorted_key[t] = key[perm[t]] and
+ *   sorted_val[t] = val[perm[t]] (each may be NULL; val carries a second
+ *   per-edge index, e.g. the source node, into the sorted order).
+ * Bit-exact and deterministic (the order within a key does not depend on
+ * the order in which the device's atomics land).  A segment of d edges
+ * costs O(d^2 / 64) per wavefront, so very large in-degrees are slow.
+ * workspace: cgtp_csr_workspace_bytes.  Keys must lie in [0, n_keys)
+ * (check untrusted keys with cgtp_validate_csr first). */
+int cgtp_csr_workspace_bytes(int64_t n_edges, int64_t n_keys, size_t *bytes);
+int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int64_t n_keys,
+                   int32_t *perm, int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val,
+                   void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
+/* Checks on the device that row_ptr is a monotone CSR over n_edges and that
+ * every index in idx[n_edges] (may be NULL) lies in [0, n_idx_range).
+ * Synchronises the stream.  Returns CGTP_OK or CGTP_ERR_GRAPH.
+ * workspace: 16 bytes. */
+int cgtp_validate_csr(const int32_t *row_ptr, int64_t n_rows, int64_t n_edges,
+                      const int32_t *idx, int64_t n_idx_range, void *workspace,
+                      cgtp_stream_t stream);
+
+/* Real spherical harmonics of edge vectors (component normalisation, see
+ * Conventions), degrees 0..lmax (lmax <= 6), [SE3] basis computation:
+ *   sh[t][l*l + m + l] = Y_lm(vec[e] / |vec[e]|),  e = perm ? perm[t] : t.
+ * vec [*][3] and sh [n][(lmax+1)^2] in dtype (F32 or F64; BF16_F32ACC
+ * reads float vectors and writes bf16). */
+int cgtp_spherical_harmonics(int32_t lmax, cgtp_dtype dtype, const void *vec,
+                             const int32_t *perm, int64_t n, void *sh, cgtp_stream_t stream);
+
+/* Forces from an energy gradient on the SH of the edges (edge order t as
+ * in the convolution, vector of edge t = vec[perm ? perm[t] : t] =
+ * pos[dst] - pos[src]):
+ *   F[a] = - sum_{t: dst=a} J_t^T g_sh[t] + sum_{t: src=a} J_t^T g_sh[t],
+ * J_t = dY/dvec at vec_t.  Reduced per atom over dst_row_ptr and over
+ * (src_row_ptr, src_perm); no atomics.  F [n_nodes][3]; dtype F32 or F64.
+ * workspace: cgtp_forces_workspace_bytes. */
+int cgtp_forces_workspace_bytes(int64_t n_edges, cgtp_dtype dtype, size_t *bytes);
+int cgtp_sh_forces(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm,
+                   const void *g_sh, const int32_t *dst_row_ptr, const int32_t *src_row_ptr,
+                   const int32_t *src_perm, int64_t n_nodes, int64_t n_edges, void *F,
+                   void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
+/* Cotangent on the SH of the force loss L = 1/2 sum_a |F[a]|^2:
+ *   gg_sh[t] = -J_t (F[dst[t]] - F[src[t]]).  dtype F32 or F64. */
+int cgtp_force_loss_sh_cotangent(int32_t lmax, cgtp_dtype dtype, const void *vec,
+                                 const int32_t *perm, const int32_t *src, const int32_t *dst,
+                                 const void *F, int64_t n_edges, void *gg_sh,
+                                 cgtp_stream_t stream);
+
+/* Description of the last error on this thread ("" if none). */
+const char *cgtp_last_error(void);
+
+/* Library version string. */
+const char *cgtp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CGTP_H */

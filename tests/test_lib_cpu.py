@@ -1,0 +1,124 @@
+"""CPU-only checks of the HIP library: it loads, exports every call that
+include/cgtp.h declares, and its host-side planner agrees with the oracle
+(coupling tensors, path lists, dimensions) and reports documented errors.
+No GPU compute is launched here."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from clebsch_gordan_tensor_cg_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from clebsch_gordan_tensor_cg_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from clebsch_gordan_tensor_cg_amd import build
+        build.build(verbose=False)
+    return binding
+
+
+def test_exports_every_declared_symbol(B):
+    hdr = open(os.path.join(ROOT, "include", "cgtp.h")).read()
+    declared = set(re.findall(r"\b(cgtp_[a-z0-9_]+)\s*\(", hdr))
+    assert declared, "no declarations found"
+    L = B.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(B.EXPORTS) == declared
+    assert "gfx950" in B.version()
+
+
+def test_planner_coupling_matches_oracle(B):
+    worst = 0.0
+    for l1 in range(7):
+        for l2 in range(7):
+            for l3 in range(abs(l1 - l2), min(l1 + l2, 6) + 1):
+                p = B.Plan(f"1x{l1}", f"1x{l2}", f"1x{l3}", mode="uvw", no_load=True)
+                R = p.coupling(0, (2 * l1 + 1, 2 * l2 + 1, 2 * l3 + 1))
+                worst = max(worst, np.abs(R - oracle.real_cg(l1, l2, l3)).max())
+    assert worst < 1e-13, worst
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
+def test_plan_dims_and_paths_match_oracle(B, name):
+    c = W.config(name)
+    op = oracle.Problem(c.irreps_in1, c.irreps_in2, c.irreps_out, c.mode, c.paths, c.shared_weights)
+    p = B.Plan(c.irreps_in1, c.irreps_in2, c.irreps_out, c.paths, c.mode, c.dtype, c.shared_weights,
+               no_load=True)
+    assert p.paths() == op.paths
+    assert (p.dim_in1, p.dim_in2, p.dim_out, p.weight_numel) == (op.dim1, op.dim2, op.dim3,
+                                                                 op.weight_numel)
+
+
+def test_generated_source_has_each_nonzero_once_per_channel_slot(B):
+    c = W.config("c1")
+    p = B.Plan(c.irreps_in1, c.irreps_in2, c.irreps_out, c.paths, c.mode, c.dtype, no_load=True)
+    src = p.source()
+    assert "cgtp_fwd" in src and "cgtp_bwd" in src
+    nnz = sum(int((np.abs(oracle.real_cg(*ls)) > 1e-14).sum())
+              for ls in [(0, 0, 0), (0, 1, 1), (0, 2, 2), (1, 0, 1), (1, 1, 0), (1, 1, 2), (1, 2, 1)])
+    # one FMA per nonzero into an accumulator in the forward kernel
+    fwd = src[src.index("cgtp_fwd"):src.index("cgtp_bwd")]
+    assert len(re.findall(r"\ba0_\d+_\d+ = fma\(", fwd)) == nnz
+
+
+@pytest.mark.parametrize("args,code", [
+    (("8x0e+", "1x0e", "8x0e"), -1),          # grammar
+    (("8x0e", "1x0e", "8x1e"), -1),           # no allowed path
+    (("8x0e+8x1o", "1x0e", "8x0e+4x1o"), 0),  # uvu skips the mismatched block when enumerating
+    (("8x7e", "1x0e", "8x7e"), -2),           # degree above 6
+    (("8x0e", "1x0", "8x0e"), 0),             # unlabelled input 2 with labelled others is allowed
+    (("8x0e+8x1", "1x0e", "8x0e"), -1),       # mixed labels in one string
+])
+def test_plan_errors(B, args, code):
+    if code == 0:
+        B.Plan(*args, no_load=True)
+        return
+    with pytest.raises(B.CgtpError) as ei:
+        B.Plan(*args, no_load=True)
+    assert ei.value.code == code
+
+
+def test_explicit_path_errors(B):
+    with pytest.raises(B.CgtpError) as ei:
+        B.Plan("8x0e+8x1o", "1x0e+1x1o", "8x0e+8x1o", paths=[(0, 1, 0)], no_load=True)  # 0e x 1o -> 0e
+    assert ei.value.code == -1
+    with pytest.raises(B.CgtpError) as ei:
+        B.Plan("8x0e", "1x0e", "4x0e", paths=[(0, 0, 0)], no_load=True)  # uvu needs mul_out == mul_in1
+    assert ei.value.code == -1
+    with pytest.raises(B.CgtpError) as ei:
+        B.Plan("8x0e", "1x0e", "8x0e", paths=[(0, 0, 3)], no_load=True)
+    assert ei.value.code == -1
+
+
+def test_compile_failure_is_reported(B, tmp_path, monkeypatch):
+    monkeypatch.setenv("CGTP_CACHE_DIR", str(tmp_path))
+    monkeypatch.setenv("CGTP_FAULT", "compile")
+    with pytest.raises(B.CgtpError) as ei:
+        B.Plan("3x0e+3x1o", "1x0e+1x1o", "3x0e+3x1o", no_load=True)
+    assert ei.value.code == -3
+    assert "CGTP_FAULT" in B.lib().cgtp_last_error().decode()
+
+
+def test_no_load_plan_refuses_execution(B):
+    import torch
+    p = B.Plan("8x0e", "1x0e", "8x0e", no_load=True)
+    x = torch.zeros(2, 8)
+    with pytest.raises(B.CgtpError) as ei:
+        B.cgtp_forward(p, x, torch.zeros(2, 1), torch.zeros(2, 8), out=torch.zeros(2, 8))
+    assert ei.value.code == -1
+
+
+def test_cache_round_trip(B, tmp_path, monkeypatch):
+    monkeypatch.setenv("CGTP_CACHE_DIR", str(tmp_path))
+    p1 = B.Plan("5x0e+5x1o", "1x0e+1x1o", "5x0e+5x1o", no_load=True)
+    assert not p1.cached
+    assert len(os.listdir(tmp_path)) == 1
+    p2 = B.Plan("5x0e+5x1o", "1x0e+1x1o", "5x0e+5x1o", no_load=True)
+    assert p2.cached
