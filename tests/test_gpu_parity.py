@@ -289,7 +289,12 @@ def _sampled_rows_check(prob, x, sh, w, src, dst, n_nodes, got_rows, rows, dtype
     # gather only the source rows used
     srcs = src[mask]
     uniq, inv = np.unique(srcs, return_inverse=True)
-    ref = prob.conv_forward(x[uniq], sh[mask], w[mask], inv.astype(np.int32), sub_dst, len(rows))
+    # one node set for sources and destinations: the gathered source rows,
+    # padded with zero rows if there are fewer of them than sampled rows
+    n_sub = max(len(uniq), len(rows))
+    x_sub = np.zeros((n_sub, x.shape[1]))
+    x_sub[:len(uniq)] = x[uniq]
+    ref = prob.conv_forward(x_sub, sh[mask], w[mask], inv.astype(np.int32), sub_dst, n_sub)[:len(rows)]
     return assert_close(got_rows, ref, dtype, "sampled rows")
 
 
