@@ -74,9 +74,8 @@ int run_fwd(const Plan &p, const void *x, const void *y, const void *w, const in
         accumulate = 1;
     }
     long long n = n_items;
-    long long wrow = (p.flags & CGTP_SHARED_WEIGHTS) ? 0 : p.wnumel;
     void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr,
-                    (void *)&out, &n, &wrow, &graph, &accumulate};
+                    (void *)&out, &n, &graph, &accumulate};
     const int64_t ipw = p.fwd.items_per_wave;
     return launch(p.k_fwd, (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
 }
@@ -88,6 +87,8 @@ struct BwdOut {
     bool acc_m = false;
     void *g_y = nullptr;  // per-edge y gradient
     bool acc_y = false;
+    void *fwd = nullptr;  // fused forward of the same operands (double backward)
+    bool acc_fwd = false;
 };
 
 int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
@@ -96,28 +97,35 @@ int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const in
     const size_t eb = out_bytes(p.dtype);
     void *m = ws;
     char *parts = ws + align256((size_t)n_edges * p.dim1 * eb);
-    const bool use_parts = o.g_y && p.bwd.n_units > 1;
+    const bool fused = o.fwd != nullptr;
+    const KernelShape &ks = fused ? p.dbl : p.bwd;
+    const bool use_parts = !fused && o.g_y && ks.n_units > 1;
     int flags = 0;
     if (o.g_w) flags |= 1 | (o.acc_w ? 8 : 0);
     if (o.want_m) flags |= 2 | (o.acc_m ? 16 : 0);
     if (o.g_y) flags |= 4 | (use_parts ? 64 : (o.acc_y ? 32 : 0));
-    if (!flags) return CGTP_OK;
+    if (fused && o.acc_fwd) flags |= 256;
+    if (!flags && !fused) return CGTP_OK;
     if (o.want_m && !o.acc_m && !blocks_covered(p.in1, p.paths, false)) {
         int rc = launch_zero(p.dtype, m, n_edges * p.dim1, s);
         if (rc) return rc;
         flags |= 16;
     }
-    void *gy_target = use_parts ? (void *)parts : o.g_y;
+    if (fused && !o.acc_fwd && !blocks_covered(p.out, p.paths, true)) {
+        int rc = launch_zero(p.dtype, o.fwd, n_nodes * p.dim3, s);
+        if (rc) return rc;
+        flags |= 256;
+    }
+    void *third = fused ? o.fwd : (use_parts ? (void *)parts : o.g_y);
     void *gw = o.g_w;
     long long n = n_nodes, ne = n_edges;
-    long long wrow = p.wnumel;
     int graph = 1;
     void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&g_out,
-                    &gw, &m, &gy_target, &n, &ne, &wrow, &graph, &flags};
-    const int64_t ipw = p.bwd.items_per_wave;
-    int rc = launch(p.k_bwd, (n_nodes + ipw - 1) / ipw * p.bwd.n_units, s, args);
+                    &gw, &m, &third, &n, &ne, &graph, &flags};
+    const int64_t ipw = ks.items_per_wave;
+    int rc = launch(fused ? p.k_dbl : p.k_bwd, (n_nodes + ipw - 1) / ipw * ks.n_units, s, args);
     if (rc) return rc;
-    if (use_parts) rc = launch_sum_parts(p.dtype, parts, p.bwd.n_units, n_edges * p.dim2, o.g_y, o.acc_y, s);
+    if (use_parts) rc = launch_sum_parts(p.dtype, parts, ks.n_units, n_edges * p.dim2, o.g_y, o.acc_y, s);
     return rc;
 }
 
@@ -399,59 +407,61 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
         (n_edges > 0 && (!x || !sh || !w || !src || !g_out)))
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
     const int64_t E = n_edges;
-    // d_g_out = f(gg_x, sh, w) + f(x, gg_sh, w) + f(x, sh, gg_w)
-    if (d_g_out) {
-        int acc = 0;
-        if (gg_x && E) {
-            if ((rc = run_fwd(p, gg_x, sh, w, src, dst_row_ptr, n_nodes, 1, d_g_out, acc, s))) return rc;
-            acc = 1;
-        }
-        if (gg_sh && E) {
-            if ((rc = run_fwd(p, x, gg_sh, w, src, dst_row_ptr, n_nodes, 1, d_g_out, acc, s))) return rc;
-            acc = 1;
-        }
-        if (gg_w && E) {
-            if ((rc = run_fwd(p, x, sh, gg_w, src, dst_row_ptr, n_nodes, 1, d_g_out, acc, s))) return rc;
-            acc = 1;
-        }
-        if (!acc && (rc = launch_zero(p.dtype, d_g_out, n_nodes * p.dim3, s))) return rc;
-    }
-    bool wrote_sh = false, wrote_w = false, wrote_m = false;
+    bool wrote_g = false, wrote_sh = false, wrote_w = false, wrote_m = false;
     if (E > 0) {
-        // a_x terms: d_sh += fsh*(g; gg_x, w), d_w += fw*(g; gg_x, sh)
-        if (gg_x && (d_sh || d_w)) {
+        // y term, one pass: d_g_out += f(x, gg_sh, w), d_x += fx*(g; gg_sh, w),
+        // d_w += fw*(g; x, gg_sh)
+        if (gg_sh && (d_g_out || d_x || d_w)) {
             BwdOut o;
-            o.g_y = d_sh;
-            o.acc_y = wrote_sh;
-            o.g_w = d_w;
-            o.acc_w = wrote_w;
-            if ((rc = run_bwd(p, gg_x, sh, w, src, dst_row_ptr, g_out, n_nodes, E, o, (char *)workspace, s))) return rc;
-            wrote_sh |= d_sh != nullptr;
-            wrote_w |= d_w != nullptr;
-        }
-        // a_w terms: d_x += fx*(g; sh, gg_w), d_sh += fsh*(g; x, gg_w)
-        if (gg_w && (d_x || d_sh)) {
-            BwdOut o;
-            o.want_m = d_x != nullptr;
-            o.acc_m = wrote_m;
-            o.g_y = d_sh;
-            o.acc_y = wrote_sh;
-            if ((rc = run_bwd(p, x, sh, gg_w, src, dst_row_ptr, g_out, n_nodes, E, o, (char *)workspace, s))) return rc;
-            wrote_m |= d_x != nullptr;
-            wrote_sh |= d_sh != nullptr;
-        }
-        // a_y terms: d_x += fx*(g; gg_sh, w), d_w += fw*(g; x, gg_sh)
-        if (gg_sh && (d_x || d_w)) {
-            BwdOut o;
+            o.fwd = d_g_out;
+            o.acc_fwd = wrote_g;
             o.want_m = d_x != nullptr;
             o.acc_m = wrote_m;
             o.g_w = d_w;
             o.acc_w = wrote_w;
             if ((rc = run_bwd(p, x, gg_sh, w, src, dst_row_ptr, g_out, n_nodes, E, o, (char *)workspace, s))) return rc;
+            wrote_g |= d_g_out != nullptr;
             wrote_m |= d_x != nullptr;
             wrote_w |= d_w != nullptr;
         }
+        // x term: d_g_out += f(gg_x, sh, w), d_sh += fsh*(g; gg_x, w), d_w += fw*(g; gg_x, sh)
+        if (gg_x) {
+            if (d_g_out) {
+                if ((rc = run_fwd(p, gg_x, sh, w, src, dst_row_ptr, n_nodes, 1, d_g_out, wrote_g, s))) return rc;
+                wrote_g = true;
+            }
+            if (d_sh || d_w) {
+                BwdOut o;
+                o.g_y = d_sh;
+                o.acc_y = wrote_sh;
+                o.g_w = d_w;
+                o.acc_w = wrote_w;
+                if ((rc = run_bwd(p, gg_x, sh, w, src, dst_row_ptr, g_out, n_nodes, E, o, (char *)workspace, s)))
+                    return rc;
+                wrote_sh |= d_sh != nullptr;
+                wrote_w |= d_w != nullptr;
+            }
+        }
+        // w term: d_g_out += f(x, sh, gg_w), d_x += fx*(g; sh, gg_w), d_sh += fsh*(g; x, gg_w)
+        if (gg_w) {
+            if (d_g_out) {
+                if ((rc = run_fwd(p, x, sh, gg_w, src, dst_row_ptr, n_nodes, 1, d_g_out, wrote_g, s))) return rc;
+                wrote_g = true;
+            }
+            if (d_x || d_sh) {
+                BwdOut o;
+                o.want_m = d_x != nullptr;
+                o.acc_m = wrote_m;
+                o.g_y = d_sh;
+                o.acc_y = wrote_sh;
+                if ((rc = run_bwd(p, x, sh, gg_w, src, dst_row_ptr, g_out, n_nodes, E, o, (char *)workspace, s)))
+                    return rc;
+                wrote_m |= d_x != nullptr;
+                wrote_sh |= d_sh != nullptr;
+            }
+        }
     }
+    if (d_g_out && !wrote_g && (rc = launch_zero(p.dtype, d_g_out, n_nodes * p.dim3, s))) return rc;
     if (d_x) {
         if (wrote_m) rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, src_perm, n_nodes, p.dim1, d_x, 0, s);
         else rc = launch_zero(p.dtype, d_x, n_nodes * p.dim1, s);

@@ -66,7 +66,7 @@ struct Plan {
     int lmax2 = 0;
     std::vector<Path> paths;
 
-    KernelShape fwd, bwd;
+    KernelShape fwd, bwd, dbl;
     std::string source;
     std::string cache_key;
     bool cached = false;
@@ -76,6 +76,7 @@ struct Plan {
     hipModule_t module = nullptr;
     hipFunction_t k_fwd = nullptr;
     hipFunction_t k_bwd = nullptr;
+    hipFunction_t k_dbl = nullptr;
     int device = -1;
 };
 

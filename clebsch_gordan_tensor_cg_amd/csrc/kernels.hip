@@ -38,21 +38,72 @@ __global__ void k_fill(T *p, int64_t n, T v) {
 }
 
 // out[s][c] (=|+=) sum_{k in [row_ptr[s], row_ptr[s+1])} rows[perm[k]][c]
+// One workgroup per segment (blockIdx.y splits wide rows); each thread owns
+// a 16-byte column chunk and keeps four source rows in flight.  Rows are
+// summed in segment order.
 template <class T>
-__global__ void k_segment_sum_rows(const T *__restrict__ rows, const int32_t *__restrict__ row_ptr,
-                                   const int32_t *__restrict__ perm, int64_t width, T *__restrict__ out,
-                                   int accumulate) {
+struct Vec16;
+template <>
+struct Vec16<float> {
+    using V = float4;
+    static constexpr int N = 4;
+    __device__ static V zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ static void add(V &a, const V &b) { a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w; }
+};
+template <>
+struct Vec16<double> {
+    using V = double2;
+    static constexpr int N = 2;
+    __device__ static V zero() { return make_double2(0.0, 0.0); }
+    __device__ static void add(V &a, const V &b) { a.x += b.x; a.y += b.y; }
+};
+
+template <class T>
+__global__ void __launch_bounds__(256) k_segment_sum_rows(const T *__restrict__ rows, const int32_t *__restrict__ row_ptr,
+                                                          const int32_t *__restrict__ perm, int64_t width,
+                                                          T *__restrict__ out, int accumulate) {
+    using VT = Vec16<T>;
+    using V = typename VT::V;
     const int64_t s = blockIdx.x;
     const int beg = row_ptr[s], end = row_ptr[s + 1];
-    for (int64_t c = blockIdx.y * (int64_t)blockDim.x + threadIdx.x; c < width;
-         c += (int64_t)gridDim.y * blockDim.x) {
-        T acc = 0;
-        for (int k = beg; k < end; ++k) {
-            const int64_t r = perm ? perm[k] : k;
-            acc += rows[r * width + c];
+    const bool vec_ok = (width % VT::N) == 0 && (((uintptr_t)rows | (uintptr_t)out) & 15) == 0;
+    const int64_t step = (int64_t)gridDim.y * blockDim.x * VT::N;
+    for (int64_t c = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * VT::N; c < width; c += step) {
+        if (vec_ok) {
+            V acc = VT::zero();
+            int k = beg;
+            for (; k + 4 <= end; k += 4) {
+                const int64_t r0 = perm ? perm[k] : k, r1 = perm ? perm[k + 1] : k + 1;
+                const int64_t r2 = perm ? perm[k + 2] : k + 2, r3 = perm ? perm[k + 3] : k + 3;
+                const V a0 = *(const V *)(rows + r0 * width + c);
+                const V a1 = *(const V *)(rows + r1 * width + c);
+                const V a2 = *(const V *)(rows + r2 * width + c);
+                const V a3 = *(const V *)(rows + r3 * width + c);
+                VT::add(acc, a0);
+                VT::add(acc, a1);
+                VT::add(acc, a2);
+                VT::add(acc, a3);
+            }
+            for (; k < end; ++k) {
+                const int64_t r = perm ? perm[k] : k;
+                VT::add(acc, *(const V *)(rows + r * width + c));
+            }
+            V *o = (V *)(out + s * width + c);
+            if (accumulate) {
+                V prev = *o;
+                VT::add(prev, acc);
+                *o = prev;
+            } else {
+                *o = acc;
+            }
+        } else {
+            for (int64_t cc = c; cc < c + VT::N && cc < width; ++cc) {
+                T acc = 0;
+                for (int k = beg; k < end; ++k) acc += rows[(int64_t)(perm ? perm[k] : k) * width + cc];
+                T *o = out + s * width + cc;
+                *o = accumulate ? *o + acc : acc;
+            }
         }
-        T *o = out + s * width + c;
-        *o = accumulate ? *o + acc : acc;
     }
 }
 
@@ -283,24 +334,33 @@ __global__ void k_edge_force(const T *__restrict__ vec, const int32_t *__restric
 }
 
 // F[a] = -sum_{t in dst seg a} v_t + sum_{k in src seg a} v_{src_perm[k]}
+// One wavefront per atom: lanes stride over the atom's edges, then a
+// butterfly sum over the wavefront.
 template <class T>
-__global__ void k_node_force(const T *__restrict__ v, const int32_t *__restrict__ dst_row_ptr,
-                             const int32_t *__restrict__ src_row_ptr, const int32_t *__restrict__ src_perm,
-                             int64_t n_nodes, T *__restrict__ F) {
-    for (int64_t a = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; a < n_nodes;
-         a += (int64_t)gridDim.x * blockDim.x) {
-        T f0 = 0, f1 = 0, f2 = 0;
-        for (int t = dst_row_ptr[a]; t < dst_row_ptr[a + 1]; ++t) {
-            f0 -= v[3 * t];
-            f1 -= v[3 * t + 1];
-            f2 -= v[3 * t + 2];
-        }
-        for (int k = src_row_ptr[a]; k < src_row_ptr[a + 1]; ++k) {
-            const int64_t t = src_perm[k];
-            f0 += v[3 * t];
-            f1 += v[3 * t + 1];
-            f2 += v[3 * t + 2];
-        }
+__global__ void __launch_bounds__(64) k_node_force(const T *__restrict__ v, const int32_t *__restrict__ dst_row_ptr,
+                                                   const int32_t *__restrict__ src_row_ptr,
+                                                   const int32_t *__restrict__ src_perm, int64_t n_nodes,
+                                                   T *__restrict__ F) {
+    const int64_t a = blockIdx.x;
+    const int lane = threadIdx.x;
+    T f0 = 0, f1 = 0, f2 = 0;
+    for (int t = dst_row_ptr[a] + lane; t < dst_row_ptr[a + 1]; t += 64) {
+        f0 -= v[3 * (int64_t)t];
+        f1 -= v[3 * (int64_t)t + 1];
+        f2 -= v[3 * (int64_t)t + 2];
+    }
+    for (int k = src_row_ptr[a] + lane; k < src_row_ptr[a + 1]; k += 64) {
+        const int64_t t = src_perm[k];
+        f0 += v[3 * t];
+        f1 += v[3 * t + 1];
+        f2 += v[3 * t + 2];
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+        f0 += __shfl_xor(f0, off, 64);
+        f1 += __shfl_xor(f1, off, 64);
+        f2 += __shfl_xor(f2, off, 64);
+    }
+    if (lane == 0) {
         F[3 * a] = f0;
         F[3 * a + 1] = f1;
         F[3 * a + 2] = f2;
@@ -412,7 +472,8 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 int launch_segment_sum_rows(cgtp_dtype dt, const void *rows, const int32_t *row_ptr, const int32_t *perm,
                             int64_t n_seg, int64_t width, void *out, int accumulate, hipStream_t s) {
     if (n_seg <= 0 || width <= 0) return CGTP_OK;
-    int64_t gy = (width + kBlock - 1) / kBlock;
+    const int per = dt == CGTP_F64 ? 2 : 4;  // elements per thread chunk
+    int64_t gy = (width + (int64_t)kBlock * per - 1) / ((int64_t)kBlock * per);
     if (gy > 65535) gy = 65535;
     dim3 grid((unsigned)n_seg, (unsigned)gy);
     if (dt == CGTP_F64)
@@ -551,12 +612,12 @@ int cgtp_sh_forces(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_
         if (rc) return rc;
     }
     if (n_nodes == 0) return CGTP_OK;
-    unsigned g = grid_for(n_nodes);
+    unsigned g = (unsigned)n_nodes;
     if (dtype == CGTP_F32)
-        hipLaunchKernelGGL(k_node_force<float>, dim3(g), dim3(kBlock), 0, s, (const float *)workspace, dst_row_ptr,
+        hipLaunchKernelGGL(k_node_force<float>, dim3(g), dim3(64), 0, s, (const float *)workspace, dst_row_ptr,
                            src_row_ptr, src_perm, n_nodes, (float *)F);
     else
-        hipLaunchKernelGGL(k_node_force<double>, dim3(g), dim3(kBlock), 0, s, (const double *)workspace, dst_row_ptr,
+        hipLaunchKernelGGL(k_node_force<double>, dim3(g), dim3(64), 0, s, (const double *)workspace, dst_row_ptr,
                            src_row_ptr, src_perm, n_nodes, (double *)F);
     return hip_check(hipGetLastError(), "node force launch");
 }

@@ -203,7 +203,8 @@ int next_pow2(int v) {
     return p;
 }
 
-void split(Plan &p, KernelShape &ks, bool backward) {
+// kind: 0 forward, 1 backward, 2 fused double backward
+void split(Plan &p, KernelShape &ks, int kind) {
     const int np = (int)p.paths.size();
     std::vector<int> parent(np);
     std::iota(parent.begin(), parent.end(), 0);
@@ -238,15 +239,19 @@ void split(Plan &p, KernelShape &ks, bool backward) {
     const int wide = (p.dtype == CGTP_F64) ? 2 : 1;
     ks.n_units = 0;
     for (auto &g : ks.groups) {
-        // registers per channel held across the edge loop
+        // registers per channel held across the edge loop: accumulators (or
+        // the cotangent row), operands of the current and the prefetched
+        // edge, and the backward's message accumulators
         int acc = 0, xin = 0, wts = 0;
         for (int b : g.out_blocks) acc += p.out[b].dim();
         for (int b : g.in1_blocks) xin += p.in1[b].dim();
         for (int a : g.paths) wts += p.paths[a].mul2;
-        int per_ch = (acc + xin + wts) * wide;
-        if (backward) per_ch += xin * wide;  // message accumulators
+        int per_ch = acc + 2 * (xin + wts);
+        if (kind >= 1) per_ch += xin;  // message accumulators
+        if (kind == 2) per_ch += acc;  // fused forward accumulators
+        per_ch *= wide;
         g.cpl = 1;
-        if (ks.lanes_per_item == 64 && g.max_mul > 64 && per_ch * 2 <= 96) g.cpl = 2;
+        if (ks.lanes_per_item == 64 && g.max_mul > 64 && per_ch * 2 <= 112) g.cpl = 2;
         g.slices = (g.max_mul + ks.lanes_per_item * g.cpl - 1) / (ks.lanes_per_item * g.cpl);
         ks.n_units += g.slices;
     }
@@ -255,8 +260,9 @@ void split(Plan &p, KernelShape &ks, bool backward) {
 }  // namespace
 
 void choose_shapes(Plan &p) {
-    split(p, p.fwd, false);
-    split(p, p.bwd, true);
+    split(p, p.fwd, 0);
+    split(p, p.bwd, 1);
+    split(p, p.dbl, 2);
 }
 
 }  // namespace cgtp

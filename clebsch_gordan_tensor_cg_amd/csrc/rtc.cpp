@@ -162,13 +162,14 @@ int compile_and_load(Plan &p, bool load, std::string &err) {
         r.destroy(&prog);
         write_file_atomic(dir, path, code);
     }
-    p.n_kernels = 1 + ((p.mode == CGTP_UVU && p.dtype != CGTP_BF16_F32ACC) ? 1 : 0);
+    p.n_kernels = 1 + ((p.mode == CGTP_UVU && p.dtype != CGTP_BF16_F32ACC) ? 2 : 0);
     if (!load) return CGTP_OK;
 
     hipError_t e = hipGetDevice(&p.device);
     if (e == hipSuccess) e = hipModuleLoadData(&p.module, code.data());
     if (e == hipSuccess) e = hipModuleGetFunction(&p.k_fwd, p.module, "cgtp_fwd");
     if (e == hipSuccess && p.n_kernels > 1) e = hipModuleGetFunction(&p.k_bwd, p.module, "cgtp_bwd");
+    if (e == hipSuccess && p.n_kernels > 2) e = hipModuleGetFunction(&p.k_dbl, p.module, "cgtp_dbl");
     if (e != hipSuccess) {
         err = std::string("loading generated code object: ") + hipGetErrorString(e);
         return CGTP_ERR_HIP;
