@@ -176,6 +176,7 @@ int cgtp_plan(const char *irreps_in1, const char *irreps_in2, const char *irreps
         p.mode = mode;
         p.dtype = dtype;
         p.flags = flags;
+        p.tune = tuning_from_env();
         auto o1 = offsets(p.in1), o2 = offsets(p.in2), o3 = offsets(p.out);
         p.dim1 = o1.back();
         p.dim2 = o2.back();

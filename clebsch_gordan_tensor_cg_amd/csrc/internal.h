@@ -56,7 +56,23 @@ struct KernelShape {
     int n_units = 0;            // sum of slices over groups
 };
 
+// Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
+// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, yvec, ntw, pf, budget, stage, cypath, depth) overrides
+// them for experiments.
+struct Tuning {
+    int cpl[3] = {0, 0, 0};  // channels per lane per kernel kind (0 = by budget)
+    int budget = 112;        // VGPR estimate allowed for two channels per lane
+    bool y_vector = true;    // load the y row with vector (not scalar) loads
+    bool nt_w = true;        // non-temporal loads of the per-edge weights
+    bool prefetch = true;    // load edge t+1 while edge t is computed
+    int stage = 64;          // edges per LDS chunk of src and y rows (0 = off)
+    int cy_path = -1;        // uniform products per path (1) or per edge (0); -1: by dtype
+    int depth = 3;           // edges of prefetch in flight (staged loop)
+};
+Tuning tuning_from_env();
+
 struct Plan {
+    Tuning tune;
     std::vector<Irrep> in1, in2, out;
     std::vector<int64_t> off1, off2, off3;
     cgtp_mode mode = CGTP_UVU;

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <complex>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <algorithm>
@@ -246,12 +247,13 @@ void split(Plan &p, KernelShape &ks, int kind) {
         for (int b : g.out_blocks) acc += p.out[b].dim();
         for (int b : g.in1_blocks) xin += p.in1[b].dim();
         for (int a : g.paths) wts += p.paths[a].mul2;
-        int per_ch = acc + 2 * (xin + wts);
+        int per_ch = acc + (1 + std::max(1, p.tune.depth)) * (xin + wts);
         if (kind >= 1) per_ch += xin;  // message accumulators
         if (kind == 2) per_ch += acc;  // fused forward accumulators
         per_ch *= wide;
         g.cpl = 1;
-        if (ks.lanes_per_item == 64 && g.max_mul > 64 && per_ch * 2 <= 112) g.cpl = 2;
+        if (ks.lanes_per_item == 64 && g.max_mul > 64 && per_ch * 2 <= p.tune.budget) g.cpl = 2;
+        if (p.tune.cpl[kind] > 0 && ks.lanes_per_item == 64) g.cpl = p.tune.cpl[kind];
         g.slices = (g.max_mul + ks.lanes_per_item * g.cpl - 1) / (ks.lanes_per_item * g.cpl);
         ks.n_units += g.slices;
     }
@@ -259,7 +261,38 @@ void split(Plan &p, KernelShape &ks, int kind) {
 
 }  // namespace
 
+Tuning tuning_from_env() {
+    Tuning t;
+    const char *e = std::getenv("CGTP_TUNE");
+    if (!e) return t;
+    std::string s = e;
+    size_t pos = 0;
+    while (pos < s.size()) {
+        size_t comma = s.find(',', pos);
+        if (comma == std::string::npos) comma = s.size();
+        std::string kv = s.substr(pos, comma - pos);
+        size_t eq = kv.find('=');
+        if (eq != std::string::npos) {
+            std::string k = kv.substr(0, eq);
+            int v = std::atoi(kv.c_str() + eq + 1);
+            if (k == "cpl_fwd") t.cpl[0] = v;
+            else if (k == "cpl_bwd") t.cpl[1] = v;
+            else if (k == "cpl_dbl") t.cpl[2] = v;
+            else if (k == "budget") t.budget = v;
+            else if (k == "yvec") t.y_vector = v != 0;
+            else if (k == "ntw") t.nt_w = v != 0;
+            else if (k == "pf") t.prefetch = v != 0;
+            else if (k == "stage") t.stage = v < 0 ? 0 : (v > 256 ? 256 : v);
+            else if (k == "cypath") t.cy_path = v;
+            else if (k == "depth") t.depth = v < 1 ? 1 : (v > 4 ? 4 : v);
+        }
+        pos = comma + 1;
+    }
+    return t;
+}
+
 void choose_shapes(Plan &p) {
+    if (p.tune.cy_path < 0) p.tune.cy_path = (p.dtype == CGTP_F64) ? 1 : 0;
     split(p, p.fwd, 0);
     split(p, p.bwd, 1);
     split(p, p.dbl, 2);
