@@ -43,7 +43,8 @@ class _Dims(ctypes.Structure):
 
 EXPORTS = [
     "cgtp_plan", "cgtp_plan_info", "cgtp_plan_paths", "cgtp_plan_coupling", "cgtp_plan_source",
-    "cgtp_plan_destroy", "cgtp_forward", "cgtp_conv_forward", "cgtp_conv_workspace_bytes",
+    "cgtp_plan_destroy", "cgtp_forward_workspace_bytes", "cgtp_forward", "cgtp_conv_forward",
+    "cgtp_conv_workspace_bytes",
     "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_csr_workspace_bytes", "cgtp_build_csr",
     "cgtp_validate_csr", "cgtp_spherical_harmonics", "cgtp_forces_workspace_bytes", "cgtp_sh_forces",
     "cgtp_force_loss_sh_cotangent", "cgtp_last_error", "cgtp_version",
@@ -66,8 +67,9 @@ def lib():
             "cgtp_plan_paths": [vp, vp, i32],
             "cgtp_plan_coupling": [vp, i32, vp, i64],
             "cgtp_plan_source": [vp, vp, i64, vp],
-            "cgtp_forward": [vp, vp, vp, vp, i64, vp, vp],
-            "cgtp_conv_forward": [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp],
+            "cgtp_forward_workspace_bytes": [vp, i64, vp],
+            "cgtp_forward": [vp, vp, vp, vp, i64, vp, vp, sz, vp],
+            "cgtp_conv_forward": [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
             "cgtp_conv_workspace_bytes": [vp, i64, i64, vp],
             "cgtp_conv_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, sz, vp],
             "cgtp_conv_double_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
@@ -181,20 +183,34 @@ def cgtp_plan(irreps_in1, irreps_in2, irreps_out, paths=None, mode="uvu", dtype=
 # ---------------------------------------------------------------------------
 # execution
 # ---------------------------------------------------------------------------
-def cgtp_forward(plan: Plan, x, y, w, out=None, stream=None):
+def cgtp_forward_workspace_bytes(plan: Plan, n_items: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().cgtp_forward_workspace_bytes(plan.handle, n_items, ctypes.byref(b)))
+    return b.value
+
+
+def cgtp_forward(plan: Plan, x, y, w, out=None, ws=None, stream=None):
     B = x.shape[0]
     if out is None:
         out = torch.empty(B, plan.dim_out, dtype=plan.out_dtype, device=x.device)
-    _check(lib().cgtp_forward(plan.handle, _ptr(x), _ptr(y), _ptr(w), B, _ptr(out), _stream(stream, x)))
+    nb = cgtp_forward_workspace_bytes(plan, B)
+    if ws is None and nb:
+        ws = workspace(nb, x.device)
+    _check(lib().cgtp_forward(plan.handle, _ptr(x), _ptr(y), _ptr(w), B, _ptr(out), _ptr(ws),
+                              ws.numel() if ws is not None else 0, _stream(stream, x)))
     return out
 
 
-def cgtp_conv_forward(plan: Plan, x, sh, w, src, dst_row_ptr, out=None, stream=None):
+def cgtp_conv_forward(plan: Plan, x, sh, w, src, dst_row_ptr, out=None, ws=None, stream=None):
     N, E = x.shape[0], src.shape[0]
     if out is None:
         out = torch.empty(N, plan.dim_out, dtype=plan.out_dtype, device=x.device)
+    nb = cgtp_forward_workspace_bytes(plan, N)
+    if ws is None and nb:
+        ws = workspace(nb, x.device)
     _check(lib().cgtp_conv_forward(plan.handle, _ptr(x), _ptr(sh), _ptr(w), _ptr(src), _ptr(dst_row_ptr),
-                                   N, E, _ptr(out), _stream(stream, x)))
+                                   N, E, _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
+                                   _stream(stream, x)))
     return out
 
 

@@ -240,9 +240,10 @@ int cgtp_plan(const char *irreps_in1, const char *irreps_in2, const char *irreps
         p.wnumel = woff;
         if (mode == CGTP_UVU && dtype == CGTP_BF16_F32ACC)
             return fail(CGTP_ERR_UNSUPPORTED, "bf16 inputs are provided for uvw plans only");
-        if (mode == CGTP_UVW) {
-            // uvw kernels are not generated yet: the plan serves coupling
-            // queries only
+        if (mode == CGTP_UVW && (dtype != CGTP_BF16_F32ACC || !(flags & CGTP_SHARED_WEIGHTS))) {
+            // uvw kernels exist for bf16 operands with one shared weight set
+            // (channel mixing on the matrix cores); other uvw plans serve
+            // coupling queries only
             *out = h;
             return CGTP_OK;
         }
@@ -312,20 +313,52 @@ void cgtp_plan_destroy(cgtp_plan_t plan) {
     delete plan;
 }
 
+static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
+                   const int32_t *row_ptr, int64_t n_items, int graph, void *out, void *ws, size_t ws_bytes,
+                   hipStream_t s) {
+    size_t need = align256((size_t)n_items * p.t_per_item * 2);
+    if (ws_bytes < need || (!ws && need)) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace too small");
+    if (((uintptr_t)ws) & 255) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    long long n = n_items;
+    void *args[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, &ws, &n, &graph};
+    const int64_t ipw = p.fwd.items_per_wave;
+    int rc = launch(p.k_fwd, (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
+    if (rc) return rc;
+    int acc = 0;
+    if (!blocks_covered(p.out, p.paths, true)) {
+        if ((rc = launch_zero(CGTP_F32, out, n_items * p.dim3, s))) return rc;
+        acc = 1;
+    }
+    for (const MixBlock &mb : p.mix)
+        if ((rc = launch_uvw_mix(p, mb, ws, w, n_items, out, acc, s))) return rc;
+    return CGTP_OK;
+}
+
+int cgtp_forward_workspace_bytes(cgtp_plan_t plan, int64_t n_items, size_t *bytes) {
+    clear_error();
+    if (!plan || !bytes || n_items < 0) return set_error(CGTP_ERR_INVALID_ARGUMENT, "bad argument");
+    const Plan &p = plan->p;
+    *bytes = p.mode == CGTP_UVW ? align256((size_t)n_items * p.t_per_item * 2) : 0;
+    return CGTP_OK;
+}
+
 int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, int64_t batch, void *out,
-                 cgtp_stream_t stream) {
+                 void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
     clear_error();
     int rc = check_loaded(plan);
     if (rc) return rc;
     if (batch < 0 || batch > 0x7fffffffLL) return set_error(CGTP_ERR_INVALID_ARGUMENT, "batch out of range");
     if (batch == 0) return CGTP_OK;
     if (!x || !y || !w || !out) return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
+    if (plan->p.mode == CGTP_UVW)
+        return run_uvw(plan->p, x, y, w, nullptr, nullptr, batch, 0, out, workspace, workspace_bytes,
+                       (hipStream_t)stream);
     return run_fwd(plan->p, x, y, w, nullptr, nullptr, batch, 0, out, 0, (hipStream_t)stream);
 }
 
 int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
-                      const int32_t *dst_row_ptr, int64_t n_nodes, int64_t n_edges, void *out,
-                      cgtp_stream_t stream) {
+                      const int32_t *dst_row_ptr, int64_t n_nodes, int64_t n_edges, void *out, void *workspace,
+                      size_t workspace_bytes, cgtp_stream_t stream) {
     clear_error();
     int rc = check_loaded(plan);
     if (rc) return rc;
@@ -334,6 +367,9 @@ int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const voi
     if (n_nodes == 0) return CGTP_OK;
     if (!dst_row_ptr || !out || (n_edges > 0 && (!x || !sh || !w || !src)))
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
+    if (plan->p.mode == CGTP_UVW)
+        return run_uvw(plan->p, x, sh, w, src, dst_row_ptr, n_nodes, 1, out, workspace, workspace_bytes,
+                       (hipStream_t)stream);
     return run_fwd(plan->p, x, sh, w, src, dst_row_ptr, n_nodes, 1, out, 0, (hipStream_t)stream);
 }
 
@@ -351,7 +387,7 @@ static int check_graph_args(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
     int rc = check_loaded(plan);
     if (rc) return rc;
     if (plan->p.mode != CGTP_UVU || !plan->p.k_bwd)
-        return set_error(CGTP_ERR_UNSUPPORTED, "backward kernels exist for uvu fp32/fp64 plans");
+        return set_error(CGTP_ERR_UNSUPPORTED, "backward kernels are provided for uvu fp32/fp64 plans");
     if (plan->p.flags & CGTP_SHARED_WEIGHTS)
         return set_error(CGTP_ERR_UNSUPPORTED, "backward with shared weights is not provided");
     if (n_nodes < 0 || n_edges < 0 || n_edges > 0x7fffffffLL || n_nodes > 0x7fffffffLL)

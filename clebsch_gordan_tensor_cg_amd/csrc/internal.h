@@ -71,6 +71,17 @@ struct Tuning {
 };
 Tuning tuning_from_env();
 
+// uvw plans: the paths into output block b3, concatenated along the
+// contraction dimension K of the channel-mixing product T_b3 . W_b3.
+struct MixBlock {
+    int b3 = 0;
+    int d3 = 1, mul3 = 0;
+    int64_t K = 0;                 // sum over its paths of mul1 * mul2
+    int64_t t_off_per_item = 0;    // offset of its T region / n_items
+    std::vector<int> paths;        // in path order
+    std::vector<int64_t> koff;     // row offset of each path inside K
+};
+
 struct Plan {
     Tuning tune;
     std::vector<Irrep> in1, in2, out;
@@ -83,6 +94,9 @@ struct Plan {
     std::vector<Path> paths;
 
     KernelShape fwd, bwd, dbl;
+    std::vector<MixBlock> mix;     // uvw only
+    std::vector<int> mix_of_path;  // uvw: index into mix for each path
+    int64_t t_per_item = 0;        // uvw: T elements per item
     std::string source;
     std::string cache_key;
     bool cached = false;
@@ -117,6 +131,10 @@ int launch_segment_sum_rows(cgtp_dtype dt, const void *rows, const int32_t *row_
                             int accumulate, hipStream_t s);
 int launch_sum_parts(cgtp_dtype dt, const void *parts, int n_parts, int64_t n, void *out,
                      int accumulate, hipStream_t s);
+int launch_zero(cgtp_dtype dt, void *p, int64_t n, hipStream_t s);
+// out[item][off3 + w*d3 + k] (=|+=) sum_K T[(item*d3 + k)*K + kk] W_b3[kk][w]
+int launch_uvw_mix(const Plan &p, const MixBlock &mb, const void *T, const void *w, int64_t n_items,
+                   void *out, int accumulate, hipStream_t s);
 
 }  // namespace cgtp
 

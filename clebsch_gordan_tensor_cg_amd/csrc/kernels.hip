@@ -464,7 +464,87 @@ struct CotLaunch {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// ---------------------------------------------------------------------------
+// uvw channel mixing on the matrix cores:
+//   out[item][off3 + w*d3 + k] (=|+=) sum_kk T[(item*d3 + k)*K + kk] * Wb[kk][w]
+// T and W are bf16 (raw 16-bit), accumulation in FP32.  Row kk of Wb is row
+// (kk - kstart[p]) of path p's weight block [mul1*mul2][mul3] at woff[p].
+// One wavefront computes 16 rows x all mul3 columns with
+// v_mfma_f32_16x16x16_bf16: lane l supplies A[l%16][4(l/16)+0..3] and
+// B[4(l/16)+0..3][l%16], and receives D[4(l/16)+i][l%16], i = 0..3.
+// ---------------------------------------------------------------------------
+constexpr int kMixMaxPaths = 64;
+struct MixTable {
+    int np;
+    int64_t kstart[kMixMaxPaths + 1];
+    int64_t woff[kMixMaxPaths];
+};
+
+typedef short cgtp_s4 __attribute__((ext_vector_type(4)));
+typedef float cgtp_f4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(64) k_uvw_mix(const uint16_t *__restrict__ T, int64_t M, int64_t K,
+                                                const uint16_t *__restrict__ W, int mul3, MixTable tab,
+                                                float *__restrict__ out, int64_t dim3, int64_t off3, int d3,
+                                                int accumulate) {
+    const int lane = threadIdx.x;
+    const int64_t row0 = (int64_t)blockIdx.x * 16;
+    const int r_a = lane % 16;      // A row / B column within the tile
+    const int kq = 4 * (lane / 16);  // first of the four K entries this lane supplies
+    const int64_t arow = row0 + r_a < M ? row0 + r_a : M - 1;
+    for (int c0 = 0; c0 < mul3; c0 += 16) {
+        const int col = c0 + r_a;
+        const int colc = col < mul3 ? col : mul3 - 1;
+        cgtp_f4 acc = {0.f, 0.f, 0.f, 0.f};
+        int p = 0;
+        for (int64_t k0 = 0; k0 < K; k0 += 16) {
+            cgtp_s4 a, b;
+            for (int i = 0; i < 4; ++i) {
+                const int64_t kk = k0 + kq + i;
+                short av = 0, bv = 0;
+                if (kk < K) {
+                    av = (short)T[arow * K + kk];
+                    while (p + 1 < tab.np && kk >= tab.kstart[p + 1]) ++p;
+                    while (p > 0 && kk < tab.kstart[p]) --p;
+                    bv = (short)W[tab.woff[p] + (kk - tab.kstart[p]) * mul3 + colc];
+                }
+                a[i] = av;
+                b[i] = bv;
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+        }
+        if (col < mul3) {
+            for (int i = 0; i < 4; ++i) {
+                const int64_t r = row0 + kq + i;
+                if (r >= M) continue;
+                const int64_t item = r / d3, k = r % d3;
+                float *o = out + item * dim3 + off3 + (int64_t)col * d3 + k;
+                *o = accumulate ? *o + acc[i] : acc[i];
+            }
+        }
+    }
+}
+
 }  // namespace
+
+int launch_uvw_mix(const Plan &p, const MixBlock &mb, const void *T, const void *w, int64_t n_items, void *out,
+                   int accumulate, hipStream_t s) {
+    if (n_items <= 0) return CGTP_OK;
+    if ((int)mb.paths.size() > kMixMaxPaths)
+        return set_error(CGTP_ERR_UNSUPPORTED, "more than 64 paths into one output block");
+    MixTable tab{};
+    tab.np = (int)mb.paths.size();
+    for (int i = 0; i < tab.np; ++i) {
+        tab.kstart[i] = mb.koff[i];
+        tab.woff[i] = p.paths[mb.paths[i]].woff;
+    }
+    tab.kstart[tab.np] = mb.K;
+    const int64_t M = n_items * mb.d3;
+    const uint16_t *Tb = (const uint16_t *)T + n_items * mb.t_off_per_item;
+    hipLaunchKernelGGL(k_uvw_mix, dim3((unsigned)((M + 15) / 16)), dim3(64), 0, s, Tb, M, mb.K, (const uint16_t *)w,
+                       mb.mul3, tab, (float *)out, p.dim3, p.off3[mb.b3], mb.d3, accumulate);
+    return hip_check(hipGetLastError(), "uvw mix launch");
+}
 
 // ---------------------------------------------------------------------------
 // internal launchers used by the generated-kernel paths

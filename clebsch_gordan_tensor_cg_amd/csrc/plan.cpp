@@ -291,8 +291,74 @@ Tuning tuning_from_env() {
     return t;
 }
 
+// uvw: every path writes its own slice of T, so groups are the input-1
+// blocks, split further into units of at most `budget` accumulators per
+// channel.
+void split_uvw(Plan &p, KernelShape &ks) {
+    ks.groups.clear();
+    int max_mul = 0;
+    for (auto &P : p.paths) max_mul = std::max(max_mul, P.mul1);
+    ks.lanes_per_item = max_mul >= 64 ? 64 : next_pow2(std::max(1, max_mul));
+    ks.items_per_wave = 64 / ks.lanes_per_item;
+    const int budget = 40;
+    for (int b = 0; b < (int)p.in1.size(); ++b) {
+        Group cur;
+        int acc = 0;
+        for (int a = 0; a < (int)p.paths.size(); ++a) {
+            const Path &P = p.paths[a];
+            if (P.i1 != b) continue;
+            const int need = P.mul2 * (2 * P.l3 + 1);
+            if (!cur.paths.empty() && acc + need > budget) {
+                ks.groups.push_back(cur);
+                cur = Group();
+                acc = 0;
+            }
+            cur.paths.push_back(a);
+            if (cur.in1_blocks.empty()) cur.in1_blocks.push_back(b);
+            cur.max_mul = std::max(cur.max_mul, P.mul1);
+            acc += need;
+        }
+        if (!cur.paths.empty()) ks.groups.push_back(cur);
+    }
+    ks.n_units = 0;
+    for (auto &g : ks.groups) {
+        g.cpl = 1;
+        g.slices = (g.max_mul + ks.lanes_per_item - 1) / ks.lanes_per_item;
+        ks.n_units += g.slices;
+    }
+}
+
+void mix_tables(Plan &p) {
+    p.mix.clear();
+    p.mix_of_path.assign(p.paths.size(), -1);
+    int64_t off = 0;
+    for (int b3 = 0; b3 < (int)p.out.size(); ++b3) {
+        MixBlock mb;
+        mb.b3 = b3;
+        mb.d3 = p.out[b3].dim();
+        mb.mul3 = p.out[b3].mul;
+        for (int a = 0; a < (int)p.paths.size(); ++a)
+            if (p.paths[a].i3 == b3) {
+                mb.koff.push_back(mb.K);
+                mb.K += (int64_t)p.paths[a].mul1 * p.paths[a].mul2;
+                mb.paths.push_back(a);
+                p.mix_of_path[a] = (int)p.mix.size();
+            }
+        if (mb.paths.empty()) continue;
+        mb.t_off_per_item = off;
+        off += mb.d3 * mb.K;
+        p.mix.push_back(mb);
+    }
+    p.t_per_item = off;
+}
+
 void choose_shapes(Plan &p) {
     if (p.tune.cy_path < 0) p.tune.cy_path = (p.dtype == CGTP_F64) ? 1 : 0;
+    if (p.mode == CGTP_UVW) {
+        mix_tables(p);
+        split_uvw(p, p.fwd);
+        return;
+    }
     split(p, p.fwd, 0);
     split(p, p.bwd, 1);
     split(p, p.dbl, 2);

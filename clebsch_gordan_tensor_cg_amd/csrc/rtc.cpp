@@ -162,7 +162,7 @@ int compile_and_load(Plan &p, bool load, std::string &err) {
         r.destroy(&prog);
         write_file_atomic(dir, path, code);
     }
-    p.n_kernels = 1 + ((p.mode == CGTP_UVU && p.dtype != CGTP_BF16_F32ACC) ? 2 : 0);
+    p.n_kernels = (p.mode == CGTP_UVU) ? 3 : 1;
     if (!load) return CGTP_OK;
 
     hipError_t e = hipGetDevice(&p.device);

@@ -139,13 +139,25 @@ int cgtp_plan_source(cgtp_plan_t plan, char *buf, int64_t cap, int64_t *len);
 void cgtp_plan_destroy(cgtp_plan_t plan);
 
 /* ---------------------------------------------------------------------- */
+/* Scratch for the forward calls: uvw plans contract in two steps (per-item */
+/* path tensors T_p = CG_p(x, y) summed over the item's edges, rounded to   */
+/* the MFMA operand type, then T . W per output block on the matrix cores,  */
+/* [SE3] "fully fused" TFN convolution: all paths into one output degree    */
+/* concatenated along K).  T lives in the workspace: this many bytes for   */
+/* n_items items (destination nodes or samples); 0 for uvu plans.          */
+/* ---------------------------------------------------------------------- */
+int cgtp_forward_workspace_bytes(cgtp_plan_t plan, int64_t n_items, size_t *bytes);
+
+/* ---------------------------------------------------------------------- */
 /* Tensor product on independent items ([KG]: the CG tensor product).      */
 /*   out[b] = sum_paths W . CG(x[b], y[b])                                 */
 /* x [batch][dim_in1], y [batch][dim_in2], w [batch][weight_numel] (or     */
 /* [weight_numel] shared), out [batch][dim_out]; element type per dtype.    */
+/* workspace: cgtp_forward_workspace_bytes(batch) bytes, 256-byte aligned   */
+/* (may be NULL for uvu plans).                                             */
 /* ---------------------------------------------------------------------- */
 int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, int64_t batch,
-                 void *out, cgtp_stream_t stream);
+                 void *out, void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
 
 /* ---------------------------------------------------------------------- */
 /* Fused graph convolution ([KG]: TP fused with the graph convolution).    */
@@ -155,14 +167,17 @@ int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, 
  * Each destination row is reduced by one workgroup and written once; no   */
 /* atomics.  src values must lie in [0, n_nodes) and row_ptr must be a      */
 /* monotone CSR with row_ptr[0] = 0, row_ptr[n_nodes] = n_edges; check     */
-/* untrusted input with cgtp_validate_csr first.                            */
+/* untrusted input with cgtp_validate_csr first.  workspace:               */
+/* cgtp_forward_workspace_bytes(n_nodes) (may be NULL for uvu plans).       */
 /* ---------------------------------------------------------------------- */
 int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
                       const int32_t *src, const int32_t *dst_row_ptr, int64_t n_nodes,
-                      int64_t n_edges, void *out, cgtp_stream_t stream);
+                      int64_t n_edges, void *out, void *workspace, size_t workspace_bytes,
+                      cgtp_stream_t stream);
 
 /* Workspace needed by cgtp_conv_backward / cgtp_conv_double_backward for a
- * graph with n_edges edges (bytes; 256-byte aligned pointer required). */
+ * graph with n_edges edges (bytes; 256-byte aligned pointer required).
+ * The backward calls are provided for uvu plans (FP32 and FP64). */
 int cgtp_conv_workspace_bytes(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges,
                               size_t *bytes);
 
