@@ -1,17 +1,19 @@
 """Benchmark of the fused CG tensor-product convolution hot path on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c2|c3|c1|c5]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload c4|c2|c3|c1|c5] [--no-cpu-baseline] [--probe-copy]
 
-Default workload (one step = the whole hot path on the 4096-atom periodic
-water-density box, cutoff 5 A, node 128x0e+128x1o, SH l<=3, uvu, fp32):
-  CSR of the edges by destination (carrying the source index) and the
-  transpose CSR by source, spherical harmonics of the edge vectors, fused
-  convolution forward, backward (g_x, g_sh, g_w for E = sum of the 0e output
-  blocks), forces from g_sh, the force-loss cotangent on the SH, and the
-  double backward (d/dx, d/dw, d/dg_out) driven by that cotangent.
-Inputs (edge vectors, node features, per-edge weights in CSR order) are
-resident in HBM before timing starts.  Prints one JSON line.
+Default workload "c4" (one step = the whole hot path on the 4096-atom
+periodic water-density box, cutoff 5 A, node 128x0e+128x1o, SH l<=3, uvu,
+fp32): CSR of the edges by destination (carrying the source index) and the
+transpose CSR by source, spherical harmonics of the edge vectors, fused
+convolution forward, backward (g_x, g_sh, g_w for E = sum of the 0e output
+blocks), forces from g_sh, the force-loss cotangent on the SH, and the double
+backward (d/dx, d/dw, d/dg_out) driven by that cotangent.  Other workloads
+time the forward path alone: c2 (same graph), c3 (16384 atoms, fp64, node
+128x0e+128x1o+128x2e), c1 (1000 independent products), c5 (100 molecules of
+18 atoms, uvw bf16 with matrix-core mixing).  Inputs are resident in HBM
+before timing starts.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "edges/sec fused CG-TP conv (fwd, fwd+bwd) + achieved HBM GB/s vs peak, 1 GPU"
 HBM_PEAK_GBS = 8000.0
-FP64_PEAK_TFLOPS = 78.6
+FP32_VECTOR_PEAK_TFLOPS = 78.6   # non-packed FMA rate: 256 CU x 2.4 GHz x 64 lanes x 2
 
 
 def parse():
@@ -36,14 +38,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c1"])
+    ap.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c1", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe-copy", action="store_true",
+                    help="run a 512 MiB device copy first (reference for counter scaling)")
     ap.add_argument("--seed", type=int, default=0)
     return ap.parse_args()
 
 
 class Timer:
-    """Per-kernel durations from HIP events recorded on the launch stream."""
+    """Per-kernel durations from HIP events recorded on the launch stream
+    (torch's current stream, which every cgtp call launches on)."""
 
     def __init__(self, torch):
         self.t = torch
@@ -62,90 +67,156 @@ class Timer:
         return {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in self.pairs.items()}
 
 
-def conv_workload(args, torch, B, W, cfg_name):
-    cfg = W.config("c2" if cfg_name in ("c4", "c2") else cfg_name)
-    dtype = cfg.dtype
-    rng = np.random.default_rng(args.seed)
-    g = W.periodic_graph(cfg.extra["n_atoms"], cutoff=cfg.extra["cutoff"], rng=rng)
-    plan = B.Plan(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.paths, cfg.mode, dtype)
-    x_np = W.normal(rng, (g.n_nodes, plan.dim_in1), dtype)
-    w_np = W.normal(rng, (g.n_edges, plan.weight_numel), dtype)
-    return cfg, g, plan, x_np, w_np
+# ---------------------------------------------------------------------------
+# algorithmic bytes: each array counted once at its storage size; gathers of
+# source-node rows that hit in cache are not counted
+# ---------------------------------------------------------------------------
+def alg_bytes_conv_fwd(N, E, d1, d2, d3, wn, eb, ob):
+    return N * d1 * eb + N * d3 * ob + E * d2 * eb + E * wn * eb + E * 4 + (N + 1) * 4
 
 
-def alg_bytes_fwd(N, E, plan, eb):
-    # each node array once, each per-edge array once (x gathers from cache
-    # not counted): x, out rows; sh, w rows; src; row_ptr
-    return (N * (plan.dim_in1 + plan.dim_out) * eb + E * (plan.dim_in2 + plan.weight_numel) * eb
-            + E * 4 + (N + 1) * 4)
-
-
-def alg_bytes_bwd(N, E, plan, eb):
+def alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb):
     # reads x, g_out, sh, w, src, row_ptr; writes g_x, g_sh, g_w
-    return (N * (2 * plan.dim_in1 + plan.dim_out) * eb + E * 2 * (plan.dim_in2 + plan.weight_numel) * eb
-            + E * 4 + (N + 1) * 4)
+    return N * (2 * d1 + d3) * eb + E * 2 * (d2 + wn) * eb + E * 4 + (N + 1) * 4
 
 
-def cpu_baseline_conv(cfg, g, x_np, w_np, full_step: bool):
-    """The oracle as it stands on a bounded sample: the edges into the first
-    quarter of the nodes (all nodes kept as sources)."""
-    import oracle
-    prob = oracle.Problem(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.mode, cfg.paths)
-    n_s = g.n_nodes // 4 if full_step else g.n_nodes // 2
-    mask = g.dst < n_s
-    src, dst, vec, w = g.src[mask], g.dst[mask], g.vec[mask], w_np[mask]
-    E_s = int(mask.sum())
-    dt = np.float64 if cfg.dtype == "f64" else np.float32
-    vec = vec.astype(dt)
-    t0 = time.perf_counter()
-    sh = oracle.spherical_harmonics(3, vec)
-    perm, rp = oracle.csr(dst, g.n_nodes)
-    perm2, rp2 = oracle.csr(src[perm], g.n_nodes)
-    out = prob.conv_forward(x_np, sh, w, src, dst, g.n_nodes)
-    if full_step:
-        G = np.zeros_like(out)
-        G[:, zero_e_columns(cfg.irreps_out)] = 1.0
-        gx, gsh, gw = prob.conv_backward(x_np, sh, w, src, dst, G)
-        F = oracle.forces(3, g.n_nodes, src, dst, vec, gsh)
-        gg = oracle.force_loss_cotangent(3, g.n_nodes, src, dst, vec, F)
-        prob.conv_double_backward(x_np, sh, w, src, dst, G, None, gg, None)
-    dt_s = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    what = "fwd+bwd+forces+double-bwd" if full_step else "fwd"
-    return {"value": E_s / dt_s, "unit": "edges/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what} over the {E_s} edges into the first {n_s} of {g.n_nodes} nodes "
-                      f"(all nodes as sources), {dt_s:.1f} s, OpenMP threads={threads}"}
+def alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb):
+    # reads x, g_out, gg_sh, w, src, row_ptr; writes d_g_out, d_x, d_w
+    return N * (2 * d1 + 2 * d3) * eb + E * (d2 + 2 * wn) * eb + E * 4 + (N + 1) * 4
+
+
+def parse_irreps(s):
+    out = []
+    for term in s.split("+"):
+        mul, rest = term.strip().split("x")
+        out.append((int(mul), int(rest[:-1] if rest[-1] in "eo" else rest), rest))
+    return out
 
 
 def zero_e_columns(irreps: str):
     """Columns of the 0e blocks of an irreps row (the energy read-out)."""
     cols, off = [], 0
-    for term in irreps.split("+"):
-        mul, rest = term.strip().split("x")
-        mul, l = int(mul), int(rest[:-1] if rest[-1] in "eo" else rest)
-        if rest == "0e":
+    for mul, l, name in parse_irreps(irreps):
+        if name == "0e":
             cols.extend(range(off, off + mul))
         off += mul * (2 * l + 1)
     return np.array(cols, dtype=np.int64)
 
 
+def tp_flops(cfg, plan):
+    """2 flops per CG nonzero per (u, v) channel pair, from the plan's own
+    coupling tensors."""
+    a, b, c = parse_irreps(cfg.irreps_in1), parse_irreps(cfg.irreps_in2), parse_irreps(cfg.irreps_out)
+    tot = 0
+    for p, (i1, i2, i3) in enumerate(plan.paths()):
+        R = plan.coupling(p, (2 * a[i1][1] + 1, 2 * b[i2][1] + 1, 2 * c[i3][1] + 1))
+        tot += 2 * int((np.abs(R) > 1e-14).sum()) * a[i1][0] * b[i2][0]
+    return tot
+
+
+def copy_probe(torch):
+    n = 512 * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e)
+    return {"bytes_read": 4 * n, "bytes_written": 4 * n, "ms": ms, "GB_per_s": 8 * n / (ms * 1e-3) / 1e9}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands on a bounded sample
+# ---------------------------------------------------------------------------
+def cpu_baseline_conv(cfg, g, x_np, w_np, full_step: bool, frac: float):
+    import oracle
+    from clebsch_gordan_tensor_cg_amd import workloads as W
+    prob = oracle.Problem(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.mode, cfg.paths,
+                          cfg.shared_weights)
+    n_s = max(1, int(g.n_nodes * frac))
+    mask = g.dst < n_s
+    src, dst, vec = g.src[mask], g.dst[mask], g.vec[mask]
+    w = w_np if cfg.shared_weights else w_np[mask]
+    E_s = int(mask.sum())
+    vec = vec.astype(np.float64 if cfg.dtype == "f64" else np.float32)
+    lmax = cfg.extra["lmax"]
+    t0 = time.perf_counter()
+    sh = oracle.spherical_harmonics(lmax, vec)
+    if cfg.dtype == "bf16":
+        sh = W.round_to(sh, "bf16")
+    perm, rp = oracle.csr(dst, g.n_nodes)
+    oracle.csr(src[perm], g.n_nodes)
+    out = prob.conv_forward(x_np, sh, w, src, dst, g.n_nodes)
+    if full_step:
+        G = np.zeros_like(out)
+        G[:, zero_e_columns(cfg.irreps_out)] = 1.0
+        gx, gsh, gw = prob.conv_backward(x_np, sh, w, src, dst, G)
+        F = oracle.forces(lmax, g.n_nodes, src, dst, vec, gsh)
+        gg = oracle.force_loss_cotangent(lmax, g.n_nodes, src, dst, vec, F)
+        prob.conv_double_backward(x_np, sh, w, src, dst, G, None, gg, None)
+    dt_s = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    what = "csr+sh+fwd+bwd+forces+force_cotangent+double_bwd" if full_step else "csr+sh+fwd"
+    return {"value": E_s / dt_s, "unit": "edges/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what} over the {E_s} edges into the first {n_s} of {g.n_nodes} nodes "
+                      f"(all nodes as sources), {dt_s:.1f} s, OpenMP threads={threads}"}
+
+
+def cpu_baseline_single(cfg, x, y, w):
+    import oracle
+    prob = oracle.Problem(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.mode, cfg.paths,
+                          cfg.shared_weights)
+    n = x.shape[0]
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < 5.0:
+        prob.tp_forward(x, y, w)
+        reps += 1
+    dt_s = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": reps * n / dt_s, "unit": "samples/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} repetitions of the {n}-sample forward, {dt_s:.1f} s, OpenMP threads={threads}"}
+
+
+# ---------------------------------------------------------------------------
+# convolution workloads
+# ---------------------------------------------------------------------------
 def bench_conv(args, torch, B, W):
-    cfg, g, plan, x_np, w_np = conv_workload(args, torch, B, W, args.workload)
+    name = args.workload
+    cfg = W.config("c2" if name in ("c4", "c2") else name)
+    full = name == "c4"
     dtype = cfg.dtype
-    full = args.workload == "c4"
+    rng = np.random.default_rng(args.seed)
+    if name == "c5":
+        g = W.molecule_batch(cfg.extra["n_graphs"], cfg.extra["n_atoms"], cutoff=cfg.extra["cutoff"], rng=rng)
+    else:
+        g = W.periodic_graph(cfg.extra["n_atoms"], cutoff=cfg.extra["cutoff"], rng=rng)
+    plan = B.Plan(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.paths, cfg.mode, dtype,
+                  cfg.shared_weights)
+    lmax = cfg.extra["lmax"]
+    x_np = W.normal(rng, (g.n_nodes, plan.dim_in1), dtype)
+    w_np = W.normal(rng, (plan.weight_numel,) if cfg.shared_weights else (g.n_edges, plan.weight_numel), dtype)
     N, E = g.n_nodes, g.n_edges
     dev = "cuda"
     td = B.TORCH_DTYPES[dtype]
-    eb = 8 if dtype == "f64" else 4
+    od = plan.out_dtype
+    eb = {"f64": 8, "f32": 4, "bf16": 2}[dtype]
+    ob = 8 if dtype == "f64" else 4
     # inputs resident in HBM: canonical edge list and vectors, node features,
-    # per-edge weights in CSR (destination-sorted) order
+    # per-edge weights already in CSR (destination-sorted) order
     src_c = torch.from_numpy(g.src).to(dev)
     dst_c = torch.from_numpy(g.dst).to(dev)
     vec = torch.from_numpy(g.vec.astype(np.float64 if dtype == "f64" else np.float32)).to(dev)
-    x = torch.from_numpy(x_np).to(dev)
-    perm_np = np.argsort(g.dst, kind="stable")
-    w = torch.from_numpy(w_np[perm_np]).to(dev)
-    # outputs and workspaces preallocated
+    x = torch.from_numpy(x_np).to(dev).to(td)
+    if cfg.shared_weights:
+        w = torch.from_numpy(w_np).to(dev).to(td)
+    else:
+        w = torch.from_numpy(w_np[np.argsort(g.dst, kind="stable")]).to(dev).to(td)
     perm = torch.empty(E, dtype=torch.int32, device=dev)
     rp = torch.empty(N + 1, dtype=torch.int32, device=dev)
     dst_s = torch.empty(E, dtype=torch.int32, device=dev)
@@ -154,13 +225,15 @@ def bench_conv(args, torch, B, W):
     src_rp = torch.empty(N + 1, dtype=torch.int32, device=dev)
     csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), dev)
     sh = torch.empty(E, plan.dim_in2, dtype=td, device=dev)
-    out = torch.empty(N, plan.dim_out, dtype=td, device=dev)
+    out = torch.empty(N, plan.dim_out, dtype=od, device=dev)
+    nb_f = B.cgtp_forward_workspace_bytes(plan, N)
+    f_ws = B.workspace(nb_f, dev) if nb_f else None
     timer = Timer(torch)
     if full:
         g_out = torch.zeros(N, plan.dim_out, dtype=td, device=dev)
         g_out[:, torch.from_numpy(zero_e_columns(cfg.irreps_out)).to(dev)] = 1.0
         ws = B.workspace(B.cgtp_conv_workspace_bytes(plan, N, E), dev)
-        f_ws = B.workspace(B.cgtp_forces_workspace_bytes(E, dtype), dev)
+        fo_ws = B.workspace(B.cgtp_forces_workspace_bytes(E, dtype), dev)
         g_x = torch.empty(N, plan.dim_in1, dtype=td, device=dev)
         g_sh = torch.empty(E, plan.dim_in2, dtype=td, device=dev)
         g_w = torch.empty(E, plan.weight_numel, dtype=td, device=dev)
@@ -171,18 +244,19 @@ def bench_conv(args, torch, B, W):
         d_w = torch.empty(E, plan.weight_numel, dtype=td, device=dev)
 
     def step(timed: bool):
-        run = timer.run if timed else (lambda name, fn: fn())
+        run = timer.run if timed else (lambda name_, fn: fn())
         run("csr", lambda: (B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s)),
                             B.cgtp_build_csr(src_s, N, sorted_key=False, ws=csr_ws,
                                              out=(src_perm, src_rp, None, None))))
-        run("sh", lambda: B.cgtp_spherical_harmonics(3, vec, perm, dtype, out=sh))
-        run("conv_fwd", lambda: B.cgtp_conv_forward(plan, x, sh, w, src_s, rp, out=out))
+        run("sh", lambda: B.cgtp_spherical_harmonics(lmax, vec, perm, dtype, out=sh))
+        run("conv_fwd", lambda: B.cgtp_conv_forward(plan, x, sh, w, src_s, rp, out=out, ws=f_ws))
         if not full:
             return
         run("conv_bwd", lambda: B.cgtp_conv_backward(plan, x, sh, w, src_s, dst_s, rp, src_rp, src_perm, g_out,
                                                      ws=ws, out=(g_x, g_sh, g_w)))
-        run("forces", lambda: B.cgtp_sh_forces(3, vec, perm, g_sh, rp, src_rp, src_perm, dtype, ws=f_ws, out=F))
-        run("force_cot", lambda: B.cgtp_force_loss_sh_cotangent(3, vec, perm, src_s, dst_s, F, dtype, out=gg))
+        run("forces", lambda: B.cgtp_sh_forces(lmax, vec, perm, g_sh, rp, src_rp, src_perm, dtype, ws=fo_ws,
+                                               out=F))
+        run("force_cot", lambda: B.cgtp_force_loss_sh_cotangent(lmax, vec, perm, src_s, dst_s, F, dtype, out=gg))
         run("double_bwd", lambda: B.cgtp_conv_double_backward(plan, x, sh, w, src_s, dst_s, rp, src_rp, src_perm,
                                                               g_out, None, gg, None, ws=ws,
                                                               out=(d_g, d_x, None, d_w)))
@@ -197,20 +271,36 @@ def bench_conv(args, torch, B, W):
         step(True)
     t1.record()
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms = total_ms / args.steps
+    ms = t0.elapsed_time(t1) / args.steps
     kms = timer.ms()
-    # dominant kernel and its roofline (algorithmic bytes / measured time)
-    ab = {"conv_fwd": alg_bytes_fwd(N, E, plan, eb)}
+
+    d1, d2, d3, wn = plan.dim_in1, plan.dim_in2, plan.dim_out, plan.weight_numel
+    kern = {}
+
+    def hbm(name_, kernel, nbytes):
+        gbs = nbytes / (kms[name_] * 1e-3) / 1e9
+        kern[name_] = {"kernel": kernel, "avg_ms": round(kms[name_], 4), "alg_bytes": int(nbytes),
+                       "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    if name == "c5":
+        hbm("conv_fwd", "cgtp_fwd (path tensors) + k_uvw_mix",
+            N * d1 * eb + N * d3 * ob + E * d2 * eb + E * 4 + (N + 1) * 4 + wn * eb)
+    else:
+        hbm("conv_fwd", "cgtp_fwd", alg_bytes_conv_fwd(N, E, d1, d2, d3, wn, eb, ob))
     if full:
-        ab["conv_bwd"] = alg_bytes_bwd(N, E, plan, eb)
-    dom = max(ab, key=lambda k: kms[k])
-    achieved = ab[dom] / (kms[dom] * 1e-3) / 1e9
-    roof = {"bound": "hbm", "kernel": {"conv_fwd": "cgtp_fwd", "conv_bwd": "cgtp_bwd (+ segment sum)"}[dom],
-            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "alg_bytes_per_launch": int(ab[dom]), "avg_ms": round(kms[dom], 4)}
-    fwd_gbs = ab["conv_fwd"] / (kms["conv_fwd"] * 1e-3) / 1e9
+        hbm("conv_bwd", "cgtp_bwd + k_segment_sum_rows", alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb))
+        hbm("double_bwd", "cgtp_dbl + k_segment_sum_rows", alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb))
+    dom = max(kern, key=lambda k: kern[k]["avg_ms"])
+    roof = {"bound": "hbm", "kernel": kern[dom]["kernel"], "achieved": kern[dom]["GB_per_s"],
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"], "traffic": None,
+            "alg_bytes_per_launch": kern[dom]["alg_bytes"], "avg_ms": kern[dom]["avg_ms"]}
+    if name == "c5":
+        # the path tensors on the vector ALUs dominate: FP32 vector peak
+        flop = tp_flops(cfg, plan) * E
+        tf = flop / (kms["conv_fwd"] * 1e-3) / 1e12
+        roof = {"bound": "alu", "kernel": kern["conv_fwd"]["kernel"], "achieved": round(tf, 3),
+                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+                "traffic": None, "alg_flop_per_launch": int(flop), "avg_ms": kern["conv_fwd"]["avg_ms"]}
     res = {
         "metric": METRIC,
         "value": E / (ms * 1e-3),
@@ -224,16 +314,54 @@ def bench_conv(args, torch, B, W):
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name if not full else W.config("c4").name, "n_atoms": N, "n_edges": E,
-                   "irreps_node": cfg.irreps_in1, "irreps_sh": cfg.irreps_in2, "n_paths": plan.n_paths,
+        "config": {"workload": W.config("c4").name if full else cfg.name, "n_atoms": N, "n_edges": E,
+                   "irreps_node": cfg.irreps_in1, "irreps_sh": cfg.irreps_in2, "irreps_out": cfg.irreps_out,
+                   "n_paths": plan.n_paths,
                    "step": ("csr+sh+fwd+bwd+forces+force_cotangent+double_bwd" if full else "csr+sh+fwd")},
         "roofline": roof,
-        "fwd": {"edges_per_s": E / (kms["conv_fwd"] * 1e-3), "ms": kms["conv_fwd"],
-                "GB_per_s": round(fwd_gbs, 1), "frac_hbm_peak": round(fwd_gbs / HBM_PEAK_GBS, 4)},
+        "fwd_edges_per_s": E / (kms["conv_fwd"] * 1e-3),
+        "kernels": kern,
         "kernel_ms": {k: round(v, 4) for k, v in kms.items()},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_conv(cfg, g, x_np, w_np, full)
+        frac = {"c4": 0.25, "c2": 0.5, "c3": 0.02, "c5": 0.03}[name]
+        res["cpu_baseline"] = cpu_baseline_conv(cfg, g, x_np, w_np, full, frac)
+    return res
+
+
+def bench_single(args, torch, B, W):
+    cfg = W.config("c1")
+    rng = np.random.default_rng(args.seed)
+    n = cfg.extra["batch"]
+    plan = B.Plan(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.paths, cfg.mode, cfg.dtype)
+    x_np = W.normal(rng, (n, plan.dim_in1), "f32")
+    y_np = W.normal(rng, (n, plan.dim_in2), "f32")
+    w_np = W.normal(rng, (n, plan.weight_numel), "f32")
+    x, y, w = (torch.from_numpy(a).cuda() for a in (x_np, y_np, w_np))
+    out = torch.empty(n, plan.dim_out, device="cuda")
+    for _ in range(args.warmup):
+        B.cgtp_forward(plan, x, y, w, out=out)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        B.cgtp_forward(plan, x, y, w, out=out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    nbytes = n * (plan.dim_in1 + plan.dim_in2 + plan.weight_numel + plan.dim_out) * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"metric": METRIC, "value": n / (ms * 1e-3), "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": cfg.name, "batch": n, "n_paths": plan.n_paths},
+           "roofline": {"bound": "hbm", "kernel": "cgtp_fwd", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                        "alg_bytes_per_launch": nbytes, "avg_ms": ms,
+                        "note": "676 KB per launch: launch latency, not bandwidth, bounds this size"}}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_single(cfg, x_np, y_np, w_np)
     return res
 
 
@@ -250,7 +378,10 @@ def main():
         from clebsch_gordan_tensor_cg_amd import build as b
         b.build(verbose=False)
     torch.cuda.set_device(0)
-    res = bench_conv(args, torch, B, W)
+    probe = copy_probe(torch) if args.probe_copy else None
+    res = bench_single(args, torch, B, W) if args.workload == "c1" else bench_conv(args, torch, B, W)
+    if probe:
+        res["copy_probe"] = probe
     print(json.dumps(res))
 
 
