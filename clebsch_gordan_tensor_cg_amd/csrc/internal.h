@@ -57,7 +57,7 @@ struct KernelShape {
 };
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
-// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, yvec, ntw, pf, budget, stage, cypath, depth) overrides
+// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, yvec, ntw, pf, budget, stage, cypath, depth, bgy) overrides
 // them for experiments.
 struct Tuning {
     int cpl[3] = {0, 0, 0};  // channels per lane per kernel kind (0 = by budget)
@@ -68,6 +68,7 @@ struct Tuning {
     int stage = 64;          // edges per LDS chunk of src and y rows (0 = off)
     int cy_path = -1;        // uniform products per path (1) or per edge (0); -1: by dtype
     int depth = 3;           // edges of prefetch in flight (staged loop)
+    bool bgy = false;        // backward via B_ij = sum_k R_ijk g_k (fewer FMAs, more VGPRs)
 };
 Tuning tuning_from_env();
 

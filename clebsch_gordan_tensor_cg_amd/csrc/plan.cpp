@@ -285,6 +285,7 @@ Tuning tuning_from_env() {
             else if (k == "stage") t.stage = v < 0 ? 0 : (v > 256 ? 256 : v);
             else if (k == "cypath") t.cy_path = v;
             else if (k == "depth") t.depth = v < 1 ? 1 : (v > 4 ? 4 : v);
+            else if (k == "bgy") t.bgy = v != 0;
         }
         pos = comma + 1;
     }
