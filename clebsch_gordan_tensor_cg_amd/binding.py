@@ -47,7 +47,8 @@ EXPORTS = [
     "cgtp_conv_workspace_bytes",
     "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_csr_workspace_bytes", "cgtp_build_csr",
     "cgtp_validate_csr", "cgtp_spherical_harmonics", "cgtp_forces_workspace_bytes", "cgtp_sh_forces",
-    "cgtp_force_loss_sh_cotangent", "cgtp_last_error", "cgtp_version",
+    "cgtp_force_loss_sh_cotangent", "cgtp_timing_enable", "cgtp_timing_collect", "cgtp_last_error",
+    "cgtp_version",
 ]
 
 _lib = None
@@ -81,6 +82,8 @@ def lib():
             "cgtp_forces_workspace_bytes": [i64, i32, vp],
             "cgtp_sh_forces": [i32, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
             "cgtp_force_loss_sh_cotangent": [i32, i32, vp, vp, vp, vp, vp, i64, vp, vp],
+            "cgtp_timing_enable": [i32],
+            "cgtp_timing_collect": [vp, vp, i32, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -338,6 +341,21 @@ def cgtp_force_loss_sh_cotangent(lmax: int, vec, perm, src, dst, F, dtype: str =
     _check(lib().cgtp_force_loss_sh_cotangent(lmax, DTYPES[dtype], _ptr(vec), _ptr(perm), _ptr(src), _ptr(dst),
                                               _ptr(F), E, _ptr(out), _stream(stream, F)))
     return out
+
+
+def cgtp_timing_enable(enable: bool = True):
+    _check(lib().cgtp_timing_enable(1 if enable else 0))
+
+
+def cgtp_timing_collect(cap: int = 1 << 16):
+    """[(kernel name, ms)] of the launches recorded since the last collect."""
+    names = ctypes.create_string_buffer(64 * cap)
+    ms = (ctypes.c_float * cap)()
+    n = ctypes.c_int32()
+    _check(lib().cgtp_timing_collect(ctypes.cast(names, ctypes.c_void_p), ctypes.cast(ms, ctypes.c_void_p), cap,
+                                     ctypes.byref(n)))
+    raw = names.raw
+    return [(raw[64 * i:64 * i + 64].split(b"\0", 1)[0].decode(), float(ms[i])) for i in range(n.value)]
 
 
 def version() -> str:

@@ -48,9 +48,10 @@ int check_loaded(cgtp_plan_t plan) {
     return CGTP_OK;
 }
 
-int launch(hipFunction_t f, int64_t blocks, hipStream_t s, void **args) {
+int launch(hipFunction_t f, const char *name, int64_t blocks, hipStream_t s, void **args) {
     if (blocks <= 0) return CGTP_OK;
     if (blocks > 0x7fffffffLL) return set_error(CGTP_ERR_INVALID_ARGUMENT, "grid too large");
+    TimedLaunch tl(name, s);
     hipError_t e = hipModuleLaunchKernel(f, (unsigned)blocks, 1, 1, 64, 1, 1, 0, s, args, nullptr);
     if (e != hipSuccess) return set_error(CGTP_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return CGTP_OK;
@@ -77,7 +78,7 @@ int run_fwd(const Plan &p, const void *x, const void *y, const void *w, const in
     void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr,
                     (void *)&out, &n, &graph, &accumulate};
     const int64_t ipw = p.fwd.items_per_wave;
-    return launch(p.k_fwd, (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
+    return launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
 }
 
 struct BwdOut {
@@ -123,7 +124,7 @@ int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const in
     void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&g_out,
                     &gw, &m, &third, &n, &ne, &graph, &flags};
     const int64_t ipw = ks.items_per_wave;
-    int rc = launch(fused ? p.k_dbl : p.k_bwd, (n_nodes + ipw - 1) / ipw * ks.n_units, s, args);
+    int rc = launch(fused ? p.k_dbl : p.k_bwd, fused ? "cgtp_dbl" : "cgtp_bwd", (n_nodes + ipw - 1) / ipw * ks.n_units, s, args);
     if (rc) return rc;
     if (use_parts) rc = launch_sum_parts(p.dtype, parts, ks.n_units, n_edges * p.dim2, o.g_y, o.acc_y, s);
     return rc;
@@ -322,7 +323,7 @@ static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, c
     long long n = n_items;
     void *args[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, &ws, &n, &graph};
     const int64_t ipw = p.fwd.items_per_wave;
-    int rc = launch(p.k_fwd, (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
+    int rc = launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
     if (rc) return rc;
     int acc = 0;
     if (!blocks_covered(p.out, p.paths, true)) {

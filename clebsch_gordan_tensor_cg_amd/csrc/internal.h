@@ -122,6 +122,24 @@ std::string generate_source(const Plan &p);
 // runtime compilation and cache
 int compile_and_load(Plan &p, bool load, std::string &err);
 
+// opt-in per-launch timing (timing.cpp): records HIP events around a launch
+class TimedLaunch {
+  public:
+    TimedLaunch(const char *name, hipStream_t s);
+    ~TimedLaunch();
+    TimedLaunch(const TimedLaunch &) = delete;
+    TimedLaunch &operator=(const TimedLaunch &) = delete;
+
+  private:
+    hipStream_t s_;
+    long idx_ = -1;
+};
+#define CGTP_LAUNCH(name, stream, ...)               \
+    do {                                             \
+        ::cgtp::TimedLaunch cgtp_tl_(name, stream);  \
+        hipLaunchKernelGGL(__VA_ARGS__);             \
+    } while (0)
+
 // error state
 int set_error(int code, const std::string &msg);
 void clear_error();

@@ -423,11 +423,11 @@ struct ShLaunch {
     static int run(cgtp_dtype dt, const void *vec, const int32_t *perm, int64_t n, void *sh, hipStream_t s) {
         unsigned g = grid_for(n);
         if (dt == CGTP_F32)
-            hipLaunchKernelGGL((k_sh<float, float, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm, n, (float *)sh);
+            CGTP_LAUNCH("k_sh", s, (k_sh<float, float, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm, n, (float *)sh);
         else if (dt == CGTP_F64)
-            hipLaunchKernelGGL((k_sh<double, double, L>), dim3(g), dim3(kBlock), 0, s, (const double *)vec, perm, n, (double *)sh);
+            CGTP_LAUNCH("k_sh", s, (k_sh<double, double, L>), dim3(g), dim3(kBlock), 0, s, (const double *)vec, perm, n, (double *)sh);
         else
-            hipLaunchKernelGGL((k_sh<float, uint16_t, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm, n, (uint16_t *)sh);
+            CGTP_LAUNCH("k_sh", s, (k_sh<float, uint16_t, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm, n, (uint16_t *)sh);
         return hip_check(hipGetLastError(), "spherical harmonics launch");
     }
 };
@@ -438,10 +438,10 @@ struct ForceLaunch {
                    hipStream_t s) {
         unsigned g = grid_for(n);
         if (dt == CGTP_F32)
-            hipLaunchKernelGGL((k_edge_force<float, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm,
+            CGTP_LAUNCH("k_edge_force", s, (k_edge_force<float, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm,
                                (const float *)g_sh, n, (float *)v);
         else
-            hipLaunchKernelGGL((k_edge_force<double, L>), dim3(g), dim3(kBlock), 0, s, (const double *)vec, perm,
+            CGTP_LAUNCH("k_edge_force", s, (k_edge_force<double, L>), dim3(g), dim3(kBlock), 0, s, (const double *)vec, perm,
                                (const double *)g_sh, n, (double *)v);
         return hip_check(hipGetLastError(), "edge force launch");
     }
@@ -453,10 +453,10 @@ struct CotLaunch {
                    const void *F, int64_t n, void *gg, hipStream_t s) {
         unsigned g = grid_for(n);
         if (dt == CGTP_F32)
-            hipLaunchKernelGGL((k_force_cotangent<float, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm,
+            CGTP_LAUNCH("k_force_cotangent", s, (k_force_cotangent<float, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm,
                                src, dst, (const float *)F, n, (float *)gg);
         else
-            hipLaunchKernelGGL((k_force_cotangent<double, L>), dim3(g), dim3(kBlock), 0, s, (const double *)vec,
+            CGTP_LAUNCH("k_force_cotangent", s, (k_force_cotangent<double, L>), dim3(g), dim3(kBlock), 0, s, (const double *)vec,
                                perm, src, dst, (const double *)F, n, (double *)gg);
         return hip_check(hipGetLastError(), "force cotangent launch");
     }
@@ -615,7 +615,7 @@ int launch_uvw_mix(const Plan &p, const MixBlock &mb, const void *T, const void 
     const uint16_t *Tb = (const uint16_t *)T + n_items * mb.t_off_per_item;
     int64_t blocks = (M + 63) / 64;
     if (blocks > 512) blocks = 512;
-    hipLaunchKernelGGL(k_uvw_mix, dim3((unsigned)blocks), dim3(256), 0, s, Tb, M, mb.K, (const uint16_t *)w,
+    CGTP_LAUNCH("k_uvw_mix", s, k_uvw_mix, dim3((unsigned)blocks), dim3(256), 0, s, Tb, M, mb.K, (const uint16_t *)w,
                        mb.mul3, tab, (float *)out, p.dim3, p.off3[mb.b3], mb.d3, accumulate);
     return hip_check(hipGetLastError(), "uvw mix launch");
 }
@@ -631,10 +631,10 @@ int launch_segment_sum_rows(cgtp_dtype dt, const void *rows, const int32_t *row_
     if (gy > 65535) gy = 65535;
     dim3 grid((unsigned)n_seg, (unsigned)gy);
     if (dt == CGTP_F64)
-        hipLaunchKernelGGL(k_segment_sum_rows<double>, grid, dim3(kBlock), 0, s, (const double *)rows, row_ptr, perm,
+        CGTP_LAUNCH("k_segment_sum_rows", s, k_segment_sum_rows<double>, grid, dim3(kBlock), 0, s, (const double *)rows, row_ptr, perm,
                            width, (double *)out, accumulate);
     else
-        hipLaunchKernelGGL(k_segment_sum_rows<float>, grid, dim3(kBlock), 0, s, (const float *)rows, row_ptr, perm,
+        CGTP_LAUNCH("k_segment_sum_rows", s, k_segment_sum_rows<float>, grid, dim3(kBlock), 0, s, (const float *)rows, row_ptr, perm,
                            width, (float *)out, accumulate);
     return hip_check(hipGetLastError(), "segment sum launch");
 }
@@ -645,10 +645,10 @@ int launch_sum_parts(cgtp_dtype dt, const void *parts, int n_parts, int64_t n, v
     unsigned g = grid_for(n);
     if (g > 65536) g = 65536;
     if (dt == CGTP_F64)
-        hipLaunchKernelGGL(k_sum_parts<double>, dim3(g), dim3(kBlock), 0, s, (const double *)parts, n_parts, n,
+        CGTP_LAUNCH("k_sum_parts", s, k_sum_parts<double>, dim3(g), dim3(kBlock), 0, s, (const double *)parts, n_parts, n,
                            (double *)out, accumulate);
     else
-        hipLaunchKernelGGL(k_sum_parts<float>, dim3(g), dim3(kBlock), 0, s, (const float *)parts, n_parts, n,
+        CGTP_LAUNCH("k_sum_parts", s, k_sum_parts<float>, dim3(g), dim3(kBlock), 0, s, (const float *)parts, n_parts, n,
                            (float *)out, accumulate);
     return hip_check(hipGetLastError(), "part sum launch");
 }
@@ -658,9 +658,9 @@ int launch_zero(cgtp_dtype dt, void *p, int64_t n, hipStream_t s) {
     unsigned g = grid_for(n);
     if (g > 65536) g = 65536;
     if (dt == CGTP_F64)
-        hipLaunchKernelGGL(k_fill<double>, dim3(g), dim3(kBlock), 0, s, (double *)p, n, 0.0);
+        CGTP_LAUNCH("k_fill", s, k_fill<double>, dim3(g), dim3(kBlock), 0, s, (double *)p, n, 0.0);
     else
-        hipLaunchKernelGGL(k_fill<float>, dim3(g), dim3(kBlock), 0, s, (float *)p, n, 0.0f);
+        CGTP_LAUNCH("k_fill", s, k_fill<float>, dim3(g), dim3(kBlock), 0, s, (float *)p, n, 0.0f);
     return hip_check(hipGetLastError(), "fill launch");
 }
 
@@ -695,19 +695,19 @@ int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int6
     int32_t *cursor = (int32_t *)(ws + align256(sizeof(int32_t) * (size_t)(n_keys + 1)));
     int32_t *tmp = (int32_t *)(ws + 2 * align256(sizeof(int32_t) * (size_t)(n_keys + 1)));
     unsigned gk = grid_for(n_keys + 1);
-    hipLaunchKernelGGL(k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, cnt, n_keys + 1, 0);
-    hipLaunchKernelGGL(k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, cursor, n_keys + 1, 0);
+    CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, cnt, n_keys + 1, 0);
+    CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, cursor, n_keys + 1, 0);
     if (n_edges > 0) {
         unsigned ge = grid_for(n_edges);
         if (ge > 65536) ge = 65536;
-        hipLaunchKernelGGL(k_count, dim3(ge), dim3(kBlock), 0, s, key, n_edges, cnt);
-        hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, cnt, n_keys, row_ptr);
-        hipLaunchKernelGGL(k_scatter, dim3(ge), dim3(kBlock), 0, s, key, n_edges, row_ptr, cursor, tmp);
+        CGTP_LAUNCH("k_count", s, k_count, dim3(ge), dim3(kBlock), 0, s, key, n_edges, cnt);
+        CGTP_LAUNCH("k_scan", s, k_scan, dim3(1), dim3(1024), 0, s, cnt, n_keys, row_ptr);
+        CGTP_LAUNCH("k_scatter", s, k_scatter, dim3(ge), dim3(kBlock), 0, s, key, n_edges, row_ptr, cursor, tmp);
         if (n_keys > 0)
-            hipLaunchKernelGGL(k_rank_segments, dim3((unsigned)n_keys), dim3(64), 0, s, row_ptr, n_keys, tmp, key,
+            CGTP_LAUNCH("k_rank_segments", s, k_rank_segments, dim3((unsigned)n_keys), dim3(64), 0, s, row_ptr, n_keys, tmp, key,
                                val, perm, sorted_key, sorted_val);
     } else {
-        hipLaunchKernelGGL(k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, row_ptr, n_keys + 1, 0);
+        CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, row_ptr, n_keys + 1, 0);
     }
     return hip_check(hipGetLastError(), "cgtp_build_csr launch");
 }
@@ -719,10 +719,10 @@ int cgtp_validate_csr(const int32_t *row_ptr, int64_t n_rows, int64_t n_edges, c
     if (!row_ptr || !workspace || n_rows < 0 || n_edges < 0)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_validate_csr: bad argument");
     int32_t *bad = (int32_t *)workspace;
-    hipLaunchKernelGGL(k_fill<int32_t>, dim3(1), dim3(64), 0, s, bad, 1, 0);
+    CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(1), dim3(64), 0, s, bad, 1, 0);
     unsigned g = grid_for(std::max(n_rows, n_edges));
     if (g > 4096) g = 4096;
-    hipLaunchKernelGGL(k_validate, dim3(g), dim3(kBlock), 0, s, row_ptr, n_rows, n_edges, idx, n_idx_range, bad);
+    CGTP_LAUNCH("k_validate", s, k_validate, dim3(g), dim3(kBlock), 0, s, row_ptr, n_rows, n_edges, idx, n_idx_range, bad);
     int32_t h = 0;
     int rc = hip_check(hipMemcpyAsync(&h, bad, sizeof h, hipMemcpyDeviceToHost, s), "validate copy");
     if (rc) return rc;
@@ -768,10 +768,10 @@ int cgtp_sh_forces(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_
     if (n_nodes == 0) return CGTP_OK;
     unsigned g = (unsigned)n_nodes;
     if (dtype == CGTP_F32)
-        hipLaunchKernelGGL(k_node_force<float>, dim3(g), dim3(64), 0, s, (const float *)workspace, dst_row_ptr,
+        CGTP_LAUNCH("k_node_force", s, k_node_force<float>, dim3(g), dim3(64), 0, s, (const float *)workspace, dst_row_ptr,
                            src_row_ptr, src_perm, n_nodes, (float *)F);
     else
-        hipLaunchKernelGGL(k_node_force<double>, dim3(g), dim3(64), 0, s, (const double *)workspace, dst_row_ptr,
+        CGTP_LAUNCH("k_node_force", s, k_node_force<double>, dim3(g), dim3(64), 0, s, (const double *)workspace, dst_row_ptr,
                            src_row_ptr, src_perm, n_nodes, (double *)F);
     return hip_check(hipGetLastError(), "node force launch");
 }

@@ -273,6 +273,15 @@ int cgtp_force_loss_sh_cotangent(int32_t lmax, cgtp_dtype dtype, const void *vec
                                  const void *F, int64_t n_edges, void *gg_sh,
                                  cgtp_stream_t stream);
 
+/* Per-launch timing, a profiling aid.  While enabled, every kernel the
+ * library launches is bracketed by two HIP events recorded on its launch
+ * stream (the caller's stream).  cgtp_timing_collect waits for the recorded
+ * events, writes up to cap records (kernel name, NUL-terminated in 64
+ * bytes, and milliseconds) oldest first, returns their number in *n and
+ * clears the record list.  Process-wide; thread-safe. */
+int cgtp_timing_enable(int enable);
+int cgtp_timing_collect(char (*names)[64], float *ms, int32_t cap, int32_t *n);
+
 /* Description of the last error on this thread ("" if none). */
 const char *cgtp_last_error(void);
 
