@@ -114,6 +114,19 @@ def tp_flops(cfg, plan):
     return tot
 
 
+def counted_traffic(workload, kernel, source):
+    """HBM bytes per launch measured with rocprofv3 counters for exactly this
+    generated source (profiles/hbm_traffic__*.json), else None."""
+    import glob
+    import hashlib
+    sha = hashlib.sha1(source.encode()).hexdigest()
+    for path in glob.glob(os.path.join(ROOT, "profiles", "hbm_traffic__*.json")):
+        for r in json.load(open(path))["records"]:
+            if r["workload"] == workload and r["kernel"] == kernel and r["source_sha1"] == sha:
+                return int((r["fetch_kib"] * r["fetch_scale"] + r["write_kib"] * r["write_scale"]) * 1024)
+    return None
+
+
 def copy_probe(torch):
     n = 512 * 1024 * 1024 // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -315,7 +328,8 @@ def bench_conv(args, torch, B, W):
     # dominant kernel: largest share of the step
     dom = max((k for k in kern if k in alg), key=lambda k: kern[k]["ms_per_step"])
     roof = {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB_per_s"], "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"], "traffic": None,
+            "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
+            "traffic": counted_traffic(name, dom, plan.source()),
             "alg_bytes_per_launch": kern[dom]["alg_bytes"], "avg_ms": round(kern[dom]["avg_ms"], 4)}
     if name == "c5":
         # the path tensors on the vector ALUs dominate: FP32 vector peak
