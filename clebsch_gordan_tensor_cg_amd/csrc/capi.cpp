@@ -92,12 +92,22 @@ struct BwdOut {
     bool acc_fwd = false;
 };
 
+// workspace layout of the backward calls: x-messages [E][dim1] in source
+// order, SH-gradient parts [units][E][dim2], message row of each edge [E]
+char *ws_parts(const Plan &p, char *ws, int64_t n_edges) {
+    return ws + align256((size_t)n_edges * p.dim1 * out_bytes(p.dtype));
+}
+int32_t *ws_mrow(const Plan &p, char *ws, int64_t n_edges) {
+    return (int32_t *)(ws_parts(p, ws, n_edges) +
+                       align256((size_t)std::max(1, p.bwd.n_units) * n_edges * p.dim2 * out_bytes(p.dtype)));
+}
+
 int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
             const int32_t *row_ptr, const void *g_out, int64_t n_nodes, int64_t n_edges, BwdOut o,
             char *ws, hipStream_t s) {
-    const size_t eb = out_bytes(p.dtype);
     void *m = ws;
-    char *parts = ws + align256((size_t)n_edges * p.dim1 * eb);
+    char *parts = ws_parts(p, ws, n_edges);
+    const int32_t *mrow = ws_mrow(p, ws, n_edges);
     const bool fused = o.fwd != nullptr;
     const KernelShape &ks = fused ? p.dbl : p.bwd;
     const bool use_parts = !fused && o.g_y && ks.n_units > 1;
@@ -122,7 +132,7 @@ int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const in
     long long n = n_nodes, ne = n_edges;
     int graph = 1;
     void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&g_out,
-                    &gw, &m, &third, &n, &ne, &graph, &flags};
+                    &gw, &m, &third, (void *)&mrow, &n, &ne, &graph, &flags};
     const int64_t ipw = ks.items_per_wave;
     int rc = launch(fused ? p.k_dbl : p.k_bwd, fused ? "cgtp_dbl" : "cgtp_bwd", (n_nodes + ipw - 1) / ipw * ks.n_units, s, args);
     if (rc) return rc;
@@ -380,7 +390,8 @@ int cgtp_conv_workspace_bytes(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges
     const Plan &p = plan->p;
     const size_t eb = out_bytes(p.dtype);
     *bytes = align256((size_t)n_edges * p.dim1 * eb) +
-             align256((size_t)std::max(1, p.bwd.n_units) * n_edges * p.dim2 * eb) + 256;
+             align256((size_t)std::max(1, p.bwd.n_units) * n_edges * p.dim2 * eb) +
+             align256((size_t)n_edges * sizeof(int32_t)) + 256;
     return CGTP_OK;
 }
 
@@ -418,13 +429,14 @@ int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const vo
         if (g_x) return launch_zero(p.dtype, g_x, n_nodes * p.dim1, s);
         return CGTP_OK;
     }
+    if (g_x && (rc = launch_invert_perm(src_perm, n_edges, ws_mrow(p, (char *)workspace, n_edges), s))) return rc;
     BwdOut o;
     o.g_w = g_w;
     o.want_m = g_x != nullptr;
     o.g_y = g_sh;
     rc = run_bwd(p, x, sh, w, src, dst_row_ptr, g_out, n_nodes, n_edges, o, (char *)workspace, s);
     if (rc) return rc;
-    if (g_x) rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, src_perm, n_nodes, p.dim1, g_x, 0, s);
+    if (g_x) rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, nullptr, n_nodes, p.dim1, g_x, 0, s);
     return rc;
 }
 
@@ -446,6 +458,9 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
     const int64_t E = n_edges;
     bool wrote_g = false, wrote_sh = false, wrote_w = false, wrote_m = false;
+    if (d_x && E > 0 && (gg_sh || gg_w) &&
+        (rc = launch_invert_perm(src_perm, E, ws_mrow(p, (char *)workspace, E), s)))
+        return rc;
     if (E > 0) {
         // y term, one pass: d_g_out += f(x, gg_sh, w), d_x += fx*(g; gg_sh, w),
         // d_w += fw*(g; x, gg_sh)
@@ -501,7 +516,7 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
     }
     if (d_g_out && !wrote_g && (rc = launch_zero(p.dtype, d_g_out, n_nodes * p.dim3, s))) return rc;
     if (d_x) {
-        if (wrote_m) rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, src_perm, n_nodes, p.dim1, d_x, 0, s);
+        if (wrote_m) rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, nullptr, n_nodes, p.dim1, d_x, 0, s);
         else rc = launch_zero(p.dtype, d_x, n_nodes * p.dim1, s);
         if (rc) return rc;
     }

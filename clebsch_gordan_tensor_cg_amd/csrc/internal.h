@@ -151,6 +151,8 @@ int launch_segment_sum_rows(cgtp_dtype dt, const void *rows, const int32_t *row_
 int launch_sum_parts(cgtp_dtype dt, const void *parts, int n_parts, int64_t n, void *out,
                      int accumulate, hipStream_t s);
 int launch_zero(cgtp_dtype dt, void *p, int64_t n, hipStream_t s);
+// inv[perm[k]] = k for k < n
+int launch_invert_perm(const int32_t *perm, int64_t n, int32_t *inv, hipStream_t s);
 // out[item][off3 + w*d3 + k] (=|+=) sum_K T[(item*d3 + k)*K + kk] W_b3[kk][w]
 int launch_uvw_mix(const Plan &p, const MixBlock &mb, const void *T, const void *w, int64_t n_items,
                    void *out, int accumulate, hipStream_t s);

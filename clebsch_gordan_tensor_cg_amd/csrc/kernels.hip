@@ -5,6 +5,7 @@
 // sums of partial buffers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <string>
 
@@ -58,34 +59,35 @@ struct Vec16<double> {
     __device__ static void add(V &a, const V &b) { a.x += b.x; a.y += b.y; }
 };
 
-template <class T>
+template <class T, bool kPerm>
 __global__ void __launch_bounds__(256) k_segment_sum_rows(const T *__restrict__ rows, const int32_t *__restrict__ row_ptr,
-                                                          const int32_t *__restrict__ perm, int64_t width,
-                                                          T *__restrict__ out, int accumulate) {
+                                                          const int32_t *__restrict__ perm, int64_t n_seg,
+                                                          int64_t width, T *__restrict__ out, int accumulate) {
     using VT = Vec16<T>;
     using V = typename VT::V;
-    const int64_t s = blockIdx.x;
-    const int beg = row_ptr[s], end = row_ptr[s + 1];
     const bool vec_ok = (width % VT::N) == 0 && (((uintptr_t)rows | (uintptr_t)out) & 15) == 0;
     const int64_t step = (int64_t)gridDim.y * blockDim.x * VT::N;
+    // persistent workgroups: each walks over segments, so the loads of one
+    // segment overlap the tail of the previous one
+    for (int64_t s = blockIdx.x; s < n_seg; s += gridDim.x) {
+    const int beg = row_ptr[s], end = row_ptr[s + 1];
     for (int64_t c = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * VT::N; c < width; c += step) {
         if (vec_ok) {
             V acc = VT::zero();
             int k = beg;
-            for (; k + 4 <= end; k += 4) {
-                const int64_t r0 = perm ? perm[k] : k, r1 = perm ? perm[k + 1] : k + 1;
-                const int64_t r2 = perm ? perm[k + 2] : k + 2, r3 = perm ? perm[k + 3] : k + 3;
-                const V a0 = *(const V *)(rows + r0 * width + c);
-                const V a1 = *(const V *)(rows + r1 * width + c);
-                const V a2 = *(const V *)(rows + r2 * width + c);
-                const V a3 = *(const V *)(rows + r3 * width + c);
-                VT::add(acc, a0);
-                VT::add(acc, a1);
-                VT::add(acc, a2);
-                VT::add(acc, a3);
+            // eight source rows in flight per thread
+            for (; k + 8 <= end; k += 8) {
+                V a[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t r = kPerm ? perm[k + u] : k + u;
+                    a[u] = *(const V *)(rows + r * width + c);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) VT::add(acc, a[u]);
             }
             for (; k < end; ++k) {
-                const int64_t r = perm ? perm[k] : k;
+                const int64_t r = kPerm ? perm[k] : k;
                 VT::add(acc, *(const V *)(rows + r * width + c));
             }
             V *o = (V *)(out + s * width + c);
@@ -99,11 +101,12 @@ __global__ void __launch_bounds__(256) k_segment_sum_rows(const T *__restrict__ 
         } else {
             for (int64_t cc = c; cc < c + VT::N && cc < width; ++cc) {
                 T acc = 0;
-                for (int k = beg; k < end; ++k) acc += rows[(int64_t)(perm ? perm[k] : k) * width + cc];
+                for (int k = beg; k < end; ++k) acc += rows[(int64_t)(kPerm ? perm[k] : k) * width + cc];
                 T *o = out + s * width + cc;
                 *o = accumulate ? *o + acc : acc;
             }
         }
+    }
     }
 }
 
@@ -116,6 +119,12 @@ __global__ void k_sum_parts(const T *__restrict__ parts, int n_parts, int64_t n,
         for (int p = 0; p < n_parts; ++p) acc += parts[p * n + i];
         out[i] = accumulate ? out[i] + acc : acc;
     }
+}
+
+// inv[perm[k]] = k; perm is a permutation of [0, n)
+__global__ void k_invert_perm(const int32_t *__restrict__ perm, int64_t n, int32_t *__restrict__ inv) {
+    for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x)
+        inv[perm[k]] = (int32_t)k;
 }
 
 // ---------------------------------------------------------------------------
@@ -627,15 +636,29 @@ int launch_segment_sum_rows(cgtp_dtype dt, const void *rows, const int32_t *row_
                             int64_t n_seg, int64_t width, void *out, int accumulate, hipStream_t s) {
     if (n_seg <= 0 || width <= 0) return CGTP_OK;
     const int per = dt == CGTP_F64 ? 2 : 4;  // elements per thread chunk
-    int64_t gy = (width + (int64_t)kBlock * per - 1) / ((int64_t)kBlock * per);
+    // just enough threads (a multiple of 64, at most 256) for one row
+    int64_t chunks = (width + per - 1) / per;
+    int threads = (int)std::min<int64_t>(kBlock, (chunks + 63) / 64 * 64);
+    int64_t gy = (chunks + threads - 1) / threads;
     if (gy > 65535) gy = 65535;
-    dim3 grid((unsigned)n_seg, (unsigned)gy);
-    if (dt == CGTP_F64)
-        CGTP_LAUNCH("k_segment_sum_rows", s, k_segment_sum_rows<double>, grid, dim3(kBlock), 0, s, (const double *)rows, row_ptr, perm,
-                           width, (double *)out, accumulate);
-    else
-        CGTP_LAUNCH("k_segment_sum_rows", s, k_segment_sum_rows<float>, grid, dim3(kBlock), 0, s, (const float *)rows, row_ptr, perm,
-                           width, (float *)out, accumulate);
+    // about eight workgroups per compute unit, each walking over segments
+    const int64_t gx = std::min<int64_t>(n_seg, 2048);
+    dim3 grid((unsigned)gx, (unsigned)gy);
+    if (dt == CGTP_F64) {
+        if (perm)
+            CGTP_LAUNCH("k_segment_sum_rows", s, (k_segment_sum_rows<double, true>), grid, dim3(threads), 0, s,
+                        (const double *)rows, row_ptr, perm, n_seg, width, (double *)out, accumulate);
+        else
+            CGTP_LAUNCH("k_segment_sum_rows", s, (k_segment_sum_rows<double, false>), grid, dim3(threads), 0, s,
+                        (const double *)rows, row_ptr, perm, n_seg, width, (double *)out, accumulate);
+    } else {
+        if (perm)
+            CGTP_LAUNCH("k_segment_sum_rows", s, (k_segment_sum_rows<float, true>), grid, dim3(threads), 0, s,
+                        (const float *)rows, row_ptr, perm, n_seg, width, (float *)out, accumulate);
+        else
+            CGTP_LAUNCH("k_segment_sum_rows", s, (k_segment_sum_rows<float, false>), grid, dim3(threads), 0, s,
+                        (const float *)rows, row_ptr, perm, n_seg, width, (float *)out, accumulate);
+    }
     return hip_check(hipGetLastError(), "segment sum launch");
 }
 
@@ -651,6 +674,14 @@ int launch_sum_parts(cgtp_dtype dt, const void *parts, int n_parts, int64_t n, v
         CGTP_LAUNCH("k_sum_parts", s, k_sum_parts<float>, dim3(g), dim3(kBlock), 0, s, (const float *)parts, n_parts, n,
                            (float *)out, accumulate);
     return hip_check(hipGetLastError(), "part sum launch");
+}
+
+int launch_invert_perm(const int32_t *perm, int64_t n, int32_t *inv, hipStream_t s) {
+    if (n <= 0) return CGTP_OK;
+    unsigned g = grid_for(n);
+    if (g > 65536) g = 65536;
+    CGTP_LAUNCH("k_invert_perm", s, k_invert_perm, dim3(g), dim3(kBlock), 0, s, perm, n, inv);
+    return hip_check(hipGetLastError(), "invert perm launch");
 }
 
 int launch_zero(cgtp_dtype dt, void *p, int64_t n, hipStream_t s) {
