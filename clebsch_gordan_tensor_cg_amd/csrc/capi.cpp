@@ -134,7 +134,9 @@ int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const in
     void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&g_out,
                     &gw, &m, &third, (void *)&mrow, &n, &ne, &graph, &flags};
     const int64_t ipw = ks.items_per_wave;
-    int rc = launch(fused ? p.k_dbl : p.k_bwd, fused ? "cgtp_dbl" : "cgtp_bwd", (n_nodes + ipw - 1) / ipw * ks.n_units, s, args);
+    hipFunction_t f = fused ? ((p.tune.full & 2) && flags == dbl_full_flags(p) ? p.k_dbl_full : p.k_dbl)
+                            : ((p.tune.full & 1) && flags == bwd_full_flags(p) ? p.k_bwd_full : p.k_bwd);
+    int rc = launch(f, fused ? "cgtp_dbl" : "cgtp_bwd", (n_nodes + ipw - 1) / ipw * ks.n_units, s, args);
     if (rc) return rc;
     if (use_parts) rc = launch_sum_parts(p.dtype, parts, ks.n_units, n_edges * p.dim2, o.g_y, o.acc_y, s);
     return rc;

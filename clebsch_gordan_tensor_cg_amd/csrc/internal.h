@@ -57,7 +57,7 @@ struct KernelShape {
 };
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
-// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, yvec, ntw, pf, budget, stage, cypath, depth, bgy) overrides
+// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, yvec, ntw, pf, budget, stage, cypath, depth, bgy, full) overrides
 // them for experiments.
 struct Tuning {
     int cpl[3] = {0, 0, 0};  // channels per lane per kernel kind (0 = by budget)
@@ -69,6 +69,7 @@ struct Tuning {
     int cy_path = -1;        // uniform products per path (1) or per edge (0); -1: by dtype
     int depth = 3;           // edges of prefetch in flight (staged loop)
     bool bgy = false;        // backward via B_ij = sum_k R_ijk g_k (fewer FMAs, more VGPRs)
+    int full = 3;            // dispatch to the folded-flag kernels: bit 0 backward, bit 1 double backward
 };
 Tuning tuning_from_env();
 
@@ -108,8 +109,17 @@ struct Plan {
     hipFunction_t k_fwd = nullptr;
     hipFunction_t k_bwd = nullptr;
     hipFunction_t k_dbl = nullptr;
+    hipFunction_t k_bwd_full = nullptr;  // k_bwd with bwd_full_flags folded in
+    hipFunction_t k_dbl_full = nullptr;  // k_dbl with dbl_full_flags folded in
     int device = -1;
 };
+
+// Flags of the full, non-accumulating backward (g_w, messages, SH gradient,
+// per-unit parts when there are several units) and fused double backward
+// (d_w and messages); the code object holds a copy of each kernel with
+// these folded in at compile time.
+inline int bwd_full_flags(const Plan &p) { return 1 | 2 | 4 | (p.bwd.n_units > 1 ? 64 : 0); }
+inline int dbl_full_flags(const Plan &) { return 1 | 2; }
 
 // planner
 int parse_irreps(const char *s, std::vector<Irrep> &out, std::string &err);

@@ -46,17 +46,17 @@ template <class T>
 struct Vec16;
 template <>
 struct Vec16<float> {
-    using V = float4;
+    typedef float V __attribute__((ext_vector_type(4)));
     static constexpr int N = 4;
-    __device__ static V zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
-    __device__ static void add(V &a, const V &b) { a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w; }
+    __device__ static V zero() { return V{0.f, 0.f, 0.f, 0.f}; }
+    __device__ static void add(V &a, const V &b) { a += b; }
 };
 template <>
 struct Vec16<double> {
-    using V = double2;
+    typedef double V __attribute__((ext_vector_type(2)));
     static constexpr int N = 2;
-    __device__ static V zero() { return make_double2(0.0, 0.0); }
-    __device__ static void add(V &a, const V &b) { a.x += b.x; a.y += b.y; }
+    __device__ static V zero() { return V{0.0, 0.0}; }
+    __device__ static void add(V &a, const V &b) { a += b; }
 };
 
 template <class T, bool kPerm>
@@ -81,7 +81,8 @@ __global__ void __launch_bounds__(256) k_segment_sum_rows(const T *__restrict__ 
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int64_t r = kPerm ? perm[k + u] : k + u;
-                    a[u] = *(const V *)(rows + r * width + c);
+                    // each row is read once: stream it past the caches
+                    a[u] = __builtin_nontemporal_load((const V *)(rows + r * width + c));
                 }
 #pragma unroll
                 for (int u = 0; u < 8; ++u) VT::add(acc, a[u]);
@@ -130,51 +131,125 @@ __global__ void k_invert_perm(const int32_t *__restrict__ perm, int64_t n, int32
 // ---------------------------------------------------------------------------
 // CSR build
 // ---------------------------------------------------------------------------
-__global__ void k_count(const int32_t *__restrict__ key, int64_t n, int32_t *__restrict__ cnt) {
-    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
-         e += (int64_t)gridDim.x * blockDim.x)
-        atomicAdd(&cnt[key[e]], 1);
+// Keys are counted in LDS: a workgroup takes a contiguous run of edges and
+// one range of at most kCsrBins keys, counts its keys there and publishes
+// only its nonzero bins, so the device-wide atomics number about
+// (#workgroups x #bins) rather than one per edge.  Keys outside
+// [0, n_keys) are skipped.
+constexpr int kCsrBins = 16384;  // 64 KiB of LDS counters per workgroup
+constexpr int kCsrThreads = 1024;
+
+__global__ void __launch_bounds__(kCsrThreads) k_count(const int32_t *__restrict__ key, int64_t n, int64_t n_keys,
+                                                       int64_t per, int32_t *__restrict__ cnt) {
+    extern __shared__ int32_t h[];
+    const int64_t k0 = (int64_t)blockIdx.y * kCsrBins;
+    const int kb = (int)std::min<int64_t>(kCsrBins, n_keys - k0);
+    const int64_t e0 = (int64_t)blockIdx.x * per, e1 = std::min<int64_t>(n, e0 + per);
+    for (int i = threadIdx.x; i < kb; i += blockDim.x) h[i] = 0;
+    __syncthreads();
+    for (int64_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
+        const int64_t k = key[e] - k0;
+        if (k >= 0 && k < kb) atomicAdd(&h[k], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kb; i += blockDim.x)
+        if (h[i]) atomicAdd(&cnt[k0 + i], h[i]);
 }
 
-// Exclusive scan of cnt[0..n) into row_ptr[0..n], one workgroup of 1024.
+// Same partition as k_count.  Each workgroup reserves, per nonzero bin, a
+// run of slots inside that key's segment with one device atomic, then
+// hands the slots out to its edges with LDS atomics.  The order inside a
+// segment is therefore arbitrary; k_rank_segments makes it canonical.
+__global__ void __launch_bounds__(kCsrThreads) k_scatter(const int32_t *__restrict__ key, int64_t n, int64_t n_keys,
+                                                         int64_t per, const int32_t *__restrict__ row_ptr,
+                                                         int32_t *__restrict__ cursor, int32_t *__restrict__ tmp) {
+    extern __shared__ int32_t h[];
+    const int64_t k0 = (int64_t)blockIdx.y * kCsrBins;
+    const int kb = (int)std::min<int64_t>(kCsrBins, n_keys - k0);
+    const int64_t e0 = (int64_t)blockIdx.x * per, e1 = std::min<int64_t>(n, e0 + per);
+    for (int i = threadIdx.x; i < kb; i += blockDim.x) h[i] = 0;
+    __syncthreads();
+    for (int64_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
+        const int64_t k = key[e] - k0;
+        if (k >= 0 && k < kb) atomicAdd(&h[k], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kb; i += blockDim.x) {
+        const int c = h[i];
+        if (c) h[i] = row_ptr[k0 + i] + atomicAdd(&cursor[k0 + i], c);
+    }
+    __syncthreads();
+    for (int64_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
+        const int64_t k = key[e] - k0;
+        if (k >= 0 && k < kb) tmp[atomicAdd(&h[k], 1)] = (int32_t)e;
+    }
+}
+
+// Key spaces too wide for a few LDS ranges: one device atomic per edge.
+__global__ void k_count_global(const int32_t *__restrict__ key, int64_t n, int64_t n_keys, int32_t *__restrict__ cnt) {
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t k = key[e];
+        if (k >= 0 && k < n_keys) atomicAdd(&cnt[k], 1);
+    }
+}
+
+__global__ void k_scatter_global(const int32_t *__restrict__ key, int64_t n, int64_t n_keys,
+                                 const int32_t *__restrict__ row_ptr, int32_t *__restrict__ cursor,
+                                 int32_t *__restrict__ tmp) {
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t k = key[e];
+        if (k >= 0 && k < n_keys) tmp[row_ptr[k] + atomicAdd(&cursor[k], 1)] = (int32_t)e;
+    }
+}
+
+// Exclusive scan of cnt[0..n) into row_ptr[0..n]; one workgroup, four
+// consecutive counts per thread, wavefront scans by shuffles.
 __global__ void __launch_bounds__(1024) k_scan(const int32_t *__restrict__ cnt, int64_t n,
                                                 int32_t *__restrict__ row_ptr) {
-    __shared__ int32_t part[1024];
-    __shared__ int32_t carry;
-    if (threadIdx.x == 0) carry = 0;
-    __syncthreads();
-    for (int64_t base = 0; base < n; base += 1024) {
-        const int64_t i = base + threadIdx.x;
-        int32_t v = i < n ? cnt[i] : 0;
-        part[threadIdx.x] = v;
-        __syncthreads();
-        for (int off = 1; off < 1024; off <<= 1) {
-            int32_t t = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-            __syncthreads();
-            part[threadIdx.x] += t;
-            __syncthreads();
+    __shared__ int32_t wsum[16];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int32_t carry = 0;
+    for (int64_t base = 0; base < n; base += 4096) {
+        const int64_t i0 = base + 4 * (int64_t)threadIdx.x;
+        int32_t v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = i0 + q < n ? cnt[i0 + q] : 0;
+        const int32_t own = v[0] + v[1] + v[2] + v[3];
+        int32_t incl = own;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t t = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += t;
         }
-        if (i < n) row_ptr[i] = carry + part[threadIdx.x] - v;
+        if (lane == 63) wsum[wid] = incl;
         __syncthreads();
-        if (threadIdx.x == 1023) carry += part[1023];
+        if (wid == 0) {
+            int32_t ws = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                const int32_t t = __shfl_up(ws, off, 64);
+                if (lane >= off) ws += t;
+            }
+            if (lane < 16) wsum[lane] = ws;
+        }
+        __syncthreads();
+        int32_t run = carry + (wid ? wsum[wid - 1] : 0) + incl - own;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (i0 + q < n) row_ptr[i0 + q] = run;
+            run += v[q];
+        }
+        carry += wsum[15];
         __syncthreads();
     }
     if (threadIdx.x == 0) row_ptr[n] = carry;
 }
 
-__global__ void k_scatter(const int32_t *__restrict__ key, int64_t n, const int32_t *__restrict__ row_ptr,
-                          int32_t *__restrict__ cursor, int32_t *__restrict__ tmp) {
-    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        const int k = key[e];
-        const int pos = atomicAdd(&cursor[k], 1);
-        tmp[row_ptr[k] + pos] = (int32_t)e;
-    }
-}
-
 // One wavefront per segment: each element's final slot is the number of
 // smaller edge ids in its segment, which reproduces the stable order no
-// matter in which order the scatter's atomics landed.
+// matter in which order the scatter's atomics landed.  Segments of up to
+// kRankLds edges are staged in LDS.
+constexpr int kRankLds = 2048;
 __global__ void __launch_bounds__(64) k_rank_segments(const int32_t *__restrict__ row_ptr, int64_t n_keys,
                                                       const int32_t *__restrict__ tmp,
                                                       const int32_t *__restrict__ key,
@@ -182,13 +257,22 @@ __global__ void __launch_bounds__(64) k_rank_segments(const int32_t *__restrict_
                                                       int32_t *__restrict__ perm,
                                                       int32_t *__restrict__ sorted_key,
                                                       int32_t *__restrict__ sorted_val) {
+    __shared__ int32_t seg[kRankLds];
     const int64_t s = blockIdx.x;
     if (s >= n_keys) return;
     const int beg = row_ptr[s], end = row_ptr[s + 1];
-    for (int i = beg + threadIdx.x; i < end; i += 64) {
-        const int32_t me = tmp[i];
+    const int deg = end - beg;
+    const bool staged = deg <= kRankLds;
+    if (staged)
+        for (int i = threadIdx.x; i < deg; i += 64) seg[i] = tmp[beg + i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < deg; i += 64) {
+        const int32_t me = staged ? seg[i] : tmp[beg + i];
         int rank = 0;
-        for (int j = beg; j < end; ++j) rank += tmp[j] < me;
+        if (staged)
+            for (int j = 0; j < deg; ++j) rank += seg[j] < me;
+        else
+            for (int j = beg; j < end; ++j) rank += tmp[j] < me;
         perm[beg + rank] = me;
         if (sorted_key) sorted_key[beg + rank] = key[me];
         if (sorted_val) sorted_val[beg + rank] = val[me];
@@ -725,20 +809,40 @@ int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int6
     int32_t *cnt = (int32_t *)ws;
     int32_t *cursor = (int32_t *)(ws + align256(sizeof(int32_t) * (size_t)(n_keys + 1)));
     int32_t *tmp = (int32_t *)(ws + 2 * align256(sizeof(int32_t) * (size_t)(n_keys + 1)));
-    unsigned gk = grid_for(n_keys + 1);
-    CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, cnt, n_keys + 1, 0);
-    CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, cursor, n_keys + 1, 0);
-    if (n_edges > 0) {
-        unsigned ge = grid_for(n_edges);
-        if (ge > 65536) ge = 65536;
-        CGTP_LAUNCH("k_count", s, k_count, dim3(ge), dim3(kBlock), 0, s, key, n_edges, cnt);
+    // cnt and cursor are adjacent: one fill clears both
+    const int64_t n_clear = (int64_t)(cursor - cnt) + n_keys + 1;
+    CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(grid_for(n_clear)), dim3(kBlock), 0, s, cnt, n_clear, 0);
+    if (n_edges > 0 && n_keys > 0) {
+        const int64_t bins = std::min<int64_t>(n_keys, kCsrBins);
+        const int64_t ranges = (n_keys + kCsrBins - 1) / kCsrBins;
+        // runs of at least four edges per counter keep the device atomics
+        // well below one per edge
+        int64_t per = std::max<int64_t>(16384, 4 * bins);
+        int64_t splits = (n_edges + per - 1) / per;
+        if (splits > 65535) {
+            splits = 65535;
+            per = (n_edges + splits - 1) / splits;
+        }
+        const dim3 grid((unsigned)splits, (unsigned)ranges);
+        const size_t lds = sizeof(int32_t) * (size_t)bins;
+        // each LDS range rereads the keys, so wide key spaces go to device atomics
+        const bool lds_path = ranges <= 8;
+        const unsigned ge = std::min<unsigned>(grid_for(n_edges), 65536u);
+        if (lds_path)
+            CGTP_LAUNCH("k_count", s, k_count, grid, dim3(kCsrThreads), lds, s, key, n_edges, n_keys, per, cnt);
+        else
+            CGTP_LAUNCH("k_count_global", s, k_count_global, dim3(ge), dim3(kBlock), 0, s, key, n_edges, n_keys, cnt);
         CGTP_LAUNCH("k_scan", s, k_scan, dim3(1), dim3(1024), 0, s, cnt, n_keys, row_ptr);
-        CGTP_LAUNCH("k_scatter", s, k_scatter, dim3(ge), dim3(kBlock), 0, s, key, n_edges, row_ptr, cursor, tmp);
-        if (n_keys > 0)
-            CGTP_LAUNCH("k_rank_segments", s, k_rank_segments, dim3((unsigned)n_keys), dim3(64), 0, s, row_ptr, n_keys, tmp, key,
-                               val, perm, sorted_key, sorted_val);
+        if (lds_path)
+            CGTP_LAUNCH("k_scatter", s, k_scatter, grid, dim3(kCsrThreads), lds, s, key, n_edges, n_keys, per, row_ptr,
+                        cursor, tmp);
+        else
+            CGTP_LAUNCH("k_scatter_global", s, k_scatter_global, dim3(ge), dim3(kBlock), 0, s, key, n_edges, n_keys,
+                        row_ptr, cursor, tmp);
+        CGTP_LAUNCH("k_rank_segments", s, k_rank_segments, dim3((unsigned)n_keys), dim3(64), 0, s, row_ptr, n_keys, tmp,
+                    key, val, perm, sorted_key, sorted_val);
     } else {
-        CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(gk), dim3(kBlock), 0, s, row_ptr, n_keys + 1, 0);
+        CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(grid_for(n_keys + 1)), dim3(kBlock), 0, s, row_ptr, n_keys + 1, 0);
     }
     return hip_check(hipGetLastError(), "cgtp_build_csr launch");
 }

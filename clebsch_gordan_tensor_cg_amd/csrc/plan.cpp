@@ -286,6 +286,7 @@ Tuning tuning_from_env() {
             else if (k == "cypath") t.cy_path = v;
             else if (k == "depth") t.depth = v < 1 ? 1 : (v > 4 ? 4 : v);
             else if (k == "bgy") t.bgy = v != 0;
+            else if (k == "full") t.full = v & 3;
         }
         pos = comma + 1;
     }

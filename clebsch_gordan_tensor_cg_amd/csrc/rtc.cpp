@@ -162,7 +162,7 @@ int compile_and_load(Plan &p, bool load, std::string &err) {
         r.destroy(&prog);
         write_file_atomic(dir, path, code);
     }
-    p.n_kernels = (p.mode == CGTP_UVU) ? 3 : 1;
+    p.n_kernels = (p.mode == CGTP_UVU) ? 5 : 1;
     if (!load) return CGTP_OK;
 
     hipError_t e = hipGetDevice(&p.device);
@@ -170,6 +170,8 @@ int compile_and_load(Plan &p, bool load, std::string &err) {
     if (e == hipSuccess) e = hipModuleGetFunction(&p.k_fwd, p.module, "cgtp_fwd");
     if (e == hipSuccess && p.n_kernels > 1) e = hipModuleGetFunction(&p.k_bwd, p.module, "cgtp_bwd");
     if (e == hipSuccess && p.n_kernels > 2) e = hipModuleGetFunction(&p.k_dbl, p.module, "cgtp_dbl");
+    if (e == hipSuccess && p.n_kernels > 3) e = hipModuleGetFunction(&p.k_bwd_full, p.module, "cgtp_bwd_full");
+    if (e == hipSuccess && p.n_kernels > 4) e = hipModuleGetFunction(&p.k_dbl_full, p.module, "cgtp_dbl_full");
     if (e != hipSuccess) {
         err = std::string("loading generated code object: ") + hipGetErrorString(e);
         return CGTP_ERR_HIP;

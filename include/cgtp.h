@@ -230,8 +230,10 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
  * Bit-exact and deterministic (the order within a key does not depend on
  * the order in which the device's atomics land).  A segment of d edges
  * costs O(d^2 / 64) per wavefront, so very large in-degrees are slow.
- * workspace: cgtp_csr_workspace_bytes.  Keys must lie in [0, n_keys)
- * (check untrusted keys with cgtp_validate_csr first). */
+ * workspace: cgtp_csr_workspace_bytes.  Keys should lie in [0, n_keys):
+ * an edge with a key outside it is left out (row_ptr[n_keys] then counts
+ * only the edges kept, perm holds only that many ids, and
+ * cgtp_validate_csr reports the shortfall). */
 int cgtp_csr_workspace_bytes(int64_t n_edges, int64_t n_keys, size_t *bytes);
 int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int64_t n_keys,
                    int32_t *perm, int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val,

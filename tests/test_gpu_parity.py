@@ -179,12 +179,19 @@ def test_conv_no_edges(B, torch):
 # ---------------------------------------------------------------------------
 # CSR build, validation, spherical harmonics, forces
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("case", ["c2", "empty", "one_node", "hub", "ragged"])
+@pytest.mark.parametrize("case", ["c2", "empty", "one_node", "hub", "ragged", "multi_range", "wide_keys",
+                                  "many_splits"])
 def test_build_csr_bit_exact(B, torch, case):
     rs = np.random.default_rng(5)
     if case == "c2":
         g = W.periodic_graph(4096, seed=0)
         key, n = g.dst, 4096
+    elif case == "multi_range":     # three LDS key ranges
+        key, n = rs.integers(0, 40000, 200000).astype(np.int32), 40000
+    elif case == "wide_keys":       # too many key ranges: device-atomic path
+        key, n = rs.integers(0, 300000, 100000).astype(np.int32), 300000
+    elif case == "many_splits":     # many edge runs per key range
+        key, n = rs.integers(0, 16384, 1500000).astype(np.int32), 16384
     elif case == "empty":
         key, n = np.zeros(0, np.int32), 7
     elif case == "one_node":
@@ -204,6 +211,20 @@ def test_build_csr_bit_exact(B, torch, case):
     np.testing.assert_array_equal(perm.cpu().numpy(), perm_ref)
     np.testing.assert_array_equal(sk.cpu().numpy(), key[perm_ref])
     np.testing.assert_array_equal(sv.cpu().numpy(), val[perm_ref])
+
+
+@pytest.mark.parametrize("n", [50, 20000])
+def test_build_csr_skips_out_of_range_keys(B, torch, n):
+    rs = np.random.default_rng(11)
+    key = rs.integers(-5, n + 5, 30000).astype(np.int32)
+    kept = np.nonzero((key >= 0) & (key < n))[0]
+    perm_k, rp_ref = oracle.csr(key[kept], n)
+    print(f"csr out of range n={n}", flush=True)
+    perm, rp, _, _ = B.cgtp_build_csr(torch.from_numpy(key).cuda(), n)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(rp.cpu().numpy(), rp_ref)
+    np.testing.assert_array_equal(perm.cpu().numpy()[:len(kept)], kept[perm_k])
+    assert not B.cgtp_validate_csr(rp, len(key), None, 0)   # row_ptr[n] != n_edges
 
 
 def test_validate_csr(B, torch):
