@@ -1,7 +1,7 @@
 """Benchmark of the fused CG tensor-product convolution hot path on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload c4|c2|c3|c1|c5] [--no-cpu-baseline] [--probe-copy]
+                    [--workload c4|c2|c3|c1|c5] [--no-cpu-baseline] [--nominal-e]
 
 Default workload "c4" (one step = the whole hot path on the 4096-atom
 periodic water-density box, cutoff 5 A, node 128x0e+128x1o, SH l<=3, uvu,
@@ -41,9 +41,16 @@ def parse():
     ap.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c1", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy", action="store_true",
-                    help="run a 512 MiB device copy first (reference for counter scaling)")
+                    help="kept for old command lines: the 512 MiB device copy now always runs first")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--bf16-weights", action="store_true",
+                    help="c2/c4: per-edge weights stored as bf16 (float arithmetic)")
+    ap.add_argument("--nominal-e", action="store_true",
+                    help="c2/c3/c4 graph with cutoff 4.153 A (about 30 neighbours, the nominal edge count)")
     return ap.parse_args()
+
+
+NOMINAL_CUTOFF = 4.153   # 0.1 / A^3 x (4/3) pi r^3 = 30 neighbours
 
 
 class Timer:
@@ -71,18 +78,22 @@ class Timer:
 # algorithmic bytes: each array counted once at its storage size; gathers of
 # source-node rows that hit in cache are not counted
 # ---------------------------------------------------------------------------
-def alg_bytes_conv_fwd(N, E, d1, d2, d3, wn, eb, ob):
-    return N * d1 * eb + N * d3 * ob + E * d2 * eb + E * wn * eb + E * 4 + (N + 1) * 4
+def alg_bytes_conv_fwd(N, E, d1, d2, d3, wn, eb, ob, wb=None):
+    wb = eb if wb is None else wb
+    return N * d1 * eb + N * d3 * ob + E * d2 * eb + E * wn * wb + E * 4 + (N + 1) * 4
 
 
-def alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb):
-    # reads x, g_out, sh, w, src, row_ptr; writes g_x, g_sh, g_w
-    return N * (2 * d1 + d3) * eb + E * 2 * (d2 + wn) * eb + E * 4 + (N + 1) * 4
+def alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb, wb=None):
+    # reads x, g_out, sh, w, src, row_ptr; writes g_x, g_sh, g_w (g_w at the
+    # arithmetic width)
+    wb = eb if wb is None else wb
+    return N * (2 * d1 + d3) * eb + E * 2 * d2 * eb + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
 
 
-def alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb):
+def alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb, wb=None):
     # reads x, g_out, gg_sh, w, src, row_ptr; writes d_g_out, d_x, d_w
-    return N * (2 * d1 + 2 * d3) * eb + E * (d2 + 2 * wn) * eb + E * 4 + (N + 1) * 4
+    wb = eb if wb is None else wb
+    return N * (2 * d1 + 2 * d3) * eb + E * d2 * eb + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
 
 
 def parse_irreps(s):
@@ -208,17 +219,24 @@ def bench_conv(args, torch, B, W):
     if name == "c5":
         g = W.molecule_batch(cfg.extra["n_graphs"], cfg.extra["n_atoms"], cutoff=cfg.extra["cutoff"], rng=rng)
     else:
-        g = W.periodic_graph(cfg.extra["n_atoms"], cutoff=cfg.extra["cutoff"], rng=rng)
+        cut = NOMINAL_CUTOFF if args.nominal_e else cfg.extra["cutoff"]
+        g = W.periodic_graph(cfg.extra["n_atoms"], cutoff=cut, rng=rng)
+    bf16w = bool(args.bf16_weights)
+    if bf16w and name not in ("c2", "c4"):
+        raise SystemExit("--bf16-weights applies to the c2 and c4 workloads")
     plan = B.Plan(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.paths, cfg.mode, dtype,
-                  cfg.shared_weights)
+                  cfg.shared_weights, bf16_weights=bf16w)
     lmax = cfg.extra["lmax"]
     x_np = W.normal(rng, (g.n_nodes, plan.dim_in1), dtype)
     w_np = W.normal(rng, (plan.weight_numel,) if cfg.shared_weights else (g.n_edges, plan.weight_numel), dtype)
+    if bf16w:
+        w_np = W.round_to(w_np, "bf16")
     N, E = g.n_nodes, g.n_edges
     dev = "cuda"
     td = B.TORCH_DTYPES[dtype]
     od = plan.out_dtype
     eb = {"f64": 8, "f32": 4, "bf16": 2}[dtype]
+    wb = 2 if bf16w else eb
     ob = 8 if dtype == "f64" else 4
     # inputs resident in HBM: canonical edge list and vectors, node features,
     # per-edge weights already in CSR (destination-sorted) order
@@ -227,9 +245,9 @@ def bench_conv(args, torch, B, W):
     vec = torch.from_numpy(g.vec.astype(np.float64 if dtype == "f64" else np.float32)).to(dev)
     x = torch.from_numpy(x_np).to(dev).to(td)
     if cfg.shared_weights:
-        w = torch.from_numpy(w_np).to(dev).to(td)
+        w = torch.from_numpy(w_np).to(dev).to(plan.weight_dtype)
     else:
-        w = torch.from_numpy(w_np[np.argsort(g.dst, kind="stable")]).to(dev).to(td)
+        w = torch.from_numpy(w_np[np.argsort(g.dst, kind="stable")]).to(dev).to(plan.weight_dtype)
     perm = torch.empty(E, dtype=torch.int32, device=dev)
     rp = torch.empty(N + 1, dtype=torch.int32, device=dev)
     dst_s = torch.empty(E, dtype=torch.int32, device=dev)
@@ -279,12 +297,16 @@ def bench_conv(args, torch, B, W):
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0.record()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         step(True)
+        marks[i + 1].record()
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     kms = timer.ms()
     # per-kernel durations: one more pass with the library's per-launch
     # events (recorded on the launch stream) enabled
@@ -307,10 +329,10 @@ def bench_conv(args, torch, B, W):
     if name == "c5":
         alg["cgtp_fwd"] = N * d1 * eb + E * d2 * eb + E * 4 + (N + 1) * 4   # path tensors (bf16) stay in cache
     else:
-        alg["cgtp_fwd"] = alg_bytes_conv_fwd(N, E, d1, d2, d3, wn, eb, ob)
+        alg["cgtp_fwd"] = alg_bytes_conv_fwd(N, E, d1, d2, d3, wn, eb, ob, wb)
     if full:
-        alg["cgtp_bwd"] = N * (d1 + d3) * eb + E * 2 * (d2 + wn) * eb + E * 4 + (N + 1) * 4
-        alg["cgtp_dbl"] = N * (d1 + 2 * d3) * eb + E * (d2 + 2 * wn) * eb + E * 4 + (N + 1) * 4
+        alg["cgtp_bwd"] = N * (d1 + d3) * eb + E * 2 * d2 * eb + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
+        alg["cgtp_dbl"] = N * (d1 + 2 * d3) * eb + E * d2 * eb + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
     kern = {}
     for k, v in launches.items():
         kern[k] = dict(v)
@@ -319,12 +341,12 @@ def bench_conv(args, torch, B, W):
             kern[k].update({"alg_bytes": int(alg[k]), "GB_per_s": round(gbs, 1),
                             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
     calls = {"conv_fwd": {"ms": kms["conv_fwd"], "GB_per_s": round(
-        alg_bytes_conv_fwd(N, E, d1, d2, d3, wn, eb, ob) / (kms["conv_fwd"] * 1e-3) / 1e9, 1)}}
+        alg_bytes_conv_fwd(N, E, d1, d2, d3, wn, eb, ob, wb) / (kms["conv_fwd"] * 1e-3) / 1e9, 1)}}
     if full:
         calls["conv_bwd"] = {"ms": kms["conv_bwd"], "GB_per_s": round(
-            alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb) / (kms["conv_bwd"] * 1e-3) / 1e9, 1)}
+            alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb, wb) / (kms["conv_bwd"] * 1e-3) / 1e9, 1)}
         calls["double_bwd"] = {"ms": kms["double_bwd"], "GB_per_s": round(
-            alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb) / (kms["double_bwd"] * 1e-3) / 1e9, 1)}
+            alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb, wb) / (kms["double_bwd"] * 1e-3) / 1e9, 1)}
     # dominant kernel: largest share of the step
     dom = max((k for k in kern if k in alg), key=lambda k: kern[k]["ms_per_step"])
     roof = {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB_per_s"], "peak": HBM_PEAK_GBS,
@@ -347,12 +369,17 @@ def bench_conv(args, torch, B, W):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(per_step)),
+        "ms_per_step_min": float(np.min(per_step)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": W.config("c4").name if full else cfg.name, "n_atoms": N, "n_edges": E,
+        "config": {"workload": (W.config("c4").name if full else cfg.name) +
+                   (f", cutoff {NOMINAL_CUTOFF} A" if args.nominal_e and name != "c5" else "") +
+                   (", bf16 weight storage" if bf16w else ""),
+                   "n_atoms": N, "n_edges": E,
                    "irreps_node": cfg.irreps_in1, "irreps_sh": cfg.irreps_in2, "irreps_out": cfg.irreps_out,
                    "n_paths": plan.n_paths,
                    "step": ("csr+sh+fwd+bwd+forces+force_cotangent+double_bwd" if full else "csr+sh+fwd")},
@@ -417,10 +444,14 @@ def main():
         from clebsch_gordan_tensor_cg_amd import build as b
         b.build(verbose=False)
     torch.cuda.set_device(0)
-    probe = copy_probe(torch) if args.probe_copy else None
+    probe = copy_probe(torch)
     res = bench_single(args, torch, B, W) if args.workload == "c1" else bench_conv(args, torch, B, W)
-    if probe:
-        res["copy_probe"] = probe
+    # context: the dominant kernel against a measured device-copy stream
+    # (512 MiB read + 512 MiB written), next to the datasheet peak
+    res["copy_probe"] = probe
+    roof = res["roofline"]
+    if roof["unit"] == "GB/s":
+        roof["frac_of_measured_copy"] = round(roof["achieved"] / probe["GB_per_s"], 4)
     print(json.dumps(res))
 
 

@@ -21,6 +21,7 @@ DTYPES = {"f32": 0, "f64": 1, "bf16": 2}
 TORCH_DTYPES = {"f32": torch.float32, "f64": torch.float64, "bf16": torch.bfloat16}
 CGTP_SHARED_WEIGHTS = 1
 CGTP_PLAN_NO_LOAD = 2
+CGTP_BF16_WEIGHTS = 4
 
 _ERRORS = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "COMPILE", -4: "HIP", -5: "GRAPH"}
 
@@ -124,15 +125,18 @@ def _stream(stream=None, like=None):
 # ---------------------------------------------------------------------------
 class Plan:
     def __init__(self, irreps_in1: str, irreps_in2: str, irreps_out: str, paths=None, mode: str = "uvu",
-                 dtype: str = "f32", shared_weights: bool = False, no_load: bool = False):
+                 dtype: str = "f32", shared_weights: bool = False, no_load: bool = False,
+                 bf16_weights: bool = False):
         self.dtype = dtype
         self.mode = mode
         self.shared_weights = shared_weights
+        self.bf16_weights = bf16_weights
         arr, n = None, 0
         if paths:
             n = len(paths)
             arr = (_Path * n)(*[_Path(*p) for p in paths])
-        flags = (CGTP_SHARED_WEIGHTS if shared_weights else 0) | (CGTP_PLAN_NO_LOAD if no_load else 0)
+        flags = ((CGTP_SHARED_WEIGHTS if shared_weights else 0) | (CGTP_PLAN_NO_LOAD if no_load else 0) |
+                 (CGTP_BF16_WEIGHTS if bf16_weights else 0))
         h = ctypes.c_void_p()
         _check(lib().cgtp_plan(irreps_in1.encode(), irreps_in2.encode(), irreps_out.encode(),
                                ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None, n,
@@ -154,6 +158,10 @@ class Plan:
     @property
     def torch_dtype(self):
         return TORCH_DTYPES[self.dtype]
+
+    @property
+    def weight_dtype(self):
+        return torch.bfloat16 if self.bf16_weights else TORCH_DTYPES[self.dtype]
 
     @property
     def out_dtype(self):
@@ -179,8 +187,8 @@ class Plan:
 
 
 def cgtp_plan(irreps_in1, irreps_in2, irreps_out, paths=None, mode="uvu", dtype="f32",
-              shared_weights=False, no_load=False) -> Plan:
-    return Plan(irreps_in1, irreps_in2, irreps_out, paths, mode, dtype, shared_weights, no_load)
+              shared_weights=False, no_load=False, bf16_weights=False) -> Plan:
+    return Plan(irreps_in1, irreps_in2, irreps_out, paths, mode, dtype, shared_weights, no_load, bf16_weights)
 
 
 # ---------------------------------------------------------------------------
@@ -372,6 +380,7 @@ def standard_plan_args():
         c = W.config(name)
         out.append(dict(irreps_in1=c.irreps_in1, irreps_in2=c.irreps_in2, irreps_out=c.irreps_out,
                         paths=c.paths, mode=c.mode, dtype=c.dtype, shared_weights=c.shared_weights))
+    out.append(dict(out[1], bf16_weights=True))   # the 4096-atom box with bf16 weight storage
     return out
 
 

@@ -167,7 +167,7 @@ int cgtp_plan(const char *irreps_in1, const char *irreps_in2, const char *irreps
     if (mode != CGTP_UVU && mode != CGTP_UVW) return set_error(CGTP_ERR_INVALID_ARGUMENT, "unknown mode");
     if (dtype != CGTP_F32 && dtype != CGTP_F64 && dtype != CGTP_BF16_F32ACC)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "unknown dtype");
-    if (flags & ~(uint32_t)(CGTP_SHARED_WEIGHTS | CGTP_PLAN_NO_LOAD))
+    if (flags & ~(uint32_t)(CGTP_SHARED_WEIGHTS | CGTP_PLAN_NO_LOAD | CGTP_BF16_WEIGHTS))
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "unknown flag bits");
     if (n_paths < 0 || (n_paths > 0 && !paths)) return set_error(CGTP_ERR_INVALID_ARGUMENT, "bad path list");
     try {
@@ -253,6 +253,8 @@ int cgtp_plan(const char *irreps_in1, const char *irreps_in2, const char *irreps
         p.wnumel = woff;
         if (mode == CGTP_UVU && dtype == CGTP_BF16_F32ACC)
             return fail(CGTP_ERR_UNSUPPORTED, "bf16 inputs are provided for uvw plans only");
+        if ((flags & CGTP_BF16_WEIGHTS) && (mode != CGTP_UVU || dtype != CGTP_F32))
+            return fail(CGTP_ERR_UNSUPPORTED, "bf16 weight storage is provided for uvu float plans only");
         if (mode == CGTP_UVW && (dtype != CGTP_BF16_F32ACC || !(flags & CGTP_SHARED_WEIGHTS))) {
             // uvw kernels exist for bf16 operands with one shared weight set
             // (channel mixing on the matrix cores); other uvw plans serve

@@ -86,8 +86,14 @@ typedef enum {
 
 enum {
     CGTP_SHARED_WEIGHTS = 1u << 0, /* one weight row for all items (uvw layers) */
-    CGTP_PLAN_NO_LOAD = 1u << 1    /* generate and compile into the on-disk cache only;
+    CGTP_PLAN_NO_LOAD = 1u << 1,   /* generate and compile into the on-disk cache only;
                                       no device contact; execution calls then fail */
+    CGTP_BF16_WEIGHTS = 1u << 2    /* uvu, CGTP_F32 only: every weight-shaped input (w,
+                                      and gg_w of the double backward) is stored as
+                                      bf16 (the upper half of a float); arithmetic,
+                                      the other inputs and every output, g_w and d_w
+                                      included, stay float.  Halves the dominant
+                                      per-edge stream. */
 };
 
 /* A path couples block i_in1 of input 1 with block i_in2 of input 2 into

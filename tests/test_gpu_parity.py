@@ -165,6 +165,50 @@ def test_conv_double_backward_small(B, torch, dtype, which):
     assert_close(ow.cpu().numpy(), dw[G.perm], dtype, "d_w")
 
 
+@pytest.mark.parametrize("k", range(len(SMALL)))
+def test_conv_bf16_weights_small(B, torch, k):
+    """bf16 weight storage, float arithmetic: the oracle gets the same
+    bf16-rounded weights, so the float tolerance applies."""
+    a, b, c = SMALL[k]
+    paths = None
+    if c is None:
+        c, paths = W.one_block_per_path(a, b, ["0e", "1o", "2e", "3o"])
+    plan = B.Plan(a, b, c, paths, "uvu", "f32", bf16_weights=True)
+    prob = oracle.Problem(a, b, c, "uvu", paths)
+    assert plan.weight_dtype == torch.bfloat16
+    src, dst = _small_graph(61, 700, 40 + k)
+    G = GraphArrays(src, dst, 61)
+    rng = np.random.default_rng(50 + k)
+    x = W.normal(rng, (61, prob.dim1), "f32")
+    sh = W.normal(rng, (G.E, prob.dim2), "f32")
+    w = W.round_to(W.normal(rng, (G.E, prob.weight_numel), "f32"), "bf16")
+    g = W.normal(rng, (61, prob.dim3), "f32")
+    aw = W.round_to(W.normal(rng, w.shape, "f32"), "bf16")
+    ay = W.normal(rng, sh.shape, "f32")
+    d = G.dev(torch)
+    f32 = lambda a: to_dev(torch, a, "f32")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
+    print(f"bf16 weights small k={k}", flush=True)
+    out = B.cgtp_conv_forward(plan, f32(x), f32(sh[G.perm]), bf(w[G.perm]), d["src"], d["dst_row_ptr"])
+    ox, oy, ow = B.cgtp_conv_backward(plan, f32(x), f32(sh[G.perm]), bf(w[G.perm]), d["src"], d["dst"],
+                                      d["dst_row_ptr"], d["src_row_ptr"], d["src_perm"], f32(g))
+    og, dx, dy, dw = B.cgtp_conv_double_backward(
+        plan, f32(x), f32(sh[G.perm]), bf(w[G.perm]), d["src"], d["dst"], d["dst_row_ptr"], d["src_row_ptr"],
+        d["src_perm"], f32(g), None, f32(ay[G.perm]), bf(aw[G.perm]))
+    torch.cuda.synchronize()
+    assert ow.dtype == torch.float32 and dw.dtype == torch.float32
+    assert_close(out.cpu().numpy(), prob.conv_forward(x, sh, w, src, dst, 61), "f32", "forward")
+    gx, gy, gw = prob.conv_backward(x, sh, w, src, dst, g)
+    assert_close(ox.cpu().numpy(), gx, "f32", "g_x")
+    assert_close(oy.cpu().numpy(), gy[G.perm], "f32", "g_sh")
+    assert_close(ow.cpu().numpy(), gw[G.perm], "f32", "g_w")
+    rg, rx, ry, rw = prob.conv_double_backward(x, sh, w, src, dst, g, None, ay, aw)
+    assert_close(og.cpu().numpy(), rg, "f32", "d_g_out")
+    assert_close(dx.cpu().numpy(), rx, "f32", "d_x")
+    assert_close(dy.cpu().numpy(), ry[G.perm], "f32", "d_sh")
+    assert_close(dw.cpu().numpy(), rw[G.perm], "f32", "d_w")
+
+
 def test_conv_no_edges(B, torch):
     plan, prob = _small_problem(B, 0, "f32")
     x = torch.randn(4, prob.dim1, device="cuda")
