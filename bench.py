@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--bf16-weights", action="store_true",
                     help="c2/c4: per-edge weights stored as bf16 (float arithmetic)")
+    ap.add_argument("--all-parity", action="store_true",
+                    help="c2/c3/c4: every output parity for l3 <= 3 (13 / 24 paths, one block per path)")
+    ap.add_argument("--morton", action="store_true",
+                    help="c2/c3/c4: atoms numbered along a Z-order curve of their positions")
     ap.add_argument("--nominal-e", action="store_true",
                     help="c2/c3/c4 graph with cutoff 4.153 A (about 30 neighbours, the nominal edge count)")
     return ap.parse_args()
@@ -212,7 +216,10 @@ def cpu_baseline_single(cfg, x, y, w):
 # ---------------------------------------------------------------------------
 def bench_conv(args, torch, B, W):
     name = args.workload
-    cfg = W.config("c2" if name in ("c4", "c2") else name)
+    base = "c2" if name in ("c4", "c2") else name
+    if (args.all_parity or args.morton) and name not in ("c2", "c3", "c4"):
+        raise SystemExit("--all-parity and --morton apply to the c2, c3 and c4 workloads")
+    cfg = W.config(base + ("a" if args.all_parity else ""))
     full = name == "c4"
     dtype = cfg.dtype
     rng = np.random.default_rng(args.seed)
@@ -220,7 +227,7 @@ def bench_conv(args, torch, B, W):
         g = W.molecule_batch(cfg.extra["n_graphs"], cfg.extra["n_atoms"], cutoff=cfg.extra["cutoff"], rng=rng)
     else:
         cut = NOMINAL_CUTOFF if args.nominal_e else cfg.extra["cutoff"]
-        g = W.periodic_graph(cfg.extra["n_atoms"], cutoff=cut, rng=rng)
+        g = W.periodic_graph(cfg.extra["n_atoms"], cutoff=cut, rng=rng, morton=args.morton)
     bf16w = bool(args.bf16_weights)
     if bf16w and name not in ("c2", "c4"):
         raise SystemExit("--bf16-weights applies to the c2 and c4 workloads")
@@ -255,6 +262,8 @@ def bench_conv(args, torch, B, W):
     src_perm = torch.empty(E, dtype=torch.int32, device=dev)
     src_rp = torch.empty(N + 1, dtype=torch.int32, device=dev)
     csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), dev)
+    order = torch.empty(N, dtype=torch.int32, device=dev)
+    ord_ws = B.workspace(4096 * 4, dev)
     sh = torch.empty(E, plan.dim_in2, dtype=td, device=dev)
     out = torch.empty(N, plan.dim_out, dtype=od, device=dev)
     nb_f = B.cgtp_forward_workspace_bytes(plan, N)
@@ -278,19 +287,20 @@ def bench_conv(args, torch, B, W):
         run = timer.run if timed else (lambda name_, fn: fn())
         run("csr", lambda: (B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s)),
                             B.cgtp_build_csr(src_s, N, sorted_key=False, ws=csr_ws,
-                                             out=(src_perm, src_rp, None, None))))
+                                             out=(src_perm, src_rp, None, None)),
+                            B.cgtp_node_order(rp, ws=ord_ws, out=order)))
         run("sh", lambda: B.cgtp_spherical_harmonics(lmax, vec, perm, dtype, out=sh))
-        run("conv_fwd", lambda: B.cgtp_conv_forward(plan, x, sh, w, src_s, rp, out=out, ws=f_ws))
+        run("conv_fwd", lambda: B.cgtp_conv_forward(plan, x, sh, w, src_s, rp, out=out, ws=f_ws, node_order=order))
         if not full:
             return
         run("conv_bwd", lambda: B.cgtp_conv_backward(plan, x, sh, w, src_s, dst_s, rp, src_rp, src_perm, g_out,
-                                                     ws=ws, out=(g_x, g_sh, g_w)))
+                                                     ws=ws, out=(g_x, g_sh, g_w), node_order=order))
         run("forces", lambda: B.cgtp_sh_forces(lmax, vec, perm, g_sh, rp, src_rp, src_perm, dtype, ws=fo_ws,
                                                out=F))
         run("force_cot", lambda: B.cgtp_force_loss_sh_cotangent(lmax, vec, perm, src_s, dst_s, F, dtype, out=gg))
         run("double_bwd", lambda: B.cgtp_conv_double_backward(plan, x, sh, w, src_s, dst_s, rp, src_rp, src_perm,
                                                               g_out, None, gg, None, ws=ws,
-                                                              out=(d_g, d_x, None, d_w)))
+                                                              out=(d_g, d_x, None, d_w), node_order=order))
 
     for _ in range(args.warmup):
         step(False)
@@ -333,6 +343,8 @@ def bench_conv(args, torch, B, W):
     if full:
         alg["cgtp_bwd"] = N * (d1 + d3) * eb + E * 2 * d2 * eb + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
         alg["cgtp_dbl"] = N * (d1 + 2 * d3) * eb + E * d2 * eb + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
+        # the same kernels with the full call's flags folded in
+        alg["cgtp_bwd_full"], alg["cgtp_dbl_full"] = alg["cgtp_bwd"], alg["cgtp_dbl"]
     kern = {}
     for k, v in launches.items():
         kern[k] = dict(v)
@@ -378,7 +390,9 @@ def bench_conv(args, torch, B, W):
         "data": "synthetic",
         "config": {"workload": (W.config("c4").name if full else cfg.name) +
                    (f", cutoff {NOMINAL_CUTOFF} A" if args.nominal_e and name != "c5" else "") +
-                   (", bf16 weight storage" if bf16w else ""),
+                   (", bf16 weight storage" if bf16w else "") +
+                   (", all output parities" if args.all_parity and full else "") +
+                   (", Morton node order" if args.morton else ""),
                    "n_atoms": N, "n_edges": E,
                    "irreps_node": cfg.irreps_in1, "irreps_sh": cfg.irreps_in2, "irreps_out": cfg.irreps_out,
                    "n_paths": plan.n_paths,

@@ -47,7 +47,7 @@ EXPORTS = [
     "cgtp_plan_destroy", "cgtp_forward_workspace_bytes", "cgtp_forward", "cgtp_conv_forward",
     "cgtp_conv_workspace_bytes",
     "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_csr_workspace_bytes", "cgtp_build_csr",
-    "cgtp_validate_csr", "cgtp_spherical_harmonics", "cgtp_forces_workspace_bytes", "cgtp_sh_forces",
+    "cgtp_validate_csr", "cgtp_node_order_workspace_bytes", "cgtp_node_order", "cgtp_spherical_harmonics", "cgtp_forces_workspace_bytes", "cgtp_sh_forces",
     "cgtp_force_loss_sh_cotangent", "cgtp_timing_enable", "cgtp_timing_collect", "cgtp_last_error",
     "cgtp_version",
 ]
@@ -71,11 +71,13 @@ def lib():
             "cgtp_plan_source": [vp, vp, i64, vp],
             "cgtp_forward_workspace_bytes": [vp, i64, vp],
             "cgtp_forward": [vp, vp, vp, vp, i64, vp, vp, sz, vp],
-            "cgtp_conv_forward": [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
+            "cgtp_conv_forward": [vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
             "cgtp_conv_workspace_bytes": [vp, i64, i64, vp],
-            "cgtp_conv_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, sz, vp],
-            "cgtp_conv_double_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+            "cgtp_conv_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, sz, vp],
+            "cgtp_conv_double_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
                                           vp, vp, vp, vp, vp, sz, vp],
+            "cgtp_node_order_workspace_bytes": [i64, vp],
+            "cgtp_node_order": [vp, i64, vp, vp, sz, vp],
             "cgtp_csr_workspace_bytes": [i64, i64, vp],
             "cgtp_build_csr": [vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
             "cgtp_validate_csr": [vp, i64, i64, vp, i64, vp, vp],
@@ -212,7 +214,7 @@ def cgtp_forward(plan: Plan, x, y, w, out=None, ws=None, stream=None):
     return out
 
 
-def cgtp_conv_forward(plan: Plan, x, sh, w, src, dst_row_ptr, out=None, ws=None, stream=None):
+def cgtp_conv_forward(plan: Plan, x, sh, w, src, dst_row_ptr, out=None, ws=None, stream=None, node_order=None):
     N, E = x.shape[0], src.shape[0]
     if out is None:
         out = torch.empty(N, plan.dim_out, dtype=plan.out_dtype, device=x.device)
@@ -220,7 +222,7 @@ def cgtp_conv_forward(plan: Plan, x, sh, w, src, dst_row_ptr, out=None, ws=None,
     if ws is None and nb:
         ws = workspace(nb, x.device)
     _check(lib().cgtp_conv_forward(plan.handle, _ptr(x), _ptr(sh), _ptr(w), _ptr(src), _ptr(dst_row_ptr),
-                                   N, E, _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
+                                   _ptr(node_order), N, E, _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
                                    _stream(stream, x)))
     return out
 
@@ -237,7 +239,7 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def cgtp_conv_backward(plan: Plan, x, sh, w, src, dst, dst_row_ptr, src_row_ptr, src_perm, g_out,
-                       need=("x", "sh", "w"), ws=None, out=None, stream=None):
+                       need=("x", "sh", "w"), ws=None, out=None, stream=None, node_order=None):
     N, E = x.shape[0], src.shape[0]
     dev = x.device
     od = plan.out_dtype
@@ -250,15 +252,15 @@ def cgtp_conv_backward(plan: Plan, x, sh, w, src, dst, dst_row_ptr, src_row_ptr,
     if ws is None:
         ws = workspace(nb, dev)
     _check(lib().cgtp_conv_backward(plan.handle, _ptr(x), _ptr(sh), _ptr(w), _ptr(src), _ptr(dst),
-                                    _ptr(dst_row_ptr), _ptr(src_row_ptr), _ptr(src_perm), _ptr(g_out),
-                                    N, E, _ptr(g_x), _ptr(g_sh), _ptr(g_w), _ptr(ws), ws.numel(),
+                                    _ptr(dst_row_ptr), _ptr(node_order), _ptr(src_row_ptr), _ptr(src_perm),
+                                    _ptr(g_out), N, E, _ptr(g_x), _ptr(g_sh), _ptr(g_w), _ptr(ws), ws.numel(),
                                     _stream(stream, x)))
     return g_x, g_sh, g_w
 
 
 def cgtp_conv_double_backward(plan: Plan, x, sh, w, src, dst, dst_row_ptr, src_row_ptr, src_perm, g_out,
                               gg_x=None, gg_sh=None, gg_w=None, need=("g_out", "x", "sh", "w"), ws=None,
-                              out=None, stream=None):
+                              out=None, stream=None, node_order=None):
     N, E = x.shape[0], src.shape[0]
     dev = x.device
     od = plan.out_dtype
@@ -273,10 +275,23 @@ def cgtp_conv_double_backward(plan: Plan, x, sh, w, src, dst, dst_row_ptr, src_r
     if ws is None:
         ws = workspace(nb, dev)
     _check(lib().cgtp_conv_double_backward(plan.handle, _ptr(x), _ptr(sh), _ptr(w), _ptr(src), _ptr(dst),
-                                           _ptr(dst_row_ptr), _ptr(src_row_ptr), _ptr(src_perm), _ptr(g_out),
-                                           _ptr(gg_x), _ptr(gg_sh), _ptr(gg_w), N, E, _ptr(d_g), _ptr(d_x),
+                                           _ptr(dst_row_ptr), _ptr(node_order), _ptr(src_row_ptr),
+                                           _ptr(src_perm), _ptr(g_out), _ptr(gg_x), _ptr(gg_sh), _ptr(gg_w), N, E, _ptr(d_g), _ptr(d_x),
                                            _ptr(d_sh), _ptr(d_w), _ptr(ws), ws.numel(), _stream(stream, x)))
     return d_g, d_x, d_sh, d_w
+
+
+def cgtp_node_order(row_ptr, ws=None, out=None, stream=None):
+    """Rows of a CSR by decreasing length (processing order for the
+    convolution calls)."""
+    n = row_ptr.shape[0] - 1
+    order = torch.empty(n, dtype=torch.int32, device=row_ptr.device) if out is None else out
+    b = ctypes.c_size_t()
+    _check(lib().cgtp_node_order_workspace_bytes(n, ctypes.byref(b)))
+    if ws is None:
+        ws = workspace(b.value, row_ptr.device)
+    _check(lib().cgtp_node_order(_ptr(row_ptr), n, _ptr(order), _ptr(ws), ws.numel(), _stream(stream, row_ptr)))
+    return order
 
 
 def cgtp_csr_workspace_bytes(n_edges: int, n_keys: int) -> int:

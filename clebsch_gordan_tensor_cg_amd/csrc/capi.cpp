@@ -68,14 +68,15 @@ bool blocks_covered(const std::vector<Irrep> &irreps, const std::vector<Path> &p
 // forward launch with an explicit operand set (used by the forward and by
 // the double backward's substituted calls)
 int run_fwd(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
-            const int32_t *row_ptr, int64_t n_items, int graph, void *out, int accumulate, hipStream_t s) {
+            const int32_t *row_ptr, const int32_t *order, int64_t n_items, int graph, void *out, int accumulate,
+            hipStream_t s) {
     if (!accumulate && !blocks_covered(p.out, p.paths, true)) {
         int rc = launch_zero(p.dtype == CGTP_F64 ? CGTP_F64 : CGTP_F32, out, n_items * p.dim3, s);
         if (rc) return rc;
         accumulate = 1;
     }
     long long n = n_items;
-    void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr,
+    void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&order,
                     (void *)&out, &n, &graph, &accumulate};
     const int64_t ipw = p.fwd.items_per_wave;
     return launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
@@ -103,8 +104,8 @@ int32_t *ws_mrow(const Plan &p, char *ws, int64_t n_edges) {
 }
 
 int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
-            const int32_t *row_ptr, const void *g_out, int64_t n_nodes, int64_t n_edges, BwdOut o,
-            char *ws, hipStream_t s) {
+            const int32_t *row_ptr, const int32_t *order, const void *g_out, int64_t n_nodes, int64_t n_edges,
+            BwdOut o, char *ws, hipStream_t s) {
     void *m = ws;
     char *parts = ws_parts(p, ws, n_edges);
     const int32_t *mrow = ws_mrow(p, ws, n_edges);
@@ -131,12 +132,14 @@ int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const in
     void *gw = o.g_w;
     long long n = n_nodes, ne = n_edges;
     int graph = 1;
-    void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&g_out,
-                    &gw, &m, &third, (void *)&mrow, &n, &ne, &graph, &flags};
+    void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&order,
+                    (void *)&g_out, &gw, &m, &third, (void *)&mrow, &n, &ne, &graph, &flags};
     const int64_t ipw = ks.items_per_wave;
-    hipFunction_t f = fused ? ((p.tune.full & 2) && flags == dbl_full_flags(p) ? p.k_dbl_full : p.k_dbl)
-                            : ((p.tune.full & 1) && flags == bwd_full_flags(p) ? p.k_bwd_full : p.k_bwd);
-    int rc = launch(f, fused ? "cgtp_dbl" : "cgtp_bwd", (n_nodes + ipw - 1) / ipw * ks.n_units, s, args);
+    const bool full = fused ? ((p.tune.full & 2) && flags == dbl_full_flags(p))
+                            : ((p.tune.full & 1) && flags == bwd_full_flags(p));
+    hipFunction_t f = fused ? (full ? p.k_dbl_full : p.k_dbl) : (full ? p.k_bwd_full : p.k_bwd);
+    const char *name = fused ? (full ? "cgtp_dbl_full" : "cgtp_dbl") : (full ? "cgtp_bwd_full" : "cgtp_bwd");
+    int rc = launch(f, name, (n_nodes + ipw - 1) / ipw * ks.n_units, s, args);
     if (rc) return rc;
     if (use_parts) rc = launch_sum_parts(p.dtype, parts, ks.n_units, n_edges * p.dim2, o.g_y, o.acc_y, s);
     return rc;
@@ -329,13 +332,13 @@ void cgtp_plan_destroy(cgtp_plan_t plan) {
 }
 
 static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
-                   const int32_t *row_ptr, int64_t n_items, int graph, void *out, void *ws, size_t ws_bytes,
-                   hipStream_t s) {
+                   const int32_t *row_ptr, const int32_t *order, int64_t n_items, int graph, void *out, void *ws,
+                   size_t ws_bytes, hipStream_t s) {
     size_t need = align256((size_t)n_items * p.t_per_item * 2);
     if (ws_bytes < need || (!ws && need)) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace too small");
     if (((uintptr_t)ws) & 255) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     long long n = n_items;
-    void *args[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, &ws, &n, &graph};
+    void *args[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, (void *)&order, &ws, &n, &graph};
     const int64_t ipw = p.fwd.items_per_wave;
     int rc = launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
     if (rc) return rc;
@@ -366,14 +369,14 @@ int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, 
     if (batch == 0) return CGTP_OK;
     if (!x || !y || !w || !out) return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
     if (plan->p.mode == CGTP_UVW)
-        return run_uvw(plan->p, x, y, w, nullptr, nullptr, batch, 0, out, workspace, workspace_bytes,
+        return run_uvw(plan->p, x, y, w, nullptr, nullptr, nullptr, batch, 0, out, workspace, workspace_bytes,
                        (hipStream_t)stream);
-    return run_fwd(plan->p, x, y, w, nullptr, nullptr, batch, 0, out, 0, (hipStream_t)stream);
+    return run_fwd(plan->p, x, y, w, nullptr, nullptr, nullptr, batch, 0, out, 0, (hipStream_t)stream);
 }
 
 int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
-                      const int32_t *dst_row_ptr, int64_t n_nodes, int64_t n_edges, void *out, void *workspace,
-                      size_t workspace_bytes, cgtp_stream_t stream) {
+                      const int32_t *dst_row_ptr, const int32_t *node_order, int64_t n_nodes, int64_t n_edges,
+                      void *out, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
     clear_error();
     int rc = check_loaded(plan);
     if (rc) return rc;
@@ -383,9 +386,9 @@ int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const voi
     if (!dst_row_ptr || !out || (n_edges > 0 && (!x || !sh || !w || !src)))
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
     if (plan->p.mode == CGTP_UVW)
-        return run_uvw(plan->p, x, sh, w, src, dst_row_ptr, n_nodes, 1, out, workspace, workspace_bytes,
-                       (hipStream_t)stream);
-    return run_fwd(plan->p, x, sh, w, src, dst_row_ptr, n_nodes, 1, out, 0, (hipStream_t)stream);
+        return run_uvw(plan->p, x, sh, w, src, dst_row_ptr, node_order, n_nodes, 1, out, workspace,
+                       workspace_bytes, (hipStream_t)stream);
+    return run_fwd(plan->p, x, sh, w, src, dst_row_ptr, node_order, n_nodes, 1, out, 0, (hipStream_t)stream);
 }
 
 int cgtp_conv_workspace_bytes(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, size_t *bytes) {
@@ -416,9 +419,10 @@ static int check_graph_args(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
 }
 
 int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
-                       const int32_t *dst, const int32_t *dst_row_ptr, const int32_t *src_row_ptr,
-                       const int32_t *src_perm, const void *g_out, int64_t n_nodes, int64_t n_edges, void *g_x,
-                       void *g_sh, void *g_w, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
+                       const int32_t *dst, const int32_t *dst_row_ptr, const int32_t *node_order,
+                       const int32_t *src_row_ptr, const int32_t *src_perm, const void *g_out, int64_t n_nodes,
+                       int64_t n_edges, void *g_x, void *g_sh, void *g_w, void *workspace, size_t workspace_bytes,
+                       cgtp_stream_t stream) {
     clear_error();
     (void)dst;
     int rc = check_graph_args(plan, n_nodes, n_edges, workspace, workspace_bytes);
@@ -438,15 +442,16 @@ int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const vo
     o.g_w = g_w;
     o.want_m = g_x != nullptr;
     o.g_y = g_sh;
-    rc = run_bwd(p, x, sh, w, src, dst_row_ptr, g_out, n_nodes, n_edges, o, (char *)workspace, s);
+    rc = run_bwd(p, x, sh, w, src, dst_row_ptr, node_order, g_out, n_nodes, n_edges, o, (char *)workspace, s);
     if (rc) return rc;
     if (g_x) rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, nullptr, n_nodes, p.dim1, g_x, 0, s);
     return rc;
 }
 
 int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
-                              const int32_t *dst, const int32_t *dst_row_ptr, const int32_t *src_row_ptr,
-                              const int32_t *src_perm, const void *g_out, const void *gg_x, const void *gg_sh,
+                              const int32_t *dst, const int32_t *dst_row_ptr, const int32_t *node_order,
+                              const int32_t *src_row_ptr, const int32_t *src_perm, const void *g_out,
+                              const void *gg_x, const void *gg_sh,
                               const void *gg_w, int64_t n_nodes, int64_t n_edges, void *d_g_out, void *d_x,
                               void *d_sh, void *d_w, void *workspace, size_t workspace_bytes,
                               cgtp_stream_t stream) {
@@ -476,7 +481,9 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
             o.acc_m = wrote_m;
             o.g_w = d_w;
             o.acc_w = wrote_w;
-            if ((rc = run_bwd(p, x, gg_sh, w, src, dst_row_ptr, g_out, n_nodes, E, o, (char *)workspace, s))) return rc;
+            if ((rc = run_bwd(p, x, gg_sh, w, src, dst_row_ptr, node_order, g_out, n_nodes, E, o, (char *)workspace,
+                              s)))
+                return rc;
             wrote_g |= d_g_out != nullptr;
             wrote_m |= d_x != nullptr;
             wrote_w |= d_w != nullptr;
@@ -484,7 +491,8 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
         // x term: d_g_out += f(gg_x, sh, w), d_sh += fsh*(g; gg_x, w), d_w += fw*(g; gg_x, sh)
         if (gg_x) {
             if (d_g_out) {
-                if ((rc = run_fwd(p, gg_x, sh, w, src, dst_row_ptr, n_nodes, 1, d_g_out, wrote_g, s))) return rc;
+                if ((rc = run_fwd(p, gg_x, sh, w, src, dst_row_ptr, node_order, n_nodes, 1, d_g_out, wrote_g, s)))
+                    return rc;
                 wrote_g = true;
             }
             if (d_sh || d_w) {
@@ -493,7 +501,8 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
                 o.acc_y = wrote_sh;
                 o.g_w = d_w;
                 o.acc_w = wrote_w;
-                if ((rc = run_bwd(p, gg_x, sh, w, src, dst_row_ptr, g_out, n_nodes, E, o, (char *)workspace, s)))
+                if ((rc = run_bwd(p, gg_x, sh, w, src, dst_row_ptr, node_order, g_out, n_nodes, E, o,
+                                  (char *)workspace, s)))
                     return rc;
                 wrote_sh |= d_sh != nullptr;
                 wrote_w |= d_w != nullptr;
@@ -502,7 +511,8 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
         // w term: d_g_out += f(x, sh, gg_w), d_x += fx*(g; sh, gg_w), d_sh += fsh*(g; x, gg_w)
         if (gg_w) {
             if (d_g_out) {
-                if ((rc = run_fwd(p, x, sh, gg_w, src, dst_row_ptr, n_nodes, 1, d_g_out, wrote_g, s))) return rc;
+                if ((rc = run_fwd(p, x, sh, gg_w, src, dst_row_ptr, node_order, n_nodes, 1, d_g_out, wrote_g, s)))
+                    return rc;
                 wrote_g = true;
             }
             if (d_x || d_sh) {
@@ -511,7 +521,8 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
                 o.acc_m = wrote_m;
                 o.g_y = d_sh;
                 o.acc_y = wrote_sh;
-                if ((rc = run_bwd(p, x, sh, gg_w, src, dst_row_ptr, g_out, n_nodes, E, o, (char *)workspace, s)))
+                if ((rc = run_bwd(p, x, sh, gg_w, src, dst_row_ptr, node_order, g_out, n_nodes, E, o,
+                                  (char *)workspace, s)))
                     return rc;
                 wrote_m |= d_x != nullptr;
                 wrote_sh |= d_sh != nullptr;

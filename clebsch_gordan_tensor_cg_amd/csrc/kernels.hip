@@ -139,6 +139,23 @@ __global__ void k_invert_perm(const int32_t *__restrict__ perm, int64_t n, int32
 constexpr int kCsrBins = 16384;  // 64 KiB of LDS counters per workgroup
 constexpr int kCsrThreads = 1024;
 
+// Visits the keys of edges [e0, e1) owned by this thread, eight loads in
+// flight at a time; a slot past e1 sees key -1 (skipped by every caller).
+template <class F>
+__device__ __forceinline__ void for_block_keys(const int32_t *__restrict__ key, int64_t e0, int64_t e1, F f) {
+    constexpr int U = 8;
+    for (int64_t base = e0 + threadIdx.x; base < e1; base += (int64_t)U * blockDim.x) {
+        int32_t k[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e = base + (int64_t)u * blockDim.x;
+            k[u] = e < e1 ? key[e] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) f(base + (int64_t)u * blockDim.x, k[u]);
+    }
+}
+
 __global__ void __launch_bounds__(kCsrThreads) k_count(const int32_t *__restrict__ key, int64_t n, int64_t n_keys,
                                                        int64_t per, int32_t *__restrict__ cnt) {
     extern __shared__ int32_t h[];
@@ -147,10 +164,10 @@ __global__ void __launch_bounds__(kCsrThreads) k_count(const int32_t *__restrict
     const int64_t e0 = (int64_t)blockIdx.x * per, e1 = std::min<int64_t>(n, e0 + per);
     for (int i = threadIdx.x; i < kb; i += blockDim.x) h[i] = 0;
     __syncthreads();
-    for (int64_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
-        const int64_t k = key[e] - k0;
-        if (k >= 0 && k < kb) atomicAdd(&h[k], 1);
-    }
+    for_block_keys(key, e0, e1, [&](int64_t, int32_t kk) {
+        const int64_t k = kk - k0;
+        if (kk >= 0 && k >= 0 && k < kb) atomicAdd(&h[k], 1);
+    });
     __syncthreads();
     for (int i = threadIdx.x; i < kb; i += blockDim.x)
         if (h[i]) atomicAdd(&cnt[k0 + i], h[i]);
@@ -169,20 +186,31 @@ __global__ void __launch_bounds__(kCsrThreads) k_scatter(const int32_t *__restri
     const int64_t e0 = (int64_t)blockIdx.x * per, e1 = std::min<int64_t>(n, e0 + per);
     for (int i = threadIdx.x; i < kb; i += blockDim.x) h[i] = 0;
     __syncthreads();
-    for (int64_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
-        const int64_t k = key[e] - k0;
-        if (k >= 0 && k < kb) atomicAdd(&h[k], 1);
+    for_block_keys(key, e0, e1, [&](int64_t, int32_t kk) {
+        const int64_t k = kk - k0;
+        if (kk >= 0 && k >= 0 && k < kb) atomicAdd(&h[k], 1);
+    });
+    __syncthreads();
+    // reservations: up to four device atomics of a thread in flight together
+    for (int i0 = threadIdx.x; i0 < kb; i0 += 4 * blockDim.x) {
+        int c[4], r[4], b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * (int)blockDim.x;
+            c[u] = i < kb ? h[i] : 0;
+            b[u] = c[u] ? row_ptr[k0 + i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = c[u] ? atomicAdd(&cursor[k0 + i0 + u * (int)blockDim.x], c[u]) : 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (c[u]) h[i0 + u * (int)blockDim.x] = b[u] + r[u];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kb; i += blockDim.x) {
-        const int c = h[i];
-        if (c) h[i] = row_ptr[k0 + i] + atomicAdd(&cursor[k0 + i], c);
-    }
-    __syncthreads();
-    for (int64_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
-        const int64_t k = key[e] - k0;
-        if (k >= 0 && k < kb) tmp[atomicAdd(&h[k], 1)] = (int32_t)e;
-    }
+    for_block_keys(key, e0, e1, [&](int64_t e, int32_t kk) {
+        const int64_t k = kk - k0;
+        if (kk >= 0 && k >= 0 && k < kb) tmp[atomicAdd(&h[k], 1)] = (int32_t)e;
+    });
 }
 
 // Key spaces too wide for a few LDS ranges: one device atomic per edge.
@@ -200,6 +228,83 @@ __global__ void k_scatter_global(const int32_t *__restrict__ key, int64_t n, int
         const int32_t k = key[e];
         if (k >= 0 && k < n_keys) tmp[row_ptr[k] + atomicAdd(&cursor[k], 1)] = (int32_t)e;
     }
+}
+
+// Node processing order: nodes by decreasing segment length (longest
+// first, so the long segments do not form the tail of a launch).  Buckets
+// are kOrderBuckets-1-min(len, kOrderBuckets-1); the order within a bucket
+// is whatever the atomics give, which changes no result (each node is
+// computed by one wavefront in its fixed edge order).
+constexpr int kOrderBuckets = 1024;
+__device__ __forceinline__ int order_bucket(const int32_t *__restrict__ rp, int64_t i) {
+    const int len = rp[i + 1] - rp[i];
+    return kOrderBuckets - 1 - (len < kOrderBuckets - 1 ? (len < 0 ? 0 : len) : kOrderBuckets - 1);
+}
+
+// The whole order in one workgroup (small graphs): count, scan and place
+// in LDS.
+__global__ void __launch_bounds__(1024) k_order_small(const int32_t *__restrict__ rp, int64_t n,
+                                                       int32_t *__restrict__ order) {
+    __shared__ int32_t h[kOrderBuckets];
+    __shared__ int32_t wsum[16];
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    h[t] = 0;
+    __syncthreads();
+    for (int64_t i = t; i < n; i += 1024) atomicAdd(&h[order_bucket(rp, i)], 1);
+    __syncthreads();
+    // exclusive scan of the 1024 bucket counts, one per thread
+    const int32_t own = h[t];
+    int32_t incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    if (wid == 0) {
+        int32_t ws = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int32_t v = __shfl_up(ws, off, 64);
+            if (lane >= off) ws += v;
+        }
+        if (lane < 16) wsum[lane] = ws;
+    }
+    __syncthreads();
+    h[t] = (wid ? wsum[wid - 1] : 0) + incl - own;
+    __syncthreads();
+    for (int64_t i = t; i < n; i += 1024) order[atomicAdd(&h[order_bucket(rp, i)], 1)] = (int32_t)i;
+}
+
+__global__ void __launch_bounds__(1024) k_order_count(const int32_t *__restrict__ rp, int64_t n,
+                                                       int32_t *__restrict__ cnt) {
+    __shared__ int32_t h[kOrderBuckets];
+    for (int i = threadIdx.x; i < kOrderBuckets; i += blockDim.x) h[i] = 0;
+    __syncthreads();
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        atomicAdd(&h[order_bucket(rp, i)], 1);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kOrderBuckets; i += blockDim.x)
+        if (h[i]) atomicAdd(&cnt[i], h[i]);
+}
+
+__global__ void __launch_bounds__(1024) k_order_scatter(const int32_t *__restrict__ rp, int64_t n,
+                                                         const int32_t *__restrict__ start,
+                                                         int32_t *__restrict__ cursor, int32_t *__restrict__ order) {
+    __shared__ int32_t h[kOrderBuckets];
+    for (int i = threadIdx.x; i < kOrderBuckets; i += blockDim.x) h[i] = 0;
+    __syncthreads();
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    for (int64_t i = i0; i < n; i += stride) atomicAdd(&h[order_bucket(rp, i)], 1);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kOrderBuckets; i += blockDim.x) {
+        const int c = h[i];
+        if (c) h[i] = start[i] + atomicAdd(&cursor[i], c);
+    }
+    __syncthreads();
+    for (int64_t i = i0; i < n; i += stride) order[atomicAdd(&h[order_bucket(rp, i)], 1)] = (int32_t)i;
 }
 
 // Exclusive scan of cnt[0..n) into row_ptr[0..n]; one workgroup, four
@@ -845,6 +950,42 @@ int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int6
         CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(grid_for(n_keys + 1)), dim3(kBlock), 0, s, row_ptr, n_keys + 1, 0);
     }
     return hip_check(hipGetLastError(), "cgtp_build_csr launch");
+}
+
+int cgtp_node_order_workspace_bytes(int64_t n_nodes, size_t *bytes) {
+    clear_error();
+    if (!bytes || n_nodes < 0) return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_node_order_workspace_bytes: bad argument");
+    *bytes = 3 * align256(sizeof(int32_t) * (kOrderBuckets + 1));
+    return CGTP_OK;
+}
+
+int cgtp_node_order(const int32_t *row_ptr, int64_t n_nodes, int32_t *order, void *workspace, size_t workspace_bytes,
+                    cgtp_stream_t stream) {
+    clear_error();
+    hipStream_t s = (hipStream_t)stream;
+    size_t need = 0;
+    cgtp_node_order_workspace_bytes(n_nodes, &need);
+    if (n_nodes < 0 || n_nodes > 0x7ffffffe) return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_node_order: n_nodes out of range");
+    if (n_nodes == 0) return CGTP_OK;
+    if (!row_ptr || !order || !workspace || workspace_bytes < need)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_node_order: NULL pointer or workspace too small");
+    if (n_nodes <= 65536) {
+        CGTP_LAUNCH("k_order_small", s, k_order_small, dim3(1), dim3(1024), 0, s, row_ptr, n_nodes, order);
+        return hip_check(hipGetLastError(), "cgtp_node_order launch");
+    }
+    const size_t part = align256(sizeof(int32_t) * (kOrderBuckets + 1));
+    int32_t *cnt = (int32_t *)workspace;
+    int32_t *cursor = (int32_t *)((char *)workspace + part);
+    int32_t *start = (int32_t *)((char *)workspace + 2 * part);
+    const int64_t n_clear = 2 * (int64_t)(part / sizeof(int32_t));
+    CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(grid_for(n_clear)), dim3(kBlock), 0, s, cnt, n_clear, 0);
+    // a few workgroups: each publishes at most kOrderBuckets counts
+    const unsigned g = (unsigned)std::min<int64_t>(64, (n_nodes + 4095) / 4096);
+    CGTP_LAUNCH("k_order_count", s, k_order_count, dim3(g), dim3(1024), 0, s, row_ptr, n_nodes, cnt);
+    CGTP_LAUNCH("k_scan", s, k_scan, dim3(1), dim3(1024), 0, s, cnt, (int64_t)kOrderBuckets, start);
+    CGTP_LAUNCH("k_order_scatter", s, k_order_scatter, dim3(g), dim3(1024), 0, s, row_ptr, n_nodes, start, cursor,
+                order);
+    return hip_check(hipGetLastError(), "cgtp_node_order launch");
 }
 
 int cgtp_validate_csr(const int32_t *row_ptr, int64_t n_rows, int64_t n_edges, const int32_t *idx,

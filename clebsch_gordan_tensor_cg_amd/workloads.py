@@ -47,14 +47,30 @@ def _canonical(src, dst, vec):
     return (src[order].astype(np.int32), dst[order].astype(np.int32), vec[order])
 
 
+def morton_order(pos: np.ndarray, box: float, bits: int = 10) -> np.ndarray:
+    """Permutation of the atoms along a Z-order (Morton) curve of their
+    positions in a cube of side `box`: interleaved bits of the quantised
+    x, y, z coordinates, ties by atom index."""
+    q = np.clip((pos / box * (1 << bits)).astype(np.int64), 0, (1 << bits) - 1)
+    code = np.zeros(len(pos), dtype=np.int64)
+    for b in range(bits):
+        for axis in range(3):
+            code |= ((q[:, axis] >> b) & 1) << (3 * b + axis)
+    return np.lexsort((np.arange(len(pos)), code))
+
+
 def periodic_graph(n_atoms: int, density: float = WATER_DENSITY, cutoff: float = 5.0,
-                   seed: int = 0, rng: np.random.Generator | None = None) -> Graph:
-    """Atoms uniform in a periodic cube; directed minimum-image pairs < cutoff."""
+                   seed: int = 0, rng: np.random.Generator | None = None, morton: bool = False) -> Graph:
+    """Atoms uniform in a periodic cube; directed minimum-image pairs < cutoff.
+    morton=True numbers the atoms along a Z-order curve of their positions
+    (same draws, same pairs; only the node ids change)."""
     from scipy.spatial import cKDTree
 
     rng = np.random.default_rng(seed) if rng is None else rng
     L = (n_atoms / density) ** (1.0 / 3.0)
     pos = rng.uniform(0.0, L, size=(n_atoms, 3))
+    if morton:
+        pos = pos[morton_order(pos, L)]
     if cutoff >= L / 2:
         raise ValueError("cutoff must be below half the box for minimum image")
     tree = cKDTree(pos, boxsize=L)
@@ -181,6 +197,9 @@ class TPConfig:
     extra: dict = field(default_factory=dict)
 
 
+ALL_PARITY_TARGETS = ["0e", "0o", "1e", "1o", "2e", "2o", "3e", "3o"]
+
+
 def config(name: str) -> TPConfig:
     """The five workloads; sizes and inputs are drawn by `make_*` below."""
     mace_targets = ["0e", "1o", "2e", "3o"]
@@ -200,6 +219,13 @@ def config(name: str) -> TPConfig:
         out, paths = one_block_per_path(x, sh_irreps(3), mace_targets)
         return TPConfig("MACE-like fused conv fwd fp64, 16384 atoms", x, sh_irreps(3), out,
                         "uvu", "f64", paths, extra=dict(n_atoms=16384, cutoff=5.0, lmax=3))
+    if name in ("c2a", "c3a"):
+        # every output parity for l3 <= 3: 13 paths (c2a, dim 7040) and 24
+        # paths (c3a), one 128-channel block per path
+        base = config(name[:2])
+        out, paths = one_block_per_path(base.irreps_in1, base.irreps_in2, ALL_PARITY_TARGETS)
+        return TPConfig(base.name + ", all output parities", base.irreps_in1, base.irreps_in2, out, "uvu",
+                        base.dtype, paths, extra=dict(base.extra))
     if name == "c5":
         return TPConfig("TFN-like uvw conv bf16-in fp32-acc, 100 x 18-atom graphs",
                         "32x0+32x1+32x2+32x3", sh_irreps(6, parity=False),

@@ -173,13 +173,18 @@ int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, 
  * Each destination row is reduced by one workgroup and written once; no   */
 /* atomics.  src values must lie in [0, n_nodes) and row_ptr must be a      */
 /* monotone CSR with row_ptr[0] = 0, row_ptr[n_nodes] = n_edges; check     */
-/* untrusted input with cgtp_validate_csr first.  workspace:               */
-/* cgtp_forward_workspace_bytes(n_nodes) (may be NULL for uvu plans).       */
+/* untrusted input with cgtp_validate_csr first.  node_order [n_nodes]     */
+/* (may be NULL: natural order) is the order in which destination rows     */
+/* are handed to the device, a permutation of 0..n_nodes-1, normally from  */
+/* cgtp_node_order; it changes timing only, never a result (an entry out   */
+/* of range leaves its slot idle, so a node missing from it is not         */
+/* written).  workspace: cgtp_forward_workspace_bytes(n_nodes) (may be     */
+/* NULL for uvu plans).                                                     */
 /* ---------------------------------------------------------------------- */
 int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
-                      const int32_t *src, const int32_t *dst_row_ptr, int64_t n_nodes,
-                      int64_t n_edges, void *out, void *workspace, size_t workspace_bytes,
-                      cgtp_stream_t stream);
+                      const int32_t *src, const int32_t *dst_row_ptr, const int32_t *node_order,
+                      int64_t n_nodes, int64_t n_edges, void *out, void *workspace,
+                      size_t workspace_bytes, cgtp_stream_t stream);
 
 /* Workspace needed by cgtp_conv_backward / cgtp_conv_double_backward for a
  * graph with n_edges edges (bytes; 256-byte aligned pointer required).
@@ -197,13 +202,15 @@ int cgtp_conv_workspace_bytes(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges
  * src_perm [n_edges] give, for each source node s, the positions (into the
  * dst-sorted arrays) of its edges: src_perm[src_row_ptr[s] ..
  * src_row_ptr[s+1]).  g_x is reduced per source node without atomics.
- * Any of g_x, g_sh, g_w may be NULL (not computed).  Shared-weight plans
- * are not supported here (UNSUPPORTED). */
+ * node_order as in cgtp_conv_forward.  Any of g_x, g_sh, g_w may be NULL
+ * (not computed).  Shared-weight plans are not supported here
+ * (UNSUPPORTED). */
 int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
                        const int32_t *src, const int32_t *dst, const int32_t *dst_row_ptr,
-                       const int32_t *src_row_ptr, const int32_t *src_perm, const void *g_out,
-                       int64_t n_nodes, int64_t n_edges, void *g_x, void *g_sh, void *g_w,
-                       void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+                       const int32_t *node_order, const int32_t *src_row_ptr,
+                       const int32_t *src_perm, const void *g_out, int64_t n_nodes,
+                       int64_t n_edges, void *g_x, void *g_sh, void *g_w, void *workspace,
+                       size_t workspace_bytes, cgtp_stream_t stream);
 
 /* Second derivatives ([KG]: higher partial derivatives for forces).  The
  * convolution f(x, sh, w) is trilinear, so for cotangents (gg_x, gg_sh,
@@ -218,8 +225,9 @@ int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const vo
  * cgtp_conv_backward (d_g_out has the shape of g_out). */
 int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
                               const int32_t *src, const int32_t *dst,
-                              const int32_t *dst_row_ptr, const int32_t *src_row_ptr,
-                              const int32_t *src_perm, const void *g_out, const void *gg_x,
+                              const int32_t *dst_row_ptr, const int32_t *node_order,
+                              const int32_t *src_row_ptr, const int32_t *src_perm,
+                              const void *g_out, const void *gg_x,
                               const void *gg_sh, const void *gg_w, int64_t n_nodes,
                               int64_t n_edges, void *d_g_out, void *d_x, void *d_sh, void *d_w,
                               void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
@@ -244,6 +252,16 @@ int cgtp_csr_workspace_bytes(int64_t n_edges, int64_t n_keys, size_t *bytes);
 int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int64_t n_keys,
                    int32_t *perm, int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val,
                    void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
+/* Processing order for the convolution calls: the n_nodes rows of a CSR
+ * sorted by decreasing length (rows of 1023 or more edges tie), so that
+ * the longest rows are started first and do not form the tail of a launch
+ * (longest-processing-time-first scheduling).  The order among rows of
+ * equal length is not fixed; it changes no result of any call.
+ * order [n_nodes]; workspace: cgtp_node_order_workspace_bytes. */
+int cgtp_node_order_workspace_bytes(int64_t n_nodes, size_t *bytes);
+int cgtp_node_order(const int32_t *row_ptr, int64_t n_nodes, int32_t *order, void *workspace,
+                    size_t workspace_bytes, cgtp_stream_t stream);
 
 /* Checks on the device that row_ptr is a monotone CSR over n_edges and that
  * every index in idx[n_edges] (may be NULL) lies in [0, n_idx_range).

@@ -209,6 +209,59 @@ def test_conv_bf16_weights_small(B, torch, k):
     assert_close(dw.cpu().numpy(), rw[G.perm], "f32", "d_w")
 
 
+@pytest.mark.parametrize("k", [1, 3])
+def test_conv_node_order_changes_nothing(B, torch, k):
+    """Any processing order gives bit-identical results (each row is reduced
+    by one wavefront in its fixed edge order), and matches the oracle."""
+    plan, prob = _small_problem(B, k, "f32")
+    src, dst = _small_graph(61, 700, 60 + k)
+    G = GraphArrays(src, dst, 61)
+    rng = np.random.default_rng(70 + k)
+    x, sh, w = (W.normal(rng, s_, "f32") for s_ in ((61, prob.dim1), (G.E, prob.dim2), (G.E, prob.weight_numel)))
+    g = W.normal(rng, (61, prob.dim3), "f32")
+    ay = W.normal(rng, sh.shape, "f32")
+    d = G.dev(torch)
+    f = lambda a: to_dev(torch, a, "f32")
+    args = (plan, f(x), f(sh[G.perm]), f(w[G.perm]), d["src"], d["dst"], d["dst_row_ptr"], d["src_row_ptr"],
+            d["src_perm"], f(g))
+    lpt = B.cgtp_node_order(d["dst_row_ptr"])
+    rand = torch.from_numpy(rng.permutation(61).astype(np.int32)).cuda()
+    print(f"node order k={k}", flush=True)
+    res = {}
+    for name, order in (("natural", None), ("lpt", lpt), ("random", rand)):
+        out = B.cgtp_conv_forward(plan, f(x), f(sh[G.perm]), f(w[G.perm]), d["src"], d["dst_row_ptr"],
+                                  node_order=order)
+        bwd = B.cgtp_conv_backward(*args, node_order=order)
+        dbl = B.cgtp_conv_double_backward(*args, None, f(ay[G.perm]), None, node_order=order, need=("g_out", "x", "w"))
+        torch.cuda.synchronize()
+        res[name] = [t.cpu().numpy() for t in (out, *bwd, *[t for t in dbl if t is not None])]
+    for name in ("lpt", "random"):
+        for a, b in zip(res["natural"], res[name]):
+            np.testing.assert_array_equal(a, b)
+    assert_close(res["natural"][0], prob.conv_forward(x, sh, w, src, dst, 61), "f32", "forward")
+
+
+@pytest.mark.parametrize("case", ["c2", "hub", "single", "isolated", "large"])
+def test_node_order_sorts_rows(B, torch, case):
+    rs = np.random.default_rng(3)
+    if case == "large":   # beyond one workgroup's share: the multi-kernel path
+        key, n = rs.integers(0, 100000, 300000).astype(np.int32), 100000
+    elif case == "c2":
+        key, n = W.periodic_graph(4096, seed=0).dst, 4096
+    elif case == "hub":   # one row far above the 1023 cap
+        key, n = np.concatenate([np.full(3000, 7), rs.integers(0, 50, 2000)]).astype(np.int32), 50
+    elif case == "single":
+        key, n = np.zeros(5, np.int32), 1
+    else:                 # rows without edges
+        key, n = rs.integers(0, 10, 200).astype(np.int32) * 3, 31
+    _, rp = oracle.csr(key, n)
+    print(f"node order {case}", flush=True)
+    order = B.cgtp_node_order(torch.from_numpy(rp).cuda()).cpu().numpy()
+    assert sorted(order.tolist()) == list(range(n))
+    deg = np.minimum(np.diff(rp)[order], 1023)
+    assert np.all(deg[:-1] >= deg[1:])
+
+
 def test_conv_no_edges(B, torch):
     plan, prob = _small_problem(B, 0, "f32")
     x = torch.randn(4, prob.dim1, device="cuda")
@@ -383,6 +436,71 @@ def test_c3_forward_fp64_full_size_sampled(B, torch):
     sh_ref = oracle.spherical_harmonics(3, g.vec)
     _sampled_rows_check(prob, x, sh_ref, w, g.src, g.dst, g.n_nodes, out[torch.from_numpy(rows).cuda()].cpu().numpy(),
                         rows, "f64")
+
+
+def test_c2a_all_parity_morton_full_size_sampled(B, torch):
+    """All output parities (13 paths, odd paths included) on the 4096-atom
+    box numbered along a Z-order curve, processed in longest-row-first
+    order: forward rows and the per-edge gradients of the edges into them."""
+    c = W.config("c2a")
+    plan, prob = _plan(B, c)
+    assert plan.n_paths == 13 and plan.dim_out == 7040
+    rng = np.random.default_rng(0)
+    g = W.periodic_graph(4096, cutoff=5.0, rng=rng, morton=True)
+    x = W.normal(rng, (g.n_nodes, prob.dim1), "f32")
+    w = W.normal(rng, (g.n_edges, prob.weight_numel), "f32")
+    gout = W.normal(rng, (g.n_nodes, prob.dim3), "f32")
+    G = GraphArrays(g.src, g.dst, g.n_nodes)
+    d = G.dev(torch)
+    vec32 = g.vec.astype(np.float32)
+    print(f"c2a forward+backward E={g.n_edges}", flush=True)
+    sh = B.cgtp_spherical_harmonics(3, torch.from_numpy(vec32).cuda(), torch.from_numpy(G.perm).cuda(), "f32")
+    order = B.cgtp_node_order(d["dst_row_ptr"])
+    args = (plan, to_dev(torch, x, "f32"), sh, to_dev(torch, w[G.perm], "f32"), d["src"])
+    out = B.cgtp_conv_forward(*args, d["dst_row_ptr"], node_order=order)
+    _, ogy, ogw = B.cgtp_conv_backward(*args, d["dst"], d["dst_row_ptr"], d["src_row_ptr"], d["src_perm"],
+                                       to_dev(torch, gout, "f32"), node_order=order)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(3).choice(g.n_nodes, 32, replace=False))
+    sh_ref = oracle.spherical_harmonics(3, vec32.astype(np.float64))
+    _sampled_rows_check(prob, x, sh_ref, w, g.src, g.dst, g.n_nodes,
+                        out[torch.from_numpy(rows).cuda()].cpu().numpy(), rows, "f32")
+    # per-edge gradients of the edges into the sampled rows
+    mask = np.isin(g.dst, rows)
+    remap = {r: i for i, r in enumerate(rows)}
+    sub_dst = np.array([remap[v] for v in g.dst[mask]], np.int32)
+    uniq, inv = np.unique(g.src[mask], return_inverse=True)
+    n_sub = max(len(uniq), len(rows))
+    x_sub = np.zeros((n_sub, prob.dim1)); x_sub[:len(uniq)] = x[uniq]
+    g_sub = np.zeros((n_sub, prob.dim3)); g_sub[:len(rows)] = gout[rows]
+    _, rgy, rgw = prob.conv_backward(x_sub, sh_ref[mask], w[mask], inv.astype(np.int32), sub_dst, g_sub)
+    pos = np.argsort(G.perm)[np.nonzero(mask)[0]]      # dst-sorted position of each masked edge
+    pos_d = torch.from_numpy(pos).cuda()
+    assert_close(ogy[pos_d].cpu().numpy(), rgy, "f32", "c2a g_sh")
+    assert_close(ogw[pos_d].cpu().numpy(), rgw, "f32", "c2a g_w")
+
+
+def test_c3a_all_parity_fp64_sampled(B, torch):
+    """24 paths in FP64 on a 4096-atom box (the 16384-atom box is covered by
+    the 17-path test; its 24-path weights alone would take 21 GB)."""
+    c = W.config("c3a")
+    plan, prob = _plan(B, c)
+    assert plan.n_paths == 24
+    rng = np.random.default_rng(0)
+    g = W.periodic_graph(4096, cutoff=5.0, rng=rng)
+    x = W.normal(rng, (g.n_nodes, prob.dim1), "f64")
+    G = GraphArrays(g.src, g.dst, g.n_nodes)
+    print(f"c3a full forward E={g.n_edges}: drawing weights", flush=True)
+    w = W.normal(rng, (g.n_edges, prob.weight_numel), "f64")
+    d = G.dev(torch)
+    sh = B.cgtp_spherical_harmonics(3, torch.from_numpy(g.vec).cuda(), torch.from_numpy(G.perm).cuda(), "f64")
+    print("c3a full forward: launch", flush=True)
+    out = B.cgtp_conv_forward(plan, to_dev(torch, x, "f64"), sh, torch.from_numpy(w[G.perm]).cuda(), d["src"],
+                              d["dst_row_ptr"], node_order=B.cgtp_node_order(d["dst_row_ptr"]))
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(4).choice(g.n_nodes, 24, replace=False))
+    _sampled_rows_check(prob, x, oracle.spherical_harmonics(3, g.vec), w, g.src, g.dst, g.n_nodes,
+                        out[torch.from_numpy(rows).cuda()].cpu().numpy(), rows, "f64")
 
 
 # ---------------------------------------------------------------------------
