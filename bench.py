@@ -49,6 +49,8 @@ def parse():
                     help="c2/c3/c4: every output parity for l3 <= 3 (13 / 24 paths, one block per path)")
     ap.add_argument("--morton", action="store_true",
                     help="c2/c3/c4: atoms numbered along a Z-order curve of their positions")
+    ap.add_argument("--natural-order", action="store_true",
+                    help="hand destination rows to the device in node-id order (no longest-first order)")
     ap.add_argument("--nominal-e", action="store_true",
                     help="c2/c3/c4 graph with cutoff 4.153 A (about 30 neighbours, the nominal edge count)")
     return ap.parse_args()
@@ -131,7 +133,8 @@ def tp_flops(cfg, plan):
 
 def counted_traffic(workload, kernel, source):
     """HBM bytes per launch measured with rocprofv3 counters for exactly this
-    generated source (profiles/hbm_traffic__*.json), else None."""
+    workload (its full description) and generated source
+    (profiles/hbm_traffic__*.json), else None."""
     import glob
     import hashlib
     sha = hashlib.sha1(source.encode()).hexdigest()
@@ -264,6 +267,7 @@ def bench_conv(args, torch, B, W):
     csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), dev)
     order = torch.empty(N, dtype=torch.int32, device=dev)
     ord_ws = B.workspace(4096 * 4, dev)
+    node_order = None if args.natural_order else order
     sh = torch.empty(E, plan.dim_in2, dtype=td, device=dev)
     out = torch.empty(N, plan.dim_out, dtype=od, device=dev)
     nb_f = B.cgtp_forward_workspace_bytes(plan, N)
@@ -288,19 +292,19 @@ def bench_conv(args, torch, B, W):
         run("csr", lambda: (B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s)),
                             B.cgtp_build_csr(src_s, N, sorted_key=False, ws=csr_ws,
                                              out=(src_perm, src_rp, None, None)),
-                            B.cgtp_node_order(rp, ws=ord_ws, out=order)))
+                            None if args.natural_order else B.cgtp_node_order(rp, ws=ord_ws, out=order)))
         run("sh", lambda: B.cgtp_spherical_harmonics(lmax, vec, perm, dtype, out=sh))
-        run("conv_fwd", lambda: B.cgtp_conv_forward(plan, x, sh, w, src_s, rp, out=out, ws=f_ws, node_order=order))
+        run("conv_fwd", lambda: B.cgtp_conv_forward(plan, x, sh, w, src_s, rp, out=out, ws=f_ws, node_order=node_order))
         if not full:
             return
         run("conv_bwd", lambda: B.cgtp_conv_backward(plan, x, sh, w, src_s, dst_s, rp, src_rp, src_perm, g_out,
-                                                     ws=ws, out=(g_x, g_sh, g_w), node_order=order))
+                                                     ws=ws, out=(g_x, g_sh, g_w), node_order=node_order))
         run("forces", lambda: B.cgtp_sh_forces(lmax, vec, perm, g_sh, rp, src_rp, src_perm, dtype, ws=fo_ws,
                                                out=F))
         run("force_cot", lambda: B.cgtp_force_loss_sh_cotangent(lmax, vec, perm, src_s, dst_s, F, dtype, out=gg))
         run("double_bwd", lambda: B.cgtp_conv_double_backward(plan, x, sh, w, src_s, dst_s, rp, src_rp, src_perm,
                                                               g_out, None, gg, None, ws=ws,
-                                                              out=(d_g, d_x, None, d_w), node_order=order))
+                                                              out=(d_g, d_x, None, d_w), node_order=node_order))
 
     for _ in range(args.warmup):
         step(False)
@@ -359,11 +363,17 @@ def bench_conv(args, torch, B, W):
             alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb, wb) / (kms["conv_bwd"] * 1e-3) / 1e9, 1)}
         calls["double_bwd"] = {"ms": kms["double_bwd"], "GB_per_s": round(
             alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb, wb) / (kms["double_bwd"] * 1e-3) / 1e9, 1)}
+    workload = ((W.config("c4").name if full else cfg.name) +
+                (f", cutoff {NOMINAL_CUTOFF} A" if args.nominal_e and name != "c5" else "") +
+                (", bf16 weight storage" if bf16w else "") +
+                (", all output parities" if args.all_parity and full else "") +
+                (", Morton node order" if args.morton else "") +
+                (", rows in node-id order" if args.natural_order else ""))
     # dominant kernel: largest share of the step
     dom = max((k for k in kern if k in alg), key=lambda k: kern[k]["ms_per_step"])
     roof = {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB_per_s"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
-            "traffic": counted_traffic(name, dom, plan.source()),
+            "traffic": counted_traffic(workload, dom, plan.source()),
             "alg_bytes_per_launch": kern[dom]["alg_bytes"], "avg_ms": round(kern[dom]["avg_ms"], 4)}
     if name == "c5":
         # the path tensors on the vector ALUs dominate: FP32 vector peak
@@ -388,12 +398,7 @@ def bench_conv(args, torch, B, W):
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": (W.config("c4").name if full else cfg.name) +
-                   (f", cutoff {NOMINAL_CUTOFF} A" if args.nominal_e and name != "c5" else "") +
-                   (", bf16 weight storage" if bf16w else "") +
-                   (", all output parities" if args.all_parity and full else "") +
-                   (", Morton node order" if args.morton else ""),
-                   "n_atoms": N, "n_edges": E,
+        "config": {"workload": workload, "n_atoms": N, "n_edges": E,
                    "irreps_node": cfg.irreps_in1, "irreps_sh": cfg.irreps_in2, "irreps_out": cfg.irreps_out,
                    "n_paths": plan.n_paths,
                    "step": ("csr+sh+fwd+bwd+forces+force_cotangent+double_bwd" if full else "csr+sh+fwd")},
