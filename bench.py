@@ -1,16 +1,21 @@
 """Benchmark of the fused CG tensor-product convolution hot path on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload c4|c2|c3|c1|c5] [--no-cpu-baseline] [--nominal-e]
+                    [--workload c4|c2|c3|c1|c5] [--no-cpu-baseline]
+                    [--separate-sh] [--bf16-weights] [--all-parity] [--morton]
+                    [--natural-order] [--nominal-e]
 
 Default workload "c4" (one step = the whole hot path on the 4096-atom
 periodic water-density box, cutoff 5 A, node 128x0e+128x1o, SH l<=3, uvu,
-fp32): CSR of the edges by destination (carrying the source index) and the
-transpose CSR by source, spherical harmonics of the edge vectors, fused
-convolution forward, backward (g_x, g_sh, g_w for E = sum of the 0e output
-blocks), forces from g_sh, the force-loss cotangent on the SH, and the double
-backward (d/dx, d/dw, d/dg_out) driven by that cotangent.  Other workloads
-time the forward path alone: c2 (same graph), c3 (16384 atoms, fp64, node
+fp32): CSR of the edges by destination (carrying the source index), the
+transpose CSR by source and the longest-row-first processing order; fused
+convolution forward with the spherical harmonics of the edge vectors
+computed inside the kernel; backward (g_x, g_w, and the forces of E = sum of
+the 0e output blocks through the SH Jacobian); the force-loss cotangent on
+the SH; and the double backward (d/dx, d/dw, d/dg_out) driven by that
+cotangent.  --separate-sh runs the SH and the forces as kernels of their own
+with SH and SH-gradient arrays in memory.  Other workloads time the
+forward path alone: c2 (same graph), c3 (16384 atoms, fp64, node
 128x0e+128x1o+128x2e), c1 (1000 independent products), c5 (100 molecules of
 18 atoms, uvw bf16 with matrix-core mixing).  Inputs are resident in HBM
 before timing starts.  Prints one JSON line.
@@ -49,6 +54,10 @@ def parse():
                     help="c2/c3/c4: every output parity for l3 <= 3 (13 / 24 paths, one block per path)")
     ap.add_argument("--morton", action="store_true",
                     help="c2/c3/c4: atoms numbered along a Z-order curve of their positions")
+    ap.add_argument("--separate-sh", action="store_true",
+                    help="SH by their own kernel into an [E][dim2] array read by the convolution, forces from "
+                         "a g_sh array (default: SH computed inside the convolution kernels from the edge "
+                         "vectors, forces from the backward's SH-gradient partials)")
     ap.add_argument("--natural-order", action="store_true",
                     help="hand destination rows to the device in node-id order (no longest-first order)")
     ap.add_argument("--nominal-e", action="store_true",
@@ -84,21 +93,20 @@ class Timer:
 # algorithmic bytes: each array counted once at its storage size; gathers of
 # source-node rows that hit in cache are not counted
 # ---------------------------------------------------------------------------
-def alg_bytes_conv_fwd(N, E, d1, d2, d3, wn, eb, ob, wb=None):
-    wb = eb if wb is None else wb
-    return N * d1 * eb + N * d3 * ob + E * d2 * eb + E * wn * wb + E * 4 + (N + 1) * 4
+# shb: bytes per edge of the SH operand -- the SH row (dim2 elements), or,
+# with the SH computed in the kernel, the edge vector and its index
+def alg_bytes_conv_fwd(N, E, d1, d3, wn, eb, ob, wb, shb):
+    return N * d1 * eb + N * d3 * ob + E * shb + E * wn * wb + E * 4 + (N + 1) * 4
 
 
-def alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb, wb=None):
-    # reads x, g_out, sh, w, src, row_ptr; writes g_x, g_sh, g_w (g_w at the
-    # arithmetic width)
-    wb = eb if wb is None else wb
-    return N * (2 * d1 + d3) * eb + E * 2 * d2 * eb + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
+def alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb, wb, shb):
+    # reads x, g_out, the SH operand, w, src, row_ptr; writes g_x, g_sh (or
+    # its partials), g_w (at the arithmetic width)
+    return N * (2 * d1 + d3) * eb + E * (shb + d2 * eb) + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
 
 
-def alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb, wb=None):
+def alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb, wb):
     # reads x, g_out, gg_sh, w, src, row_ptr; writes d_g_out, d_x, d_w
-    wb = eb if wb is None else wb
     return N * (2 * d1 + 2 * d3) * eb + E * d2 * eb + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
 
 
@@ -232,6 +240,7 @@ def bench_conv(args, torch, B, W):
         cut = NOMINAL_CUTOFF if args.nominal_e else cfg.extra["cutoff"]
         g = W.periodic_graph(cfg.extra["n_atoms"], cutoff=cut, rng=rng, morton=args.morton)
     bf16w = bool(args.bf16_weights)
+    sh_in_conv = not args.separate_sh
     if bf16w and name not in ("c2", "c4"):
         raise SystemExit("--bf16-weights applies to the c2 and c4 workloads")
     plan = B.Plan(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.paths, cfg.mode, dtype,
@@ -293,16 +302,29 @@ def bench_conv(args, torch, B, W):
                             B.cgtp_build_csr(src_s, N, sorted_key=False, ws=csr_ws,
                                              out=(src_perm, src_rp, None, None)),
                             None if args.natural_order else B.cgtp_node_order(rp, ws=ord_ws, out=order)))
-        run("sh", lambda: B.cgtp_spherical_harmonics(lmax, vec, perm, dtype, out=sh))
-        run("conv_fwd", lambda: B.cgtp_conv_forward(plan, x, sh, w, src_s, rp, out=out, ws=f_ws, node_order=node_order))
-        if not full:
-            return
-        run("conv_bwd", lambda: B.cgtp_conv_backward(plan, x, sh, w, src_s, dst_s, rp, src_rp, src_perm, g_out,
-                                                     ws=ws, out=(g_x, g_sh, g_w), node_order=node_order))
-        run("forces", lambda: B.cgtp_sh_forces(lmax, vec, perm, g_sh, rp, src_rp, src_perm, dtype, ws=fo_ws,
-                                               out=F))
+        if sh_in_conv:
+            # SH computed inside the convolution kernels; forces straight from
+            # the backward's per-unit SH-gradient partials
+            run("conv_fwd", lambda: B.cgtp_conv_forward_vec(plan, x, vec, perm, w, src_s, rp, out=out, ws=f_ws,
+                                                            node_order=node_order))
+            if not full:
+                return
+            run("conv_bwd", lambda: B.cgtp_conv_backward_vec(plan, x, vec, perm, w, src_s, rp, src_rp, src_perm,
+                                                             g_out, ws=ws, out=(g_x, None, g_w, F),
+                                                             node_order=node_order))
+        else:
+            run("sh", lambda: B.cgtp_spherical_harmonics(lmax, vec, perm, dtype, out=sh))
+            run("conv_fwd", lambda: B.cgtp_conv_forward(plan, x, sh, w, src_s, rp, out=out, ws=f_ws,
+                                                        node_order=node_order))
+            if not full:
+                return
+            run("conv_bwd", lambda: B.cgtp_conv_backward(plan, x, sh, w, src_s, dst_s, rp, src_rp, src_perm, g_out,
+                                                         ws=ws, out=(g_x, g_sh, g_w), node_order=node_order))
+            run("forces", lambda: B.cgtp_sh_forces(lmax, vec, perm, g_sh, rp, src_rp, src_perm, dtype, ws=fo_ws,
+                                                   out=F))
         run("force_cot", lambda: B.cgtp_force_loss_sh_cotangent(lmax, vec, perm, src_s, dst_s, F, dtype, out=gg))
-        run("double_bwd", lambda: B.cgtp_conv_double_backward(plan, x, sh, w, src_s, dst_s, rp, src_rp, src_perm,
+        run("double_bwd", lambda: B.cgtp_conv_double_backward(plan, x, None if sh_in_conv else sh, w, src_s,
+                                                              dst_s, rp, src_rp, src_perm,
                                                               g_out, None, gg, None, ws=ws,
                                                               out=(d_g, d_x, None, d_w), node_order=node_order))
 
@@ -340,12 +362,15 @@ def bench_conv(args, torch, B, W):
     # at its storage size; the backward's per-edge x-messages are an
     # intermediate and not counted)
     alg = {}
+    vb = 8 if dtype == "f64" else 4
+    shb = 3 * vb + 4 if sh_in_conv else d2 * eb
     if name == "c5":
-        alg["cgtp_fwd"] = N * d1 * eb + E * d2 * eb + E * 4 + (N + 1) * 4   # path tensors (bf16) stay in cache
+        alg["cgtp_fwd"] = N * d1 * eb + E * shb + E * 4 + (N + 1) * 4   # path tensors (bf16) stay in cache
     else:
-        alg["cgtp_fwd"] = alg_bytes_conv_fwd(N, E, d1, d2, d3, wn, eb, ob, wb)
+        alg["cgtp_fwd"] = alg_bytes_conv_fwd(N, E, d1, d3, wn, eb, ob, wb, shb)
     if full:
-        alg["cgtp_bwd"] = N * (d1 + d3) * eb + E * 2 * d2 * eb + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
+        # the kernels' own traffic: no x-row writes, node rows counted once
+        alg["cgtp_bwd"] = N * (d1 + d3) * eb + E * (shb + d2 * eb) + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
         alg["cgtp_dbl"] = N * (d1 + 2 * d3) * eb + E * d2 * eb + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
         # the same kernels with the full call's flags folded in
         alg["cgtp_bwd_full"], alg["cgtp_dbl_full"] = alg["cgtp_bwd"], alg["cgtp_dbl"]
@@ -357,10 +382,10 @@ def bench_conv(args, torch, B, W):
             kern[k].update({"alg_bytes": int(alg[k]), "GB_per_s": round(gbs, 1),
                             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
     calls = {"conv_fwd": {"ms": kms["conv_fwd"], "GB_per_s": round(
-        alg_bytes_conv_fwd(N, E, d1, d2, d3, wn, eb, ob, wb) / (kms["conv_fwd"] * 1e-3) / 1e9, 1)}}
+        alg_bytes_conv_fwd(N, E, d1, d3, wn, eb, ob, wb, shb) / (kms["conv_fwd"] * 1e-3) / 1e9, 1)}}
     if full:
         calls["conv_bwd"] = {"ms": kms["conv_bwd"], "GB_per_s": round(
-            alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb, wb) / (kms["conv_bwd"] * 1e-3) / 1e9, 1)}
+            alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb, wb, shb) / (kms["conv_bwd"] * 1e-3) / 1e9, 1)}
         calls["double_bwd"] = {"ms": kms["double_bwd"], "GB_per_s": round(
             alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb, wb) / (kms["double_bwd"] * 1e-3) / 1e9, 1)}
     workload = ((W.config("c4").name if full else cfg.name) +
@@ -368,7 +393,8 @@ def bench_conv(args, torch, B, W):
                 (", bf16 weight storage" if bf16w else "") +
                 (", all output parities" if args.all_parity and full else "") +
                 (", Morton node order" if args.morton else "") +
-                (", rows in node-id order" if args.natural_order else ""))
+                (", rows in node-id order" if args.natural_order else "") +
+                (", SH by a separate kernel" if not sh_in_conv else ""))
     # dominant kernel: largest share of the step
     dom = max((k for k in kern if k in alg), key=lambda k: kern[k]["ms_per_step"])
     roof = {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB_per_s"], "peak": HBM_PEAK_GBS,

@@ -67,9 +67,11 @@ bool blocks_covered(const std::vector<Irrep> &irreps, const std::vector<Path> &p
 
 // forward launch with an explicit operand set (used by the forward and by
 // the double backward's substituted calls)
+// vec/vperm: edge vectors from which the kernels compute the SH rows
+// themselves (y unused), or NULL
 int run_fwd(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
             const int32_t *row_ptr, const int32_t *order, int64_t n_items, int graph, void *out, int accumulate,
-            hipStream_t s) {
+            hipStream_t s, const void *vec = nullptr, const int32_t *vperm = nullptr) {
     if (!accumulate && !blocks_covered(p.out, p.paths, true)) {
         int rc = launch_zero(p.dtype == CGTP_F64 ? CGTP_F64 : CGTP_F32, out, n_items * p.dim3, s);
         if (rc) return rc;
@@ -77,7 +79,7 @@ int run_fwd(const Plan &p, const void *x, const void *y, const void *w, const in
     }
     long long n = n_items;
     void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&order,
-                    (void *)&out, &n, &graph, &accumulate};
+                    (void *)&vec, (void *)&vperm, (void *)&out, &n, &graph, &accumulate};
     const int64_t ipw = p.fwd.items_per_wave;
     return launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
 }
@@ -91,6 +93,7 @@ struct BwdOut {
     bool acc_y = false;
     void *fwd = nullptr;  // fused forward of the same operands (double backward)
     bool acc_fwd = false;
+    bool keep_parts = false;  // leave the per-unit y-gradient partials in the workspace
 };
 
 // workspace layout of the backward calls: x-messages [E][dim1] in source
@@ -102,10 +105,14 @@ int32_t *ws_mrow(const Plan &p, char *ws, int64_t n_edges) {
     return (int32_t *)(ws_parts(p, ws, n_edges) +
                        align256((size_t)std::max(1, p.bwd.n_units) * n_edges * p.dim2 * out_bytes(p.dtype)));
 }
+// per-edge force vectors [E][3] of the backward with forces
+char *ws_force(const Plan &p, char *ws, int64_t n_edges) {
+    return (char *)ws_mrow(p, ws, n_edges) + align256((size_t)n_edges * sizeof(int32_t));
+}
 
 int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
             const int32_t *row_ptr, const int32_t *order, const void *g_out, int64_t n_nodes, int64_t n_edges,
-            BwdOut o, char *ws, hipStream_t s) {
+            BwdOut o, char *ws, hipStream_t s, const void *vec = nullptr, const int32_t *vperm = nullptr) {
     void *m = ws;
     char *parts = ws_parts(p, ws, n_edges);
     const int32_t *mrow = ws_mrow(p, ws, n_edges);
@@ -133,7 +140,8 @@ int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const in
     long long n = n_nodes, ne = n_edges;
     int graph = 1;
     void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&order,
-                    (void *)&g_out, &gw, &m, &third, (void *)&mrow, &n, &ne, &graph, &flags};
+                    (void *)&vec, (void *)&vperm, (void *)&g_out, &gw, &m, &third, (void *)&mrow, &n, &ne, &graph,
+                    &flags};
     const int64_t ipw = ks.items_per_wave;
     const bool full = fused ? ((p.tune.full & 2) && flags == dbl_full_flags(p))
                             : ((p.tune.full & 1) && flags == bwd_full_flags(p));
@@ -141,7 +149,7 @@ int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const in
     const char *name = fused ? (full ? "cgtp_dbl_full" : "cgtp_dbl") : (full ? "cgtp_bwd_full" : "cgtp_bwd");
     int rc = launch(f, name, (n_nodes + ipw - 1) / ipw * ks.n_units, s, args);
     if (rc) return rc;
-    if (use_parts) rc = launch_sum_parts(p.dtype, parts, ks.n_units, n_edges * p.dim2, o.g_y, o.acc_y, s);
+    if (use_parts && !o.keep_parts) rc = launch_sum_parts(p.dtype, parts, ks.n_units, n_edges * p.dim2, o.g_y, o.acc_y, s);
     return rc;
 }
 
@@ -201,6 +209,16 @@ int cgtp_plan(const char *irreps_in1, const char *irreps_in2, const char *irreps
         p.off2.assign(o2.begin(), o2.end() - 1);
         p.off3.assign(o3.begin(), o3.end() - 1);
         for (auto &ir : p.in2) p.lmax2 = std::max(p.lmax2, ir.l);
+        {
+            // input 2 laid out as one SH row (1x0 + 1x1 + ... + 1xL, parity
+            // absent or (-1)^l): the SH can be computed inside the kernels
+            bool sh = p.in2.size() <= 7;
+            for (size_t l = 0; l < p.in2.size() && sh; ++l) {
+                const Irrep &ir = p.in2[l];
+                sh = ir.mul == 1 && ir.l == (int)l && (ir.parity == 0 || ir.parity == ((l & 1) ? -1 : 1));
+            }
+            p.sh_lmax = sh ? (int)p.in2.size() - 1 : -1;
+        }
 
         std::vector<cgtp_path> list;
         if (n_paths > 0) {
@@ -333,12 +351,13 @@ void cgtp_plan_destroy(cgtp_plan_t plan) {
 
 static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
                    const int32_t *row_ptr, const int32_t *order, int64_t n_items, int graph, void *out, void *ws,
-                   size_t ws_bytes, hipStream_t s) {
+                   size_t ws_bytes, hipStream_t s, const void *vec = nullptr, const int32_t *vperm = nullptr) {
     size_t need = align256((size_t)n_items * p.t_per_item * 2);
     if (ws_bytes < need || (!ws && need)) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace too small");
     if (((uintptr_t)ws) & 255) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     long long n = n_items;
-    void *args[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, (void *)&order, &ws, &n, &graph};
+    void *args[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, (void *)&order, (void *)&vec,
+                    (void *)&vperm, &ws, &n, &graph};
     const int64_t ipw = p.fwd.items_per_wave;
     int rc = launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
     if (rc) return rc;
@@ -374,21 +393,47 @@ int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, 
     return run_fwd(plan->p, x, y, w, nullptr, nullptr, nullptr, batch, 0, out, 0, (hipStream_t)stream);
 }
 
-int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
-                      const int32_t *dst_row_ptr, const int32_t *node_order, int64_t n_nodes, int64_t n_edges,
-                      void *out, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
-    clear_error();
+static int conv_forward_impl(cgtp_plan_t plan, const void *x, const void *sh, const void *vec, const int32_t *vperm,
+                             const void *w, const int32_t *src, const int32_t *dst_row_ptr, const int32_t *node_order,
+                             int64_t n_nodes, int64_t n_edges, void *out, void *workspace, size_t workspace_bytes,
+                             cgtp_stream_t stream) {
     int rc = check_loaded(plan);
     if (rc) return rc;
     if (n_nodes < 0 || n_edges < 0 || n_edges > 0x7fffffffLL || n_nodes > 0x7fffffffLL)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "sizes out of range");
     if (n_nodes == 0) return CGTP_OK;
-    if (!dst_row_ptr || !out || (n_edges > 0 && (!x || !sh || !w || !src)))
+    if (!dst_row_ptr || !out || (n_edges > 0 && (!x || !(sh || vec) || !w || !src)))
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
     if (plan->p.mode == CGTP_UVW)
         return run_uvw(plan->p, x, sh, w, src, dst_row_ptr, node_order, n_nodes, 1, out, workspace,
-                       workspace_bytes, (hipStream_t)stream);
-    return run_fwd(plan->p, x, sh, w, src, dst_row_ptr, node_order, n_nodes, 1, out, 0, (hipStream_t)stream);
+                       workspace_bytes, (hipStream_t)stream, vec, vperm);
+    return run_fwd(plan->p, x, sh, w, src, dst_row_ptr, node_order, n_nodes, 1, out, 0, (hipStream_t)stream, vec, vperm);
+}
+
+static int check_vec_plan(cgtp_plan_t plan) {
+    if (plan && (plan->p.sh_lmax < 0 || plan->p.tune.stage <= 0))
+        return set_error(CGTP_ERR_UNSUPPORTED,
+                         "SH from edge vectors needs input 2 = 1x0+1x1+...+1xL (one SH row) and LDS staging");
+    return CGTP_OK;
+}
+
+int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
+                      const int32_t *dst_row_ptr, const int32_t *node_order, int64_t n_nodes, int64_t n_edges,
+                      void *out, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
+    clear_error();
+    return conv_forward_impl(plan, x, sh, nullptr, nullptr, w, src, dst_row_ptr, node_order, n_nodes, n_edges, out,
+                             workspace, workspace_bytes, stream);
+}
+
+int cgtp_conv_forward_vec(cgtp_plan_t plan, const void *x, const void *vec, const int32_t *vec_perm, const void *w,
+                          const int32_t *src, const int32_t *dst_row_ptr, const int32_t *node_order, int64_t n_nodes,
+                          int64_t n_edges, void *out, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
+    clear_error();
+    int rc = check_vec_plan(plan);
+    if (rc) return rc;
+    if (n_edges > 0 && !vec) return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
+    return conv_forward_impl(plan, x, nullptr, vec, vec_perm, w, src, dst_row_ptr, node_order, n_nodes, n_edges, out,
+                             workspace, workspace_bytes, stream);
 }
 
 int cgtp_conv_workspace_bytes(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, size_t *bytes) {
@@ -398,7 +443,7 @@ int cgtp_conv_workspace_bytes(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges
     const size_t eb = out_bytes(p.dtype);
     *bytes = align256((size_t)n_edges * p.dim1 * eb) +
              align256((size_t)std::max(1, p.bwd.n_units) * n_edges * p.dim2 * eb) +
-             align256((size_t)n_edges * sizeof(int32_t)) + 256;
+             align256((size_t)n_edges * sizeof(int32_t)) + align256((size_t)n_edges * 3 * eb) + 256;
     return CGTP_OK;
 }
 
@@ -418,6 +463,49 @@ static int check_graph_args(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
     return CGTP_OK;
 }
 
+static int conv_backward_impl(cgtp_plan_t plan, const void *x, const void *sh, const void *vec,
+                              const int32_t *vperm, const void *w, const int32_t *src, const int32_t *dst_row_ptr,
+                              const int32_t *node_order, const int32_t *src_row_ptr, const int32_t *src_perm,
+                              const void *g_out, int64_t n_nodes, int64_t n_edges, void *g_x, void *g_sh, void *g_w,
+                              void *F, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
+    int rc = check_graph_args(plan, n_nodes, n_edges, workspace, workspace_bytes);
+    if (rc) return rc;
+    const Plan &p = plan->p;
+    hipStream_t s = (hipStream_t)stream;
+    if (n_nodes == 0) return CGTP_OK;
+    if (!dst_row_ptr || ((g_x || F) && (!src_row_ptr || (n_edges > 0 && !src_perm))) ||
+        (n_edges > 0 && (!x || !(sh || vec) || !w || !src || !g_out)))
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
+    if (n_edges == 0) {
+        if (g_x && (rc = launch_zero(p.dtype, g_x, n_nodes * p.dim1, s))) return rc;
+        if (F) return launch_zero(p.dtype, F, n_nodes * 3, s);
+        return CGTP_OK;
+    }
+    char *ws = (char *)workspace;
+    if (g_x && (rc = launch_invert_perm(src_perm, n_edges, ws_mrow(p, ws, n_edges), s))) return rc;
+    BwdOut o;
+    o.g_w = g_w;
+    o.want_m = g_x != nullptr;
+    o.g_y = g_sh;
+    // forces without g_sh: the y-gradient stays as per-unit partials in the
+    // workspace and the force kernel sums them
+    const bool parts_force = F && !g_sh;
+    if (parts_force) {
+        o.g_y = ws_parts(p, ws, n_edges);
+        o.keep_parts = true;
+    }
+    rc = run_bwd(p, x, sh, w, src, dst_row_ptr, node_order, g_out, n_nodes, n_edges, o, ws, s, vec, vperm);
+    if (rc) return rc;
+    if (g_x && (rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, nullptr, n_nodes, p.dim1, g_x, 0, s)))
+        return rc;
+    if (F) {
+        const int n_parts = parts_force && p.bwd.n_units > 1 ? p.bwd.n_units : 1;
+        rc = launch_sh_forces(p.sh_lmax, p.dtype, vec, vperm, parts_force ? o.g_y : g_sh, n_parts, n_edges * p.dim2,
+                              dst_row_ptr, src_row_ptr, src_perm, n_nodes, n_edges, F, ws_force(p, ws, n_edges), s);
+    }
+    return rc;
+}
+
 int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
                        const int32_t *dst, const int32_t *dst_row_ptr, const int32_t *node_order,
                        const int32_t *src_row_ptr, const int32_t *src_perm, const void *g_out, int64_t n_nodes,
@@ -425,27 +513,21 @@ int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const vo
                        cgtp_stream_t stream) {
     clear_error();
     (void)dst;
-    int rc = check_graph_args(plan, n_nodes, n_edges, workspace, workspace_bytes);
+    return conv_backward_impl(plan, x, sh, nullptr, nullptr, w, src, dst_row_ptr, node_order, src_row_ptr, src_perm,
+                              g_out, n_nodes, n_edges, g_x, g_sh, g_w, nullptr, workspace, workspace_bytes, stream);
+}
+
+int cgtp_conv_backward_vec(cgtp_plan_t plan, const void *x, const void *vec, const int32_t *vec_perm, const void *w,
+                           const int32_t *src, const int32_t *dst_row_ptr, const int32_t *node_order,
+                           const int32_t *src_row_ptr, const int32_t *src_perm, const void *g_out, int64_t n_nodes,
+                           int64_t n_edges, void *g_x, void *g_sh, void *g_w, void *F, void *workspace,
+                           size_t workspace_bytes, cgtp_stream_t stream) {
+    clear_error();
+    int rc = check_vec_plan(plan);
     if (rc) return rc;
-    const Plan &p = plan->p;
-    hipStream_t s = (hipStream_t)stream;
-    if (n_nodes == 0) return CGTP_OK;
-    if (!dst_row_ptr || (g_x && (!src_row_ptr || (n_edges > 0 && !src_perm))) ||
-        (n_edges > 0 && (!x || !sh || !w || !src || !g_out)))
-        return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
-    if (n_edges == 0) {
-        if (g_x) return launch_zero(p.dtype, g_x, n_nodes * p.dim1, s);
-        return CGTP_OK;
-    }
-    if (g_x && (rc = launch_invert_perm(src_perm, n_edges, ws_mrow(p, (char *)workspace, n_edges), s))) return rc;
-    BwdOut o;
-    o.g_w = g_w;
-    o.want_m = g_x != nullptr;
-    o.g_y = g_sh;
-    rc = run_bwd(p, x, sh, w, src, dst_row_ptr, node_order, g_out, n_nodes, n_edges, o, (char *)workspace, s);
-    if (rc) return rc;
-    if (g_x) rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, nullptr, n_nodes, p.dim1, g_x, 0, s);
-    return rc;
+    if (n_edges > 0 && !vec) return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
+    return conv_backward_impl(plan, x, nullptr, vec, vec_perm, w, src, dst_row_ptr, node_order, src_row_ptr, src_perm,
+                              g_out, n_nodes, n_edges, g_x, g_sh, g_w, F, workspace, workspace_bytes, stream);
 }
 
 int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
@@ -463,7 +545,7 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
     hipStream_t s = (hipStream_t)stream;
     if (n_nodes == 0) return CGTP_OK;
     if (!dst_row_ptr || (d_x && (!src_row_ptr || (n_edges > 0 && !src_perm))) ||
-        (n_edges > 0 && (!x || !sh || !w || !src || !g_out)))
+        (n_edges > 0 && (!x || !w || !src || !g_out || ((gg_x || gg_w) && !sh))))
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
     const int64_t E = n_edges;
     bool wrote_g = false, wrote_sh = false, wrote_w = false, wrote_m = false;

@@ -93,6 +93,7 @@ struct Plan {
     uint32_t flags = 0;
     int64_t dim1 = 0, dim2 = 0, dim3 = 0, wnumel = 0;
     int lmax2 = 0;
+    int sh_lmax = -1;  // input 2 is the SH row of degrees 0..sh_lmax (one copy each), else -1
     std::vector<Path> paths;
 
     KernelShape fwd, bwd, dbl;
@@ -162,6 +163,10 @@ int launch_sum_parts(cgtp_dtype dt, const void *parts, int n_parts, int64_t n, v
                      int accumulate, hipStream_t s);
 int launch_zero(cgtp_dtype dt, void *p, int64_t n, hipStream_t s);
 // inv[perm[k]] = k for k < n
+// forces from (a sum of n_parts partial) SH gradients, v: n_edges x 3 scratch
+int launch_sh_forces(int lmax, cgtp_dtype dt, const void *vec, const int32_t *perm, const void *g_sh, int n_parts,
+                     int64_t part_stride, const int32_t *dst_row_ptr, const int32_t *src_row_ptr,
+                     const int32_t *src_perm, int64_t n_nodes, int64_t n_edges, void *F, void *v, hipStream_t s);
 int launch_invert_perm(const int32_t *perm, int64_t n, int32_t *inv, hipStream_t s);
 // out[item][off3 + w*d3 + k] (=|+=) sum_K T[(item*d3 + k)*K + kk] W_b3[kk][w]
 int launch_uvw_mix(const Plan &p, const MixBlock &mb, const void *T, const void *w, int64_t n_items,

@@ -507,10 +507,12 @@ __device__ inline void sh_grad_contract(const ShPoly<T, L> &P, const T *c, T G[3
     }
 }
 
-// per-edge force vector v_t = J_t^T g_t = (I - u u^T) G / |r|
+// per-edge force vector v_t = J_t^T g_t = (I - u u^T) G / |r|; g_t is the
+// sum of n_parts partial rows part_stride elements apart
 template <class T, int L>
 __global__ void k_edge_force(const T *__restrict__ vec, const int32_t *__restrict__ perm,
-                             const T *__restrict__ g_sh, int64_t n, T *__restrict__ v) {
+                             const T *__restrict__ g_sh, int n_parts, int64_t part_stride, int64_t n,
+                             T *__restrict__ v) {
     constexpr int NS = (L + 1) * (L + 1);
     for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n;
          t += (int64_t)gridDim.x * blockDim.x) {
@@ -523,6 +525,9 @@ __global__ void k_edge_force(const T *__restrict__ vec, const int32_t *__restric
         T c[NS];
 #pragma unroll
         for (int k = 0; k < NS; ++k) c[k] = g_sh[t * NS + k];
+        for (int q = 1; q < n_parts; ++q)
+#pragma unroll
+            for (int k = 0; k < NS; ++k) c[k] += g_sh[q * part_stride + t * NS + k];
         T G[3];
         sh_grad_contract<T, L>(P, c, G);
         const T ug = u[0] * G[0] + u[1] * G[1] + u[2] * G[2];
@@ -632,15 +637,15 @@ struct ShLaunch {
 
 template <int L>
 struct ForceLaunch {
-    static int run(cgtp_dtype dt, const void *vec, const int32_t *perm, const void *g_sh, int64_t n, void *v,
-                   hipStream_t s) {
+    static int run(cgtp_dtype dt, const void *vec, const int32_t *perm, const void *g_sh, int n_parts,
+                   int64_t part_stride, int64_t n, void *v, hipStream_t s) {
         unsigned g = grid_for(n);
         if (dt == CGTP_F32)
             CGTP_LAUNCH("k_edge_force", s, (k_edge_force<float, L>), dim3(g), dim3(kBlock), 0, s, (const float *)vec, perm,
-                               (const float *)g_sh, n, (float *)v);
+                        (const float *)g_sh, n_parts, part_stride, n, (float *)v);
         else
             CGTP_LAUNCH("k_edge_force", s, (k_edge_force<double, L>), dim3(g), dim3(kBlock), 0, s, (const double *)vec, perm,
-                               (const double *)g_sh, n, (double *)v);
+                        (const double *)g_sh, n_parts, part_stride, n, (double *)v);
         return hip_check(hipGetLastError(), "edge force launch");
     }
 };
@@ -865,6 +870,24 @@ int launch_sum_parts(cgtp_dtype dt, const void *parts, int n_parts, int64_t n, v
     return hip_check(hipGetLastError(), "part sum launch");
 }
 
+int launch_sh_forces(int lmax, cgtp_dtype dt, const void *vec, const int32_t *perm, const void *g_sh, int n_parts,
+                     int64_t part_stride, const int32_t *dst_row_ptr, const int32_t *src_row_ptr,
+                     const int32_t *src_perm, int64_t n_nodes, int64_t n_edges, void *F, void *v, hipStream_t s) {
+    if (n_edges > 0) {
+        int rc = dispatch_l<ForceLaunch>(lmax, dt, vec, perm, g_sh, n_parts, part_stride, n_edges, v, s);
+        if (rc) return rc;
+    }
+    if (n_nodes == 0) return CGTP_OK;
+    unsigned g = (unsigned)n_nodes;
+    if (dt == CGTP_F32)
+        CGTP_LAUNCH("k_node_force", s, k_node_force<float>, dim3(g), dim3(64), 0, s, (const float *)v, dst_row_ptr,
+                    src_row_ptr, src_perm, n_nodes, (float *)F);
+    else
+        CGTP_LAUNCH("k_node_force", s, k_node_force<double>, dim3(g), dim3(64), 0, s, (const double *)v, dst_row_ptr,
+                    src_row_ptr, src_perm, n_nodes, (double *)F);
+    return hip_check(hipGetLastError(), "node force launch");
+}
+
 int launch_invert_perm(const int32_t *perm, int64_t n, int32_t *inv, hipStream_t s) {
     if (n <= 0) return CGTP_OK;
     unsigned g = grid_for(n);
@@ -1037,19 +1060,8 @@ int cgtp_sh_forces(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_
     if (n_nodes < 0 || n_edges < 0 || (n_nodes > 0 && (!F || !dst_row_ptr || !src_row_ptr)) ||
         (n_edges > 0 && (!vec || !g_sh || !src_perm || !workspace)) || workspace_bytes < need)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sh_forces: bad argument");
-    if (n_edges > 0) {
-        int rc = dispatch_l<ForceLaunch>(lmax, dtype, vec, perm, g_sh, n_edges, workspace, s);
-        if (rc) return rc;
-    }
-    if (n_nodes == 0) return CGTP_OK;
-    unsigned g = (unsigned)n_nodes;
-    if (dtype == CGTP_F32)
-        CGTP_LAUNCH("k_node_force", s, k_node_force<float>, dim3(g), dim3(64), 0, s, (const float *)workspace, dst_row_ptr,
-                           src_row_ptr, src_perm, n_nodes, (float *)F);
-    else
-        CGTP_LAUNCH("k_node_force", s, k_node_force<double>, dim3(g), dim3(64), 0, s, (const double *)workspace, dst_row_ptr,
-                           src_row_ptr, src_perm, n_nodes, (double *)F);
-    return hip_check(hipGetLastError(), "node force launch");
+    return launch_sh_forces(lmax, dtype, vec, perm, g_sh, 1, 0, dst_row_ptr, src_row_ptr, src_perm, n_nodes, n_edges,
+                            F, workspace, s);
 }
 
 int cgtp_force_loss_sh_cotangent(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm,

@@ -186,6 +186,18 @@ int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const voi
                       int64_t n_nodes, int64_t n_edges, void *out, void *workspace,
                       size_t workspace_bytes, cgtp_stream_t stream);
 
+/* The same convolution with the SH of the edges computed inside the kernel
+ * from the edge vectors ([SE3] basis computation, moved into the
+ * convolution): edge t uses sh[t] = Y(vec[e] / |vec[e]|), e = vec_perm ?
+ * vec_perm[t] : t, with the conventions of cgtp_spherical_harmonics; vec
+ * [*][3] float (double for CGTP_F64 plans).  Needs a plan whose input 2 is
+ * one SH row, 1x0+1x1+...+1xL with L <= 6 (parity labels absent or
+ * (-1)^l); other plans return UNSUPPORTED.  The SH never reach memory. */
+int cgtp_conv_forward_vec(cgtp_plan_t plan, const void *x, const void *vec, const int32_t *vec_perm,
+                          const void *w, const int32_t *src, const int32_t *dst_row_ptr,
+                          const int32_t *node_order, int64_t n_nodes, int64_t n_edges, void *out,
+                          void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
 /* Workspace needed by cgtp_conv_backward / cgtp_conv_double_backward for a
  * graph with n_edges edges (bytes; 256-byte aligned pointer required).
  * The backward calls are provided for uvu plans (FP32 and FP64). */
@@ -212,6 +224,22 @@ int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const vo
                        int64_t n_edges, void *g_x, void *g_sh, void *g_w, void *workspace,
                        size_t workspace_bytes, cgtp_stream_t stream);
 
+/* Backward with the SH computed from the edge vectors (as in
+ * cgtp_conv_forward_vec) and, when F [n_nodes][3] is given, the forces of
+ * the energy <g_out, out> on the atoms whose positions give the edge
+ * vectors (vec = pos[dst] - pos[src]), without writing the SH gradient:
+ *   F[a] = - sum_{t: dst=a} J_t^T g_sh[t] + sum_{t: src=a} J_t^T g_sh[t],
+ * J_t = dY/dvec at vec_t, reduced per atom over dst_row_ptr and over
+ * (src_row_ptr, src_perm) without atomics (as cgtp_sh_forces).  Any of g_x,
+ * g_sh, g_w, F may be NULL.  Other arguments and the workspace as in
+ * cgtp_conv_backward. */
+int cgtp_conv_backward_vec(cgtp_plan_t plan, const void *x, const void *vec, const int32_t *vec_perm,
+                           const void *w, const int32_t *src, const int32_t *dst_row_ptr,
+                           const int32_t *node_order, const int32_t *src_row_ptr,
+                           const int32_t *src_perm, const void *g_out, int64_t n_nodes,
+                           int64_t n_edges, void *g_x, void *g_sh, void *g_w, void *F,
+                           void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
 /* Second derivatives ([KG]: higher partial derivatives for forces).  The
  * convolution f(x, sh, w) is trilinear, so for cotangents (gg_x, gg_sh,
  * gg_w) on the backward's outputs the derivatives of
@@ -221,7 +249,8 @@ int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const vo
  *   d_x     = fx*(g_out; gg_sh, w) + fx*(g_out; sh, gg_w)
  *   d_sh    = fsh*(g_out; gg_x, w) + fsh*(g_out; x, gg_w)
  *   d_w     = fw*(g_out; gg_x, sh) + fw*(g_out; x, gg_sh)
- * NULL cotangents are zero; NULL outputs are skipped.  Shapes as in
+ * NULL cotangents are zero; NULL outputs are skipped; sh is read only for
+ * the gg_x and gg_w terms (may be NULL when both are NULL).  Shapes as in
  * cgtp_conv_backward (d_g_out has the shape of g_out). */
 int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
                               const int32_t *src, const int32_t *dst,

@@ -262,6 +262,83 @@ def test_node_order_sorts_rows(B, torch, case):
     assert np.all(deg[:-1] >= deg[1:])
 
 
+def _edge_vectors(rs, n_edges, dtype):
+    """Random edge vectors, lengths in [0.5, 2)."""
+    v = rs.standard_normal((n_edges, 3))
+    v *= (0.5 + 1.5 * rs.random((n_edges, 1))) / np.linalg.norm(v, axis=1, keepdims=True)
+    return v.astype(np.float64 if dtype == "f64" else np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("k", [0, 1, 2])
+def test_conv_sh_from_vectors_small(B, torch, k, dtype):
+    """SH computed inside the kernels from the edge vectors; backward with
+    fused forces, against the oracle given the same vectors."""
+    plan, prob = _small_problem(B, k, dtype)
+    lmax = {0: 2, 1: 3, 2: 3}[k]
+    src, dst = _small_graph(61, 700, 80 + k)
+    G = GraphArrays(src, dst, 61)
+    rng = np.random.default_rng(90 + k)
+    x = W.normal(rng, (61, prob.dim1), dtype)
+    w = W.normal(rng, (G.E, prob.weight_numel), dtype)
+    g = W.normal(rng, (61, prob.dim3), dtype)
+    vec = _edge_vectors(rng, G.E, dtype)
+    sh = oracle.spherical_harmonics(lmax, vec.astype(np.float64))
+    d = G.dev(torch)
+    dv = lambda a: to_dev(torch, a, dtype)
+    vec_d, perm_d = torch.from_numpy(vec).cuda(), torch.from_numpy(G.perm).cuda()
+    order = B.cgtp_node_order(d["dst_row_ptr"])
+    print(f"sh from vectors k={k} {dtype}", flush=True)
+    out = B.cgtp_conv_forward_vec(plan, dv(x), vec_d, perm_d, dv(w[G.perm]), d["src"], d["dst_row_ptr"],
+                                  node_order=order)
+    ox, osh, ow, oF = B.cgtp_conv_backward_vec(plan, dv(x), vec_d, perm_d, dv(w[G.perm]), d["src"],
+                                               d["dst_row_ptr"], d["src_row_ptr"], d["src_perm"], dv(g),
+                                               need=("x", "sh", "w", "F"), node_order=order)
+    _, _, _, oF2 = B.cgtp_conv_backward_vec(plan, dv(x), vec_d, perm_d, dv(w[G.perm]), d["src"],
+                                            d["dst_row_ptr"], d["src_row_ptr"], d["src_perm"], dv(g), need=("F",))
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), prob.conv_forward(x, sh, w, src, dst, 61), dtype, "forward")
+    gx, gy, gw = prob.conv_backward(x, sh, w, src, dst, g)
+    assert_close(ox.cpu().numpy(), gx, dtype, "g_x")
+    assert_close(osh.cpu().numpy(), gy[G.perm], dtype, "g_sh")
+    assert_close(ow.cpu().numpy(), gw[G.perm], dtype, "g_w")
+    F_ref = oracle.forces(lmax, 61, src, dst, vec.astype(np.float64), gy)
+    assert_close(oF.cpu().numpy(), F_ref, dtype, "forces (g_sh written)")
+    assert_close(oF2.cpu().numpy(), F_ref, dtype, "forces (from unit partials)")
+
+
+def test_conv_sh_from_vectors_needs_sh_input(B, torch):
+    plan, prob = _small_problem(B, 3, "f32")     # input 2 = 2x0e+1x1o: not one SH row
+    z = torch.zeros(1, device="cuda")
+    e = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rp = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    with pytest.raises(B.CgtpError) as ei:
+        B.cgtp_conv_forward_vec(plan, torch.zeros(1, prob.dim1, device="cuda"), torch.ones(1, 3, device="cuda"),
+                                None, torch.zeros(1, prob.weight_numel, device="cuda"), e, rp)
+    assert ei.value.code == -2
+    del z
+
+
+def test_uvw_sh_from_vectors(B, torch):
+    """bf16 uvw with the SH (l <= 6) computed in the kernel and rounded to
+    bf16 there, against the oracle on unrounded SH."""
+    plan, prob = _uvw_case(B, 2)
+    src, dst = _small_graph(45, 500, 11)
+    G = GraphArrays(src, dst, 45)
+    rng = np.random.default_rng(12)
+    x = W.normal(rng, (45, prob.dim1), "bf16")
+    w = W.normal(rng, (prob.weight_numel,), "bf16")
+    vec = _edge_vectors(rng, G.E, "f32")
+    sh = oracle.spherical_harmonics(6, vec.astype(np.float64))
+    d = G.dev(torch)
+    print("uvw sh from vectors", flush=True)
+    out = B.cgtp_conv_forward_vec(plan, to_dev(torch, x, "bf16"), torch.from_numpy(vec).cuda(),
+                                  torch.from_numpy(G.perm).cuda(), to_dev(torch, w, "bf16"), d["src"],
+                                  d["dst_row_ptr"])
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), prob.conv_forward(x, sh, w, src, dst, 45), "bf16", "uvw forward")
+
+
 def test_conv_no_edges(B, torch):
     plan, prob = _small_problem(B, 0, "f32")
     x = torch.randn(4, prob.dim1, device="cuda")
