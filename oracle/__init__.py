@@ -79,6 +79,8 @@ def lib():
         L.orc_force_loss_cotangent.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
         L.orc_csr.restype = i32
         L.orc_csr.argtypes = [vp, i64, i64, vp, vp]
+        L.orc_sparse_attention.restype = i32
+        L.orc_sparse_attention.argtypes = [i64, i64, i64, vp, vp, i32, i32, d, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -333,3 +335,19 @@ def csr(key, n_nodes):
     rc = lib().orc_csr(_p(key), len(key), n_nodes, _p(perm), _p(row_ptr))
     assert rc == 0
     return perm, row_ptr
+
+
+def sparse_attention(q, k, v, src, dst, n_rows, scale=None):
+    """Graph sparse attention, per head (Fused3S abstract: SDDMM, softmax,
+    SpMM).  q [n_rows][H][d], k and v [n_cols][H][d]; edges src -> dst in
+    any order; scale defaults to 1/sqrt(d).  Rows without edges are zero."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    src, dst = _i32(src), _i32(dst)
+    H, d = q.shape[1], q.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.empty((n_rows, H, d))
+    rc = lib().orc_sparse_attention(n_rows, k.shape[0], len(src), _p(src), _p(dst), H, d, float(scale),
+                                    _p(q), _p(k), _p(v), _p(out))
+    assert rc == 0
+    return out

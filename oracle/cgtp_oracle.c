@@ -600,3 +600,75 @@ int orc_csr(const int32_t *key, int64_t n_edges, int64_t n_nodes, int32_t *perm,
     free(cnt);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Sparse attention over a graph: "Fused3S: Fast Sparse Attention on    */
+/* Tensor Cores" (abstract) splits it into sampled dense-dense matrix    */
+/* multiplication, softmax normalisation and sparse matrix               */
+/* multiplication.  Written here as those three steps, per head h:       */
+/*   s_e   = scale * <q[dst e][h], k[src e][h]>          (SDDMM)         */
+/*   p_e   = exp(s_e) / sum_{e': dst e' = dst e} exp(s_e')   (softmax)   */
+/*   out[i][h] = sum_{e: dst e = i} p_e v[src e][h]      (SpMM)          */
+/* Rows with no edge are zero.  q [n_rows][H][d], k and v [n_cols][H][d], */
+/* out [n_rows][H][d]; edges in any order.                               */
+/* ------------------------------------------------------------------ */
+
+int orc_sparse_attention(int64_t n_rows, int64_t n_cols, int64_t n_edges, const int32_t *src,
+                         const int32_t *dst, int n_heads, int head_dim, double scale, const double *q,
+                         const double *k, const double *v, double *out) {
+    /* edges of each row, in edge order */
+    int64_t *start = calloc((size_t)n_rows + 1, sizeof(int64_t));
+    int64_t *idx = malloc(sizeof(int64_t) * (size_t)(n_edges > 0 ? n_edges : 1));
+    for (int64_t e = 0; e < n_edges; ++e) {
+        if (src[e] < 0 || src[e] >= n_cols || dst[e] < 0 || dst[e] >= n_rows) {
+            free(start);
+            free(idx);
+            return -1;
+        }
+        start[dst[e] + 1]++;
+    }
+    for (int64_t i = 0; i < n_rows; ++i) start[i + 1] += start[i];
+    {
+        int64_t *fill = malloc(sizeof(int64_t) * (size_t)(n_rows + 1));
+        memcpy(fill, start, sizeof(int64_t) * (size_t)(n_rows + 1));
+        for (int64_t e = 0; e < n_edges; ++e) idx[fill[dst[e]]++] = e;
+        free(fill);
+    }
+    const int64_t rowlen = (int64_t)n_heads * head_dim;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t deg = start[i + 1] - start[i];
+        double *s = malloc(sizeof(double) * (size_t)(deg > 0 ? deg : 1));
+        for (int h = 0; h < n_heads; ++h) {
+            double *o = out + i * rowlen + (int64_t)h * head_dim;
+            for (int c = 0; c < head_dim; ++c) o[c] = 0.0;
+            if (deg == 0) continue;
+            const double *qi = q + i * rowlen + (int64_t)h * head_dim;
+            /* SDDMM: scores of the row's edges */
+            double smax = -HUGE_VAL;
+            for (int64_t t = 0; t < deg; ++t) {
+                const double *kj = k + (int64_t)src[idx[start[i] + t]] * rowlen + (int64_t)h * head_dim;
+                double dot = 0.0;
+                for (int c = 0; c < head_dim; ++c) dot += qi[c] * kj[c];
+                s[t] = scale * dot;
+                if (s[t] > smax) smax = s[t];
+            }
+            /* softmax over the row (shifted by the row maximum) */
+            double z = 0.0;
+            for (int64_t t = 0; t < deg; ++t) {
+                s[t] = exp(s[t] - smax);
+                z += s[t];
+            }
+            /* SpMM */
+            for (int64_t t = 0; t < deg; ++t) {
+                const double *vj = v + (int64_t)src[idx[start[i] + t]] * rowlen + (int64_t)h * head_dim;
+                const double p = s[t] / z;
+                for (int c = 0; c < head_dim; ++c) o[c] += p * vj[c];
+            }
+        }
+        free(s);
+    }
+    free(start);
+    free(idx);
+    return 0;
+}
