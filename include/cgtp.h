@@ -292,6 +292,23 @@ int cgtp_node_order_workspace_bytes(int64_t n_nodes, size_t *bytes);
 int cgtp_node_order(const int32_t *row_ptr, int64_t n_nodes, int32_t *order, void *workspace,
                     size_t workspace_bytes, cgtp_stream_t stream);
 
+/* Graph sparse attention ([F3S]: sampled dense-dense product, softmax and
+ * sparse-dense product fused in one kernel on the matrix cores):
+ *   s_t = scale <q[i][h], k[col[t]][h]>   for t in [row_ptr[i], row_ptr[i+1])
+ *   out[i][h] = sum_t (exp(s_t) / sum_t' exp(s_t')) v[col[t]][h]
+ * q [n_rows][n_heads][head_dim], k and v [n_cols][n_heads][head_dim], bf16
+ * (dtype CGTP_BF16_F32ACC; q and k 8-byte aligned); out [n_rows][n_heads]
+ * [head_dim] float; head_dim a multiple of 16, at most 128.  Scores and
+ * probabilities stay on the chip; products accumulate in float, the
+ * probabilities enter the second product rounded to bf16.  A row may not
+ * list the same column twice; edges whose column lies outside [0, n_cols)
+ * are ignored; rows without edges are zero.  n_cols < 2^28 - 1.  No
+ * workspace; asynchronous on the stream. */
+int cgtp_sparse_attention(cgtp_dtype dtype, int32_t n_heads, int32_t head_dim, float scale,
+                          const void *q, const void *k, const void *v, const int32_t *col,
+                          const int32_t *row_ptr, int64_t n_rows, int64_t n_cols,
+                          int64_t n_edges, void *out, cgtp_stream_t stream);
+
 /* Checks on the device that row_ptr is a monotone CSR over n_edges and that
  * every index in idx[n_edges] (may be NULL) lies in [0, n_idx_range).
  * Synchronises the stream.  Returns CGTP_OK or CGTP_ERR_GRAPH.
