@@ -45,7 +45,8 @@ class _Dims(ctypes.Structure):
 EXPORTS = [
     "cgtp_plan", "cgtp_plan_info", "cgtp_plan_paths", "cgtp_plan_coupling", "cgtp_plan_source",
     "cgtp_plan_destroy", "cgtp_forward_workspace_bytes", "cgtp_forward", "cgtp_conv_forward",
-    "cgtp_conv_workspace_bytes", "cgtp_conv_forward_vec", "cgtp_conv_backward_vec",
+    "cgtp_conv_workspace_bytes", "cgtp_conv_forward_vec", "cgtp_conv_backward_vec", "cgtp_sparse_attention",
+    "cgtp_sparse_attention_layout_bytes", "cgtp_sparse_attention_prepare",
     "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_csr_workspace_bytes", "cgtp_build_csr",
     "cgtp_validate_csr", "cgtp_node_order_workspace_bytes", "cgtp_node_order", "cgtp_spherical_harmonics", "cgtp_forces_workspace_bytes", "cgtp_sh_forces",
     "cgtp_force_loss_sh_cotangent", "cgtp_timing_enable", "cgtp_timing_collect", "cgtp_last_error",
@@ -77,6 +78,9 @@ def lib():
             "cgtp_conv_double_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
                                           vp, vp, vp, vp, vp, sz, vp],
             "cgtp_node_order_workspace_bytes": [i64, vp],
+            "cgtp_sparse_attention": [i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, i64, i64, vp, sz, vp, vp],
+            "cgtp_sparse_attention_layout_bytes": [i64, i64, vp],
+            "cgtp_sparse_attention_prepare": [vp, vp, i64, i64, i64, vp, sz, vp],
             "cgtp_conv_forward_vec": [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
             "cgtp_conv_backward_vec": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, sz,
                                        vp],
@@ -333,6 +337,32 @@ def cgtp_node_order(row_ptr, ws=None, out=None, stream=None):
         ws = workspace(b.value, row_ptr.device)
     _check(lib().cgtp_node_order(_ptr(row_ptr), n, _ptr(order), _ptr(ws), ws.numel(), _stream(stream, row_ptr)))
     return order
+
+
+def cgtp_sparse_attention_prepare(col, row_ptr, n_cols: int, out=None, stream=None):
+    """Compacted window layout of a CSR graph for cgtp_sparse_attention."""
+    n_rows = row_ptr.shape[0] - 1
+    b = ctypes.c_size_t()
+    _check(lib().cgtp_sparse_attention_layout_bytes(n_rows, col.shape[0], ctypes.byref(b)))
+    layout = workspace(b.value, row_ptr.device) if out is None else out
+    _check(lib().cgtp_sparse_attention_prepare(_ptr(col), _ptr(row_ptr), n_rows, n_cols, col.shape[0], _ptr(layout),
+                                               layout.numel(), _stream(stream, row_ptr)))
+    return layout
+
+
+def cgtp_sparse_attention(q, k, v, row_ptr, n_edges: int, layout, scale=None, out=None, stream=None):
+    """Graph sparse attention per head: q [n_rows][H][D], k and v
+    [n_cols][H][D] (bf16) over a graph prepared by
+    cgtp_sparse_attention_prepare; returns float32 [n_rows][H][D]."""
+    n_rows = row_ptr.shape[0] - 1
+    H, D = q.shape[1], q.shape[2]
+    if scale is None:
+        scale = 1.0 / D ** 0.5
+    if out is None:
+        out = torch.empty(n_rows, H, D, dtype=torch.float32, device=q.device)
+    _check(lib().cgtp_sparse_attention(DTYPES["bf16"], H, D, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
+                                       n_rows, n_edges, _ptr(layout), layout.numel(), _ptr(out), _stream(stream, q)))
+    return out
 
 
 def cgtp_csr_workspace_bytes(n_edges: int, n_keys: int) -> int:

@@ -6,19 +6,19 @@
 //   s_e = scale <q[i][h], k[j][h]>  for every edge e = (j -> i) of the CSR
 //   out[i][h] = sum_e softmax_i(s)_e v[j][h]
 //
-// MI355X design: a workgroup takes a window of 16 consecutive destination
-// rows (the M/N size of the 16x16x16 bf16 MFMA) and one group of four heads
-// (one wavefront per head).  The window's edges are compacted in LDS: keys
-// (column, row) are sorted, each distinct column becomes one column of the
-// window with a 16-bit mask of the rows that hold it, and the distinct
-// columns are processed 16 at a time:
+// MI355X design: rows are taken in windows of 16 consecutive destination
+// rows (the M/N size of the 16x16x16 bf16 MFMA).  A first kernel compacts
+// each window's edges in LDS: keys (column, row) are sorted, and each
+// distinct column becomes one column of the window with a 16-bit mask of
+// the rows that hold it.  A second kernel takes one (window, head) per
+// workgroup and processes the distinct columns 16 at a time:
 //   S^T = K_cols Q^T          one MFMA per 16 of the head dimension
 //   online softmax per row    (running max and sum, masked entries = 0)
 //   O  += P V_cols            P rounded to bf16, FP32 accumulation
 // Computing S transposed leaves each lane with four scores of one row, which
 // is exactly the A-operand layout that the P V product needs, so P never
-// goes through LDS.  Windows with more edges than fit in LDS are taken in
-// batches that continue the same running softmax.
+// goes through LDS.  Windows with more edges than fit in LDS are compacted
+// in batches whose entries follow one another.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -35,6 +35,7 @@ constexpr int kWin = 16;         // destination rows per window
 constexpr int kCap = 2048;       // window edges compacted per batch
 constexpr int kThreads = 256;    // four wavefronts, one head each
 constexpr int kMaxChunks = 8;    // head dimension up to 128
+constexpr int kDepth = 2;        // tiles loaded ahead of the one computed
 
 typedef short a_s4 __attribute__((ext_vector_type(4)));
 typedef float a_f4 __attribute__((ext_vector_type(4)));
@@ -45,41 +46,29 @@ __device__ __forceinline__ short to_bf16(float v) {
     return (short)(u >> 16);
 }
 
-__global__ void __launch_bounds__(kThreads) k_sparse_attention_bf16(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const int32_t *__restrict__ col, const int32_t *__restrict__ row_ptr, int64_t n_rows, int64_t n_cols, int H,
-    int D, float scale, float *__restrict__ out) {
-    __shared__ uint32_t key[kCap];       // (column << 4) | row in window, sorted
-    __shared__ int32_t ucol[kCap];       // distinct columns of the batch, padded with -1
-    __shared__ uint16_t umask[kCap];     // rows of the window holding each distinct column
+// Window compaction: the edges of 16 consecutive rows, taken kCap at a time,
+// sorted by (column, row); each distinct column of a batch becomes one entry
+// (column, 16-bit mask of the rows holding it).  The entries of window w go
+// to [row_ptr[16 w] + 16 w, ...), padded with empty entries to a multiple of
+// 16; win_n[w] = their padded count.  Batches of a window with more than kCap
+// edges follow one another (a column may then appear once per batch, each
+// time with its own rows).
+__global__ void __launch_bounds__(kThreads) k_attention_compact(const int32_t *__restrict__ col,
+                                                                 const int32_t *__restrict__ row_ptr, int64_t n_rows,
+                                                                 int64_t n_cols, int32_t *__restrict__ ucol,
+                                                                 uint16_t *__restrict__ umask,
+                                                                 int32_t *__restrict__ win_n) {
+    __shared__ uint32_t key[kCap];
     __shared__ int32_t rp[kWin + 1];
     __shared__ int32_t part[kThreads];
     __shared__ int32_t n_unique;
-
-    const int64_t r0 = (int64_t)blockIdx.x * kWin;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int h = blockIdx.y * (kThreads / 64) + wave;
-    const bool head_live = h < H;
+    const int64_t w = blockIdx.x, r0 = w * kWin;
     const int nrw = (int)std::min<int64_t>(kWin, n_rows - r0);
-    const int nchunk = D / 16;
     if (threadIdx.x <= kWin) rp[threadIdx.x] = row_ptr[r0 + std::min<int>(threadIdx.x, nrw)];
     __syncthreads();
     const int e_beg = rp[0], e_end = rp[nrw];
-
-    // Q^T fragments of the window (B operand: B[kk][r] = q[r0 + r][h][kk]);
-    // lane holds row lane%16, head-dim entries 4(lane/16)..+3 of each chunk
-    a_s4 qf[kMaxChunks];
-    a_f4 acc[kMaxChunks];
-    const int rq = lane & 15, quad = lane >> 4;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-        qf[c] = a_s4{0, 0, 0, 0};
-        acc[c] = a_f4{0.f, 0.f, 0.f, 0.f};
-        if (c < nchunk && head_live && rq < nrw)
-            qf[c] = *(const a_s4 *)(q + ((r0 + rq) * H + h) * (int64_t)D + c * 16 + 4 * quad);
-    }
-    float m_run = -INFINITY, l_run = 0.f;   // softmax state of row lane%16
-
+    const int64_t base = (int64_t)e_beg + kWin * w;   // first entry of the window
+    int written = 0;                                  // entries of the window so far
     for (int b0 = e_beg; b0 < e_end; b0 += kCap) {
         const int nb = std::min(kCap, e_end - b0);
         int np2 = 1;
@@ -110,8 +99,8 @@ __global__ void __launch_bounds__(kThreads) k_sparse_attention_bf16(
                 }
                 __syncthreads();
             }
-        // distinct columns: each thread owns a run of sorted keys, counts the
-        // run heads, and after an exclusive scan writes its columns and masks
+        // each thread owns a run of sorted keys: count the run heads, scan,
+        // then write its distinct columns and their row masks
         const int per = (nb + kThreads - 1) / kThreads;
         const int t0 = threadIdx.x * per, t1 = std::min(nb, t0 + per);
         int heads = 0;
@@ -131,98 +120,176 @@ __global__ void __launch_bounds__(kThreads) k_sparse_attention_bf16(
             n_unique = run;
         }
         __syncthreads();
-        int u = part[threadIdx.x];
+        int u = written + part[threadIdx.x];
         for (int t = t0; t < t1; ++t) {
             const uint32_t kv = key[t];
             if (kv == 0xffffffffu || (t > 0 && (key[t - 1] >> 4) == (kv >> 4))) continue;
             uint32_t m = 0;
-            for (int t2 = t; t2 < nb && (key[t2] >> 4) == (kv >> 4) && key[t2] != 0xffffffffu; ++t2)
+            for (int t2 = t; t2 < nb && key[t2] != 0xffffffffu && (key[t2] >> 4) == (kv >> 4); ++t2)
                 m |= 1u << (key[t2] & 15u);
-            ucol[u] = (int32_t)(kv >> 4);
-            umask[u] = (uint16_t)m;
+            ucol[base + u] = (int32_t)(kv >> 4);
+            umask[base + u] = (uint16_t)m;
             ++u;
         }
-        __syncthreads();
-        const int nu = n_unique;
-        const int nu16 = (nu + 15) & ~15;
-        for (int t = nu + threadIdx.x; t < nu16; t += kThreads) {
-            ucol[t] = -1;
-            umask[t] = 0;
-        }
-        __syncthreads();
-
-        if (head_live) {
-            for (int cb = 0; cb < nu16; cb += 16) {
-                // S^T[c][r] = <k[col c], q[r]>: A = K rows of the 16 columns
-                const int ca = ucol[cb + rq];
-                a_f4 st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < kMaxChunks; ++c) {
-                    if (c >= nchunk) break;
-                    a_s4 a = {0, 0, 0, 0};
-                    if (ca >= 0) a = *(const a_s4 *)(k + ((int64_t)ca * H + h) * D + c * 16 + 4 * quad);
-                    st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, qf[c], st, 0, 0, 0);
-                }
-                // lane holds S[row rq][columns cb + 4 quad + i]
-                float s[4], p[4];
-                float tmax = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool on = (umask[cb + 4 * quad + i] >> rq) & 1u;
-                    s[i] = on ? st[i] * scale : -INFINITY;
-                    tmax = fmaxf(tmax, s[i]);
-                }
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-                const float m_new = fmaxf(m_run, tmax);
-                const float corr = m_new == -INFINITY ? 1.f : __expf(m_run - m_new);
-                float psum = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[i] = s[i] == -INFINITY ? 0.f : __expf(s[i] - m_new);
-                    psum += p[i];
-                }
-                psum += __shfl_xor(psum, 16, 64);
-                psum += __shfl_xor(psum, 32, 64);
-                l_run = l_run * corr + psum;
-                m_run = m_new;
-                // the accumulator rows are 4 quad + i: their corrections
-                float co[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) co[i] = __shfl(corr, 4 * quad + i, 64);
-                const a_s4 pa = {to_bf16(p[0]), to_bf16(p[1]), to_bf16(p[2]), to_bf16(p[3])};
-                int cv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) cv[i] = ucol[cb + 4 * quad + i];
-#pragma unroll
-                for (int c = 0; c < kMaxChunks; ++c) {
-                    if (c >= nchunk) break;
-                    // B[kk][dd] = v[col kk][h][16 c + dd]: lane holds rows 4 quad + i, column rq
-                    a_s4 vb;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        vb[i] = cv[i] >= 0 ? (short)v[((int64_t)cv[i] * H + h) * D + c * 16 + rq] : (short)0;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[c][i] *= co[i];
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[c], 0, 0, 0);
-                }
-            }
-        }
-        __syncthreads();   // LDS is rewritten by the next batch
+        written += n_unique;
+        __syncthreads();   // key, part and n_unique are reused by the next batch
     }
-    if (!head_live) return;
-    // out[r][h][16 c + rq] = O[r][.] / l[r] for the rows 4 quad + i
-    float lo[4];
+    const int padded = (written + 15) & ~15;
+    for (int t = written + threadIdx.x; t < padded; t += kThreads) {
+        ucol[base + t] = -1;
+        umask[base + t] = 0;
+    }
+    if (threadIdx.x == 0) win_n[w] = padded;
+}
+
+// Layout of the compacted windows inside the caller's buffer.
+struct AttnLayout {
+    int32_t *ucol;
+    uint16_t *umask;
+    int32_t *win_n;
+    size_t bytes;
+    AttnLayout(void *p, int64_t n_rows, int64_t n_edges) {
+        const size_t n_win = (size_t)((n_rows + kWin - 1) / kWin);
+        const size_t cap = (size_t)n_edges + kWin * n_win;
+        ucol = (int32_t *)p;
+        umask = (uint16_t *)((char *)p + align256(cap * sizeof(int32_t)));
+        win_n = (int32_t *)((char *)umask + align256(cap * sizeof(uint16_t)));
+        bytes = align256(cap * sizeof(int32_t)) + align256(cap * sizeof(uint16_t)) + align256(n_win * sizeof(int32_t));
+    }
+};
+
+// One workgroup per (window, head); its four wavefronts take every fourth
+// 16-column tile of the window and keep their own running softmax, merged
+// through LDS at the end.  The next tile's K and V operands are loaded
+// before the current tile is computed.
+template <int NC>   // head dimension = 16 NC
+__global__ void __launch_bounds__(kThreads) k_sparse_attention_bf16(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ ucol, const uint16_t *__restrict__ umask,
+    const int32_t *__restrict__ win_n, int64_t n_rows, int H, float scale, float *__restrict__ out) {
+    constexpr int kWaves = kThreads / 64;
+    constexpr int kMaxChunks = NC, nchunk = NC, D = 16 * NC;
+    __shared__ float s_m[kWaves][kWin], s_l[kWaves][kWin];
+    __shared__ float s_o[kWaves][kWin][D];
+    const int64_t w = blockIdx.x, r0 = w * kWin;
+    const int h = blockIdx.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rq = lane & 15, quad = lane >> 4;
+    const int nrw = (int)std::min<int64_t>(kWin, n_rows - r0);
+    const int64_t base = (int64_t)row_ptr[r0] + kWin * w;
+    const int ntile = win_n[w] / 16;
+
+    // Q^T fragments (B operand: B[kk][r] = q[r0 + r][h][kk]); lane holds row
+    // rq, head-dimension entries 4 quad..+3 of each chunk of 16
+    a_s4 qf[kMaxChunks];
+    a_f4 acc[kMaxChunks];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lo[i] = __shfl(l_run, 4 * quad + i, 64);
+    for (int c = 0; c < kMaxChunks; ++c) {
+        qf[c] = a_s4{0, 0, 0, 0};
+        acc[c] = a_f4{0.f, 0.f, 0.f, 0.f};
+        if (c < nchunk && rq < nrw) qf[c] = *(const a_s4 *)(q + ((r0 + rq) * H + h) * (int64_t)D + c * 16 + 4 * quad);
+    }
+    float m_run = -INFINITY, l_run = 0.f;   // softmax state of row rq
+
+    // operands of one tile: K rows (A operand), V entries (B operand) and
+    // the row masks; kDepth tiles are in flight ahead of the one computed
+    struct Tile {
+        a_s4 ka[kMaxChunks], vb[kMaxChunks];
+        uint32_t mk[4];
+    };
+    auto load_tile = [&](int tile, Tile &T) {
+        if (tile >= ntile) return;
+        const int64_t e0 = base + 16 * (int64_t)tile;
+        const int ca = ucol[e0 + rq];
+        int cv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cv[i] = ucol[e0 + 4 * quad + i];
+            T.mk[i] = umask[e0 + 4 * quad + i];
+        }
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) {
+            if (c >= nchunk) break;
+            T.ka[c] = ca >= 0 ? *(const a_s4 *)(k + ((int64_t)ca * H + h) * D + c * 16 + 4 * quad) : a_s4{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                T.vb[c][i] = cv[i] >= 0 ? (short)v[((int64_t)cv[i] * H + h) * D + c * 16 + rq] : (short)0;
+        }
+    };
+    Tile ring[kDepth + 1];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) load_tile(wave + d * kWaves, ring[d]);
+    for (int tile = wave; tile < ntile; tile += kWaves) {
+        load_tile(tile + kDepth * kWaves, ring[kDepth]);
+        const Tile &T = ring[0];
+        // S^T[c][r] = <k[col c], q[r]>; lane holds S[row rq][columns 4 quad + i]
+        a_f4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) {
+            if (c >= nchunk) break;
+            st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(T.ka[c], qf[c], st, 0, 0, 0);
+        }
+        float s[4], p[4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[i] = ((T.mk[i] >> rq) & 1u) ? st[i] * scale : -INFINITY;
+            tmax = fmaxf(tmax, s[i]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run, tmax);
+        const float corr = m_new == -INFINITY ? 1.f : __expf(m_run - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = s[i] == -INFINITY ? 0.f : __expf(s[i] - m_new);
+            psum += p[i];
+        }
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        l_run = l_run * corr + psum;
+        m_run = m_new;
+        // the accumulator rows are 4 quad + i: their corrections
+        float co[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) co[i] = __shfl(corr, 4 * quad + i, 64);
+        // P is already in the A-operand layout: lane holds P[row rq][4 quad + i]
+        const a_s4 pa = {to_bf16(p[0]), to_bf16(p[1]), to_bf16(p[2]), to_bf16(p[3])};
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) {
+            if (c >= nchunk) break;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[c][i] *= co[i];
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, T.vb[c], acc[c], 0, 0, 0);
+        }
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) ring[d] = ring[d + 1];
+    }
+    // merge the wavefronts' states: O = sum_w O_w e^(m_w - M) / sum_w l_w e^(m_w - M)
+    if (quad == 0) {
+        s_m[wave][rq] = m_run;
+        s_l[wave][rq] = l_run;
+    }
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
         if (c >= nchunk) break;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * quad + i;
-            if (r < nrw) out[((r0 + r) * H + h) * D + c * 16 + rq] = lo[i] > 0.f ? acc[c][i] / lo[i] : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) s_o[wave][4 * quad + i][16 * c + rq] = acc[c][i];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nrw * D; idx += kThreads) {
+        const int r = idx / D, dd = idx % D;
+        float M = -INFINITY;
+        for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, s_m[wv][r]);
+        float num = 0.f, den = 0.f;
+        if (M != -INFINITY)
+            for (int wv = 0; wv < kWaves; ++wv) {
+                const float f = s_m[wv][r] == -INFINITY ? 0.f : __expf(s_m[wv][r] - M);
+                num += s_o[wv][r][dd] * f;
+                den += s_l[wv][r] * f;
+            }
+        out[((r0 + r) * H + h) * D + dd] = den > 0.f ? num / den : 0.f;
     }
 }
 
@@ -238,27 +305,69 @@ using namespace cgtp;
 
 extern "C" {
 
+int cgtp_sparse_attention_layout_bytes(int64_t n_rows, int64_t n_edges, size_t *bytes) {
+    clear_error();
+    if (!bytes || n_rows < 0 || n_edges < 0)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention_layout_bytes: bad argument");
+    *bytes = AttnLayout(nullptr, n_rows, n_edges).bytes;
+    return CGTP_OK;
+}
+
+int cgtp_sparse_attention_prepare(const int32_t *col, const int32_t *row_ptr, int64_t n_rows, int64_t n_cols,
+                                  int64_t n_edges, void *layout, size_t layout_bytes, cgtp_stream_t stream) {
+    clear_error();
+    if (n_rows < 0 || n_cols < 0 || n_edges < 0 || n_rows > 0x7fffffffLL || n_edges > 0x7fffffffLL ||
+        n_cols >= (1LL << 28) - 1)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention_prepare: sizes out of range");
+    if (n_rows == 0) return CGTP_OK;
+    const AttnLayout L(layout, n_rows, n_edges);
+    if (!row_ptr || !layout || layout_bytes < L.bytes || (n_edges > 0 && !col))
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention_prepare: NULL buffer or layout too small");
+    if (((uintptr_t)layout) & 255)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention_prepare: layout must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t n_win = (n_rows + kWin - 1) / kWin;
+    CGTP_LAUNCH("k_attention_compact", s, k_attention_compact, dim3((unsigned)n_win), dim3(kThreads), 0, s, col, row_ptr,
+                n_rows, n_cols, L.ucol, L.umask, L.win_n);
+    return hip_ok(hipGetLastError(), "sparse attention prepare launch");
+}
+
 int cgtp_sparse_attention(cgtp_dtype dtype, int32_t n_heads, int32_t head_dim, float scale, const void *q,
-                          const void *k, const void *v, const int32_t *col, const int32_t *row_ptr, int64_t n_rows,
-                          int64_t n_cols, int64_t n_edges, void *out, cgtp_stream_t stream) {
+                          const void *k, const void *v, const int32_t *row_ptr, int64_t n_rows, int64_t n_edges,
+                          const void *layout, size_t layout_bytes, void *out, cgtp_stream_t stream) {
     clear_error();
     if (dtype != CGTP_BF16_F32ACC)
         return set_error(CGTP_ERR_UNSUPPORTED, "cgtp_sparse_attention: bf16 inputs (CGTP_BF16_F32ACC) only");
-    if (n_heads < 1 || head_dim < 16 || head_dim > 16 * kMaxChunks || head_dim % 16 != 0)
-        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention: head_dim must be 16..128, a multiple of 16");
-    if (n_rows < 0 || n_cols < 0 || n_edges < 0 || n_rows > 0x7fffffffLL || n_edges > 0x7fffffffLL ||
-        n_cols >= (1LL << 28) - 1)
+    if (n_heads < 1 || n_heads > 65535 || head_dim < 16 || head_dim > 16 * kMaxChunks || head_dim % 16 != 0)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT,
+                         "cgtp_sparse_attention: head_dim must be 16..128, a multiple of 16; n_heads 1..65535");
+    if (n_rows < 0 || n_edges < 0 || n_rows > 0x7fffffffLL || n_edges > 0x7fffffffLL)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention: sizes out of range");
     if (n_rows == 0) return CGTP_OK;
-    if (!row_ptr || !out || (n_edges > 0 && (!q || !k || !v || !col)))
-        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention: NULL buffer");
+    const AttnLayout L(const_cast<void *>(layout), n_rows, n_edges);
+    if (!row_ptr || !out || !layout || layout_bytes < L.bytes || (n_edges > 0 && (!q || !k || !v)))
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention: NULL buffer or layout too small");
     if ((((uintptr_t)q) | ((uintptr_t)k)) & 7)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention: q and k must be 8-byte aligned");
     hipStream_t s = (hipStream_t)stream;
-    const dim3 grid((unsigned)((n_rows + kWin - 1) / kWin), (unsigned)((n_heads + 3) / 4));
-    CGTP_LAUNCH("k_sparse_attention_bf16", s, k_sparse_attention_bf16, grid, dim3(kThreads), 0, s,
-                (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, col, row_ptr, n_rows, n_cols,
-                (int)n_heads, (int)head_dim, scale, (float *)out);
+    const dim3 grid((unsigned)((n_rows + kWin - 1) / kWin), (unsigned)n_heads);
+    switch (head_dim / 16) {
+#define CGTP_ATTN_CASE(NC)                                                                                          \
+    case NC:                                                                                                         \
+        CGTP_LAUNCH("k_sparse_attention_bf16", s, k_sparse_attention_bf16<NC>, grid, dim3(kThreads), 0, s,           \
+                    (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, row_ptr, L.ucol, L.umask, L.win_n, \
+                    n_rows, (int)n_heads, scale, (float *)out);                                                      \
+        break;
+        CGTP_ATTN_CASE(1)
+        CGTP_ATTN_CASE(2)
+        CGTP_ATTN_CASE(3)
+        CGTP_ATTN_CASE(4)
+        CGTP_ATTN_CASE(5)
+        CGTP_ATTN_CASE(6)
+        CGTP_ATTN_CASE(7)
+        CGTP_ATTN_CASE(8)
+#undef CGTP_ATTN_CASE
+    }
     return hip_ok(hipGetLastError(), "sparse attention launch");
 }
 

@@ -19,7 +19,6 @@ thread_local std::string g_error;
 
 size_t elem_bytes(cgtp_dtype d) { return d == CGTP_F64 ? 8 : (d == CGTP_BF16_F32ACC ? 2 : 4); }
 size_t out_bytes(cgtp_dtype d) { return d == CGTP_F64 ? 8 : 4; }
-size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool path_ok(const Irrep &a, const Irrep &b, const Irrep &c) {
     if (c.l < std::abs(a.l - b.l) || c.l > a.l + b.l) return false;

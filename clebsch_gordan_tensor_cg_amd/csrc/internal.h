@@ -115,6 +115,9 @@ struct Plan {
     int device = -1;
 };
 
+// workspace sub-buffers start on 256-byte boundaries
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
 // Flags of the full, non-accumulating backward (g_w, messages, SH gradient,
 // per-unit parts when there are several units) and fused double backward
 // (d_w and messages); the code object holds a copy of each kernel with

@@ -665,7 +665,6 @@ struct CotLaunch {
     }
 };
 
-size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // ---------------------------------------------------------------------------
 // uvw channel mixing on the matrix cores:

@@ -296,18 +296,29 @@ int cgtp_node_order(const int32_t *row_ptr, int64_t n_nodes, int32_t *order, voi
  * sparse-dense product fused in one kernel on the matrix cores):
  *   s_t = scale <q[i][h], k[col[t]][h]>   for t in [row_ptr[i], row_ptr[i+1])
  *   out[i][h] = sum_t (exp(s_t) / sum_t' exp(s_t')) v[col[t]][h]
- * q [n_rows][n_heads][head_dim], k and v [n_cols][n_heads][head_dim], bf16
- * (dtype CGTP_BF16_F32ACC; q and k 8-byte aligned); out [n_rows][n_heads]
- * [head_dim] float; head_dim a multiple of 16, at most 128.  Scores and
- * probabilities stay on the chip; products accumulate in float, the
- * probabilities enter the second product rounded to bf16.  A row may not
- * list the same column twice; edges whose column lies outside [0, n_cols)
- * are ignored; rows without edges are zero.  n_cols < 2^28 - 1.  No
- * workspace; asynchronous on the stream. */
+ * Two calls.  cgtp_sparse_attention_prepare compacts the graph once: rows
+ * are grouped in windows of 16, and each window's distinct columns are
+ * listed with a 16-bit mask of the rows that hold them.  The layout goes into
+ * a caller-owned buffer of cgtp_sparse_attention_layout_bytes(n_rows,
+ * n_edges) bytes (256-byte aligned).  It depends only on (col, row_ptr), so
+ * it serves every head, layer and call on the same graph.
+ * cgtp_sparse_attention then computes
+ * the attention from q [n_rows][n_heads][head_dim] and k, v
+ * [n_cols][n_heads][head_dim], bf16 (dtype CGTP_BF16_F32ACC; q and k 8-byte
+ * aligned), into out [n_rows][n_heads][head_dim] float; head_dim a multiple
+ * of 16, at most 128.  Scores and probabilities stay on the chip; products
+ * accumulate in float, the probabilities enter the second product rounded
+ * to bf16.  A row may not list the same column twice; edges whose column
+ * lies outside [0, n_cols) are ignored; rows without edges are zero;
+ * n_cols < 2^28 - 1.  Both calls are asynchronous on the stream. */
+int cgtp_sparse_attention_layout_bytes(int64_t n_rows, int64_t n_edges, size_t *bytes);
+int cgtp_sparse_attention_prepare(const int32_t *col, const int32_t *row_ptr, int64_t n_rows,
+                                  int64_t n_cols, int64_t n_edges, void *layout,
+                                  size_t layout_bytes, cgtp_stream_t stream);
 int cgtp_sparse_attention(cgtp_dtype dtype, int32_t n_heads, int32_t head_dim, float scale,
-                          const void *q, const void *k, const void *v, const int32_t *col,
-                          const int32_t *row_ptr, int64_t n_rows, int64_t n_cols,
-                          int64_t n_edges, void *out, cgtp_stream_t stream);
+                          const void *q, const void *k, const void *v, const int32_t *row_ptr,
+                          int64_t n_rows, int64_t n_edges, const void *layout, size_t layout_bytes,
+                          void *out, cgtp_stream_t stream);
 
 /* Checks on the device that row_ptr is a monotone CSR over n_edges and that
  * every index in idx[n_edges] (may be NULL) lies in [0, n_idx_range).
