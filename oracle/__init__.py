@@ -351,3 +351,35 @@ def sparse_attention(q, k, v, src, dst, n_rows, scale=None):
                                     _p(q), _p(k), _p(v), _p(out))
     assert rc == 0
     return out
+
+
+# --------------------------------------------------------------------------
+# Per-edge radial weights ("Faster training and inference with NVIDIA's
+# open-source SE(3)-Transformer", fused keys and values section: the radial
+# profile inside a TFN layer is a fully connected network).  Reading: one
+# hidden layer of width H on the edge length r, SiLU activation, a linear
+# output layer with bias producing the layer's whole weight row:
+#   phi_h(r) = silu(a_h r + c_h),  silu(z) = z / (1 + e^-z)
+#   W_e = w[0] + sum_{h=1..H} phi_h(|r_e|) w[h]        (w: [H+1][weight_numel])
+# The edge's weights then enter the tensor product as per-item weights.
+# --------------------------------------------------------------------------
+def radial_hidden(r, radial):
+    """phi [E][H] for edge lengths r [E]; radial = [2][H] (a, then c)."""
+    r = _f64(r).reshape(-1, 1)
+    radial = _f64(radial)
+    z = r * radial[0][None, :] + radial[1][None, :]
+    return z / (1.0 + np.exp(-z))
+
+
+def radial_weights(r, radial, w):
+    """Per-edge weight rows W [E][weight_numel] from the radial network."""
+    w = _f64(w)
+    phi = radial_hidden(r, radial)
+    return w[0][None, :] + phi @ w[1:]
+
+
+def conv_forward_radial(prob, x, sh, r, radial, w, src, dst, n_nodes):
+    """Convolution whose per-edge weights come from the radial network of
+    the edge lengths r (prob must hold per-item weights)."""
+    assert not prob.shared_weights
+    return prob.conv_forward(x, sh, radial_weights(r, radial, w), src, dst, n_nodes)

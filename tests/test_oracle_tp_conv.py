@@ -305,3 +305,48 @@ def test_csr_matches_stable_argsort():
         perm, row_ptr = oracle.csr(key, n)
         np.testing.assert_array_equal(perm, np.argsort(key, kind="stable"))
         np.testing.assert_array_equal(row_ptr, np.concatenate([[0], np.cumsum(np.bincount(key, minlength=n))]))
+
+
+# ---------------------------------------------------------------------------
+# radial weights (TFN with per-edge weights from a fully connected network)
+# ---------------------------------------------------------------------------
+def test_radial_weights_closed_forms():
+    rs = np.random.default_rng(5)
+    r = rs.uniform(0.5, 5.0, 7)
+    radial = rs.standard_normal((2, 3))
+    w = rs.standard_normal((4, 6))
+    W = oracle.radial_weights(r, radial, w)
+    # written out entry by entry with math.exp
+    import math
+    for e in range(7):
+        for j in range(6):
+            acc = w[0, j]
+            for h in range(3):
+                z = radial[0, h] * r[e] + radial[1, h]
+                acc += z / (1.0 + math.exp(-z)) * w[h + 1, j]
+            assert abs(W[e, j] - acc) < 1e-12
+    # silu(0) = 0: zero first layer leaves the bias row
+    np.testing.assert_allclose(oracle.radial_weights(r, np.zeros((2, 3)), w), np.broadcast_to(w[0], (7, 6)))
+
+
+def test_radial_conv_reduces_to_shared_weights():
+    """With a = 0 every edge gets the same row w0 + sum_h silu(c_h) w_h: the
+    convolution equals the shared-weight convolution with that row."""
+    a, b, c = "3x0+2x1", "1x0+1x1+1x2", "4x0+4x1+2x2"
+    per = oracle.Problem(a, b, c, "uvw")
+    shared = oracle.Problem(a, b, c, "uvw", shared_weights=True)
+    rs = np.random.default_rng(6)
+    n, E = 9, 40
+    src, dst = rs.integers(0, n, E).astype(np.int32), rs.integers(0, n, E).astype(np.int32)
+    x = rs.standard_normal((n, per.dim1))
+    sh = rs.standard_normal((E, per.dim2))
+    r = rs.uniform(1, 4, E)
+    radial = np.stack([np.zeros(3), rs.standard_normal(3)])
+    w = rs.standard_normal((4, per.weight_numel))
+    z = radial[1]
+    row = w[0] + (z / (1 + np.exp(-z))) @ w[1:]
+    got = oracle.conv_forward_radial(per, x, sh, r, radial, w, src, dst, n)
+    np.testing.assert_allclose(got, shared.conv_forward(x, sh, row, src, dst, n), rtol=1e-12, atol=1e-12)
+    # and linearity in the output-layer rows: w -> 2 w doubles the output
+    np.testing.assert_allclose(oracle.conv_forward_radial(per, x, sh, r, radial, 2 * w, src, dst, n), 2 * got,
+                               rtol=1e-12, atol=1e-12)
