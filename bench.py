@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c1", "c5", "attn", "attn_mol"])
+    ap.add_argument("--workload", default="c4", choices=["c4", "c2", "c3", "c1", "c5", "c5r", "attn", "attn_mol"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy", action="store_true",
                     help="kept for old command lines: the 512 MiB device copy now always runs first")
@@ -477,6 +477,106 @@ def bench_single(args, torch, B, W):
 
 
 # ---------------------------------------------------------------------------
+# TFN layer with per-edge radial weights (uvw, bf16 in, FP32 accumulation)
+# ---------------------------------------------------------------------------
+RADIAL_HIDDEN = 8
+
+
+def bench_radial(args, torch, B, W):
+    cfg = W.config("c5")
+    H = RADIAL_HIDDEN
+    rng = np.random.default_rng(args.seed)
+    g = W.molecule_batch(cfg.extra["n_graphs"], cfg.extra["n_atoms"], cutoff=cfg.extra["cutoff"], rng=rng)
+    plan = B.Plan(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.paths, "uvw", "bf16", True, radial_hidden=H)
+    N, E = g.n_nodes, g.n_edges
+    x_np = W.normal(rng, (N, plan.dim_in1), "bf16")
+    w_np = W.normal(rng, (H + 1, plan.weight_numel), "bf16") * np.float32(0.5)
+    radial_np = np.stack([rng.uniform(-1.0, 1.0, H), rng.uniform(-1.0, 1.0, H)]).astype(np.float32)
+    dev = "cuda"
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(torch.bfloat16)
+    x, w = bf(x_np), bf(w_np)
+    radial = torch.from_numpy(radial_np).to(dev)
+    src_c, dst_c = torch.from_numpy(g.src).to(dev), torch.from_numpy(g.dst).to(dev)
+    vec = torch.from_numpy(g.vec.astype(np.float32)).to(dev)
+    perm = torch.empty(E, dtype=torch.int32, device=dev)
+    rp = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    dst_s = torch.empty(E, dtype=torch.int32, device=dev)
+    src_s = torch.empty(E, dtype=torch.int32, device=dev)
+    order = torch.empty(N, dtype=torch.int32, device=dev)
+    csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), dev)
+    ord_ws = B.workspace(4096 * 4, dev)
+    out = torch.empty(N, plan.dim_out, dtype=torch.float32, device=dev)
+    f_ws = B.workspace(B.cgtp_forward_workspace_bytes(plan, N), dev)
+
+    def step():
+        B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s))
+        B.cgtp_node_order(rp, ws=ord_ws, out=order)
+        B.cgtp_conv_forward_radial(plan, x, vec, perm, radial, w, src_s, rp, out=out, ws=f_ws, node_order=order)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record()
+    for i in range(args.steps):
+        step()
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    B.cgtp_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    B.cgtp_timing_enable(False)
+    per_kernel = {}
+    for kname, kms_ in B.cgtp_timing_collect():
+        per_kernel.setdefault(kname, []).append(kms_)
+    kern = {k: {"calls_per_step": len(v) / args.steps, "avg_ms": float(np.mean(v)),
+                "ms_per_step": float(np.sum(v)) / args.steps} for k, v in per_kernel.items()}
+    # path-tensor kernel: the CG products (as in the shared-weight layer) plus
+    # one FMA per radial row for every (path, u, v, k) of every edge
+    a_ir, c_ir = parse_irreps(cfg.irreps_in1), parse_irreps(cfg.irreps_out)
+    outer = sum(2 * H * a_ir[i1][0] * (2 * c_ir[i3][1] + 1) for (i1, _, i3) in plan.paths())
+    flop = (tp_flops(cfg, plan) + outer) * E
+    t_ms = kern["cgtp_fwd"]["avg_ms"]
+    tf = flop / (t_ms * 1e-3) / 1e12
+    mix_flop = sum(2 * N * (2 * c_ir[b][1] + 1) * c_ir[b][0] * (H + 1) *
+                   sum(a_ir[i1][0] for (i1, _, i3) in plan.paths() if i3 == b) for b in range(len(c_ir)))
+    mix_ms = kern["k_uvw_mix"]["ms_per_step"]
+    res = {"metric": METRIC, "value": E / (ms * 1e-3), "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_median": float(np.median(per_step)),
+           "ms_per_step_min": float(np.min(per_step)), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": cfg.name + f", per-edge radial weights (hidden width {H})", "n_atoms": N,
+                      "n_edges": E, "n_paths": plan.n_paths,
+                      "step": "csr + node order + radial uvw conv (SH and radial network in the kernel)"},
+           "roofline": {"bound": "alu", "kernel": "cgtp_fwd", "achieved": round(tf, 3),
+                        "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                        "alg_flop_per_launch": int(flop), "avg_ms": round(t_ms, 4)},
+           "mixing": {"kernel": "k_uvw_mix", "ms_per_step": round(mix_ms, 4),
+                      "TFLOP_per_s": round(mix_flop / (mix_ms * 1e-3) / 1e12, 3), "peak_bf16_mfma": 2500.0},
+           "kernels": kern}
+    if not args.no_cpu_baseline:
+        import oracle
+        prob = oracle.Problem(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, "uvw", cfg.paths, shared_weights=False)
+        n_s = max(1, N // 100)
+        mask = g.dst < n_s
+        v64 = g.vec[mask].astype(np.float32).astype(np.float64)
+        t0 = time.perf_counter()
+        sh = oracle.spherical_harmonics(6, v64)
+        oracle.conv_forward_radial(prob, x_np, sh, np.linalg.norm(v64, axis=1), radial_np, w_np, g.src[mask],
+                                   g.dst[mask], N)
+        dt = time.perf_counter() - t0
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        res["cpu_baseline"] = {"value": int(mask.sum()) / dt, "unit": "edges/s", "cores": threads, "kind": "oracle",
+                               "sample": f"radial network + SH + conv over the {int(mask.sum())} edges into the first "
+                                         f"{n_s} of {N} nodes, {dt:.1f} s, OpenMP threads={threads}"}
+    return res
+
+
+# ---------------------------------------------------------------------------
 # fused graph sparse attention (SDDMM, softmax, SpMM on the matrix cores)
 # ---------------------------------------------------------------------------
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -579,6 +679,8 @@ def main():
     probe = copy_probe(torch)
     if args.workload == "c1":
         res = bench_single(args, torch, B, W)
+    elif args.workload == "c5r":
+        res = bench_radial(args, torch, B, W)
     elif args.workload in ("attn", "attn_mol"):
         res = bench_attention(args, torch, B, W)
     else:

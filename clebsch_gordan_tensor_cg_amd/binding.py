@@ -45,7 +45,7 @@ class _Dims(ctypes.Structure):
 EXPORTS = [
     "cgtp_plan", "cgtp_plan_info", "cgtp_plan_paths", "cgtp_plan_coupling", "cgtp_plan_source",
     "cgtp_plan_destroy", "cgtp_forward_workspace_bytes", "cgtp_forward", "cgtp_conv_forward",
-    "cgtp_conv_workspace_bytes", "cgtp_conv_forward_vec", "cgtp_conv_backward_vec", "cgtp_sparse_attention",
+    "cgtp_conv_workspace_bytes", "cgtp_conv_forward_vec", "cgtp_conv_backward_vec", "cgtp_conv_forward_radial", "cgtp_sparse_attention",
     "cgtp_sparse_attention_layout_bytes", "cgtp_sparse_attention_prepare",
     "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_csr_workspace_bytes", "cgtp_build_csr",
     "cgtp_validate_csr", "cgtp_node_order_workspace_bytes", "cgtp_node_order", "cgtp_spherical_harmonics", "cgtp_forces_workspace_bytes", "cgtp_sh_forces",
@@ -78,6 +78,7 @@ def lib():
             "cgtp_conv_double_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
                                           vp, vp, vp, vp, vp, sz, vp],
             "cgtp_node_order_workspace_bytes": [i64, vp],
+            "cgtp_conv_forward_radial": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
             "cgtp_sparse_attention": [i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, i64, i64, vp, sz, vp, vp],
             "cgtp_sparse_attention_layout_bytes": [i64, i64, vp],
             "cgtp_sparse_attention_prepare": [vp, vp, i64, i64, i64, vp, sz, vp],
@@ -135,17 +136,18 @@ def _stream(stream=None, like=None):
 class Plan:
     def __init__(self, irreps_in1: str, irreps_in2: str, irreps_out: str, paths=None, mode: str = "uvu",
                  dtype: str = "f32", shared_weights: bool = False, no_load: bool = False,
-                 bf16_weights: bool = False):
+                 bf16_weights: bool = False, radial_hidden: int = 0):
         self.dtype = dtype
         self.mode = mode
         self.shared_weights = shared_weights
         self.bf16_weights = bf16_weights
+        self.radial_hidden = radial_hidden
         arr, n = None, 0
         if paths:
             n = len(paths)
             arr = (_Path * n)(*[_Path(*p) for p in paths])
         flags = ((CGTP_SHARED_WEIGHTS if shared_weights else 0) | (CGTP_PLAN_NO_LOAD if no_load else 0) |
-                 (CGTP_BF16_WEIGHTS if bf16_weights else 0))
+                 (CGTP_BF16_WEIGHTS if bf16_weights else 0) | (int(radial_hidden) << 16))
         h = ctypes.c_void_p()
         _check(lib().cgtp_plan(irreps_in1.encode(), irreps_in2.encode(), irreps_out.encode(),
                                ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None, n,
@@ -246,6 +248,22 @@ def cgtp_conv_forward_vec(plan: Plan, x, vec, vec_perm, w, src, dst_row_ptr, out
     _check(lib().cgtp_conv_forward_vec(plan.handle, _ptr(x), _ptr(vec), _ptr(vec_perm), _ptr(w), _ptr(src),
                                        _ptr(dst_row_ptr), _ptr(node_order), N, E, _ptr(out), _ptr(ws),
                                        ws.numel() if ws is not None else 0, _stream(stream, x)))
+    return out
+
+
+def cgtp_conv_forward_radial(plan: Plan, x, vec, vec_perm, radial, w, src, dst_row_ptr, out=None, ws=None,
+                             stream=None, node_order=None):
+    """uvw convolution with per-edge weights from the radial network:
+    radial float32 [2][H], w bf16 [H+1][weight_numel]."""
+    N, E = x.shape[0], src.shape[0]
+    if out is None:
+        out = torch.empty(N, plan.dim_out, dtype=torch.float32, device=x.device)
+    nb = cgtp_forward_workspace_bytes(plan, N)
+    if ws is None and nb:
+        ws = workspace(nb, x.device)
+    _check(lib().cgtp_conv_forward_radial(plan.handle, _ptr(x), _ptr(vec), _ptr(vec_perm), _ptr(radial), _ptr(w),
+                                          _ptr(src), _ptr(dst_row_ptr), _ptr(node_order), N, E, _ptr(out), _ptr(ws),
+                                          ws.numel() if ws is not None else 0, _stream(stream, x)))
     return out
 
 

@@ -177,8 +177,13 @@ int cgtp_plan(const char *irreps_in1, const char *irreps_in2, const char *irreps
     if (mode != CGTP_UVU && mode != CGTP_UVW) return set_error(CGTP_ERR_INVALID_ARGUMENT, "unknown mode");
     if (dtype != CGTP_F32 && dtype != CGTP_F64 && dtype != CGTP_BF16_F32ACC)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "unknown dtype");
-    if (flags & ~(uint32_t)(CGTP_SHARED_WEIGHTS | CGTP_PLAN_NO_LOAD | CGTP_BF16_WEIGHTS))
+    if (flags & ~(uint32_t)(CGTP_SHARED_WEIGHTS | CGTP_PLAN_NO_LOAD | CGTP_BF16_WEIGHTS | CGTP_RADIAL_HIDDEN(255)))
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "unknown flag bits");
+    const int radial_h = (int)((flags >> 16) & 255u);
+    if (radial_h > 0 && (mode != CGTP_UVW || dtype != CGTP_BF16_F32ACC || !(flags & CGTP_SHARED_WEIGHTS) ||
+                         radial_h > 64))
+        return set_error(CGTP_ERR_UNSUPPORTED,
+                         "radial weights: uvw, bf16 inputs, CGTP_SHARED_WEIGHTS and a hidden width of 1..64");
     if (n_paths < 0 || (n_paths > 0 && !paths)) return set_error(CGTP_ERR_INVALID_ARGUMENT, "bad path list");
     try {
         cgtp_plan_t h = new cgtp_plan_s;
@@ -199,6 +204,7 @@ int cgtp_plan(const char *irreps_in1, const char *irreps_in2, const char *irreps
         p.mode = mode;
         p.dtype = dtype;
         p.flags = flags;
+        p.radial_h = (int)((flags >> 16) & 255u);
         p.tune = tuning_from_env();
         auto o1 = offsets(p.in1), o2 = offsets(p.in2), o3 = offsets(p.out);
         p.dim1 = o1.back();
@@ -218,6 +224,8 @@ int cgtp_plan(const char *irreps_in1, const char *irreps_in2, const char *irreps
             }
             p.sh_lmax = sh ? (int)p.in2.size() - 1 : -1;
         }
+        if (p.radial_h > 0 && p.sh_lmax < 0)
+            return fail(CGTP_ERR_UNSUPPORTED, "radial weights need input 2 = one SH row (computed from edge vectors)");
 
         std::vector<cgtp_path> list;
         if (n_paths > 0) {
@@ -350,13 +358,14 @@ void cgtp_plan_destroy(cgtp_plan_t plan) {
 
 static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
                    const int32_t *row_ptr, const int32_t *order, int64_t n_items, int graph, void *out, void *ws,
-                   size_t ws_bytes, hipStream_t s, const void *vec = nullptr, const int32_t *vperm = nullptr) {
+                   size_t ws_bytes, hipStream_t s, const void *vec = nullptr, const int32_t *vperm = nullptr,
+                   const float *radial = nullptr) {
     size_t need = align256((size_t)n_items * p.t_per_item * 2);
     if (ws_bytes < need || (!ws && need)) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace too small");
     if (((uintptr_t)ws) & 255) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     long long n = n_items;
     void *args[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, (void *)&order, (void *)&vec,
-                    (void *)&vperm, &ws, &n, &graph};
+                    (void *)&vperm, (void *)&radial, &ws, &n, &graph};
     const int64_t ipw = p.fwd.items_per_wave;
     int rc = launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
     if (rc) return rc;
@@ -386,6 +395,8 @@ int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, 
     if (batch < 0 || batch > 0x7fffffffLL) return set_error(CGTP_ERR_INVALID_ARGUMENT, "batch out of range");
     if (batch == 0) return CGTP_OK;
     if (!x || !y || !w || !out) return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
+    if (plan->p.radial_h > 0)
+        return set_error(CGTP_ERR_UNSUPPORTED, "radial plans run through cgtp_conv_forward_radial");
     if (plan->p.mode == CGTP_UVW)
         return run_uvw(plan->p, x, y, w, nullptr, nullptr, nullptr, batch, 0, out, workspace, workspace_bytes,
                        (hipStream_t)stream);
@@ -395,9 +406,11 @@ int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, 
 static int conv_forward_impl(cgtp_plan_t plan, const void *x, const void *sh, const void *vec, const int32_t *vperm,
                              const void *w, const int32_t *src, const int32_t *dst_row_ptr, const int32_t *node_order,
                              int64_t n_nodes, int64_t n_edges, void *out, void *workspace, size_t workspace_bytes,
-                             cgtp_stream_t stream) {
+                             cgtp_stream_t stream, bool radial_call = false, const float *radial = nullptr) {
     int rc = check_loaded(plan);
     if (rc) return rc;
+    if ((plan->p.radial_h > 0) && !radial_call)
+        return set_error(CGTP_ERR_UNSUPPORTED, "radial plans run through cgtp_conv_forward_radial");
     if (n_nodes < 0 || n_edges < 0 || n_edges > 0x7fffffffLL || n_nodes > 0x7fffffffLL)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "sizes out of range");
     if (n_nodes == 0) return CGTP_OK;
@@ -405,7 +418,7 @@ static int conv_forward_impl(cgtp_plan_t plan, const void *x, const void *sh, co
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
     if (plan->p.mode == CGTP_UVW)
         return run_uvw(plan->p, x, sh, w, src, dst_row_ptr, node_order, n_nodes, 1, out, workspace,
-                       workspace_bytes, (hipStream_t)stream, vec, vperm);
+                       workspace_bytes, (hipStream_t)stream, vec, vperm, radial);
     return run_fwd(plan->p, x, sh, w, src, dst_row_ptr, node_order, n_nodes, 1, out, 0, (hipStream_t)stream, vec, vperm);
 }
 
@@ -422,6 +435,20 @@ int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const voi
     clear_error();
     return conv_forward_impl(plan, x, sh, nullptr, nullptr, w, src, dst_row_ptr, node_order, n_nodes, n_edges, out,
                              workspace, workspace_bytes, stream);
+}
+
+int cgtp_conv_forward_radial(cgtp_plan_t plan, const void *x, const void *vec, const int32_t *vec_perm,
+                             const float *radial, const void *w, const int32_t *src, const int32_t *dst_row_ptr,
+                             const int32_t *node_order, int64_t n_nodes, int64_t n_edges, void *out, void *workspace,
+                             size_t workspace_bytes, cgtp_stream_t stream) {
+    clear_error();
+    int rc = check_vec_plan(plan);
+    if (rc) return rc;
+    if (plan->p.radial_h <= 0)
+        return set_error(CGTP_ERR_UNSUPPORTED, "cgtp_conv_forward_radial needs a plan with CGTP_RADIAL_HIDDEN(H)");
+    if (n_edges > 0 && (!vec || !radial)) return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
+    return conv_forward_impl(plan, x, nullptr, vec, vec_perm, w, src, dst_row_ptr, node_order, n_nodes, n_edges, out,
+                             workspace, workspace_bytes, stream, true, radial);
 }
 
 int cgtp_conv_forward_vec(cgtp_plan_t plan, const void *x, const void *vec, const int32_t *vec_perm, const void *w,

@@ -78,7 +78,8 @@ Tuning tuning_from_env();
 struct MixBlock {
     int b3 = 0;
     int d3 = 1, mul3 = 0;
-    int64_t K = 0;                 // sum over its paths of mul1 * mul2
+    int64_t K = 0;                 // sum over its paths of mul1 * mul2 (one copy of the paths)
+    int64_t Kr = 0;                // contraction length: K times (radial hidden width + 1)
     int64_t t_off_per_item = 0;    // offset of its T region / n_items
     std::vector<int> paths;        // in path order
     std::vector<int64_t> koff;     // row offset of each path inside K
@@ -94,6 +95,7 @@ struct Plan {
     int64_t dim1 = 0, dim2 = 0, dim3 = 0, wnumel = 0;
     int lmax2 = 0;
     int sh_lmax = -1;  // input 2 is the SH row of degrees 0..sh_lmax (one copy each), else -1
+    int radial_h = 0;  // uvw with per-edge weights from a radial network of this hidden width (0: none)
     std::vector<Path> paths;
 
     KernelShape fwd, bwd, dbl;

@@ -677,7 +677,7 @@ struct CotLaunch {
 // B[4(l/16)+0..3][l%16], and receives D[4(l/16)+i][l%16], i = 0..3.
 // ---------------------------------------------------------------------------
 constexpr int kMixMaxPaths = 64;
-constexpr int kMixKMax = 512;  // contraction rows staged at once (64 KB of bf16 at 64 columns)
+constexpr int kMixKC = 256;   // contraction rows staged per step (32 KB of bf16 at 64 columns)
 struct MixTable {
     int np;
     int64_t kstart[kMixMaxPaths + 1];
@@ -687,14 +687,19 @@ struct MixTable {
 typedef short cgtp_s4 __attribute__((ext_vector_type(4)));
 typedef float cgtp_f4 __attribute__((ext_vector_type(4)));
 
-__global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T, int64_t M, int64_t K,
-                                                 const uint16_t *__restrict__ W, int mul3, MixTable tab,
-                                                 float *__restrict__ out, int64_t dim3, int64_t off3, int d3,
-                                                 int accumulate) {
-    // The weight block (K x 64 columns, K <= kMixKMax) is staged in LDS once
-    // per workgroup; each wavefront then streams 16-row tiles of T through it.
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[kMixKMax * 64];
-    __shared__ int64_t wrow[kMixKMax];
+// out[item][off3 + w*d3 + k] (=|+=) sum_r T[item*d3 + k][r] W'[r][w]: the
+// channel mixing of one output block on the matrix cores.  Contraction row
+// r = h*Kb + kk (h < n_rep, kk < Kb) reads weight row
+// h*wstride + woff_p + (kk - kstart_p)*mul3 of the path p holding kk (n_rep
+// copies of the paths: the rows of a radial network's output layer).  A
+// workgroup owns 64 rows of T (16 per wavefront) and 64 output columns;
+// the weights are staged in LDS kMixKC rows at a time.
+__global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T, int64_t M, int64_t K, int64_t Kb,
+                                                 const uint16_t *__restrict__ W, int64_t wstride, int mul3,
+                                                 MixTable tab, float *__restrict__ out, int64_t dim3, int64_t off3,
+                                                 int d3, int accumulate) {
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[kMixKC * 64];
+    __shared__ int64_t wrow[kMixKC];
     __shared__ int64_t s_kstart[kMixMaxPaths + 1];
     __shared__ int64_t s_woff[kMixMaxPaths];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -704,84 +709,91 @@ __global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T,
     __syncthreads();
     const int r_a = lane & 15;
     const int kq = 4 * (lane >> 4);
-    const int64_t n_tiles = (M + 15) / 16;
+    const int64_t n_groups = (M + 63) / 64;
     const bool vec_ok = (K % 4) == 0 && (((uintptr_t)T) & 7) == 0;
     // whole 16-byte weight segments: 8-aligned rows and offsets, full columns
-    bool wvec = (mul3 % 64) == 0 && (((uintptr_t)W) & 15) == 0;
+    bool wvec = (mul3 % 64) == 0 && (((uintptr_t)W) & 15) == 0 && (wstride % 8) == 0;
     for (int p = 0; p < tab.np; ++p) wvec = wvec && (tab.woff[p] % 8) == 0;
     for (int cb = 0; cb < mul3; cb += 64) {
         const int ncol = mul3 - cb < 64 ? mul3 - cb : 64;
-        __syncthreads();
-        for (int kr = tid; kr < K; kr += 256) {
-            int p = 0;
-            while (p + 1 < tab.np && kr >= s_kstart[p + 1]) ++p;
-            wrow[kr] = s_woff[p] + (kr - s_kstart[p]) * mul3 + cb;
-        }
-        __syncthreads();
-        if (wvec) {
-            // 8 threads per weight row, 16 bytes each, four rows in flight
-            for (int base = tid; base < K * 8; base += 1024) {
-                uint4 v[4];
-                int idx[4];
-                for (int u = 0; u < 4; ++u) {
-                    idx[u] = base + u * 256;
-                    v[u] = make_uint4(0, 0, 0, 0);
-                    if (idx[u] < K * 8 && (idx[u] & 7) * 8 < ncol)
-                        v[u] = *(const uint4 *)(W + wrow[idx[u] >> 3] + (idx[u] & 7) * 8);
-                }
-                for (int u = 0; u < 4; ++u)
-                    if (idx[u] < K * 8) *(uint4 *)(Ws + (idx[u] >> 3) * 64 + (idx[u] & 7) * 8) = v[u];
-            }
-        } else {
-            for (int idx = tid; idx < K * 64; idx += 256) {
-                const int kr = idx >> 6, c = idx & 63;
-                Ws[idx] = c < ncol ? W[wrow[kr] + c] : (uint16_t)0;
-            }
-        }
-        __syncthreads();
-        for (int64_t tile = (int64_t)blockIdx.x * 4 + wv; tile < n_tiles; tile += (int64_t)gridDim.x * 4) {
-            const int64_t row0 = tile * 16;
+        for (int64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x) {
+            const int64_t row0 = grp * 64 + wv * 16;
             const int64_t arow = row0 + r_a < M ? row0 + r_a : M - 1;
             const uint16_t *__restrict__ Trow = T + arow * K;
             cgtp_f4 acc[4];
             for (int ct = 0; ct < 4; ++ct) acc[ct] = (cgtp_f4){0.f, 0.f, 0.f, 0.f};
-            // this lane's A fragments, eight k steps at a time, loaded before
-            // the eight steps' matrix operations
-            for (int kb = 0; kb < K; kb += 128) {
-                uint2 af[8];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const int k0 = kb + s * 16;
-                    af[s] = make_uint2(0, 0);
-                    if (k0 >= K) continue;
-                    if (vec_ok && k0 + kq + 4 <= K) {
-                        af[s] = *(const uint2 *)(Trow + k0 + kq);
-                    } else {
-                        uint32_t h[4];
-                        for (int i = 0; i < 4; ++i) h[i] = k0 + kq + i < K ? Trow[k0 + kq + i] : 0u;
-                        af[s] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            for (int64_t k0 = 0; k0 < K; k0 += kMixKC) {
+                const int kc = (int)(K - k0 < kMixKC ? K - k0 : kMixKC);
+                __syncthreads();   // the previous step's weights are no longer read
+                for (int kr = tid; kr < kc; kr += 256) {
+                    const int64_t r = k0 + kr, h = r / Kb, kk = r % Kb;
+                    int p = 0;
+                    while (p + 1 < tab.np && kk >= s_kstart[p + 1]) ++p;
+                    wrow[kr] = h * wstride + s_woff[p] + (kk - s_kstart[p]) * mul3 + cb;
+                }
+                __syncthreads();
+                if (wvec) {
+                    // 8 threads per weight row, 16 bytes each, four rows in flight
+                    for (int base = tid; base < kc * 8; base += 1024) {
+                        uint4 v[4];
+                        int idx[4];
+                        for (int u = 0; u < 4; ++u) {
+                            idx[u] = base + u * 256;
+                            v[u] = make_uint4(0, 0, 0, 0);
+                            if (idx[u] < kc * 8 && (idx[u] & 7) * 8 < ncol)
+                                v[u] = *(const uint4 *)(W + wrow[idx[u] >> 3] + (idx[u] & 7) * 8);
+                        }
+                        for (int u = 0; u < 4; ++u)
+                            if (idx[u] < kc * 8) *(uint4 *)(Ws + (idx[u] >> 3) * 64 + (idx[u] & 7) * 8) = v[u];
+                    }
+                } else {
+                    for (int idx = tid; idx < kc * 64; idx += 256) {
+                        const int kr = idx >> 6, c = idx & 63;
+                        Ws[idx] = c < ncol ? W[wrow[kr] + c] : (uint16_t)0;
                     }
                 }
+                __syncthreads();
+                if (row0 >= M) continue;   // this wavefront has no rows (it still joined the barriers)
+                // this lane's A fragments, eight k steps at a time, loaded
+                // before the eight steps' matrix operations
+                for (int kb = 0; kb < kc; kb += 128) {
+                    uint2 af[8];
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const int k0 = kb + s * 16;
-                    if (k0 >= K) continue;
-                    cgtp_s4 a;
-                    a[0] = (short)(af[s].x & 0xffff);
-                    a[1] = (short)(af[s].x >> 16);
-                    a[2] = (short)(af[s].y & 0xffff);
-                    a[3] = (short)(af[s].y >> 16);
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) {
-                        cgtp_s4 b;
-                        for (int i = 0; i < 4; ++i) {
-                            const int kr = k0 + kq + i;
-                            b[i] = kr < K ? (short)Ws[kr * 64 + ct * 16 + r_a] : (short)0;
+                    for (int st = 0; st < 8; ++st) {
+                        const int kl = kb + st * 16;
+                        af[st] = make_uint2(0, 0);
+                        if (kl >= kc) continue;
+                        const int64_t kg = k0 + kl;
+                        if (vec_ok && kl + kq + 4 <= kc) {
+                            af[st] = *(const uint2 *)(Trow + kg + kq);
+                        } else {
+                            uint32_t hv[4];
+                            for (int i = 0; i < 4; ++i) hv[i] = kl + kq + i < kc ? Trow[kg + kq + i] : 0u;
+                            af[st] = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
                         }
-                        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc[ct], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int st = 0; st < 8; ++st) {
+                        const int kl = kb + st * 16;
+                        if (kl >= kc) continue;
+                        cgtp_s4 a;
+                        a[0] = (short)(af[st].x & 0xffff);
+                        a[1] = (short)(af[st].x >> 16);
+                        a[2] = (short)(af[st].y & 0xffff);
+                        a[3] = (short)(af[st].y >> 16);
+#pragma unroll
+                        for (int ct = 0; ct < 4; ++ct) {
+                            cgtp_s4 b;
+                            for (int i = 0; i < 4; ++i) {
+                                const int kr = kl + kq + i;
+                                b[i] = kr < kc ? (short)Ws[kr * 64 + ct * 16 + r_a] : (short)0;
+                            }
+                            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc[ct], 0, 0, 0);
+                        }
                     }
                 }
             }
+            if (row0 >= M) continue;
             for (int ct = 0; ct < 4; ++ct) {
                 const int col = cb + ct * 16 + r_a;
                 if (col >= mul3) continue;
@@ -804,8 +816,6 @@ int launch_uvw_mix(const Plan &p, const MixBlock &mb, const void *T, const void 
     if (n_items <= 0) return CGTP_OK;
     if ((int)mb.paths.size() > kMixMaxPaths)
         return set_error(CGTP_ERR_UNSUPPORTED, "more than 64 paths into one output block");
-    if (mb.K > kMixKMax)
-        return set_error(CGTP_ERR_UNSUPPORTED, "more than 512 contraction rows (sum of mul1*mul2) into one output block");
     MixTable tab{};
     tab.np = (int)mb.paths.size();
     for (int i = 0; i < tab.np; ++i) {
@@ -816,9 +826,9 @@ int launch_uvw_mix(const Plan &p, const MixBlock &mb, const void *T, const void 
     const int64_t M = n_items * mb.d3;
     const uint16_t *Tb = (const uint16_t *)T + n_items * mb.t_off_per_item;
     int64_t blocks = (M + 63) / 64;
-    if (blocks > 512) blocks = 512;
-    CGTP_LAUNCH("k_uvw_mix", s, k_uvw_mix, dim3((unsigned)blocks), dim3(256), 0, s, Tb, M, mb.K, (const uint16_t *)w,
-                       mb.mul3, tab, (float *)out, p.dim3, p.off3[mb.b3], mb.d3, accumulate);
+    if (blocks > 1024) blocks = 1024;
+    CGTP_LAUNCH("k_uvw_mix", s, k_uvw_mix, dim3((unsigned)blocks), dim3(256), 0, s, Tb, M, mb.Kr, mb.K,
+                (const uint16_t *)w, p.wnumel, mb.mul3, tab, (float *)out, p.dim3, p.off3[mb.b3], mb.d3, accumulate);
     return hip_check(hipGetLastError(), "uvw mix launch");
 }
 

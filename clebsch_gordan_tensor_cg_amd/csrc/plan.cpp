@@ -302,14 +302,15 @@ void split_uvw(Plan &p, KernelShape &ks) {
     for (auto &P : p.paths) max_mul = std::max(max_mul, P.mul1);
     ks.lanes_per_item = max_mul >= 64 ? 64 : next_pow2(std::max(1, max_mul));
     ks.items_per_wave = 64 / ks.lanes_per_item;
-    const int budget = 40;
+    // accumulators per lane: one per (path, v, k), times H+1 with radial weights
+    const int budget = p.radial_h > 0 ? 64 : 40;
     for (int b = 0; b < (int)p.in1.size(); ++b) {
         Group cur;
         int acc = 0;
         for (int a = 0; a < (int)p.paths.size(); ++a) {
             const Path &P = p.paths[a];
             if (P.i1 != b) continue;
-            const int need = P.mul2 * (2 * P.l3 + 1);
+            const int need = P.mul2 * (2 * P.l3 + 1) * (p.radial_h + 1);
             if (!cur.paths.empty() && acc + need > budget) {
                 ks.groups.push_back(cur);
                 cur = Group();
@@ -347,8 +348,10 @@ void mix_tables(Plan &p) {
                 p.mix_of_path[a] = (int)p.mix.size();
             }
         if (mb.paths.empty()) continue;
+        // radial: columns (h, path, u, v), h = 0..H, each h a full copy of the paths
+        mb.Kr = mb.K * (p.radial_h + 1);
         mb.t_off_per_item = off;
-        off += mb.d3 * mb.K;
+        off += mb.d3 * mb.Kr;
         p.mix.push_back(mb);
     }
     p.t_per_item = off;

@@ -88,13 +88,19 @@ enum {
     CGTP_SHARED_WEIGHTS = 1u << 0, /* one weight row for all items (uvw layers) */
     CGTP_PLAN_NO_LOAD = 1u << 1,   /* generate and compile into the on-disk cache only;
                                       no device contact; execution calls then fail */
-    CGTP_BF16_WEIGHTS = 1u << 2    /* uvu, CGTP_F32 only: every weight-shaped input (w,
+    CGTP_BF16_WEIGHTS = 1u << 2,   /* uvu, CGTP_F32 only: every weight-shaped input (w,
                                       and gg_w of the double backward) is stored as
                                       bf16 (the upper half of a float); arithmetic,
                                       the other inputs and every output, g_w and d_w
                                       included, stay float.  Halves the dominant
                                       per-edge stream. */
 };
+/* Radial weights ([SE3]: the radial profile inside a TFN layer is a fully
+ * connected network): a uvw, CGTP_BF16_F32ACC, CGTP_SHARED_WEIGHTS plan whose
+ * input 2 is one SH row, with flag CGTP_RADIAL_HIDDEN(H), 1 <= H <= 64,
+ * takes per-edge weights from a network of hidden width H on the edge
+ * length (cgtp_conv_forward_radial). */
+#define CGTP_RADIAL_HIDDEN(h) ((uint32_t)(h) << 16)
 
 /* A path couples block i_in1 of input 1 with block i_in2 of input 2 into
  * block i_out of the output. */
@@ -197,6 +203,25 @@ int cgtp_conv_forward_vec(cgtp_plan_t plan, const void *x, const void *vec, cons
                           const void *w, const int32_t *src, const int32_t *dst_row_ptr,
                           const int32_t *node_order, int64_t n_nodes, int64_t n_edges, void *out,
                           void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
+/* Convolution with per-edge weights from the radial network (plan flag
+ * CGTP_RADIAL_HIDDEN(H)):
+ *   phi_h(e) = silu(radial[h] r_e + radial[H + h]),  r_e = |vec[e]|,
+ *   silu(z) = z / (1 + e^-z), h = 0..H-1;
+ *   W_e = w[0] + sum_h phi_h(e) w[1 + h]     (w: bf16 [H+1][weight_numel])
+ *   out[n] = sum_t TP_uvw(x[src[t]], Y(vec[t]), W_t)
+ * radial: float [2][H] (first-layer slopes, then offsets).  The SH and
+ * phi are computed inside the kernel from the edge vectors (as in
+ * cgtp_conv_forward_vec).  Because the output layer is linear, the mixing
+ * runs after aggregation: per node the path tensors are summed once per
+ * row of w (phi-weighted), and the mixing on the matrix cores has an
+ * (H+1)-fold contraction.  workspace: cgtp_forward_workspace_bytes. */
+int cgtp_conv_forward_radial(cgtp_plan_t plan, const void *x, const void *vec,
+                             const int32_t *vec_perm, const float *radial, const void *w,
+                             const int32_t *src, const int32_t *dst_row_ptr,
+                             const int32_t *node_order, int64_t n_nodes, int64_t n_edges,
+                             void *out, void *workspace, size_t workspace_bytes,
+                             cgtp_stream_t stream);
 
 /* Workspace needed by cgtp_conv_backward / cgtp_conv_double_backward for a
  * graph with n_edges edges (bytes; 256-byte aligned pointer required).
