@@ -360,8 +360,9 @@ static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, c
                    const int32_t *row_ptr, const int32_t *order, int64_t n_items, int graph, void *out, void *ws,
                    size_t ws_bytes, hipStream_t s, const void *vec = nullptr, const int32_t *vperm = nullptr,
                    const float *radial = nullptr) {
-    size_t need = align256((size_t)n_items * p.t_per_item * 2);
+    size_t need = align256((size_t)n_items * p.t_per_item * 2) + align256(mix_part_bytes(p, n_items));
     if (ws_bytes < need || (!ws && need)) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace too small");
+    void *part = (char *)ws + align256((size_t)n_items * p.t_per_item * 2);
     if (((uintptr_t)ws) & 255) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     long long n = n_items;
     void *args[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, (void *)&order, (void *)&vec,
@@ -375,7 +376,7 @@ static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, c
         acc = 1;
     }
     for (const MixBlock &mb : p.mix)
-        if ((rc = launch_uvw_mix(p, mb, ws, w, n_items, out, acc, s))) return rc;
+        if ((rc = launch_uvw_mix(p, mb, ws, w, n_items, out, acc, part, s))) return rc;
     return CGTP_OK;
 }
 
@@ -383,7 +384,8 @@ int cgtp_forward_workspace_bytes(cgtp_plan_t plan, int64_t n_items, size_t *byte
     clear_error();
     if (!plan || !bytes || n_items < 0) return set_error(CGTP_ERR_INVALID_ARGUMENT, "bad argument");
     const Plan &p = plan->p;
-    *bytes = p.mode == CGTP_UVW ? align256((size_t)n_items * p.t_per_item * 2) : 0;
+    *bytes = p.mode == CGTP_UVW ? align256((size_t)n_items * p.t_per_item * 2) + align256(mix_part_bytes(p, n_items))
+                                : 0;
     return CGTP_OK;
 }
 

@@ -694,10 +694,21 @@ typedef float cgtp_f4 __attribute__((ext_vector_type(4)));
 // copies of the paths: the rows of a radial network's output layer).  A
 // workgroup owns 64 rows of T (16 per wavefront) and 64 output columns;
 // the weights are staged in LDS kMixKC rows at a time.
+// out[item][off3 + w*d3 + k] (=|+=) sum_r T[item*d3 + k][r] W'[r][w]: the
+// channel mixing of one output block on the matrix cores.  Contraction row
+// r = h*Kb + kk (h < n_rep, kk < Kb) reads weight row
+// h*wstride + woff_p + (kk - kstart_p)*mul3 of the path p holding kk (n_rep
+// copies of the paths: the rows of a radial network's output layer).  A
+// workgroup owns 64 rows of T (16 per wavefront) and 64 output columns;
+// the weights are staged in LDS kMixKC rows at a time.
+// Split contraction: with n_split > 1, workgroup (g, s) sums only the
+// contraction rows [s*kspan, (s+1)*kspan) of row group g and writes its
+// partial tile to part[s][row][column]; k_uvw_mix_reduce adds the parts.
 __global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T, int64_t M, int64_t K, int64_t Kb,
                                                  const uint16_t *__restrict__ W, int64_t wstride, int mul3,
                                                  MixTable tab, float *__restrict__ out, int64_t dim3, int64_t off3,
-                                                 int d3, int accumulate) {
+                                                 int d3, int accumulate, int n_split, int64_t kspan,
+                                                 float *__restrict__ part) {
     __shared__ __attribute__((aligned(16))) uint16_t Ws[kMixKC * 64];
     __shared__ int64_t wrow[kMixKC];
     __shared__ int64_t s_kstart[kMixMaxPaths + 1];
@@ -710,20 +721,22 @@ __global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T,
     const int r_a = lane & 15;
     const int kq = 4 * (lane >> 4);
     const int64_t n_groups = (M + 63) / 64;
+    const int split = (int)(blockIdx.x % n_split);
+    const int64_t k_begin = split * kspan, k_end = std::min<int64_t>(K, k_begin + kspan);
     const bool vec_ok = (K % 4) == 0 && (((uintptr_t)T) & 7) == 0;
     // whole 16-byte weight segments: 8-aligned rows and offsets, full columns
     bool wvec = (mul3 % 64) == 0 && (((uintptr_t)W) & 15) == 0 && (wstride % 8) == 0;
     for (int p = 0; p < tab.np; ++p) wvec = wvec && (tab.woff[p] % 8) == 0;
     for (int cb = 0; cb < mul3; cb += 64) {
         const int ncol = mul3 - cb < 64 ? mul3 - cb : 64;
-        for (int64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x) {
+        for (int64_t grp = blockIdx.x / n_split; grp < n_groups; grp += gridDim.x / n_split) {
             const int64_t row0 = grp * 64 + wv * 16;
             const int64_t arow = row0 + r_a < M ? row0 + r_a : M - 1;
             const uint16_t *__restrict__ Trow = T + arow * K;
             cgtp_f4 acc[4];
             for (int ct = 0; ct < 4; ++ct) acc[ct] = (cgtp_f4){0.f, 0.f, 0.f, 0.f};
-            for (int64_t k0 = 0; k0 < K; k0 += kMixKC) {
-                const int kc = (int)(K - k0 < kMixKC ? K - k0 : kMixKC);
+            for (int64_t k0 = k_begin; k0 < k_end; k0 += kMixKC) {
+                const int kc = (int)(k_end - k0 < kMixKC ? k_end - k0 : kMixKC);
                 __syncthreads();   // the previous step's weights are no longer read
                 for (int kr = tid; kr < kc; kr += 256) {
                     const int64_t r = k0 + kr, h = r / Kb, kk = r % Kb;
@@ -800,6 +813,10 @@ __global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T,
                 for (int i = 0; i < 4; ++i) {
                     const int64_t r = row0 + kq + i;
                     if (r >= M) continue;
+                    if (n_split > 1) {
+                        part[((int64_t)split * M + r) * mul3 + col] = acc[ct][i];
+                        continue;
+                    }
                     const int64_t item = r / d3, k = r % d3;
                     float *o = out + item * dim3 + off3 + (int64_t)col * d3 + k;
                     *o = accumulate ? *o + acc[ct][i] : acc[ct][i];
@@ -809,10 +826,44 @@ __global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T,
     }
 }
 
+// out[item][off3 + col*d3 + k] (=|+=) sum_s part[s][item*d3 + k][col]
+__global__ void k_uvw_mix_reduce(const float *__restrict__ part, int n_split, int64_t M, int mul3,
+                                 float *__restrict__ out, int64_t dim3, int64_t off3, int d3, int accumulate) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < M * mul3;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / mul3, col = i % mul3;
+        float acc = 0.f;
+        for (int sp = 0; sp < n_split; ++sp) acc += part[(int64_t)sp * M * mul3 + i];
+        const int64_t item = r / d3, k = r % d3;
+        float *o = out + item * dim3 + off3 + col * d3 + k;
+        *o = accumulate ? *o + acc : acc;
+    }
+}
+
 }  // namespace
 
+// contraction splits of a mixing block: enough workgroups to fill the chip
+// (about 512), each split a whole number of staging steps
+int mix_splits(const MixBlock &mb, int64_t n_items) {
+    const int64_t groups = (n_items * mb.d3 + 63) / 64;
+    const int64_t steps = (mb.Kr + kMixKC - 1) / kMixKC;
+    // a short contraction is not worth the extra reduction launch
+    if (steps <= 2) return 1;
+    int64_t sp = (512 + groups - 1) / groups;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(sp, steps));
+}
+
+size_t mix_part_bytes(const Plan &p, int64_t n_items) {
+    size_t b = 0;
+    for (const MixBlock &mb : p.mix) {
+        const int sp = mix_splits(mb, n_items);
+        if (sp > 1) b = std::max(b, (size_t)sp * n_items * mb.d3 * mb.mul3 * sizeof(float));
+    }
+    return b;
+}
+
 int launch_uvw_mix(const Plan &p, const MixBlock &mb, const void *T, const void *w, int64_t n_items, void *out,
-                   int accumulate, hipStream_t s) {
+                   int accumulate, void *part, hipStream_t s) {
     if (n_items <= 0) return CGTP_OK;
     if ((int)mb.paths.size() > kMixMaxPaths)
         return set_error(CGTP_ERR_UNSUPPORTED, "more than 64 paths into one output block");
@@ -825,10 +876,20 @@ int launch_uvw_mix(const Plan &p, const MixBlock &mb, const void *T, const void 
     tab.kstart[tab.np] = mb.K;
     const int64_t M = n_items * mb.d3;
     const uint16_t *Tb = (const uint16_t *)T + n_items * mb.t_off_per_item;
-    int64_t blocks = (M + 63) / 64;
-    if (blocks > 1024) blocks = 1024;
-    CGTP_LAUNCH("k_uvw_mix", s, k_uvw_mix, dim3((unsigned)blocks), dim3(256), 0, s, Tb, M, mb.Kr, mb.K,
-                (const uint16_t *)w, p.wnumel, mb.mul3, tab, (float *)out, p.dim3, p.off3[mb.b3], mb.d3, accumulate);
+    const int sp = mix_splits(mb, n_items);
+    const int64_t steps = (mb.Kr + kMixKC - 1) / kMixKC;
+    const int64_t kspan = (steps + sp - 1) / sp * kMixKC;
+    int64_t groups = (M + 63) / 64;
+    if (groups * sp > 4096) groups = 4096 / sp;
+    CGTP_LAUNCH("k_uvw_mix", s, k_uvw_mix, dim3((unsigned)(groups * sp)), dim3(256), 0, s, Tb, M, mb.Kr, mb.K,
+                (const uint16_t *)w, p.wnumel, mb.mul3, tab, (float *)out, p.dim3, p.off3[mb.b3], mb.d3, accumulate, sp,
+                kspan, (float *)part);
+    if (sp > 1) {
+        unsigned g = grid_for(M * mb.mul3);
+        if (g > 8192) g = 8192;
+        CGTP_LAUNCH("k_uvw_mix_reduce", s, k_uvw_mix_reduce, dim3(g), dim3(kBlock), 0, s, (const float *)part, sp, M,
+                    mb.mul3, (float *)out, p.dim3, p.off3[mb.b3], mb.d3, accumulate);
+    }
     return hip_check(hipGetLastError(), "uvw mix launch");
 }
 
