@@ -375,8 +375,7 @@ static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, c
         if ((rc = launch_zero(CGTP_F32, out, n_items * p.dim3, s))) return rc;
         acc = 1;
     }
-    for (const MixBlock &mb : p.mix)
-        if ((rc = launch_uvw_mix(p, mb, ws, w, n_items, out, acc, part, s))) return rc;
+    if ((rc = launch_uvw_mix(p, ws, w, n_items, out, acc, part, s))) return rc;
     return CGTP_OK;
 }
 

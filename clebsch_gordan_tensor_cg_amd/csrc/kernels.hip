@@ -678,10 +678,17 @@ struct CotLaunch {
 // ---------------------------------------------------------------------------
 constexpr int kMixMaxPaths = 64;
 constexpr int kMixKC = 256;   // contraction rows staged per step (32 KB of bf16 at 64 columns)
-struct MixTable {
-    int np;
-    int64_t kstart[kMixMaxPaths + 1];
-    int64_t woff[kMixMaxPaths];
+constexpr int kMixMaxBlocks = 4;   // output blocks mixed by one launch
+// one output block of a mixing launch
+struct MixBlockArgs {
+    int32_t np, d3, mul3, n_split;
+    int64_t M, K, Kb, off3, t_off, part_off, kspan, wg_start;
+    int32_t kstart[kMixMaxPaths + 1];
+    int32_t woff[kMixMaxPaths];
+};
+struct MixArgs {
+    int32_t nb;
+    MixBlockArgs b[kMixMaxBlocks];
 };
 
 typedef short cgtp_s4 __attribute__((ext_vector_type(4)));
@@ -704,32 +711,51 @@ typedef float cgtp_f4 __attribute__((ext_vector_type(4)));
 // Split contraction: with n_split > 1, workgroup (g, s) sums only the
 // contraction rows [s*kspan, (s+1)*kspan) of row group g and writes its
 // partial tile to part[s][row][column]; k_uvw_mix_reduce adds the parts.
-__global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T, int64_t M, int64_t K, int64_t Kb,
-                                                 const uint16_t *__restrict__ W, int64_t wstride, int mul3,
-                                                 MixTable tab, float *__restrict__ out, int64_t dim3, int64_t off3,
-                                                 int d3, int accumulate, int n_split, int64_t kspan,
-                                                 float *__restrict__ part) {
+// All output blocks of a layer in one launch: workgroups
+// [wg_start_b, wg_start_{b+1}) serve block b.
+__global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T0, const uint16_t *__restrict__ W,
+                                                 int64_t wstride, MixArgs args, float *__restrict__ out, int64_t dim3,
+                                                 int accumulate, float *__restrict__ part0) {
     __shared__ __attribute__((aligned(16))) uint16_t Ws[kMixKC * 64];
     __shared__ int64_t wrow[kMixKC];
     __shared__ int64_t s_kstart[kMixMaxPaths + 1];
     __shared__ int64_t s_woff[kMixMaxPaths];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    // the path table is indexed by runtime values: keep it in LDS
-    if (tid <= tab.np) s_kstart[tid] = tab.kstart[tid];
-    if (tid < tab.np) s_woff[tid] = tab.woff[tid];
+    // this workgroup's block; its fields are read with constant indices
+    int bsel = 0;
+#pragma unroll
+    for (int i = 1; i < kMixMaxBlocks; ++i)
+        if (i < args.nb && (int64_t)blockIdx.x >= args.b[i].wg_start) bsel = i;
+    int np = 0, d3 = 1, mul3 = 0, n_split = 1;
+    int64_t M = 0, K = 0, Kb = 1, off3 = 0, t_off = 0, part_off = 0, kspan = 0, wg_start = 0;
+#pragma unroll
+    for (int i = 0; i < kMixMaxBlocks; ++i)
+        if (i == bsel) {
+            np = args.b[i].np, d3 = args.b[i].d3, mul3 = args.b[i].mul3, n_split = args.b[i].n_split;
+            M = args.b[i].M, K = args.b[i].K, Kb = args.b[i].Kb, off3 = args.b[i].off3, t_off = args.b[i].t_off;
+            part_off = args.b[i].part_off, kspan = args.b[i].kspan, wg_start = args.b[i].wg_start;
+            // the path table is indexed by runtime values: keep it in LDS
+            if (tid <= np) s_kstart[tid] = args.b[i].kstart[tid];
+            if (tid < np) s_woff[tid] = args.b[i].woff[tid];
+        }
     __syncthreads();
+    const uint16_t *__restrict__ T = T0 + t_off;
+    float *__restrict__ part = part0 + part_off;
+    const int64_t wg = blockIdx.x - wg_start;
+    const int64_t wg_count = (bsel + 1 < args.nb ? args.b[bsel + 1 < kMixMaxBlocks ? bsel + 1 : 0].wg_start
+                                                  : (int64_t)gridDim.x) - wg_start;
     const int r_a = lane & 15;
     const int kq = 4 * (lane >> 4);
     const int64_t n_groups = (M + 63) / 64;
-    const int split = (int)(blockIdx.x % n_split);
+    const int split = (int)(wg % n_split);
     const int64_t k_begin = split * kspan, k_end = std::min<int64_t>(K, k_begin + kspan);
     const bool vec_ok = (K % 4) == 0 && (((uintptr_t)T) & 7) == 0;
     // whole 16-byte weight segments: 8-aligned rows and offsets, full columns
     bool wvec = (mul3 % 64) == 0 && (((uintptr_t)W) & 15) == 0 && (wstride % 8) == 0;
-    for (int p = 0; p < tab.np; ++p) wvec = wvec && (tab.woff[p] % 8) == 0;
+    for (int p = 0; p < np; ++p) wvec = wvec && (s_woff[p] % 8) == 0;
     for (int cb = 0; cb < mul3; cb += 64) {
         const int ncol = mul3 - cb < 64 ? mul3 - cb : 64;
-        for (int64_t grp = blockIdx.x / n_split; grp < n_groups; grp += gridDim.x / n_split) {
+        for (int64_t grp = wg / n_split; grp < n_groups; grp += wg_count / n_split) {
             const int64_t row0 = grp * 64 + wv * 16;
             const int64_t arow = row0 + r_a < M ? row0 + r_a : M - 1;
             const uint16_t *__restrict__ Trow = T + arow * K;
@@ -741,7 +767,7 @@ __global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T,
                 for (int kr = tid; kr < kc; kr += 256) {
                     const int64_t r = k0 + kr, h = r / Kb, kk = r % Kb;
                     int p = 0;
-                    while (p + 1 < tab.np && kk >= s_kstart[p + 1]) ++p;
+                    while (p + 1 < np && kk >= s_kstart[p + 1]) ++p;
                     wrow[kr] = h * wstride + s_woff[p] + (kk - s_kstart[p]) * mul3 + cb;
                 }
                 __syncthreads();
@@ -826,11 +852,28 @@ __global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T,
     }
 }
 
-// out[item][off3 + col*d3 + k] (=|+=) sum_s part[s][item*d3 + k][col]
-__global__ void k_uvw_mix_reduce(const float *__restrict__ part, int n_split, int64_t M, int mul3,
-                                 float *__restrict__ out, int64_t dim3, int64_t off3, int d3, int accumulate) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < M * mul3;
-         i += (int64_t)gridDim.x * blockDim.x) {
+// out[item][off3 + col*d3 + k] (=|+=) sum_s part[s][item*d3 + k][col] for
+// every split block of the launch (elements enumerated block after block)
+__global__ void k_uvw_mix_reduce(const float *__restrict__ part0, MixArgs args, int64_t total, float *__restrict__ out,
+                                 int64_t dim3, int accumulate) {
+    for (int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i0 < total;
+         i0 += (int64_t)gridDim.x * blockDim.x) {
+        int64_t i = i0;
+        int d3 = 1, mul3 = 1, n_split = 1;
+        int64_t M = 0, off3 = 0, part_off = 0;
+#pragma unroll
+        for (int b = 0, done = 0; b < kMixMaxBlocks; ++b) {
+            if (done || b >= args.nb || args.b[b].n_split < 2) continue;
+            const int64_t cnt = args.b[b].M * args.b[b].mul3;
+            if (i < cnt) {
+                d3 = args.b[b].d3, mul3 = args.b[b].mul3, n_split = args.b[b].n_split;
+                M = args.b[b].M, off3 = args.b[b].off3, part_off = args.b[b].part_off;
+                done = 1;
+            } else {
+                i -= cnt;
+            }
+        }
+        const float *__restrict__ part = part0 + part_off;
         const int64_t r = i / mul3, col = i % mul3;
         float acc = 0.f;
         for (int sp = 0; sp < n_split; ++sp) acc += part[(int64_t)sp * M * mul3 + i];
@@ -854,41 +897,61 @@ int mix_splits(const MixBlock &mb, int64_t n_items) {
 }
 
 size_t mix_part_bytes(const Plan &p, int64_t n_items) {
-    size_t b = 0;
+    size_t b = 0;   // every split block has its own partial tiles (blocks run together)
     for (const MixBlock &mb : p.mix) {
         const int sp = mix_splits(mb, n_items);
-        if (sp > 1) b = std::max(b, (size_t)sp * n_items * mb.d3 * mb.mul3 * sizeof(float));
+        if (sp > 1) b += (size_t)sp * n_items * mb.d3 * mb.mul3;
     }
-    return b;
+    return b * sizeof(float);
 }
 
-int launch_uvw_mix(const Plan &p, const MixBlock &mb, const void *T, const void *w, int64_t n_items, void *out,
-                   int accumulate, void *part, hipStream_t s) {
+int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items, void *out, int accumulate,
+                   void *part, hipStream_t s) {
     if (n_items <= 0) return CGTP_OK;
-    if ((int)mb.paths.size() > kMixMaxPaths)
-        return set_error(CGTP_ERR_UNSUPPORTED, "more than 64 paths into one output block");
-    MixTable tab{};
-    tab.np = (int)mb.paths.size();
-    for (int i = 0; i < tab.np; ++i) {
-        tab.kstart[i] = mb.koff[i];
-        tab.woff[i] = p.paths[mb.paths[i]].woff;
-    }
-    tab.kstart[tab.np] = mb.K;
-    const int64_t M = n_items * mb.d3;
-    const uint16_t *Tb = (const uint16_t *)T + n_items * mb.t_off_per_item;
-    const int sp = mix_splits(mb, n_items);
-    const int64_t steps = (mb.Kr + kMixKC - 1) / kMixKC;
-    const int64_t kspan = (steps + sp - 1) / sp * kMixKC;
-    int64_t groups = (M + 63) / 64;
-    if (groups * sp > 4096) groups = 4096 / sp;
-    CGTP_LAUNCH("k_uvw_mix", s, k_uvw_mix, dim3((unsigned)(groups * sp)), dim3(256), 0, s, Tb, M, mb.Kr, mb.K,
-                (const uint16_t *)w, p.wnumel, mb.mul3, tab, (float *)out, p.dim3, p.off3[mb.b3], mb.d3, accumulate, sp,
-                kspan, (float *)part);
-    if (sp > 1) {
-        unsigned g = grid_for(M * mb.mul3);
-        if (g > 8192) g = 8192;
-        CGTP_LAUNCH("k_uvw_mix_reduce", s, k_uvw_mix_reduce, dim3(g), dim3(kBlock), 0, s, (const float *)part, sp, M,
-                    mb.mul3, (float *)out, p.dim3, p.off3[mb.b3], mb.d3, accumulate);
+    int64_t part_off = 0;
+    for (size_t b0 = 0; b0 < p.mix.size(); b0 += kMixMaxBlocks) {
+        MixArgs args{};
+        args.nb = (int)std::min<size_t>(kMixMaxBlocks, p.mix.size() - b0);
+        int64_t wg = 0, red = 0;
+        for (int i = 0; i < args.nb; ++i) {
+            const MixBlock &mb = p.mix[b0 + i];
+            if ((int)mb.paths.size() > kMixMaxPaths)
+                return set_error(CGTP_ERR_UNSUPPORTED, "more than 64 paths into one output block");
+            MixBlockArgs &a = args.b[i];
+            a.np = (int)mb.paths.size();
+            for (int j = 0; j < a.np; ++j) {
+                a.kstart[j] = (int32_t)mb.koff[j];
+                a.woff[j] = (int32_t)p.paths[mb.paths[j]].woff;
+            }
+            a.kstart[a.np] = (int32_t)mb.K;
+            a.d3 = mb.d3;
+            a.mul3 = mb.mul3;
+            a.M = n_items * mb.d3;
+            a.K = mb.Kr;
+            a.Kb = mb.K;
+            a.off3 = p.off3[mb.b3];
+            a.t_off = n_items * mb.t_off_per_item;
+            a.n_split = mix_splits(mb, n_items);
+            const int64_t steps = (mb.Kr + kMixKC - 1) / kMixKC;
+            a.kspan = (steps + a.n_split - 1) / a.n_split * kMixKC;
+            a.part_off = part_off;
+            if (a.n_split > 1) {
+                part_off += (int64_t)a.n_split * a.M * a.mul3;
+                red += a.M * a.mul3;
+            }
+            int64_t groups = (a.M + 63) / 64;
+            if (groups * a.n_split > 4096) groups = std::max<int64_t>(1, 4096 / a.n_split);
+            a.wg_start = wg;
+            wg += groups * a.n_split;
+        }
+        CGTP_LAUNCH("k_uvw_mix", s, k_uvw_mix, dim3((unsigned)wg), dim3(256), 0, s, (const uint16_t *)T,
+                    (const uint16_t *)w, p.wnumel, args, (float *)out, p.dim3, accumulate, (float *)part);
+        if (red > 0) {
+            unsigned g = grid_for(red);
+            if (g > 8192) g = 8192;
+            CGTP_LAUNCH("k_uvw_mix_reduce", s, k_uvw_mix_reduce, dim3(g), dim3(kBlock), 0, s, (const float *)part, args,
+                        red, (float *)out, p.dim3, accumulate);
+        }
     }
     return hip_check(hipGetLastError(), "uvw mix launch");
 }
