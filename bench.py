@@ -189,7 +189,8 @@ def cpu_baseline_conv(cfg, g, x_np, w_np, full_step: bool, frac: float):
     if cfg.dtype == "bf16":
         sh = W.round_to(sh, "bf16")
     perm, rp = oracle.csr(dst, g.n_nodes)
-    oracle.csr(src[perm], g.n_nodes)
+    if full_step:
+        oracle.csr(src[perm], g.n_nodes)
     out = prob.conv_forward(x_np, sh, w, src, dst, g.n_nodes)
     if full_step:
         G = np.zeros_like(out)
@@ -298,9 +299,10 @@ def bench_conv(args, torch, B, W):
 
     def step(timed: bool):
         run = timer.run if timed else (lambda name_, fn: fn())
+        # the transpose CSR (by source) serves only the backward passes
         run("csr", lambda: (B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s)),
                             B.cgtp_build_csr(src_s, N, sorted_key=False, ws=csr_ws,
-                                             out=(src_perm, src_rp, None, None)),
+                                             out=(src_perm, src_rp, None, None)) if full else None,
                             None if args.natural_order else B.cgtp_node_order(rp, ws=ord_ws, out=order)))
         if sh_in_conv:
             # SH computed inside the convolution kernels; forces straight from
@@ -427,7 +429,8 @@ def bench_conv(args, torch, B, W):
         "config": {"workload": workload, "n_atoms": N, "n_edges": E,
                    "irreps_node": cfg.irreps_in1, "irreps_sh": cfg.irreps_in2, "irreps_out": cfg.irreps_out,
                    "n_paths": plan.n_paths,
-                   "step": ("csr+sh+fwd+bwd+forces+force_cotangent+double_bwd" if full else "csr+sh+fwd")},
+                   "step": ("csr+sh+fwd+bwd+forces+force_cotangent+double_bwd" if full
+                            else "csr (by destination) + node order + sh + fwd")},
         "roofline": roof,
         "fwd_edges_per_s": E / (kms["conv_fwd"] * 1e-3),
         "calls": calls,
