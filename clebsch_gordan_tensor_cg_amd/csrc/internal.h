@@ -57,7 +57,8 @@ struct KernelShape {
 };
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
-// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, yvec, ntw, pf, budget, stage, cypath, depth, bgy, full) overrides
+// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, yvec, ntw, pf, budget, stage, cypath, depth, bgy, full, ubudget)
+// overrides
 // them for experiments.
 struct Tuning {
     int cpl[3] = {0, 0, 0};  // channels per lane per kernel kind (0 = by budget)
@@ -70,6 +71,7 @@ struct Tuning {
     int depth = 3;           // edges of prefetch in flight (staged loop)
     bool bgy = false;        // backward via B_ij = sum_k R_ijk g_k (fewer FMAs, more VGPRs)
     int full = 3;            // dispatch to the folded-flag kernels: bit 0 backward, bit 1 double backward
+    int ubudget = 0;         // uvw accumulators per lane and unit (0: 32, or 144 with radial weights)
 };
 Tuning tuning_from_env();
 

@@ -287,6 +287,7 @@ Tuning tuning_from_env() {
             else if (k == "depth") t.depth = v < 1 ? 1 : (v > 4 ? 4 : v);
             else if (k == "bgy") t.bgy = v != 0;
             else if (k == "full") t.full = v & 3;
+            else if (k == "ubudget") t.ubudget = v < 1 ? 0 : v;
         }
         pos = comma + 1;
     }
@@ -303,7 +304,8 @@ void split_uvw(Plan &p, KernelShape &ks) {
     ks.lanes_per_item = max_mul >= 64 ? 64 : next_pow2(std::max(1, max_mul));
     ks.items_per_wave = 64 / ks.lanes_per_item;
     // accumulators per lane: one per (path, v, k), times H+1 with radial weights
-    const int budget = p.radial_h > 0 ? 64 : 40;
+    // defaults from sweeps of the 44-path l <= 6 layer (100 x 18 atoms)
+    const int budget = p.tune.ubudget > 0 ? p.tune.ubudget : (p.radial_h > 0 ? 144 : 32);
     for (int b = 0; b < (int)p.in1.size(); ++b) {
         Group cur;
         int acc = 0;
@@ -358,7 +360,9 @@ void mix_tables(Plan &p) {
 }
 
 void choose_shapes(Plan &p) {
-    if (p.tune.cy_path < 0) p.tune.cy_path = (p.dtype == CGTP_F64) ? 1 : 0;
+    // uniform products per path where registers are tight: FP64 (two VGPRs
+    // each) and the bf16 uvw layers (SH rows up to l = 6); per edge otherwise
+    if (p.tune.cy_path < 0) p.tune.cy_path = (p.dtype == CGTP_F64 || p.dtype == CGTP_BF16_F32ACC) ? 1 : 0;
     if (p.mode == CGTP_UVW) {
         mix_tables(p);
         split_uvw(p, p.fwd);
