@@ -21,6 +21,9 @@
  *         Fields", abstract: FP64 / FP32 / BF16-with-FP32-accumulation
  *         policies; mismatched module layouts give wrong results, so the
  *         layout below is fixed and documented.
+ *   [F3S] "Fused3S: Fast Sparse Attention on Tensor Cores", abstract:
+ *         sparse attention as sampled dense-dense product, softmax and
+ *         sparse-dense product, fused on the matrix units.
  *
  * Conventions (fixed; every call uses them):
  *   - Irreps strings: "MULxLp" terms joined by '+', p in {e,o} or absent
@@ -155,8 +158,9 @@ void cgtp_plan_destroy(cgtp_plan_t plan);
 /* path tensors T_p = CG_p(x, y) summed over the item's edges, rounded to   */
 /* the MFMA operand type, then T . W per output block on the matrix cores,  */
 /* [SE3] "fully fused" TFN convolution: all paths into one output degree    */
-/* concatenated along K).  T lives in the workspace: this many bytes for   */
-/* n_items items (destination nodes or samples); 0 for uvu plans.          */
+/* concatenated along K).  T, and the partial tiles of long contractions,  */
+/* live in the workspace: this many bytes for n_items items (destination   */
+/* nodes or samples); 0 for uvu plans.                                      */
 /* ---------------------------------------------------------------------- */
 int cgtp_forward_workspace_bytes(cgtp_plan_t plan, int64_t n_items, size_t *bytes);
 
@@ -172,21 +176,20 @@ int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, 
                  void *out, void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
 
 /* ---------------------------------------------------------------------- */
-/* Fused graph convolution ([KG]: TP fused with the graph convolution).    */
-/*   out[n] = sum_{t in [row_ptr[n], row_ptr[n+1])} TP(x[src[t]], sh[t], w[t])
- * x [n_nodes][dim_in1]; sh [n_edges][dim_in2]; w [n_edges][weight_numel]   */
-/* (or shared); src [n_edges]; dst_row_ptr [n_nodes+1]; out [n_nodes][dim_out].
- * Each destination row is reduced by one workgroup and written once; no   */
-/* atomics.  src values must lie in [0, n_nodes) and row_ptr must be a      */
-/* monotone CSR with row_ptr[0] = 0, row_ptr[n_nodes] = n_edges; check     */
-/* untrusted input with cgtp_validate_csr first.  node_order [n_nodes]     */
-/* (may be NULL: natural order) is the order in which destination rows     */
-/* are handed to the device, a permutation of 0..n_nodes-1, normally from  */
-/* cgtp_node_order; it changes timing only, never a result (an entry out   */
-/* of range leaves its slot idle, so a node missing from it is not         */
-/* written).  workspace: cgtp_forward_workspace_bytes(n_nodes) (may be     */
-/* NULL for uvu plans).                                                     */
-/* ---------------------------------------------------------------------- */
+/* Fused graph convolution ([KG]: TP fused with the graph convolution).
+ *   out[n] = sum_{t in [row_ptr[n], row_ptr[n+1])} TP(x[src[t]], sh[t], w[t])
+ * x [n_nodes][dim_in1]; sh [n_edges][dim_in2]; w [n_edges][weight_numel]
+ * (or shared); src [n_edges]; dst_row_ptr [n_nodes+1]; out
+ * [n_nodes][dim_out].  Each destination row is reduced by one wavefront
+ * per path group and written once; no atomics.  src values must lie in
+ * [0, n_nodes) and row_ptr must be a monotone CSR with row_ptr[0] = 0,
+ * row_ptr[n_nodes] = n_edges; check untrusted input with cgtp_validate_csr
+ * first.  node_order [n_nodes] (may be NULL: natural order) is the order
+ * in which destination rows are handed to the device, a permutation of
+ * 0..n_nodes-1, normally from cgtp_node_order; it changes timing only,
+ * never a result (an entry out of range leaves its slot idle, so a node
+ * missing from it is not written).  workspace:
+ * cgtp_forward_workspace_bytes(n_nodes) (may be NULL for uvu plans). */
 int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
                       const int32_t *src, const int32_t *dst_row_ptr, const int32_t *node_order,
                       int64_t n_nodes, int64_t n_edges, void *out, void *workspace,
