@@ -121,6 +121,25 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _want(plan, **tensors):
+    """Argument check of the marshalling layer: feature-like tensors in the
+    plan's storage type, weight-like tensors in its weight storage type,
+    index tensors int32 (None entries are skipped)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if name in ("w", "gg_w"):
+            want = plan.weight_dtype
+        elif name in ("src", "dst", "dst_row_ptr", "src_row_ptr", "src_perm", "vec_perm", "node_order"):
+            want = torch.int32
+        elif name == "vec":
+            want = torch.float64 if plan.dtype == "f64" else torch.float32
+        else:
+            want = plan.torch_dtype
+        if t.dtype != want:
+            raise TypeError(f"{name}: expected {want}, got {t.dtype}")
+
+
 def _stream(stream=None, like=None):
     """Stream handle: the given stream, else torch's current stream on the
     tensors' device (host tensors: the NULL stream, for argument checks)."""
@@ -212,6 +231,7 @@ def cgtp_forward_workspace_bytes(plan: Plan, n_items: int) -> int:
 
 
 def cgtp_forward(plan: Plan, x, y, w, out=None, ws=None, stream=None):
+    _want(plan, x=x, y=y, w=w)
     B = x.shape[0]
     if out is None:
         out = torch.empty(B, plan.dim_out, dtype=plan.out_dtype, device=x.device)
@@ -224,6 +244,7 @@ def cgtp_forward(plan: Plan, x, y, w, out=None, ws=None, stream=None):
 
 
 def cgtp_conv_forward(plan: Plan, x, sh, w, src, dst_row_ptr, out=None, ws=None, stream=None, node_order=None):
+    _want(plan, x=x, sh=sh, w=w, src=src, dst_row_ptr=dst_row_ptr, node_order=node_order)
     N, E = x.shape[0], src.shape[0]
     if out is None:
         out = torch.empty(N, plan.dim_out, dtype=plan.out_dtype, device=x.device)
@@ -239,6 +260,7 @@ def cgtp_conv_forward(plan: Plan, x, sh, w, src, dst_row_ptr, out=None, ws=None,
 def cgtp_conv_forward_vec(plan: Plan, x, vec, vec_perm, w, src, dst_row_ptr, out=None, ws=None, stream=None,
                           node_order=None):
     """Convolution with the SH computed in the kernel from the edge vectors."""
+    _want(plan, x=x, vec=vec, vec_perm=vec_perm, w=w, src=src, dst_row_ptr=dst_row_ptr, node_order=node_order)
     N, E = x.shape[0], src.shape[0]
     if out is None:
         out = torch.empty(N, plan.dim_out, dtype=plan.out_dtype, device=x.device)
@@ -255,6 +277,9 @@ def cgtp_conv_forward_radial(plan: Plan, x, vec, vec_perm, radial, w, src, dst_r
                              stream=None, node_order=None):
     """uvw convolution with per-edge weights from the radial network:
     radial float32 [2][H], w bf16 [H+1][weight_numel]."""
+    _want(plan, x=x, vec=vec, vec_perm=vec_perm, w=w, src=src, dst_row_ptr=dst_row_ptr, node_order=node_order)
+    if radial.dtype != torch.float32:
+        raise TypeError(f"radial: expected torch.float32, got {radial.dtype}")
     N, E = x.shape[0], src.shape[0]
     if out is None:
         out = torch.empty(N, plan.dim_out, dtype=torch.float32, device=x.device)
@@ -271,6 +296,8 @@ def cgtp_conv_backward_vec(plan: Plan, x, vec, vec_perm, w, src, dst_row_ptr, sr
                            need=("x", "w", "F"), ws=None, out=None, stream=None, node_order=None):
     """Backward with in-kernel SH; returns (g_x, g_sh, g_w, F), None where not
     requested."""
+    _want(plan, x=x, vec=vec, vec_perm=vec_perm, w=w, src=src, dst_row_ptr=dst_row_ptr, src_row_ptr=src_row_ptr,
+          src_perm=src_perm, g_out=g_out, node_order=node_order)
     N, E = x.shape[0], src.shape[0]
     dev = x.device
     od = plan.out_dtype
@@ -303,6 +330,8 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 def cgtp_conv_backward(plan: Plan, x, sh, w, src, dst, dst_row_ptr, src_row_ptr, src_perm, g_out,
                        need=("x", "sh", "w"), ws=None, out=None, stream=None, node_order=None):
+    _want(plan, x=x, sh=sh, w=w, src=src, dst=dst, dst_row_ptr=dst_row_ptr, src_row_ptr=src_row_ptr,
+          src_perm=src_perm, g_out=g_out, node_order=node_order)
     N, E = x.shape[0], src.shape[0]
     dev = x.device
     od = plan.out_dtype
@@ -324,6 +353,8 @@ def cgtp_conv_backward(plan: Plan, x, sh, w, src, dst, dst_row_ptr, src_row_ptr,
 def cgtp_conv_double_backward(plan: Plan, x, sh, w, src, dst, dst_row_ptr, src_row_ptr, src_perm, g_out,
                               gg_x=None, gg_sh=None, gg_w=None, need=("g_out", "x", "sh", "w"), ws=None,
                               out=None, stream=None, node_order=None):
+    _want(plan, x=x, sh=sh, w=w, src=src, dst=dst, dst_row_ptr=dst_row_ptr, src_row_ptr=src_row_ptr,
+          src_perm=src_perm, g_out=g_out, gg_x=gg_x, gg_sh=gg_sh, gg_w=gg_w, node_order=node_order)
     N, E = x.shape[0], src.shape[0]
     dev = x.device
     od = plan.out_dtype
