@@ -122,3 +122,50 @@ def test_cache_round_trip(B, tmp_path, monkeypatch):
     assert len(os.listdir(tmp_path)) == 1
     p2 = B.Plan("5x0e+5x1o", "1x0e+1x1o", "5x0e+5x1o", no_load=True)
     assert p2.cached
+
+
+def test_plan_flag_combinations(B, tmp_path, monkeypatch):
+    """Documented flag rules: bf16 weight storage for uvu float plans only;
+    radial weights for bf16 uvw shared-weight plans whose input 2 is one SH
+    row, hidden width 1..64."""
+    monkeypatch.setenv("CGTP_CACHE_DIR", str(tmp_path))
+    sh3 = "1x0e+1x1o+1x2e+1x3o"
+    B.Plan("8x0e+8x1o", sh3, "8x0e+8x1o", bf16_weights=True, no_load=True)
+    for args, kw in [
+        (("8x0e", "1x0e", "8x0e", None, "uvu", "f64"), dict(bf16_weights=True)),
+        (("8x0", "1x0", "8x0", None, "uvw", "bf16", True), dict(bf16_weights=True)),
+        (("8x0", "1x0+1x1", "8x0+8x1", None, "uvw", "bf16", False), dict(radial_hidden=4)),   # not shared
+        (("8x0", "1x0+1x1", "8x0+8x1", None, "uvw", "f32", True), dict(radial_hidden=4)),     # not bf16
+        (("8x0", "2x0+1x1", "8x0+8x1", None, "uvw", "bf16", True), dict(radial_hidden=4)),    # not an SH row
+        (("8x0", "1x0+1x1", "8x0+8x1", None, "uvw", "bf16", True), dict(radial_hidden=65)),   # too wide
+    ]:
+        with pytest.raises(B.CgtpError) as ei:
+            B.Plan(*args, **kw, no_load=True)
+        assert ei.value.code == -2, (args, kw)
+    p = B.Plan("8x0+8x1", "1x0+1x1+1x2", "8x0+8x1", None, "uvw", "bf16", True, radial_hidden=3, no_load=True)
+    # radial plans: (H+1) copies of every path along the mixing contraction
+    plain = B.Plan("8x0+8x1", "1x0+1x1+1x2", "8x0+8x1", None, "uvw", "bf16", True, no_load=True)
+    assert B.cgtp_forward_workspace_bytes(p, 100) >= 4 * B.cgtp_forward_workspace_bytes(plain, 100) - 1024
+
+
+def test_graph_helper_sizes(B):
+    import ctypes
+    b = ctypes.c_size_t()
+    assert B.lib().cgtp_node_order_workspace_bytes(100000, ctypes.byref(b)) == 0 and b.value > 0
+    assert B.lib().cgtp_sparse_attention_layout_bytes(1000, 5000, ctypes.byref(b)) == 0
+    # distinct columns of 63 windows: at most the edges plus 16 padding slots per window
+    assert b.value >= 4 * (5000 + 16 * 63) + 2 * (5000 + 16 * 63)
+    assert B.lib().cgtp_node_order_workspace_bytes(-1, ctypes.byref(b)) == -1
+    assert B.lib().cgtp_sparse_attention_layout_bytes(-1, 5, ctypes.byref(b)) == -1
+
+
+def test_sh_from_vectors_needs_sh_row_plan(B):
+    """cgtp_conv_forward_vec refuses plans whose input 2 is not one SH row
+    before any device work (checked on the host)."""
+    import torch
+    p = B.Plan("8x0e+8x1o", "2x0e+1x1o", "8x0e+8x1o", no_load=True)
+    e = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(B.CgtpError) as ei:
+        B.cgtp_conv_forward_vec(p, torch.zeros(2, p.dim_in1), torch.ones(1, 3), None, torch.zeros(1, p.weight_numel),
+                                e, torch.tensor([0, 1, 1], dtype=torch.int32))
+    assert ei.value.code in (-1, -2)
