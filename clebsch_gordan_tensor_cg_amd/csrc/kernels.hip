@@ -230,6 +230,187 @@ __global__ void k_scatter_global(const int32_t *__restrict__ key, int64_t n, int
     }
 }
 
+// Small key arrays in two launches and without device atomics.
+// k_csr_small_count (one workgroup) counts the keys of each of kSmallCsrRuns
+// contiguous edge runs in LDS, scans the key totals into row_ptr and writes,
+// per (run, key), the slot of the run's first edge with that key (16 bits:
+// every slot is below 65536).  k_csr_small_place (one wavefront per run)
+// walks its run in edge order, 64 edges at a time: one ballot per key bit
+// finds the lanes holding the same key, which ranks each edge among the
+// chunk's equal keys and elects the highest such lane to advance the run's
+// slot for that key.  The placement is therefore stable (edge order inside
+// every segment) without a sort.
+constexpr int kSmallCsrRuns = 32;
+constexpr int64_t kSmallCsrMaxKeys = 2048;
+constexpr int64_t kSmallCsrMaxEdges = 65535;
+constexpr int kSmallCsrChunks = 32;          // 64-edge chunks of one run (a run holds at most 2048 edges)
+static_assert(kSmallCsrMaxKeys == 2048, "the key-match ballots cover 11 bits");
+constexpr int kSmallCsrKeysPerThread = 32;   // keys per thread and round of the counting workgroup
+__host__ __device__ constexpr bool small_csr(int64_t n_edges, int64_t n_keys) {
+    return n_edges > 0 && n_keys > 0 && n_edges <= kSmallCsrMaxEdges && n_keys <= kSmallCsrMaxKeys;
+}
+
+__host__ __device__ constexpr int64_t small_csr_stride(int64_t n_keys) { return (n_keys + 1) & ~int64_t(1); }
+// runs of 2^s edges, the smallest power of two with kSmallCsrRuns runs covering n
+__host__ __device__ constexpr int small_csr_run_shift(int64_t n) {
+    int sh = 0;
+    while ((int64_t(kSmallCsrRuns) << sh) < n) ++sh;
+    return sh;
+}
+// bytes of the per-(run, key) slot table in the workspace
+__host__ __device__ constexpr size_t small_csr_table_bytes(int64_t n_keys) {
+    return sizeof(uint16_t) * kSmallCsrRuns * (size_t)small_csr_stride(n_keys);
+}
+
+// counters: word [j][k] holds run 2j's count of key k in its low half and
+// run 2j+1's in its high half (a run holds at most 2048 edges, so no carry)
+__global__ void __launch_bounds__(1024) k_csr_small_count(const int32_t *__restrict__ key, int64_t n, int64_t n_keys,
+                                                          int32_t *__restrict__ row_ptr,
+                                                          uint32_t *__restrict__ table) {
+    extern __shared__ uint32_t cpair[];   // [kSmallCsrRuns / 2][n_keys]
+    __shared__ int32_t wsum[16];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int nk = (int)n_keys;
+    const int rsh = small_csr_run_shift(n);
+    for (int i = t; i < (kSmallCsrRuns / 2) * nk; i += blockDim.x) cpair[i] = 0;
+    __syncthreads();
+    // 32 keys of a thread in flight at once: one round for up to 32768 edges
+    for (int h = 0; h * 32 * 1024 < n; ++h) {
+        int32_t kr[kSmallCsrKeysPerThread];
+#pragma unroll
+        for (int u = 0; u < kSmallCsrKeysPerThread; ++u) {
+            const int e = t + (h * kSmallCsrKeysPerThread + u) * 1024;
+            const int32_t kv = key[e < n ? e : n - 1];   // clamped: no branch around the load
+            kr[u] = e < n ? kv : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kSmallCsrKeysPerThread; ++u) {
+            const int k = kr[u];
+            if (k >= 0 && k < nk) {
+                const int r = (t + (h * kSmallCsrKeysPerThread + u) * 1024) >> rsh;
+                atomicAdd(&cpair[(r >> 1) * nk + k], (r & 1) ? 65536u : 1u);
+            }
+        }
+    }
+    __syncthreads();
+    // two consecutive keys per thread: totals, scan, row_ptr and run slots
+    int tot[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int k = 2 * t + q;
+        tot[q] = 0;
+        if (k < nk)
+            for (int j = 0; j < kSmallCsrRuns / 2; ++j) {
+                const uint32_t c = cpair[j * nk + k];
+                tot[q] += (int)(c & 0xffffu) + (int)(c >> 16);
+            }
+    }
+    const int own = tot[0] + tot[1];
+    int incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wv; ++w) before += wsum[w];
+    const int first = before + incl - own;
+    if (2 * t < nk) {
+        int acc[2] = {first, first + tot[0]};
+        row_ptr[2 * t] = acc[0];
+        if (2 * t + 1 < nk) row_ptr[2 * t + 1] = acc[1];
+        const int64_t words = small_csr_stride(nk) / 2;
+        for (int j = 0; j < kSmallCsrRuns / 2; ++j) {
+            const uint32_t c0 = cpair[j * nk + 2 * t];
+            const uint32_t c1 = 2 * t + 1 < nk ? cpair[j * nk + 2 * t + 1] : 0u;
+            // run 2j, then run 2j+1: keys 2t (low half) and 2t+1 (high half)
+            table[(2 * j) * words + t] = (uint32_t)acc[0] | ((uint32_t)acc[1] << 16);
+            acc[0] += (int)(c0 & 0xffffu);
+            acc[1] += (int)(c1 & 0xffffu);
+            table[(2 * j + 1) * words + t] = (uint32_t)acc[0] | ((uint32_t)acc[1] << 16);
+            acc[0] += (int)(c0 >> 16);
+            acc[1] += (int)(c1 >> 16);
+        }
+    }
+    if (t == (int)blockDim.x - 1) row_ptr[nk] = before + incl;   // every valid key counted
+}
+
+// lanes of this wavefront whose key equals this lane's key (valid lanes
+// only); keys lie in [0, 2^nbits)
+__device__ __forceinline__ uint64_t same_key_lanes(int32_t k, bool valid, int nbits) {
+    uint64_t m = __ballot(valid);
+    uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {   // kSmallCsrMaxKeys = 2^11
+        if (b >= nbits) break;       // uniform
+        const uint32_t mine = (uint32_t)(((int32_t)((uint32_t)k << (31 - b))) >> 31);   // 0 or ~0
+        const uint64_t bb = __ballot(mine != 0u);
+        lo &= ~((uint32_t)bb ^ mine);
+        hi &= ~((uint32_t)(bb >> 32) ^ mine);
+    }
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__global__ void __launch_bounds__(64) k_csr_small_place(const int32_t *__restrict__ key,
+                                                        const int32_t *__restrict__ val, int64_t n, int64_t n_keys,
+                                                        int nbits, const uint16_t *__restrict__ table,
+                                                        int32_t *__restrict__ perm, int32_t *__restrict__ sorted_key,
+                                                        int32_t *__restrict__ sorted_val) {
+    extern __shared__ uint16_t slot_of[];   // [n_keys]: this run's next slot per key
+    const int lane = threadIdx.x;
+    const int nk = (int)n_keys;
+    const int64_t run = int64_t(1) << small_csr_run_shift(n);
+    const int64_t e0 = blockIdx.x * run, e1 = e0 + run < n ? e0 + run : n;
+    const uint16_t *__restrict__ row = table + blockIdx.x * small_csr_stride(nk);
+    // the whole run's keys and values in flight at once, one per lane and chunk
+    int32_t kb[kSmallCsrChunks], vb[kSmallCsrChunks] = {};
+#pragma unroll
+    for (int u = 0; u < kSmallCsrChunks; ++u) {
+        const int64_t e = e0 + 64 * u + lane;
+        const int64_t ec = e < e1 ? e : (e0 < e1 ? e1 - 1 : 0);   // clamped: no branch around the loads
+        const int32_t kv = key[ec];
+        kb[u] = e < e1 ? kv : -1;
+        if (sorted_val) vb[u] = val[ec];
+    }
+    // the run's slot row, as 32-bit words, all in flight together
+    constexpr int kRowWords = (int)(kSmallCsrMaxKeys / 2 / 64);
+    const int words = (int)(small_csr_stride(nk) / 2);
+    uint32_t rw[kRowWords];
+#pragma unroll
+    for (int u = 0; u < kRowWords; ++u) {
+        const int i = lane + 64 * u;
+        rw[u] = i < words ? ((const uint32_t *)row)[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kRowWords; ++u) {
+        const int i = lane + 64 * u;
+        if (i < words) ((uint32_t *)slot_of)[i] = rw[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kSmallCsrChunks; ++u) {
+        if (e0 + 64 * u >= e1) break;   // uniform across the wavefront
+        const int64_t e = e0 + 64 * u + lane;
+        const int32_t k = kb[u];
+        const bool valid = k >= 0 && k < nk;
+        const uint64_t m = same_key_lanes(k, valid, nbits);
+        const int base = valid ? (int)slot_of[k] : 0;   // read by every lane before the update
+        if (valid) {
+            const int slot = base + lanes_below(m);
+            perm[slot] = (int32_t)e;
+            if (sorted_key) sorted_key[slot] = k;
+            if (sorted_val) sorted_val[slot] = vb[u];
+        }
+        if (valid && ((m >> lane) >> 1) == 0) slot_of[k] = (uint16_t)(base + __popcll(m));
+    }
+}
+
 // Node processing order: nodes by decreasing segment length (longest
 // first, so the long segments do not form the tail of a launch).  Buckets
 // are kOrderBuckets-1-min(len, kOrderBuckets-1); the order within a bucket
@@ -1051,6 +1232,7 @@ int cgtp_csr_workspace_bytes(int64_t n_edges, int64_t n_keys, size_t *bytes) {
     if (!bytes || n_edges < 0 || n_keys < 0)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_csr_workspace_bytes: bad argument");
     *bytes = align256(sizeof(int32_t) * (size_t)(n_keys + 1)) * 2 + align256(sizeof(int32_t) * (size_t)(n_edges + 1));
+    if (small_csr(n_edges, n_keys)) *bytes = std::max(*bytes, align256(small_csr_table_bytes(n_keys)));
     return CGTP_OK;
 }
 
@@ -1066,6 +1248,22 @@ int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int6
     if (!row_ptr || (n_edges > 0 && (!key || !perm || (sorted_val && !val))) || !workspace ||
         workspace_bytes < need)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_build_csr: NULL pointer or workspace too small");
+    if (small_csr(n_edges, n_keys)) {
+        int nbits = 0;
+        while ((int64_t(1) << nbits) < n_keys) ++nbits;
+        const size_t lds = sizeof(uint32_t) * (kSmallCsrRuns / 2) * (size_t)n_keys;   // up to 128 KiB
+        static const hipError_t lds_ok = hipFuncSetAttribute(
+            (const void *)k_csr_small_count, hipFuncAttributeMaxDynamicSharedMemorySize,
+            (int)(sizeof(uint32_t) * (kSmallCsrRuns / 2) * kSmallCsrMaxKeys));
+        if (lds_ok != hipSuccess) return hip_check(lds_ok, "cgtp_build_csr: LDS size attribute");
+        uint32_t *table = (uint32_t *)workspace;
+        CGTP_LAUNCH("k_csr_small_count", s, k_csr_small_count, dim3(1), dim3(1024), lds, s, key, n_edges, n_keys,
+                    row_ptr, table);
+        CGTP_LAUNCH("k_csr_small_place", s, k_csr_small_place, dim3(kSmallCsrRuns), dim3(64),
+                    sizeof(uint16_t) * (size_t)small_csr_stride(n_keys), s, key, val, n_edges, n_keys, nbits,
+                    (const uint16_t *)table, perm, sorted_key, sorted_val);
+        return hip_check(hipGetLastError(), "cgtp_build_csr launch");
+    }
     char *ws = (char *)workspace;
     int32_t *cnt = (int32_t *)ws;
     int32_t *cursor = (int32_t *)(ws + align256(sizeof(int32_t) * (size_t)(n_keys + 1)));

@@ -13,6 +13,7 @@ namespace {
 struct Rec {
     std::string name;
     hipEvent_t a = nullptr, b = nullptr;
+    bool ok = true;   // both events recorded
 };
 std::mutex g_mu;
 bool g_on = false;
@@ -24,8 +25,12 @@ TimedLaunch::TimedLaunch(const char *name, hipStream_t s) : s_(s) {
     if (!g_on) return;
     Rec r;
     r.name = name;
-    if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
-    hipEventRecord(r.a, s);
+    if (hipEventCreate(&r.a) != hipSuccess) return;
+    if (hipEventCreate(&r.b) != hipSuccess || hipEventRecord(r.a, s) != hipSuccess) {
+        (void)hipEventDestroy(r.a);
+        if (r.b) (void)hipEventDestroy(r.b);
+        return;
+    }
     g_recs.push_back(r);
     idx_ = (long)g_recs.size() - 1;
 }
@@ -33,7 +38,7 @@ TimedLaunch::TimedLaunch(const char *name, hipStream_t s) : s_(s) {
 TimedLaunch::~TimedLaunch() {
     if (idx_ < 0) return;
     std::lock_guard<std::mutex> lk(g_mu);
-    if (idx_ < (long)g_recs.size()) hipEventRecord(g_recs[idx_].b, s_);
+    if (idx_ < (long)g_recs.size() && hipEventRecord(g_recs[idx_].b, s_) != hipSuccess) g_recs[idx_].ok = false;
 }
 
 }  // namespace cgtp
@@ -62,7 +67,7 @@ int cgtp_timing_collect(char (*names)[64], float *ms, int32_t cap, int32_t *n) {
     int rc = CGTP_OK;
     for (Rec &r : recs) {
         float t = -1.0f;
-        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+        if (!r.ok || hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
             rc = set_error(CGTP_ERR_HIP, "cgtp_timing_collect: event query failed");
         if (k < cap) {
             std::strncpy(names[k], r.name.c_str(), 63);
@@ -70,8 +75,8 @@ int cgtp_timing_collect(char (*names)[64], float *ms, int32_t cap, int32_t *n) {
             ms[k] = t;
             ++k;
         }
-        hipEventDestroy(r.a);
-        hipEventDestroy(r.b);
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
     }
     *n = k;
     return rc;

@@ -299,8 +299,10 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
  *   sorted_val[t] = val[perm[t]] (each may be NULL; val carries a second
  *   per-edge index, e.g. the source node, into the sorted order).
  * Bit-exact and deterministic (the order within a key does not depend on
- * the order in which the device's atomics land).  A segment of d edges
- * costs O(d^2 / 64) per wavefront, so very large in-degrees are slow.
+ * the order in which the device's atomics land).  Up to 65535 edges and
+ * 2048 keys the sort takes two launches, linear in the edges.  Beyond, a
+ * segment of d edges costs O(d^2 / 64) per wavefront, so very large
+ * in-degrees are slow.
  * workspace: cgtp_csr_workspace_bytes.  Keys should lie in [0, n_keys):
  * an edge with a key outside it is left out (row_ptr[n_keys] then counts
  * only the edges kept, perm holds only that many ids, and

@@ -354,10 +354,23 @@ def test_conv_no_edges(B, torch):
 # CSR build, validation, spherical harmonics, forces
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("case", ["c2", "empty", "one_node", "hub", "ragged", "multi_range", "wide_keys",
-                                  "many_splits"])
+                                  "many_splits", "molecules", "small_max", "one_key_max", "past_small_edges",
+                                  "past_small_keys"])
 def test_build_csr_bit_exact(B, torch, case):
     rs = np.random.default_rng(5)
-    if case == "c2":
+    # two-launch path: at most 65535 edges and 2048 keys
+    if case == "molecules":
+        g = W.molecule_batch(100, 18, seed=0)
+        key, n = g.dst, g.n_nodes
+    elif case == "small_max":
+        key, n = rs.integers(0, 2048, 65535).astype(np.int32), 2048
+    elif case == "one_key_max":
+        key, n = np.zeros(65535, np.int32), 1
+    elif case == "past_small_edges":
+        key, n = rs.integers(0, 2048, 65536).astype(np.int32), 2048
+    elif case == "past_small_keys":
+        key, n = rs.integers(0, 2049, 65535).astype(np.int32), 2049
+    elif case == "c2":
         g = W.periodic_graph(4096, seed=0)
         key, n = g.dst, 4096
     elif case == "multi_range":     # three LDS key ranges
