@@ -342,9 +342,7 @@ __global__ void __launch_bounds__(1024) k_csr_small_count(const int32_t *__restr
 __device__ __forceinline__ uint64_t same_key_lanes(int32_t k, bool valid, int nbits) {
     uint64_t m = __ballot(valid);
     uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
-#pragma unroll
-    for (int b = 0; b < 11; ++b) {   // kSmallCsrMaxKeys = 2^11
-        if (b >= nbits) break;       // uniform
+    for (int b = 0; b < nbits; ++b) {   // nbits <= 11
         const uint32_t mine = (uint32_t)(((int32_t)((uint32_t)k << (31 - b))) >> 31);   // 0 or ~0
         const uint64_t bb = __ballot(mine != 0u);
         lo &= ~((uint32_t)bb ^ mine);
@@ -852,13 +850,13 @@ struct CotLaunch {
 //   out[item][off3 + w*d3 + k] (=|+=) sum_kk T[(item*d3 + k)*K + kk] * Wb[kk][w]
 // T and W are bf16 (raw 16-bit), accumulation in FP32.  Row kk of Wb is row
 // (kk - kstart[p]) of path p's weight block [mul1*mul2][mul3] at woff[p].
-// A workgroup of four wavefronts stages a chunk of Wb (256 rows x 64
+// A workgroup of four wavefronts stages a chunk of Wb (kMixKC rows x 64
 // columns) in LDS; each wavefront computes 16 rows x 64 columns with
 // v_mfma_f32_16x16x16_bf16: lane l supplies A[l%16][4(l/16)+0..3] and
 // B[4(l/16)+0..3][l%16], and receives D[4(l/16)+i][l%16], i = 0..3.
 // ---------------------------------------------------------------------------
 constexpr int kMixMaxPaths = 64;
-constexpr int kMixKC = 256;   // contraction rows staged per step (32 KB of bf16 at 64 columns)
+constexpr int kMixKC = 512;   // contraction rows staged per step (64 KiB of bf16 at 64 columns)
 constexpr int kMixMaxBlocks = 4;   // output blocks mixed by one launch
 // one output block of a mixing launch
 struct MixBlockArgs {
@@ -880,26 +878,36 @@ typedef float cgtp_f4 __attribute__((ext_vector_type(4)));
 // r = h*Kb + kk (h < n_rep, kk < Kb) reads weight row
 // h*wstride + woff_p + (kk - kstart_p)*mul3 of the path p holding kk (n_rep
 // copies of the paths: the rows of a radial network's output layer).  A
-// workgroup owns 64 rows of T (16 per wavefront) and 64 output columns;
-// the weights are staged in LDS kMixKC rows at a time.
-// out[item][off3 + w*d3 + k] (=|+=) sum_r T[item*d3 + k][r] W'[r][w]: the
-// channel mixing of one output block on the matrix cores.  Contraction row
-// r = h*Kb + kk (h < n_rep, kk < Kb) reads weight row
-// h*wstride + woff_p + (kk - kstart_p)*mul3 of the path p holding kk (n_rep
-// copies of the paths: the rows of a radial network's output layer).  A
-// workgroup owns 64 rows of T (16 per wavefront) and 64 output columns;
-// the weights are staged in LDS kMixKC rows at a time.
+// workgroup owns 64 rows of T (16 per wavefront) and 64 output columns and
+// stages the weights in LDS kMixKC rows at a time, rows interleaved in groups
+// of four: element (r, c) of a chunk sits at ((r/4)*64 + c)*4 + r%4 (before
+// the chunk swizzle below), so a lane's B fragment (four consecutive rows of
+// one column) is one 8-byte read.
+// Per step the A fragments and the weight tiles are loaded together (one
+// round trip), the tiles are transposed in registers and written to LDS.
 // Split contraction: with n_split > 1, workgroup (g, s) sums only the
 // contraction rows [s*kspan, (s+1)*kspan) of row group g and writes its
 // partial tile to part[s][row][column]; k_uvw_mix_reduce adds the parts.
 // All output blocks of a layer in one launch: workgroups
 // [wg_start_b, wg_start_{b+1}) serve block b.
-__global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T0, const uint16_t *__restrict__ W,
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+// 16-byte chunk j of row group q is stored at chunk j ^ mix_swizzle(q) of that
+// group (bits 3 and 1..0 of the chunk index): the tile writes of a wavefront
+// then spread over all sixteen 16-byte bank groups, and the B-fragment reads
+// touch each group twice at most
+__device__ __forceinline__ int mix_swizzle(int q) { return ((q & 1) << 3) | ((q >> 1) & 3); }
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+// kFast: every contraction length a multiple of 16, full 64-column weight
+// rows in 16-byte segments and 8-byte aligned path tensors, so loads need no
+// guards (the general variant checks every element).
+template <bool kFast>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_uvw_mix(const uint16_t *__restrict__ T0, const uint16_t *__restrict__ W,
                                                  int64_t wstride, MixArgs args, float *__restrict__ out, int64_t dim3,
                                                  int accumulate, float *__restrict__ part0) {
     __shared__ __attribute__((aligned(16))) uint16_t Ws[kMixKC * 64];
     __shared__ int64_t wrow[kMixKC];
-    __shared__ int64_t s_kstart[kMixMaxPaths + 1];
+    __shared__ int32_t s_kstart[kMixMaxPaths + 1];
     __shared__ int64_t s_woff[kMixMaxPaths];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // this workgroup's block; its fields are read with constant indices
@@ -944,89 +952,120 @@ __global__ void __launch_bounds__(256) k_uvw_mix(const uint16_t *__restrict__ T0
             for (int ct = 0; ct < 4; ++ct) acc[ct] = (cgtp_f4){0.f, 0.f, 0.f, 0.f};
             for (int64_t k0 = k_begin; k0 < k_end; k0 += kMixKC) {
                 const int kc = (int)(k_end - k0 < kMixKC ? k_end - k0 : kMixKC);
-                __syncthreads();   // the previous step's weights are no longer read
+                __syncthreads();   // the previous step's weights and row table are no longer read
                 for (int kr = tid; kr < kc; kr += 256) {
-                    const int64_t r = k0 + kr, h = r / Kb, kk = r % Kb;
+                    const int r = (int)(k0 + kr), h = r / (int)Kb, kk = r - h * (int)Kb;
                     int p = 0;
                     while (p + 1 < np && kk >= s_kstart[p + 1]) ++p;
-                    wrow[kr] = h * wstride + s_woff[p] + (kk - s_kstart[p]) * mul3 + cb;
+                    wrow[kr] = h * wstride + s_woff[p] + (int64_t)(kk - s_kstart[p]) * mul3 + cb;
                 }
                 __syncthreads();
-                if (wvec) {
-                    // 8 threads per weight row, 16 bytes each, four rows in flight
-                    for (int base = tid; base < kc * 8; base += 1024) {
-                        uint4 v[4];
-                        int idx[4];
-                        for (int u = 0; u < 4; ++u) {
-                            idx[u] = base + u * 256;
-                            v[u] = make_uint4(0, 0, 0, 0);
-                            if (idx[u] < kc * 8 && (idx[u] & 7) * 8 < ncol)
-                                v[u] = *(const uint4 *)(W + wrow[idx[u] >> 3] + (idx[u] & 7) * 8);
+                // this lane's A fragments for the whole step, issued with the weight loads
+                const int n_st = (kc + 15) / 16;
+                const uint16_t *__restrict__ Tk = Trow + k0 + kq;
+                // A fragments in two halves: the first is loaded with the weight
+                // tiles, the second after the staging barrier, under the first
+                // half's matrix operations
+                constexpr int kHalf = kMixKC / 32;
+                cgtp_s4 af[2][kHalf];
+                auto load_a = [&](int hf) {
+#pragma unroll
+                    for (int j = 0; j < kHalf; ++j) {
+                        const int st = hf * kHalf + j;
+                        if constexpr (kFast) {
+                            // whole 16-row steps; a step past the chunk rereads its last
+                            // step (its weight rows are zero)
+                            af[hf][j] = *(const cgtp_s4 *)(Tk + 16 * (st < n_st ? st : n_st - 1));
+                        } else if (vec_ok && st * 16 + 16 <= kc) {   // uniform: the whole step is inside
+                            af[hf][j] = *(const cgtp_s4 *)(Tk + st * 16);
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                af[hf][j][i] = st * 16 + kq + i < kc ? (short)Tk[st * 16 + i] : (short)0;
                         }
-                        for (int u = 0; u < 4; ++u)
-                            if (idx[u] < kc * 8) *(uint4 *)(Ws + (idx[u] >> 3) * 64 + (idx[u] & 7) * 8) = v[u];
                     }
-                } else {
-                    for (int idx = tid; idx < kc * 64; idx += 256) {
-                        const int kr = idx >> 6, c = idx & 63;
-                        Ws[idx] = c < ncol ? W[wrow[kr] + c] : (uint16_t)0;
+                };
+                load_a(0);
+                // weight tiles of 4 rows x 8 columns: tile t covers rows 4(t/8)..+3 and
+                // columns 8(t%8)..+7; four tiles per thread
+#pragma unroll
+                for (int j = 0; j < kMixKC * 64 / 32 / 256; ++j) {
+                    const int ti = tid + 256 * j, q = ti >> 3, c8 = (ti & 7) * 8;
+                    uint4 v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kr = 4 * q + i;
+                        if constexpr (kFast) {   // clamped row, zero past the chunk
+                            const uint4 t = *(const uint4 *)(W + wrow[kr < kc ? kr : kc - 1] + c8);
+                            v[i] = kr < kc ? t : make_uint4(0, 0, 0, 0);
+                            continue;
+                        }
+                        v[i] = make_uint4(0, 0, 0, 0);
+                        if (kr >= kc || c8 >= ncol) continue;
+                        const uint16_t *__restrict__ src = W + wrow[kr] + c8;
+                        if (wvec) {
+                            v[i] = *(const uint4 *)src;
+                        } else {
+                            uint32_t e[8];
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) e[c] = c8 + c < ncol ? src[c] : 0u;
+                            v[i] = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                                              e[6] | (e[7] << 16));
+                        }
                     }
+                    const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+                    const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+                    const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
+                    const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
+                    uint4 *dst = (uint4 *)Ws + q * 32;
+                    const int fq = mix_swizzle(q);
+#pragma unroll
+                    for (int h = 0; h < 4; ++h)   // columns c8+2h and c8+2h+1
+                        dst[((c8 >> 1) + h) ^ fq] = make_uint4(lo_halves(w0[h], w1[h]), lo_halves(w2[h], w3[h]),
+                                                               hi_halves(w0[h], w1[h]), hi_halves(w2[h], w3[h]));
                 }
                 __syncthreads();
                 if (row0 >= M) continue;   // this wavefront has no rows (it still joined the barriers)
-                // this lane's A fragments, eight k steps at a time, loaded
-                // before the eight steps' matrix operations
-                for (int kb = 0; kb < kc; kb += 128) {
-                    uint2 af[8];
+                if (n_st > kHalf) load_a(1);
+                // blocks of eight steps; the steps of the last block past the chunk
+                // meet zero weight rows
 #pragma unroll
-                    for (int st = 0; st < 8; ++st) {
-                        const int kl = kb + st * 16;
-                        af[st] = make_uint2(0, 0);
-                        if (kl >= kc) continue;
-                        const int64_t kg = k0 + kl;
-                        if (vec_ok && kl + kq + 4 <= kc) {
-                            af[st] = *(const uint2 *)(Trow + kg + kq);
-                        } else {
-                            uint32_t hv[4];
-                            for (int i = 0; i < 4; ++i) hv[i] = kl + kq + i < kc ? Trow[kg + kq + i] : 0u;
-                            af[st] = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
-                        }
-                    }
+                for (int c = 0; c < kMixKC / 128; ++c) {
+                    if (c * 8 >= n_st) break;   // uniform
 #pragma unroll
-                    for (int st = 0; st < 8; ++st) {
-                        const int kl = kb + st * 16;
-                        if (kl >= kc) continue;
-                        cgtp_s4 a;
-                        a[0] = (short)(af[st].x & 0xffff);
-                        a[1] = (short)(af[st].x >> 16);
-                        a[2] = (short)(af[st].y & 0xffff);
-                        a[3] = (short)(af[st].y >> 16);
+                    for (int j = 0; j < 8; ++j) {
+                        const int st = c * 8 + j;
+                        const int q = 4 * st + (lane >> 4), fq = mix_swizzle(q);
+                        const cgtp_s4 *bq = (const cgtp_s4 *)Ws + q * 64 + (r_a & 1);
 #pragma unroll
-                        for (int ct = 0; ct < 4; ++ct) {
-                            cgtp_s4 b;
-                            for (int i = 0; i < 4; ++i) {
-                                const int kr = kl + kq + i;
-                                b[i] = kr < kc ? (short)Ws[kr * 64 + ct * 16 + r_a] : (short)0;
-                            }
-                            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc[ct], 0, 0, 0);
-                        }
+                        for (int ct = 0; ct < 4; ++ct)
+                            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                                af[st / kHalf][st % kHalf], bq[2 * ((8 * ct + (r_a >> 1)) ^ fq)], acc[ct], 0, 0, 0);
                     }
                 }
             }
             if (row0 >= M) continue;
+            // rows row0+kq+i, i = 0..3: (item, k) of the first by one division, then stepped
+            const int64_t rq = row0 + kq;
+            const int64_t item_q = rq / d3;
+            const int k_q = (int)(rq - item_q * d3);
+#pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 const int col = cb + ct * 16 + r_a;
                 if (col >= mul3) continue;
+                int64_t item = item_q;
+                int k = k_q;
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int64_t r = row0 + kq + i;
-                    if (r >= M) continue;
-                    if (n_split > 1) {
-                        part[((int64_t)split * M + r) * mul3 + col] = acc[ct][i];
-                        continue;
+                    if (rq + i < M) {
+                        if (n_split > 1) {
+                            part[((int64_t)split * M + rq + i) * mul3 + col] = acc[ct][i];
+                        } else {
+                            float *o = out + item * dim3 + off3 + (int64_t)col * d3 + k;
+                            *o = accumulate ? *o + acc[ct][i] : acc[ct][i];
+                        }
                     }
-                    const int64_t item = r / d3, k = r % d3;
-                    float *o = out + item * dim3 + off3 + (int64_t)col * d3 + k;
-                    *o = accumulate ? *o + acc[ct][i] : acc[ct][i];
+                    if (++k == d3) k = 0, ++item;
                 }
             }
         }
@@ -1094,8 +1133,13 @@ int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items,
         MixArgs args{};
         args.nb = (int)std::min<size_t>(kMixMaxBlocks, p.mix.size() - b0);
         int64_t wg = 0, red = 0;
+        // unguarded loads: 16-row contraction steps, whole 16-byte weight
+        // segments, 8-byte aligned path-tensor rows
+        bool fast = (((uintptr_t)T) & 7) == 0 && (((uintptr_t)w) & 15) == 0 && p.wnumel % 8 == 0;
         for (int i = 0; i < args.nb; ++i) {
             const MixBlock &mb = p.mix[b0 + i];
+            fast = fast && mb.Kr % 16 == 0 && mb.mul3 % 64 == 0 && (n_items * mb.t_off_per_item) % 4 == 0;
+            for (int pi : mb.paths) fast = fast && p.paths[pi].woff % 8 == 0;
             if ((int)mb.paths.size() > kMixMaxPaths)
                 return set_error(CGTP_ERR_UNSUPPORTED, "more than 64 paths into one output block");
             MixBlockArgs &a = args.b[i];
@@ -1125,8 +1169,12 @@ int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items,
             a.wg_start = wg;
             wg += groups * a.n_split;
         }
-        CGTP_LAUNCH("k_uvw_mix", s, k_uvw_mix, dim3((unsigned)wg), dim3(256), 0, s, (const uint16_t *)T,
-                    (const uint16_t *)w, p.wnumel, args, (float *)out, p.dim3, accumulate, (float *)part);
+        if (fast)
+            CGTP_LAUNCH("k_uvw_mix", s, k_uvw_mix<true>, dim3((unsigned)wg), dim3(256), 0, s, (const uint16_t *)T,
+                        (const uint16_t *)w, p.wnumel, args, (float *)out, p.dim3, accumulate, (float *)part);
+        else
+            CGTP_LAUNCH("k_uvw_mix", s, k_uvw_mix<false>, dim3((unsigned)wg), dim3(256), 0, s, (const uint16_t *)T,
+                        (const uint16_t *)w, p.wnumel, args, (float *)out, p.dim3, accumulate, (float *)part);
         if (red > 0) {
             unsigned g = grid_for(red);
             if (g > 8192) g = 8192;
