@@ -3,18 +3,20 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload c4|c2|c3|c1|c5] [--no-cpu-baseline]
                     [--separate-sh] [--bf16-weights] [--all-parity] [--morton]
-                    [--natural-order] [--nominal-e]
+                    [--natural-order] [--nominal-e] [--unfused]
 
 Default workload "c4" (one step = the whole hot path on the 4096-atom
 periodic water-density box, cutoff 5 A, node 128x0e+128x1o, SH l<=3, uvu,
 fp32): CSR of the edges by destination (carrying the source index), the
-transpose CSR by source and the longest-row-first processing order; fused
-convolution forward with the spherical harmonics of the edge vectors
-computed inside the kernel; backward (g_x, g_w, and the forces of E = sum of
-the 0e output blocks through the SH Jacobian); the force-loss cotangent on
-the SH; and the double backward (d/dx, d/dw, d/dg_out) driven by that
-cotangent.  --separate-sh runs the SH and the forces as kernels of their own
-with SH and SH-gradient arrays in memory.  Other workloads time the
+transpose CSR by source and the longest-row-first processing order; the
+convolution forward and backward in one pass over the edges (out, g_x, g_w,
+and the forces of E = sum of the 0e output blocks through the SH Jacobian;
+E is linear in out, so g_out = dE/dout is known before the forward), with
+the spherical harmonics of the edge vectors computed inside the kernel; the
+force-loss cotangent on the SH; and the double backward (d/dx, d/dw,
+d/dg_out) driven by that cotangent.  --unfused runs the forward and the
+backward as separate calls.  --separate-sh runs the SH and the forces as
+kernels of their own with SH and SH-gradient arrays in memory.  Other workloads time the
 forward path alone: c2 (same graph), c3 (16384 atoms, fp64, node
 128x0e+128x1o+128x2e), c1 (1000 independent products), c5 (100 molecules of
 18 atoms, uvw bf16 with matrix-core mixing).  Inputs are resident in HBM
@@ -60,6 +62,8 @@ def parse():
                          "vectors, forces from the backward's SH-gradient partials)")
     ap.add_argument("--natural-order", action="store_true",
                     help="hand destination rows to the device in node-id order (no longest-first order)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="c4: forward and backward as separate calls (default: one pass over the edges)")
     ap.add_argument("--nominal-e", action="store_true",
                     help="c2/c3/c4 graph with cutoff 4.153 A (about 30 neighbours, the nominal edge count)")
     return ap.parse_args()
@@ -103,6 +107,11 @@ def alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb, wb, shb):
     # reads x, g_out, the SH operand, w, src, row_ptr; writes g_x, g_sh (or
     # its partials), g_w (at the arithmetic width)
     return N * (2 * d1 + d3) * eb + E * (shb + d2 * eb) + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
+
+
+def alg_bytes_conv_fb(N, E, d1, d2, d3, wn, eb, ob, wb, shb):
+    # the backward's arrays plus the forward's output rows
+    return alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb, wb, shb) + N * d3 * ob
 
 
 def alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb, wb):
@@ -233,6 +242,9 @@ def bench_conv(args, torch, B, W):
         raise SystemExit("--all-parity and --morton apply to the c2, c3 and c4 workloads")
     cfg = W.config(base + ("a" if args.all_parity else ""))
     full = name == "c4"
+    if args.unfused and not full:
+        raise SystemExit("--unfused applies to the c4 workload")
+    fused = full and not args.unfused
     dtype = cfg.dtype
     rng = np.random.default_rng(args.seed)
     if name == "c5":
@@ -304,7 +316,13 @@ def bench_conv(args, torch, B, W):
                             B.cgtp_build_csr(src_s, N, sorted_key=False, ws=csr_ws,
                                              out=(src_perm, src_rp, None, None)) if full else None,
                             None if args.natural_order else B.cgtp_node_order(rp, ws=ord_ws, out=order)))
-        if sh_in_conv:
+        if sh_in_conv and fused:
+            # one pass: out, g_x, g_w and the forces (from the per-unit
+            # SH-gradient partials), SH computed inside the kernel
+            run("conv_fb", lambda: B.cgtp_conv_forward_backward_vec(
+                plan, x, vec, perm, w, src_s, rp, src_rp, src_perm, g_out, ws=ws, out=(out, g_x, None, g_w, F),
+                node_order=node_order))
+        elif sh_in_conv:
             # SH computed inside the convolution kernels; forces straight from
             # the backward's per-unit SH-gradient partials
             run("conv_fwd", lambda: B.cgtp_conv_forward_vec(plan, x, vec, perm, w, src_s, rp, out=out, ws=f_ws,
@@ -314,6 +332,13 @@ def bench_conv(args, torch, B, W):
             run("conv_bwd", lambda: B.cgtp_conv_backward_vec(plan, x, vec, perm, w, src_s, rp, src_rp, src_perm,
                                                              g_out, ws=ws, out=(g_x, None, g_w, F),
                                                              node_order=node_order))
+        elif fused:
+            run("sh", lambda: B.cgtp_spherical_harmonics(lmax, vec, perm, dtype, out=sh))
+            run("conv_fb", lambda: B.cgtp_conv_forward_backward(plan, x, sh, w, src_s, rp, src_rp, src_perm, g_out,
+                                                                ws=ws, out=(out, g_x, g_sh, g_w),
+                                                                node_order=node_order))
+            run("forces", lambda: B.cgtp_sh_forces(lmax, vec, perm, g_sh, rp, src_rp, src_perm, dtype, ws=fo_ws,
+                                                   out=F))
         else:
             run("sh", lambda: B.cgtp_spherical_harmonics(lmax, vec, perm, dtype, out=sh))
             run("conv_fwd", lambda: B.cgtp_conv_forward(plan, x, sh, w, src_s, rp, out=out, ws=f_ws,
@@ -375,7 +400,8 @@ def bench_conv(args, torch, B, W):
         alg["cgtp_bwd"] = N * (d1 + d3) * eb + E * (shb + d2 * eb) + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
         alg["cgtp_dbl"] = N * (d1 + 2 * d3) * eb + E * d2 * eb + E * wn * (wb + eb) + E * 4 + (N + 1) * 4
         # the same kernels with the full call's flags folded in
-        alg["cgtp_bwd_full"], alg["cgtp_dbl_full"] = alg["cgtp_bwd"], alg["cgtp_dbl"]
+        alg["cgtp_fb"] = alg["cgtp_bwd"] + N * d3 * ob   # plus the forward's output rows
+        alg["cgtp_bwd_full"], alg["cgtp_dbl_full"], alg["cgtp_fb_full"] = alg["cgtp_bwd"], alg["cgtp_dbl"], alg["cgtp_fb"]
     kern = {}
     for k, v in launches.items():
         kern[k] = dict(v)
@@ -383,11 +409,17 @@ def bench_conv(args, torch, B, W):
             gbs = alg[k] / (v["avg_ms"] * 1e-3) / 1e9
             kern[k].update({"alg_bytes": int(alg[k]), "GB_per_s": round(gbs, 1),
                             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
-    calls = {"conv_fwd": {"ms": kms["conv_fwd"], "GB_per_s": round(
-        alg_bytes_conv_fwd(N, E, d1, d3, wn, eb, ob, wb, shb) / (kms["conv_fwd"] * 1e-3) / 1e9, 1)}}
-    if full:
+    calls = {}
+    if "conv_fwd" in kms:
+        calls["conv_fwd"] = {"ms": kms["conv_fwd"], "GB_per_s": round(
+            alg_bytes_conv_fwd(N, E, d1, d3, wn, eb, ob, wb, shb) / (kms["conv_fwd"] * 1e-3) / 1e9, 1)}
+    if "conv_fb" in kms:
+        calls["conv_fb"] = {"ms": kms["conv_fb"], "GB_per_s": round(
+            alg_bytes_conv_fb(N, E, d1, d2, d3, wn, eb, ob, wb, shb) / (kms["conv_fb"] * 1e-3) / 1e9, 1)}
+    if full and "conv_bwd" in kms:
         calls["conv_bwd"] = {"ms": kms["conv_bwd"], "GB_per_s": round(
             alg_bytes_conv_bwd(N, E, d1, d2, d3, wn, eb, wb, shb) / (kms["conv_bwd"] * 1e-3) / 1e9, 1)}
+    if full:
         calls["double_bwd"] = {"ms": kms["double_bwd"], "GB_per_s": round(
             alg_bytes_conv_dbl(N, E, d1, d2, d3, wn, eb, wb) / (kms["double_bwd"] * 1e-3) / 1e9, 1)}
     workload = ((W.config("c4").name if full else cfg.name) +
@@ -396,6 +428,7 @@ def bench_conv(args, torch, B, W):
                 (", all output parities" if args.all_parity and full else "") +
                 (", Morton node order" if args.morton else "") +
                 (", rows in node-id order" if args.natural_order else "") +
+                (", forward and backward as separate calls" if full and not fused else "") +
                 (", SH by a separate kernel" if not sh_in_conv else ""))
     # dominant kernel: largest share of the step
     dom = max((k for k in kern if k in alg), key=lambda k: kern[k]["ms_per_step"])
@@ -429,10 +462,12 @@ def bench_conv(args, torch, B, W):
         "config": {"workload": workload, "n_atoms": N, "n_edges": E,
                    "irreps_node": cfg.irreps_in1, "irreps_sh": cfg.irreps_in2, "irreps_out": cfg.irreps_out,
                    "n_paths": plan.n_paths,
-                   "step": ("csr+sh+fwd+bwd+forces+force_cotangent+double_bwd" if full
+                   "step": (("csr+sh+fwd+bwd+forces+force_cotangent+double_bwd" +
+                             (" (forward and backward in one pass: g_out = dE/dout does not depend on out)"
+                              if fused else "")) if full
                             else "csr (by destination) + node order + sh + fwd")},
         "roofline": roof,
-        "fwd_edges_per_s": E / (kms["conv_fwd"] * 1e-3),
+        "fwd_edges_per_s": E / (kms["conv_fwd"] * 1e-3) if "conv_fwd" in kms else None,
         "calls": calls,
         "kernels": kern,
         "call_ms": {k: round(v, 4) for k, v in kms.items()},

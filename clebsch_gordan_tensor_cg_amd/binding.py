@@ -46,6 +46,7 @@ EXPORTS = [
     "cgtp_plan", "cgtp_plan_info", "cgtp_plan_paths", "cgtp_plan_coupling", "cgtp_plan_source",
     "cgtp_plan_destroy", "cgtp_forward_workspace_bytes", "cgtp_forward", "cgtp_conv_forward",
     "cgtp_conv_workspace_bytes", "cgtp_conv_forward_vec", "cgtp_conv_backward_vec", "cgtp_conv_forward_radial", "cgtp_sparse_attention",
+    "cgtp_conv_forward_backward", "cgtp_conv_forward_backward_vec",
     "cgtp_sparse_attention_layout_bytes", "cgtp_sparse_attention_prepare",
     "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_csr_workspace_bytes", "cgtp_build_csr",
     "cgtp_validate_csr", "cgtp_node_order_workspace_bytes", "cgtp_node_order", "cgtp_spherical_harmonics", "cgtp_forces_workspace_bytes", "cgtp_sh_forces",
@@ -85,6 +86,9 @@ def lib():
             "cgtp_conv_forward_vec": [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
             "cgtp_conv_backward_vec": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, sz,
                                        vp],
+            "cgtp_conv_forward_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
+            "cgtp_conv_forward_backward_vec": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp,
+                                               vp, sz, vp],
             "cgtp_node_order": [vp, i64, vp, vp, sz, vp],
             "cgtp_csr_workspace_bytes": [i64, i64, vp],
             "cgtp_build_csr": [vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
@@ -315,6 +319,57 @@ def cgtp_conv_backward_vec(plan: Plan, x, vec, vec_perm, w, src, dst_row_ptr, sr
                                         _ptr(g_out), N, E, _ptr(g_x), _ptr(g_sh), _ptr(g_w), _ptr(F), _ptr(ws),
                                         ws.numel(), _stream(stream, x)))
     return g_x, g_sh, g_w, F
+
+
+def cgtp_conv_forward_backward(plan: Plan, x, sh, w, src, dst_row_ptr, src_row_ptr, src_perm, g_out,
+                               need=("x", "sh", "w"), ws=None, out=None, stream=None, node_order=None):
+    """Forward and backward in one pass (g_out must not depend on out);
+    returns (out, g_x, g_sh, g_w), None where not requested."""
+    _want(plan, x=x, sh=sh, w=w, src=src, dst_row_ptr=dst_row_ptr, src_row_ptr=src_row_ptr, src_perm=src_perm,
+          g_out=g_out, node_order=node_order)
+    N, E = x.shape[0], src.shape[0]
+    dev = x.device
+    od = plan.out_dtype
+    if out is None:
+        o = torch.empty(N, plan.dim_out, dtype=od, device=dev)
+        g_x = torch.empty(N, plan.dim_in1, dtype=od, device=dev) if "x" in need else None
+        g_sh = torch.empty(E, plan.dim_in2, dtype=od, device=dev) if "sh" in need else None
+        g_w = torch.empty(E, plan.weight_numel, dtype=od, device=dev) if "w" in need else None
+    else:
+        o, g_x, g_sh, g_w = out
+    if ws is None:
+        ws = workspace(cgtp_conv_workspace_bytes(plan, N, E), dev)
+    _check(lib().cgtp_conv_forward_backward(plan.handle, _ptr(x), _ptr(sh), _ptr(w), _ptr(src), _ptr(dst_row_ptr),
+                                            _ptr(node_order), _ptr(src_row_ptr), _ptr(src_perm), _ptr(g_out), N, E,
+                                            _ptr(o), _ptr(g_x), _ptr(g_sh), _ptr(g_w), _ptr(ws), ws.numel(),
+                                            _stream(stream, x)))
+    return o, g_x, g_sh, g_w
+
+
+def cgtp_conv_forward_backward_vec(plan: Plan, x, vec, vec_perm, w, src, dst_row_ptr, src_row_ptr, src_perm, g_out,
+                                   need=("x", "w", "F"), ws=None, out=None, stream=None, node_order=None):
+    """Forward and backward in one pass with in-kernel SH; returns
+    (out, g_x, g_sh, g_w, F), None where not requested."""
+    _want(plan, x=x, vec=vec, vec_perm=vec_perm, w=w, src=src, dst_row_ptr=dst_row_ptr, src_row_ptr=src_row_ptr,
+          src_perm=src_perm, g_out=g_out, node_order=node_order)
+    N, E = x.shape[0], src.shape[0]
+    dev = x.device
+    od = plan.out_dtype
+    if out is None:
+        o = torch.empty(N, plan.dim_out, dtype=od, device=dev)
+        g_x = torch.empty(N, plan.dim_in1, dtype=od, device=dev) if "x" in need else None
+        g_sh = torch.empty(E, plan.dim_in2, dtype=od, device=dev) if "sh" in need else None
+        g_w = torch.empty(E, plan.weight_numel, dtype=od, device=dev) if "w" in need else None
+        F = torch.empty(N, 3, dtype=od, device=dev) if "F" in need else None
+    else:
+        o, g_x, g_sh, g_w, F = out
+    if ws is None:
+        ws = workspace(cgtp_conv_workspace_bytes(plan, N, E), dev)
+    _check(lib().cgtp_conv_forward_backward_vec(plan.handle, _ptr(x), _ptr(vec), _ptr(vec_perm), _ptr(w), _ptr(src),
+                                                _ptr(dst_row_ptr), _ptr(node_order), _ptr(src_row_ptr),
+                                                _ptr(src_perm), _ptr(g_out), N, E, _ptr(o), _ptr(g_x), _ptr(g_sh),
+                                                _ptr(g_w), _ptr(F), _ptr(ws), ws.numel(), _stream(stream, x)))
+    return o, g_x, g_sh, g_w, F
 
 
 def cgtp_conv_workspace_bytes(plan: Plan, n_nodes: int, n_edges: int) -> int:

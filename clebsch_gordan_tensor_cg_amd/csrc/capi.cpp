@@ -90,19 +90,21 @@ struct BwdOut {
     bool acc_m = false;
     void *g_y = nullptr;  // per-edge y gradient
     bool acc_y = false;
-    void *fwd = nullptr;  // fused forward of the same operands (double backward)
+    void *fwd = nullptr;  // fused forward of the same operands (double backward, or with fb)
     bool acc_fwd = false;
+    bool fb = false;      // forward and backward of one operand set (fwd = f(x, y, w))
     bool keep_parts = false;  // leave the per-unit y-gradient partials in the workspace
 };
 
 // workspace layout of the backward calls: x-messages [E][dim1] in source
 // order, SH-gradient parts [units][E][dim2], message row of each edge [E]
+int parts_units(const Plan &p) { return std::max(1, std::max(p.bwd.n_units, p.fb.n_units)); }
 char *ws_parts(const Plan &p, char *ws, int64_t n_edges) {
     return ws + align256((size_t)n_edges * p.dim1 * out_bytes(p.dtype));
 }
 int32_t *ws_mrow(const Plan &p, char *ws, int64_t n_edges) {
     return (int32_t *)(ws_parts(p, ws, n_edges) +
-                       align256((size_t)std::max(1, p.bwd.n_units) * n_edges * p.dim2 * out_bytes(p.dtype)));
+                       align256((size_t)parts_units(p) * n_edges * p.dim2 * out_bytes(p.dtype)));
 }
 // per-edge force vectors [E][3] of the backward with forces
 char *ws_force(const Plan &p, char *ws, int64_t n_edges) {
@@ -115,38 +117,48 @@ int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const in
     void *m = ws;
     char *parts = ws_parts(p, ws, n_edges);
     const int32_t *mrow = ws_mrow(p, ws, n_edges);
-    const bool fused = o.fwd != nullptr;
-    const KernelShape &ks = fused ? p.dbl : p.bwd;
+    const bool fused = o.fwd != nullptr && !o.fb;   // the double backward's y term
+    const bool fb = o.fb;
+    const KernelShape &ks = fused ? p.dbl : fb ? p.fb : p.bwd;
     const bool use_parts = !fused && o.g_y && ks.n_units > 1;
     int flags = 0;
     if (o.g_w) flags |= 1 | (o.acc_w ? 8 : 0);
     if (o.want_m) flags |= 2 | (o.acc_m ? 16 : 0);
     if (o.g_y) flags |= 4 | (use_parts ? 64 : (o.acc_y ? 32 : 0));
-    if (fused && o.acc_fwd) flags |= 256;
-    if (!flags && !fused) return CGTP_OK;
+    if ((fused || fb) && o.acc_fwd) flags |= 256;
+    if (!flags && !fused && !fb) return CGTP_OK;
     if (o.want_m && !o.acc_m && !blocks_covered(p.in1, p.paths, false)) {
         int rc = launch_zero(p.dtype, m, n_edges * p.dim1, s);
         if (rc) return rc;
         flags |= 16;
     }
-    if (fused && !o.acc_fwd && !blocks_covered(p.out, p.paths, true)) {
+    if ((fused || fb) && !o.acc_fwd && !blocks_covered(p.out, p.paths, true)) {
         int rc = launch_zero(p.dtype, o.fwd, n_nodes * p.dim3, s);
         if (rc) return rc;
         flags |= 256;
     }
     void *third = fused ? o.fwd : (use_parts ? (void *)parts : o.g_y);
+    void *fourth = o.fwd;
     void *gw = o.g_w;
     long long n = n_nodes, ne = n_edges;
     int graph = 1;
     void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&order,
                     (void *)&vec, (void *)&vperm, (void *)&g_out, &gw, &m, &third, (void *)&mrow, &n, &ne, &graph,
                     &flags};
+    void *args_fb[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&order,
+                       (void *)&vec, (void *)&vperm, (void *)&g_out, &gw, &m, &third, &fourth, (void *)&mrow, &n, &ne,
+                       &graph, &flags};
     const int64_t ipw = ks.items_per_wave;
     const bool full = fused ? ((p.tune.full & 2) && flags == dbl_full_flags(p))
+                      : fb  ? ((p.tune.full & 4) && flags == fb_full_flags(p))
                             : ((p.tune.full & 1) && flags == bwd_full_flags(p));
-    hipFunction_t f = fused ? (full ? p.k_dbl_full : p.k_dbl) : (full ? p.k_bwd_full : p.k_bwd);
-    const char *name = fused ? (full ? "cgtp_dbl_full" : "cgtp_dbl") : (full ? "cgtp_bwd_full" : "cgtp_bwd");
-    int rc = launch(f, name, (n_nodes + ipw - 1) / ipw * ks.n_units, s, args);
+    hipFunction_t f = fused ? (full ? p.k_dbl_full : p.k_dbl)
+                      : fb  ? (full ? p.k_fb_full : p.k_fb)
+                            : (full ? p.k_bwd_full : p.k_bwd);
+    const char *name = fused ? (full ? "cgtp_dbl_full" : "cgtp_dbl")
+                       : fb  ? (full ? "cgtp_fb_full" : "cgtp_fb")
+                             : (full ? "cgtp_bwd_full" : "cgtp_bwd");
+    int rc = launch(f, name, (n_nodes + ipw - 1) / ipw * ks.n_units, s, fb ? args_fb : args);
     if (rc) return rc;
     if (use_parts && !o.keep_parts) rc = launch_sum_parts(p.dtype, parts, ks.n_units, n_edges * p.dim2, o.g_y, o.acc_y, s);
     return rc;
@@ -469,7 +481,7 @@ int cgtp_conv_workspace_bytes(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges
     const Plan &p = plan->p;
     const size_t eb = out_bytes(p.dtype);
     *bytes = align256((size_t)n_edges * p.dim1 * eb) +
-             align256((size_t)std::max(1, p.bwd.n_units) * n_edges * p.dim2 * eb) +
+             align256((size_t)parts_units(p) * n_edges * p.dim2 * eb) +
              align256((size_t)n_edges * sizeof(int32_t)) + align256((size_t)n_edges * 3 * eb) + 256;
     return CGTP_OK;
 }
@@ -494,7 +506,8 @@ static int conv_backward_impl(cgtp_plan_t plan, const void *x, const void *sh, c
                               const int32_t *vperm, const void *w, const int32_t *src, const int32_t *dst_row_ptr,
                               const int32_t *node_order, const int32_t *src_row_ptr, const int32_t *src_perm,
                               const void *g_out, int64_t n_nodes, int64_t n_edges, void *g_x, void *g_sh, void *g_w,
-                              void *F, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
+                              void *F, void *workspace, size_t workspace_bytes, cgtp_stream_t stream,
+                              void *out = nullptr) {
     int rc = check_graph_args(plan, n_nodes, n_edges, workspace, workspace_bytes);
     if (rc) return rc;
     const Plan &p = plan->p;
@@ -504,13 +517,23 @@ static int conv_backward_impl(cgtp_plan_t plan, const void *x, const void *sh, c
         (n_edges > 0 && (!x || !(sh || vec) || !w || !src || !g_out)))
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
     if (n_edges == 0) {
+        if (out && (rc = launch_zero(p.dtype, out, n_nodes * p.dim3, s))) return rc;
         if (g_x && (rc = launch_zero(p.dtype, g_x, n_nodes * p.dim1, s))) return rc;
         if (F) return launch_zero(p.dtype, F, n_nodes * 3, s);
         return CGTP_OK;
     }
+    // FP64 plans: forward and backward as two launches (the one-pass kernel
+    // is kept to FP32; its FP64 form, which needs more than 256 registers, is
+    // switched off)
+    if (out && p.dtype == CGTP_F64) {
+        if ((rc = run_fwd(p, x, sh, w, src, dst_row_ptr, node_order, n_nodes, 1, out, 0, s, vec, vperm))) return rc;
+        out = nullptr;
+    }
     char *ws = (char *)workspace;
     if (g_x && (rc = launch_invert_perm(src_perm, n_edges, ws_mrow(p, ws, n_edges), s))) return rc;
     BwdOut o;
+    o.fwd = out;
+    o.fb = out != nullptr;
     o.g_w = g_w;
     o.want_m = g_x != nullptr;
     o.g_y = g_sh;
@@ -526,7 +549,8 @@ static int conv_backward_impl(cgtp_plan_t plan, const void *x, const void *sh, c
     if (g_x && (rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, nullptr, n_nodes, p.dim1, g_x, 0, s)))
         return rc;
     if (F) {
-        const int n_parts = parts_force && p.bwd.n_units > 1 ? p.bwd.n_units : 1;
+        const int units = (out ? p.fb : p.bwd).n_units;
+        const int n_parts = parts_force && units > 1 ? units : 1;
         rc = launch_sh_forces(p.sh_lmax, p.dtype, vec, vperm, parts_force ? o.g_y : g_sh, n_parts, n_edges * p.dim2,
                               dst_row_ptr, src_row_ptr, src_perm, n_nodes, n_edges, F, ws_force(p, ws, n_edges), s);
     }
@@ -555,6 +579,32 @@ int cgtp_conv_backward_vec(cgtp_plan_t plan, const void *x, const void *vec, con
     if (n_edges > 0 && !vec) return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
     return conv_backward_impl(plan, x, nullptr, vec, vec_perm, w, src, dst_row_ptr, node_order, src_row_ptr, src_perm,
                               g_out, n_nodes, n_edges, g_x, g_sh, g_w, F, workspace, workspace_bytes, stream);
+}
+
+int cgtp_conv_forward_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
+                               const int32_t *dst_row_ptr, const int32_t *node_order, const int32_t *src_row_ptr,
+                               const int32_t *src_perm, const void *g_out, int64_t n_nodes, int64_t n_edges, void *out,
+                               void *g_x, void *g_sh, void *g_w, void *workspace, size_t workspace_bytes,
+                               cgtp_stream_t stream) {
+    clear_error();
+    if (!out) return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_conv_forward_backward: out is NULL");
+    return conv_backward_impl(plan, x, sh, nullptr, nullptr, w, src, dst_row_ptr, node_order, src_row_ptr, src_perm,
+                              g_out, n_nodes, n_edges, g_x, g_sh, g_w, nullptr, workspace, workspace_bytes, stream, out);
+}
+
+int cgtp_conv_forward_backward_vec(cgtp_plan_t plan, const void *x, const void *vec, const int32_t *vec_perm,
+                                   const void *w, const int32_t *src, const int32_t *dst_row_ptr,
+                                   const int32_t *node_order, const int32_t *src_row_ptr, const int32_t *src_perm,
+                                   const void *g_out, int64_t n_nodes, int64_t n_edges, void *out, void *g_x,
+                                   void *g_sh, void *g_w, void *F, void *workspace, size_t workspace_bytes,
+                                   cgtp_stream_t stream) {
+    clear_error();
+    int rc = check_vec_plan(plan);
+    if (rc) return rc;
+    if (!out) return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_conv_forward_backward_vec: out is NULL");
+    if (n_edges > 0 && !vec) return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
+    return conv_backward_impl(plan, x, nullptr, vec, vec_perm, w, src, dst_row_ptr, node_order, src_row_ptr, src_perm,
+                              g_out, n_nodes, n_edges, g_x, g_sh, g_w, F, workspace, workspace_bytes, stream, out);
 }
 
 int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,

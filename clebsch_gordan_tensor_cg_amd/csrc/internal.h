@@ -57,11 +57,11 @@ struct KernelShape {
 };
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
-// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, yvec, ntw, pf, budget, stage, cypath, depth, bgy, full, ubudget)
+// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, full, ubudget)
 // overrides
 // them for experiments.
 struct Tuning {
-    int cpl[3] = {0, 0, 0};  // channels per lane per kernel kind (0 = by budget)
+    int cpl[4] = {0, 0, 0, 0};  // channels per lane per kernel kind (0 = by budget)
     int budget = 112;        // VGPR estimate allowed for two channels per lane
     bool y_vector = true;    // load the y row with vector (not scalar) loads
     bool nt_w = true;        // non-temporal loads of the per-edge weights
@@ -70,7 +70,7 @@ struct Tuning {
     int cy_path = -1;        // uniform products per path (1) or per edge (0); -1: by dtype
     int depth = 3;           // edges of prefetch in flight (staged loop)
     bool bgy = false;        // backward via B_ij = sum_k R_ijk g_k (fewer FMAs, more VGPRs)
-    int full = 3;            // dispatch to the folded-flag kernels: bit 0 backward, bit 1 double backward
+    int full = 7;            // dispatch to the folded-flag kernels: bit 0 backward, bit 1 double backward, bit 2 fused forward+backward
     int ubudget = 0;         // uvw accumulators per lane and unit (0: 32, or 144 with radial weights)
 };
 Tuning tuning_from_env();
@@ -100,7 +100,7 @@ struct Plan {
     int radial_h = 0;  // uvw with per-edge weights from a radial network of this hidden width (0: none)
     std::vector<Path> paths;
 
-    KernelShape fwd, bwd, dbl;
+    KernelShape fwd, bwd, dbl, fb;   // fb: forward and backward in one pass
     std::vector<MixBlock> mix;     // uvw only
     std::vector<int> mix_of_path;  // uvw: index into mix for each path
     int64_t t_per_item = 0;        // uvw: T elements per item
@@ -116,6 +116,8 @@ struct Plan {
     hipFunction_t k_dbl = nullptr;
     hipFunction_t k_bwd_full = nullptr;  // k_bwd with bwd_full_flags folded in
     hipFunction_t k_dbl_full = nullptr;  // k_dbl with dbl_full_flags folded in
+    hipFunction_t k_fb = nullptr;        // forward + backward of the same edges in one pass
+    hipFunction_t k_fb_full = nullptr;   // k_fb with fb_full_flags folded in
     int device = -1;
 };
 
@@ -128,6 +130,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // these folded in at compile time.
 inline int bwd_full_flags(const Plan &p) { return 1 | 2 | 4 | (p.bwd.n_units > 1 ? 64 : 0); }
 inline int dbl_full_flags(const Plan &) { return 1 | 2; }
+inline int fb_full_flags(const Plan &p) { return 1 | 2 | 4 | (p.fb.n_units > 1 ? 64 : 0); }
 
 // planner
 int parse_irreps(const char *s, std::vector<Irrep> &out, std::string &err);

@@ -204,7 +204,7 @@ int next_pow2(int v) {
     return p;
 }
 
-// kind: 0 forward, 1 backward, 2 fused double backward
+// kind: 0 forward, 1 backward, 2 fused double backward, 3 forward and backward in one pass
 void split(Plan &p, KernelShape &ks, int kind) {
     const int np = (int)p.paths.size();
     std::vector<int> parent(np);
@@ -249,7 +249,7 @@ void split(Plan &p, KernelShape &ks, int kind) {
         for (int a : g.paths) wts += p.paths[a].mul2;
         int per_ch = acc + (1 + std::max(1, p.tune.depth)) * (xin + wts);
         if (kind >= 1) per_ch += xin;  // message accumulators
-        if (kind == 2) per_ch += acc;  // fused forward accumulators
+        if (kind >= 2) per_ch += acc;  // fused forward accumulators
         per_ch *= wide;
         g.cpl = 1;
         if (ks.lanes_per_item == 64 && g.max_mul > 64 && per_ch * 2 <= p.tune.budget) g.cpl = 2;
@@ -278,6 +278,7 @@ Tuning tuning_from_env() {
             if (k == "cpl_fwd") t.cpl[0] = v;
             else if (k == "cpl_bwd") t.cpl[1] = v;
             else if (k == "cpl_dbl") t.cpl[2] = v;
+            else if (k == "cpl_fb") t.cpl[3] = v;
             else if (k == "budget") t.budget = v;
             else if (k == "yvec") t.y_vector = v != 0;
             else if (k == "ntw") t.nt_w = v != 0;
@@ -286,7 +287,7 @@ Tuning tuning_from_env() {
             else if (k == "cypath") t.cy_path = v;
             else if (k == "depth") t.depth = v < 1 ? 1 : (v > 4 ? 4 : v);
             else if (k == "bgy") t.bgy = v != 0;
-            else if (k == "full") t.full = v & 3;
+            else if (k == "full") t.full = v & 7;
             else if (k == "ubudget") t.ubudget = v < 1 ? 0 : v;
         }
         pos = comma + 1;
@@ -371,6 +372,7 @@ void choose_shapes(Plan &p) {
     split(p, p.fwd, 0);
     split(p, p.bwd, 1);
     split(p, p.dbl, 2);
+    split(p, p.fb, 3);
 }
 
 }  // namespace cgtp

@@ -162,7 +162,7 @@ int compile_and_load(Plan &p, bool load, std::string &err) {
         r.destroy(&prog);
         write_file_atomic(dir, path, code);
     }
-    p.n_kernels = (p.mode == CGTP_UVU) ? 5 : 1;
+    p.n_kernels = (p.mode == CGTP_UVU) ? 7 : 1;
     if (!load) return CGTP_OK;
 
     hipError_t e = hipGetDevice(&p.device);
@@ -172,6 +172,8 @@ int compile_and_load(Plan &p, bool load, std::string &err) {
     if (e == hipSuccess && p.n_kernels > 2) e = hipModuleGetFunction(&p.k_dbl, p.module, "cgtp_dbl");
     if (e == hipSuccess && p.n_kernels > 3) e = hipModuleGetFunction(&p.k_bwd_full, p.module, "cgtp_bwd_full");
     if (e == hipSuccess && p.n_kernels > 4) e = hipModuleGetFunction(&p.k_dbl_full, p.module, "cgtp_dbl_full");
+    if (e == hipSuccess && p.n_kernels > 5) e = hipModuleGetFunction(&p.k_fb, p.module, "cgtp_fb");
+    if (e == hipSuccess && p.n_kernels > 6) e = hipModuleGetFunction(&p.k_fb_full, p.module, "cgtp_fb_full");
     if (e != hipSuccess) {
         err = std::string("loading generated code object: ") + hipGetErrorString(e);
         return CGTP_ERR_HIP;

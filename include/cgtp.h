@@ -121,7 +121,7 @@ typedef struct {
 } cgtp_plan_dims;
 
 /* ---------------------------------------------------------------------- */
-/* Planning ("static analysis at model compile-time", [KG]).               */
+/* Planning: the analysis done once per model before any launch ([KG]).  */
 /* ---------------------------------------------------------------------- */
 
 /* Parses the irreps, validates `paths` (n_paths > 0) or enumerates every
@@ -157,7 +157,7 @@ void cgtp_plan_destroy(cgtp_plan_t plan);
 /* Scratch for the forward calls: uvw plans contract in two steps (per-item */
 /* path tensors T_p = CG_p(x, y) summed over the item's edges, rounded to   */
 /* the MFMA operand type, then T . W per output block on the matrix cores,  */
-/* [SE3] "fully fused" TFN convolution: all paths into one output degree    */
+/* [SE3]: the TFN convolution with all paths into one output degree fused, */
 /* concatenated along K).  T, and the partial tiles of long contractions,  */
 /* live in the workspace: this many bytes for n_items items (destination   */
 /* nodes or samples); 0 for uvu plans.                                      */
@@ -267,6 +267,32 @@ int cgtp_conv_backward_vec(cgtp_plan_t plan, const void *x, const void *vec, con
                            const int32_t *src_perm, const void *g_out, int64_t n_nodes,
                            int64_t n_edges, void *g_x, void *g_sh, void *g_w, void *F,
                            void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
+/* Forward and backward in one pass over the edges, for an output cotangent
+ * g_out that does not depend on out (an energy linear in the outputs, as
+ * the sum of the 0e channels): out = the forward of cgtp_conv_forward, and
+ * g_x, g_sh, g_w as cgtp_conv_backward, each per-edge weight row read once
+ * for both ([KG]: the gradient kernels; the fusion of the convolution).
+ * out [n_nodes][dim_out] must not be NULL; g_x, g_sh, g_w may be NULL.
+ * Other arguments and the workspace as in cgtp_conv_backward.  FP64 plans
+ * compute the same results with the forward and the backward as two
+ * launches. */
+int cgtp_conv_forward_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
+                               const int32_t *src, const int32_t *dst_row_ptr,
+                               const int32_t *node_order, const int32_t *src_row_ptr,
+                               const int32_t *src_perm, const void *g_out, int64_t n_nodes,
+                               int64_t n_edges, void *out, void *g_x, void *g_sh, void *g_w,
+                               void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
+/* cgtp_conv_forward_backward with the SH computed from the edge vectors and
+ * the forces F (may be NULL) as in cgtp_conv_backward_vec. */
+int cgtp_conv_forward_backward_vec(cgtp_plan_t plan, const void *x, const void *vec,
+                                   const int32_t *vec_perm, const void *w, const int32_t *src,
+                                   const int32_t *dst_row_ptr, const int32_t *node_order,
+                                   const int32_t *src_row_ptr, const int32_t *src_perm,
+                                   const void *g_out, int64_t n_nodes, int64_t n_edges,
+                                   void *out, void *g_x, void *g_sh, void *g_w, void *F,
+                                   void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
 
 /* Second derivatives ([KG]: higher partial derivatives for forces).  The
  * convolution f(x, sh, w) is trilinear, so for cotangents (gg_x, gg_sh,
