@@ -522,9 +522,10 @@ static int conv_backward_impl(cgtp_plan_t plan, const void *x, const void *sh, c
         if (F) return launch_zero(p.dtype, F, n_nodes * 3, s);
         return CGTP_OK;
     }
-    // FP64 plans: forward and backward as two launches (the one-pass kernel
-    // is kept to FP32; its FP64 form, which needs more than 256 registers, is
-    // switched off)
+    // FP64 plans: forward and backward as two launches.  The one-pass kernel
+    // is used for FP32 only: its FP64 form took a device memory fault on a
+    // 128-channel plan with the SH computed from edge vectors, with no cause
+    // found in the generated code, so it is switched off.
     if (out && p.dtype == CGTP_F64) {
         if ((rc = run_fwd(p, x, sh, w, src, dst_row_ptr, node_order, n_nodes, 1, out, 0, s, vec, vperm))) return rc;
         out = nullptr;

@@ -511,8 +511,8 @@ def test_conv_forward_backward_vec_small(B, torch, k, dtype):
     """One pass with the SH computed from the edge vectors and the forces
     from the per-unit SH-gradient partials (and with g_sh written)."""
     if k == 2 and dtype == "f64":
-        pytest.skip("this case took a GPU memory fault with the one-pass FP64 kernel (more than 256 registers); "
-                    "no cause found in the code, FP64 one-pass switched off, case kept off the GPU")
+        pytest.skip("this case took a device memory fault with the one-pass FP64 kernel; no cause found in the "
+                    "generated code, so the FP64 one-pass kernel is switched off and the case is kept off the GPU")
     plan, prob = _small_problem(B, k, dtype)
     lmax = {0: 2, 1: 3, 2: 3}[k]
     src, dst = _small_graph(61, 700, 160 + k)
