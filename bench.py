@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload c4|c2|c3|c1|c5] [--no-cpu-baseline]
                     [--separate-sh] [--bf16-weights] [--all-parity] [--morton]
-                    [--natural-order] [--nominal-e] [--unfused]
+                    [--natural-order] [--nominal-e] [--unfused] [--graph]
 
 Default workload "c4" (one step = the whole hot path on the 4096-atom
 periodic water-density box, cutoff 5 A, node 128x0e+128x1o, SH l<=3, uvu,
@@ -20,7 +20,9 @@ kernels of their own with SH and SH-gradient arrays in memory.  Other workloads 
 forward path alone: c2 (same graph), c3 (16384 atoms, fp64, node
 128x0e+128x1o+128x2e), c1 (1000 independent products), c5 (100 molecules of
 18 atoms, uvw bf16 with matrix-core mixing).  Inputs are resident in HBM
-before timing starts.  Prints one JSON line.
+before timing starts.  --graph times replays of the step captured once into
+a HIP graph instead of the calls as Python issues them.  Prints one JSON
+line.
 """
 from __future__ import annotations
 
@@ -62,6 +64,9 @@ def parse():
                          "vectors, forces from the backward's SH-gradient partials)")
     ap.add_argument("--natural-order", action="store_true",
                     help="hand destination rows to the device in node-id order (no longest-first order)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured once into a HIP graph (default: the library calls as "
+                         "Python issues them; graph replay measured slower for these steps)")
     ap.add_argument("--unfused", action="store_true",
                     help="c4: forward and backward as separate calls (default: one pass over the edges)")
     ap.add_argument("--nominal-e", action="store_true",
@@ -70,6 +75,36 @@ def parse():
 
 
 NOMINAL_CUTOFF = 4.153   # 0.1 / A^3 x (4/3) pi r^3 = 30 neighbours
+
+
+def time_steps(torch, args, step):
+    """args.warmup untimed steps, then args.steps timed steps between HIP
+    events (synchronized before and after), with nothing recorded between
+    the calls of a step.  With --graph the step is captured once into a HIP
+    graph (torch.cuda.CUDAGraph is a hipGraph on ROCm) and replayed: every
+    kernel of the step runs on each replay.  Returns (mean ms per step,
+    per-step ms, launch mode, graph)."""
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    run, graph = step, None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        run()
+        torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record()
+    for i in range(args.steps):
+        run()
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    mode = "eager" if graph is None else "hip graph of the step (captured once, replayed)"
+    return marks[0].elapsed_time(marks[-1]) / args.steps, per_step, mode, graph
 
 
 class Timer:
@@ -355,21 +390,15 @@ def bench_conv(args, torch, B, W):
                                                               g_out, None, gg, None, ws=ws,
                                                               out=(d_g, d_x, None, d_w), node_order=node_order))
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    ms, per_step, launch_mode, graph = time_steps(torch, args, lambda: step(False))
+    # per-call durations: an eager pass with events between the calls
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    t0.record()
     marks[0].record()
     for i in range(args.steps):
         step(True)
         marks[i + 1].record()
-    t1.record()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-    per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    eager_ms = marks[0].elapsed_time(marks[-1]) / args.steps
     kms = timer.ms()
     # per-kernel durations: one more pass with the library's per-launch
     # events (recorded on the launch stream) enabled
@@ -467,6 +496,8 @@ def bench_conv(args, torch, B, W):
                               if fused else "")) if full
                             else "csr (by destination) + node order + sh + fwd")},
         "roofline": roof,
+        "launch": launch_mode,
+        "ms_per_step_with_call_events": round(eager_ms, 4),
         "fwd_edges_per_s": E / (kms["conv_fwd"] * 1e-3) if "conv_fwd" in kms else None,
         "calls": calls,
         "kernels": kern,
@@ -488,22 +519,13 @@ def bench_single(args, torch, B, W):
     w_np = W.normal(rng, (n, plan.weight_numel), "f32")
     x, y, w = (torch.from_numpy(a).cuda() for a in (x_np, y_np, w_np))
     out = torch.empty(n, plan.dim_out, device="cuda")
-    for _ in range(args.warmup):
-        B.cgtp_forward(plan, x, y, w, out=out)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(args.steps):
-        B.cgtp_forward(plan, x, y, w, out=out)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms, per_step, launch_mode, graph = time_steps(torch, args, lambda: B.cgtp_forward(plan, x, y, w, out=out))
     nbytes = n * (plan.dim_in1 + plan.dim_in2 + plan.weight_numel + plan.dim_out) * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     res = {"metric": METRIC, "value": n / (ms * 1e-3), "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_median": float(np.median(per_step)),
+           "ms_per_step_min": float(np.min(per_step)), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic", "launch": launch_mode,
            "config": {"workload": cfg.name, "batch": n, "n_paths": plan.n_paths},
            "roofline": {"bound": "hbm", "kernel": "cgtp_fwd", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,
@@ -551,17 +573,7 @@ def bench_radial(args, torch, B, W):
         B.cgtp_node_order(rp, ws=ord_ws, out=order)
         B.cgtp_conv_forward_radial(plan, x, vec, perm, radial, w, src_s, rp, out=out, ws=f_ws, node_order=order)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    marks[0].record()
-    for i in range(args.steps):
-        step()
-        marks[i + 1].record()
-    torch.cuda.synchronize()
-    per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
-    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    ms, per_step, launch_mode, graph = time_steps(torch, args, step)
     B.cgtp_timing_enable(True)
     for _ in range(args.steps):
         step()
@@ -586,6 +598,7 @@ def bench_radial(args, torch, B, W):
            "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_median": float(np.median(per_step)),
            "ms_per_step_min": float(np.min(per_step)), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "launch": launch_mode,
            "config": {"workload": cfg.name + f", per-edge radial weights (hidden width {H})", "n_atoms": N,
                       "n_edges": E, "n_paths": plan.n_paths,
                       "step": "csr + node order + radial uvw conv (SH and radial network in the kernel)"},
@@ -650,17 +663,7 @@ def bench_attention(args, torch, B, W):
     torch.cuda.synchronize()
     prepare_ms = p0.elapsed_time(p1)
     call = lambda: B.cgtp_sparse_attention(q, k, v, rp, E, layout, out=out)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    marks[0].record()
-    for i in range(args.steps):
-        call()
-        marks[i + 1].record()
-    torch.cuda.synchronize()
-    per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
-    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    ms, per_step, launch_mode, graph = time_steps(torch, args, call)
     B.cgtp_timing_enable(True)
     for _ in range(args.steps):
         call()
@@ -674,7 +677,7 @@ def bench_attention(args, torch, B, W):
     res = {"metric": METRIC, "value": E / (ms * 1e-3), "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_median": float(np.median(per_step)),
            "ms_per_step_min": float(np.min(per_step)), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "launch": launch_mode,
            "config": {"workload": what, "n_nodes": N, "n_edges": E, "heads": H, "head_dim": D,
                       "step": "fused SDDMM + softmax + SpMM (CSR and window compaction built once, outside the step)",
                       "prepare_ms": round(prepare_ms, 4)},
@@ -704,7 +707,7 @@ def bench_attention(args, torch, B, W):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "one GPU only: --gpus must be 1 (no path across GPUs is built)",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
     import torch

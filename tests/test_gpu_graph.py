@@ -1,0 +1,133 @@
+"""Steps of the path captured into a HIP graph (torch.cuda.CUDAGraph is a
+hipGraph on ROCm) and replayed, as bench.py times them.  Each step's calls
+launch only kernels (zeroing included) on torch's current stream, so they can
+be captured.  Every replay, with eager work and synchronizations between the
+replays, must give outputs bit-identical to the eager step: the kernels are
+deterministic."""
+import numpy as np
+import pytest
+
+from clebsch_gordan_tensor_cg_amd import workloads as W
+from tests.gpu_util import binding
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    return binding()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    return t
+
+
+def _replays_match_eager(torch, step, outputs, name, replays=3):
+    step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outputs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(replays):
+        print(f"graph {name}: replay {r}", flush=True)
+        for o in outputs:      # eager work between the replays: poison the outputs
+            o.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (o, want) in enumerate(zip(outputs, ref)):
+            assert torch.equal(o, want), f"{name}: output {i} differs on replay {r}"
+        step()                 # and an eager step
+        torch.cuda.synchronize()
+
+
+def test_graph_uvw_step(B, torch):
+    """CSR (two-launch small path), node order and the uvw convolution with
+    the SH from the edge vectors and the mixing on the matrix cores."""
+    c = W.config("c5")
+    g = W.molecule_batch(12, 18, cutoff=c.extra["cutoff"], seed=1)
+    plan = B.Plan(c.irreps_in1, c.irreps_in2, c.irreps_out, c.paths, "uvw", "bf16", True)
+    rng = np.random.default_rng(2)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
+    x = bf(W.normal(rng, (g.n_nodes, plan.dim_in1), "bf16"))
+    w = bf(W.normal(rng, (plan.weight_numel,), "bf16"))
+    src_c, dst_c = torch.from_numpy(g.src).cuda(), torch.from_numpy(g.dst).cuda()
+    vec = torch.from_numpy(g.vec.astype(np.float32)).cuda()
+    N, E = g.n_nodes, g.n_edges
+    perm, rp, dst_s, src_s = (torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, N + 1, E, E))
+    order = torch.empty(N, dtype=torch.int32, device="cuda")
+    out = torch.empty(N, plan.dim_out, device="cuda")
+    csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), "cuda")
+    ord_ws = B.workspace(4096 * 4, "cuda")
+    f_ws = B.workspace(B.cgtp_forward_workspace_bytes(plan, N), "cuda")
+
+    def step():
+        B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s))
+        B.cgtp_node_order(rp, ws=ord_ws, out=order)
+        B.cgtp_conv_forward_vec(plan, x, vec, perm, w, src_s, rp, out=out, ws=f_ws, node_order=order)
+
+    _replays_match_eager(torch, step, [perm, rp, src_s, out], "uvw step")
+
+
+def test_graph_full_step(B, torch):
+    """The full step's calls on a small uvu graph: CSR by destination and by
+    source, node order, forward and backward in one pass with forces, the
+    force-loss cotangent and the double backward."""
+    a, b = "16x0e+16x1o", "1x0e+1x1o+1x2e+1x3o"
+    cout, paths = W.one_block_per_path(a, b, ["0e", "1o", "2e", "3o"])
+    plan = B.Plan(a, b, cout, paths, "uvu", "f32")
+    g = W.periodic_graph(400, cutoff=4.0, seed=3)
+    N, E = g.n_nodes, g.n_edges
+    rng = np.random.default_rng(4)
+    x = torch.from_numpy(W.normal(rng, (N, plan.dim_in1), "f32")).cuda()
+    w = torch.from_numpy(W.normal(rng, (E, plan.weight_numel), "f32")[np.argsort(g.dst, kind="stable")]).cuda()
+    g_out = torch.from_numpy(W.normal(rng, (N, plan.dim_out), "f32")).cuda()
+    src_c, dst_c = torch.from_numpy(g.src).cuda(), torch.from_numpy(g.dst).cuda()
+    vec = torch.from_numpy(g.vec.astype(np.float32)).cuda()
+    i32 = lambda n: torch.empty(n, dtype=torch.int32, device="cuda")
+    f32 = lambda *s: torch.empty(*s, device="cuda")
+    perm, rp, dst_s, src_s, src_perm, src_rp, order = i32(E), i32(N + 1), i32(E), i32(E), i32(E), i32(N + 1), i32(N)
+    out, g_x, g_w, F = f32(N, plan.dim_out), f32(N, plan.dim_in1), f32(E, plan.weight_numel), f32(N, 3)
+    gg, d_g, d_x, d_w = f32(E, 16), f32(N, plan.dim_out), f32(N, plan.dim_in1), f32(E, plan.weight_numel)
+    csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), "cuda")
+    ord_ws = B.workspace(4096 * 4, "cuda")
+    ws = B.workspace(B.cgtp_conv_workspace_bytes(plan, N, E), "cuda")
+
+    def step():
+        B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s))
+        B.cgtp_build_csr(src_s, N, sorted_key=False, ws=csr_ws, out=(src_perm, src_rp, None, None))
+        B.cgtp_node_order(rp, ws=ord_ws, out=order)
+        B.cgtp_conv_forward_backward_vec(plan, x, vec, perm, w, src_s, rp, src_rp, src_perm, g_out, ws=ws,
+                                         out=(out, g_x, None, g_w, F), node_order=order)
+        B.cgtp_force_loss_sh_cotangent(3, vec, perm, src_s, dst_s, F, "f32", out=gg)
+        B.cgtp_conv_double_backward(plan, x, None, w, src_s, dst_s, rp, src_rp, src_perm, g_out, None, gg, None,
+                                    ws=ws, out=(d_g, d_x, None, d_w), node_order=order)
+
+    _replays_match_eager(torch, step, [perm, rp, src_perm, src_rp, out, g_x, g_w, F, gg, d_g, d_x, d_w],
+                         "full step")
+
+
+def test_graph_attention_and_single_tp(B, torch):
+    g = W.molecule_batch(8, 18, seed=5)
+    rng = np.random.default_rng(6)
+    H, D = 4, 16
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
+    q, k, v = (bf(W.normal(rng, (g.n_nodes, H, D), "bf16")) for _ in range(3))
+    order = np.argsort(g.dst, kind="stable")
+    rp = torch.from_numpy(np.concatenate([[0], np.cumsum(np.bincount(g.dst, minlength=g.n_nodes))]).astype(np.int32))
+    rp = rp.cuda()
+    col = torch.from_numpy(g.src[order].astype(np.int32)).cuda()
+    layout = B.cgtp_sparse_attention_prepare(col, rp, g.n_nodes)
+    att = torch.empty(g.n_nodes, H, D, device="cuda")
+    _replays_match_eager(torch, lambda: B.cgtp_sparse_attention(q, k, v, rp, g.n_edges, layout, out=att), [att],
+                         "attention")
+    c = W.config("c1")
+    plan = B.Plan(c.irreps_in1, c.irreps_in2, c.irreps_out, c.paths, c.mode, c.dtype)
+    x, y, w = (torch.from_numpy(W.normal(rng, (200, d), "f32")).cuda()
+               for d in (plan.dim_in1, plan.dim_in2, plan.weight_numel))
+    o = torch.empty(200, plan.dim_out, device="cuda")
+    _replays_match_eager(torch, lambda: B.cgtp_forward(plan, x, y, w, out=o), [o], "single product")
