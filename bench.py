@@ -323,7 +323,6 @@ def bench_conv(args, torch, B, W):
     src_rp = torch.empty(N + 1, dtype=torch.int32, device=dev)
     csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), dev)
     order = torch.empty(N, dtype=torch.int32, device=dev)
-    ord_ws = B.workspace(4096 * 4, dev)
     node_order = None if args.natural_order else order
     sh = torch.empty(E, plan.dim_in2, dtype=td, device=dev)
     out = torch.empty(N, plan.dim_out, dtype=od, device=dev)
@@ -347,10 +346,13 @@ def bench_conv(args, torch, B, W):
     def step(timed: bool):
         run = timer.run if timed else (lambda name_, fn: fn())
         # the transpose CSR (by source) serves only the backward passes
-        run("csr", lambda: (B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s)),
+        # the node order comes out of the destination CSR's own launches
+        run("csr", lambda: (B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s))
+                            if args.natural_order else
+                            B.cgtp_build_csr_order(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s),
+                                                   order=order),
                             B.cgtp_build_csr(src_s, N, sorted_key=False, ws=csr_ws,
-                                             out=(src_perm, src_rp, None, None)) if full else None,
-                            None if args.natural_order else B.cgtp_node_order(rp, ws=ord_ws, out=order)))
+                                             out=(src_perm, src_rp, None, None)) if full else None))
         if sh_in_conv and fused:
             # one pass: out, g_x, g_w and the forces (from the per-unit
             # SH-gradient partials), SH computed inside the kernel
@@ -564,13 +566,11 @@ def bench_radial(args, torch, B, W):
     src_s = torch.empty(E, dtype=torch.int32, device=dev)
     order = torch.empty(N, dtype=torch.int32, device=dev)
     csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), dev)
-    ord_ws = B.workspace(4096 * 4, dev)
     out = torch.empty(N, plan.dim_out, dtype=torch.float32, device=dev)
     f_ws = B.workspace(B.cgtp_forward_workspace_bytes(plan, N), dev)
 
     def step():
-        B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s))
-        B.cgtp_node_order(rp, ws=ord_ws, out=order)
+        B.cgtp_build_csr_order(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s), order=order)
         B.cgtp_conv_forward_radial(plan, x, vec, perm, radial, w, src_s, rp, out=out, ws=f_ws, node_order=order)
 
     ms, per_step, launch_mode, graph = time_steps(torch, args, step)

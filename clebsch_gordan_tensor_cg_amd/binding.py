@@ -49,6 +49,7 @@ EXPORTS = [
     "cgtp_conv_forward_backward", "cgtp_conv_forward_backward_vec",
     "cgtp_sparse_attention_layout_bytes", "cgtp_sparse_attention_prepare",
     "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_csr_workspace_bytes", "cgtp_build_csr",
+    "cgtp_build_csr_order",
     "cgtp_validate_csr", "cgtp_node_order_workspace_bytes", "cgtp_node_order", "cgtp_spherical_harmonics", "cgtp_forces_workspace_bytes", "cgtp_sh_forces",
     "cgtp_force_loss_sh_cotangent", "cgtp_timing_enable", "cgtp_timing_collect", "cgtp_last_error",
     "cgtp_version",
@@ -92,6 +93,7 @@ def lib():
             "cgtp_node_order": [vp, i64, vp, vp, sz, vp],
             "cgtp_csr_workspace_bytes": [i64, i64, vp],
             "cgtp_build_csr": [vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
+            "cgtp_build_csr_order": [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp],
             "cgtp_validate_csr": [vp, i64, i64, vp, i64, vp, vp],
             "cgtp_spherical_harmonics": [i32, i32, vp, vp, i64, vp, vp],
             "cgtp_forces_workspace_bytes": [i64, i32, vp],
@@ -475,8 +477,7 @@ def cgtp_csr_workspace_bytes(n_edges: int, n_keys: int) -> int:
     return b.value
 
 
-def cgtp_build_csr(key, n_keys: int, val=None, sorted_key: bool = True, ws=None, out=None, stream=None):
-    """Returns (perm, row_ptr, sorted_key or None, sorted_val or None)."""
+def _csr_outputs(key, n_keys, val, sorted_key, ws, out):
     E = key.shape[0]
     dev = key.device
     if out is None:
@@ -488,9 +489,28 @@ def cgtp_build_csr(key, n_keys: int, val=None, sorted_key: bool = True, ws=None,
         perm, row_ptr, sk, sv = out
     if ws is None:
         ws = workspace(cgtp_csr_workspace_bytes(E, n_keys), dev)
+    return E, perm, row_ptr, sk, sv, ws
+
+
+def cgtp_build_csr(key, n_keys: int, val=None, sorted_key: bool = True, ws=None, out=None, stream=None):
+    """Returns (perm, row_ptr, sorted_key or None, sorted_val or None)."""
+    E, perm, row_ptr, sk, sv, ws = _csr_outputs(key, n_keys, val, sorted_key, ws, out)
     _check(lib().cgtp_build_csr(_ptr(key), _ptr(val), E, n_keys, _ptr(perm), _ptr(row_ptr), _ptr(sk), _ptr(sv),
                                 _ptr(ws), ws.numel(), _stream(stream, key)))
     return perm, row_ptr, sk, sv
+
+
+def cgtp_build_csr_order(key, n_keys: int, val=None, sorted_key: bool = True, ws=None, out=None, order=None,
+                         stream=None):
+    """cgtp_build_csr plus the longest-first node order (cgtp_node_order's)
+    from the same launches.  Returns (perm, row_ptr, sorted_key or None,
+    sorted_val or None, order)."""
+    E, perm, row_ptr, sk, sv, ws = _csr_outputs(key, n_keys, val, sorted_key, ws, out)
+    if order is None:
+        order = torch.empty(n_keys, dtype=torch.int32, device=key.device)
+    _check(lib().cgtp_build_csr_order(_ptr(key), _ptr(val), E, n_keys, _ptr(perm), _ptr(row_ptr), _ptr(sk),
+                                      _ptr(sv), _ptr(order), _ptr(ws), ws.numel(), _stream(stream, key)))
+    return perm, row_ptr, sk, sv, order
 
 
 def cgtp_validate_csr(row_ptr, n_edges: int, idx=None, n_idx_range: int = 0, stream=None) -> bool:

@@ -137,6 +137,48 @@ __global__ void k_invert_perm(const int32_t *__restrict__ perm, int64_t n, int32
 // (#workgroups x #bins) rather than one per edge.  Keys outside
 // [0, n_keys) are skipped.
 constexpr int kCsrBins = 16384;  // 64 KiB of LDS counters per workgroup
+// Node processing order: nodes by decreasing segment length (longest
+// first, so the long segments do not form the tail of a launch).  Buckets
+// are kOrderBuckets-1-min(len, kOrderBuckets-1); the order within a bucket
+// is whatever the atomics give, which changes no result (each node is
+// computed by one wavefront in its fixed edge order).
+constexpr int kOrderBuckets = 1024;
+constexpr int64_t kOrderSmallMax = 65536;   // rows ordered by one workgroup
+__device__ __forceinline__ int lpt_bucket(int len) {
+    return kOrderBuckets - 1 - (len < kOrderBuckets - 1 ? (len < 0 ? 0 : len) : kOrderBuckets - 1);
+}
+__device__ __forceinline__ int order_bucket(const int32_t *__restrict__ rp, int64_t i) {
+    return lpt_bucket(rp[i + 1] - rp[i]);
+}
+
+// Turns the kOrderBuckets counts in h into exclusive starts.  Called by all
+// 1024 threads of a workgroup (one bucket each) after the counts are in
+// place; wsum: 16 words of LDS.  Ends with a barrier.
+__device__ __forceinline__ void lpt_bucket_starts(int32_t *h, int32_t *wsum) {
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int32_t own = h[t];
+    int32_t incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    if (wid == 0) {
+        int32_t ws = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int32_t v = __shfl_up(ws, off, 64);
+            if (lane >= off) ws += v;
+        }
+        if (lane < 16) wsum[lane] = ws;
+    }
+    __syncthreads();
+    h[t] = (wid ? wsum[wid - 1] : 0) + incl - own;
+    __syncthreads();
+}
+
 constexpr int kCsrThreads = 1024;
 
 // Visits the keys of edges [e0, e1) owned by this thread, eight loads in
@@ -264,15 +306,20 @@ __host__ __device__ constexpr size_t small_csr_table_bytes(int64_t n_keys) {
 
 // counters: word [j][k] holds run 2j's count of key k in its low half and
 // run 2j+1's in its high half (a run holds at most 2048 edges, so no carry)
+// With order non-NULL the same workgroup also writes the longest-first node
+// order (as k_order_small) from the key totals it already holds.
 __global__ void __launch_bounds__(1024) k_csr_small_count(const int32_t *__restrict__ key, int64_t n, int64_t n_keys,
                                                           int32_t *__restrict__ row_ptr,
-                                                          uint32_t *__restrict__ table) {
+                                                          uint32_t *__restrict__ table,
+                                                          int32_t *__restrict__ order) {
     extern __shared__ uint32_t cpair[];   // [kSmallCsrRuns / 2][n_keys]
     __shared__ int32_t wsum[16];
+    __shared__ int32_t hb[kOrderBuckets];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int nk = (int)n_keys;
     const int rsh = small_csr_run_shift(n);
     for (int i = t; i < (kSmallCsrRuns / 2) * nk; i += blockDim.x) cpair[i] = 0;
+    if (order) hb[t] = 0;
     __syncthreads();
     // 32 keys of a thread in flight at once: one round for up to 32768 edges
     for (int h = 0; h * 32 * 1024 < n; ++h) {
@@ -335,6 +382,16 @@ __global__ void __launch_bounds__(1024) k_csr_small_count(const int32_t *__restr
         }
     }
     if (t == (int)blockDim.x - 1) row_ptr[nk] = before + incl;   // every valid key counted
+    if (order) {   // uniform: the whole workgroup takes this branch or none of it
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            if (2 * t + q < nk) atomicAdd(&hb[lpt_bucket(tot[q])], 1);
+        __syncthreads();   // also orders the reads of wsum above before its reuse
+        lpt_bucket_starts(hb, wsum);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            if (2 * t + q < nk) order[atomicAdd(&hb[lpt_bucket(tot[q])], 1)] = 2 * t + q;
+    }
 }
 
 // lanes of this wavefront whose key equals this lane's key (valid lanes
@@ -409,16 +466,6 @@ __global__ void __launch_bounds__(64) k_csr_small_place(const int32_t *__restric
     }
 }
 
-// Node processing order: nodes by decreasing segment length (longest
-// first, so the long segments do not form the tail of a launch).  Buckets
-// are kOrderBuckets-1-min(len, kOrderBuckets-1); the order within a bucket
-// is whatever the atomics give, which changes no result (each node is
-// computed by one wavefront in its fixed edge order).
-constexpr int kOrderBuckets = 1024;
-__device__ __forceinline__ int order_bucket(const int32_t *__restrict__ rp, int64_t i) {
-    const int len = rp[i + 1] - rp[i];
-    return kOrderBuckets - 1 - (len < kOrderBuckets - 1 ? (len < 0 ? 0 : len) : kOrderBuckets - 1);
-}
 
 // The whole order in one workgroup (small graphs): count, scan and place
 // in LDS.
@@ -426,33 +473,12 @@ __global__ void __launch_bounds__(1024) k_order_small(const int32_t *__restrict_
                                                        int32_t *__restrict__ order) {
     __shared__ int32_t h[kOrderBuckets];
     __shared__ int32_t wsum[16];
-    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int t = threadIdx.x;
     h[t] = 0;
     __syncthreads();
     for (int64_t i = t; i < n; i += 1024) atomicAdd(&h[order_bucket(rp, i)], 1);
     __syncthreads();
-    // exclusive scan of the 1024 bucket counts, one per thread
-    const int32_t own = h[t];
-    int32_t incl = own;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int32_t v = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += v;
-    }
-    if (lane == 63) wsum[wid] = incl;
-    __syncthreads();
-    if (wid == 0) {
-        int32_t ws = lane < 16 ? wsum[lane] : 0;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const int32_t v = __shfl_up(ws, off, 64);
-            if (lane >= off) ws += v;
-        }
-        if (lane < 16) wsum[lane] = ws;
-    }
-    __syncthreads();
-    h[t] = (wid ? wsum[wid - 1] : 0) + incl - own;
-    __syncthreads();
+    lpt_bucket_starts(h, wsum);
     for (int64_t i = t; i < n; i += 1024) order[atomicAdd(&h[order_bucket(rp, i)], 1)] = (int32_t)i;
 }
 
@@ -488,9 +514,12 @@ __global__ void __launch_bounds__(1024) k_order_scatter(const int32_t *__restric
 
 // Exclusive scan of cnt[0..n) into row_ptr[0..n]; one workgroup, four
 // consecutive counts per thread, wavefront scans by shuffles.
+// With order non-NULL (n at most 65536 rows) it then writes the longest-first
+// node order of the rows whose lengths cnt holds, as k_order_small does.
 __global__ void __launch_bounds__(1024) k_scan(const int32_t *__restrict__ cnt, int64_t n,
-                                                int32_t *__restrict__ row_ptr) {
+                                                int32_t *__restrict__ row_ptr, int32_t *__restrict__ order) {
     __shared__ int32_t wsum[16];
+    __shared__ int32_t hb[kOrderBuckets];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     int32_t carry = 0;
     for (int64_t base = 0; base < n; base += 4096) {
@@ -527,6 +556,15 @@ __global__ void __launch_bounds__(1024) k_scan(const int32_t *__restrict__ cnt, 
         __syncthreads();
     }
     if (threadIdx.x == 0) row_ptr[n] = carry;
+    if (order) {   // uniform across the workgroup
+        const int t = threadIdx.x;
+        hb[t] = 0;
+        __syncthreads();
+        for (int64_t i = t; i < n; i += 1024) atomicAdd(&hb[lpt_bucket(cnt[i])], 1);
+        __syncthreads();
+        lpt_bucket_starts(hb, wsum);
+        for (int64_t i = t; i < n; i += 1024) order[atomicAdd(&hb[lpt_bucket(cnt[i])], 1)] = (int32_t)i;
+    }
 }
 
 // One wavefront per segment: each element's final slot is the number of
@@ -1287,6 +1325,13 @@ int cgtp_csr_workspace_bytes(int64_t n_edges, int64_t n_keys, size_t *bytes) {
 int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int64_t n_keys, int32_t *perm,
                    int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val, void *workspace,
                    size_t workspace_bytes, cgtp_stream_t stream) {
+    return cgtp_build_csr_order(key, val, n_edges, n_keys, perm, row_ptr, sorted_key, sorted_val, nullptr,
+                                workspace, workspace_bytes, stream);
+}
+
+int cgtp_build_csr_order(const int32_t *key, const int32_t *val, int64_t n_edges, int64_t n_keys, int32_t *perm,
+                         int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val, int32_t *order,
+                         void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
     clear_error();
     hipStream_t s = (hipStream_t)stream;
     size_t need = 0;
@@ -1296,6 +1341,7 @@ int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int6
     if (!row_ptr || (n_edges > 0 && (!key || !perm || (sorted_val && !val))) || !workspace ||
         workspace_bytes < need)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_build_csr: NULL pointer or workspace too small");
+    if (order && n_keys == 0) order = nullptr;   // nothing to order
     if (small_csr(n_edges, n_keys)) {
         int nbits = 0;
         while ((int64_t(1) << nbits) < n_keys) ++nbits;
@@ -1306,7 +1352,7 @@ int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int6
         if (lds_ok != hipSuccess) return hip_check(lds_ok, "cgtp_build_csr: LDS size attribute");
         uint32_t *table = (uint32_t *)workspace;
         CGTP_LAUNCH("k_csr_small_count", s, k_csr_small_count, dim3(1), dim3(1024), lds, s, key, n_edges, n_keys,
-                    row_ptr, table);
+                    row_ptr, table, order);
         CGTP_LAUNCH("k_csr_small_place", s, k_csr_small_place, dim3(kSmallCsrRuns), dim3(64),
                     sizeof(uint16_t) * (size_t)small_csr_stride(n_keys), s, key, val, n_edges, n_keys, nbits,
                     (const uint16_t *)table, perm, sorted_key, sorted_val);
@@ -1339,7 +1385,9 @@ int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int6
             CGTP_LAUNCH("k_count", s, k_count, grid, dim3(kCsrThreads), lds, s, key, n_edges, n_keys, per, cnt);
         else
             CGTP_LAUNCH("k_count_global", s, k_count_global, dim3(ge), dim3(kBlock), 0, s, key, n_edges, n_keys, cnt);
-        CGTP_LAUNCH("k_scan", s, k_scan, dim3(1), dim3(1024), 0, s, cnt, n_keys, row_ptr);
+        int32_t *fold = n_keys <= kOrderSmallMax ? order : nullptr;   // order from the counts, same launch
+        CGTP_LAUNCH("k_scan", s, k_scan, dim3(1), dim3(1024), 0, s, cnt, n_keys, row_ptr, fold);
+        if (fold) order = nullptr;
         if (lds_path)
             CGTP_LAUNCH("k_scatter", s, k_scatter, grid, dim3(kCsrThreads), lds, s, key, n_edges, n_keys, per, row_ptr,
                         cursor, tmp);
@@ -1351,7 +1399,17 @@ int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int6
     } else {
         CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(grid_for(n_keys + 1)), dim3(kBlock), 0, s, row_ptr, n_keys + 1, 0);
     }
-    return hip_check(hipGetLastError(), "cgtp_build_csr launch");
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_check(e, "cgtp_build_csr launch");
+    if (!order) return CGTP_OK;
+    // not folded into the counting launches (no edges, or more rows than one
+    // workgroup orders): the separate order launches; a wide key space leaves
+    // the CSR's workspace, free again in stream order, larger than they need
+    if (n_keys <= kOrderSmallMax) {
+        CGTP_LAUNCH("k_order_small", s, k_order_small, dim3(1), dim3(1024), 0, s, row_ptr, n_keys, order);
+        return hip_check(hipGetLastError(), "cgtp_build_csr order launch");
+    }
+    return cgtp_node_order(row_ptr, n_keys, order, workspace, workspace_bytes, stream);
 }
 
 int cgtp_node_order_workspace_bytes(int64_t n_nodes, size_t *bytes) {
@@ -1371,7 +1429,7 @@ int cgtp_node_order(const int32_t *row_ptr, int64_t n_nodes, int32_t *order, voi
     if (n_nodes == 0) return CGTP_OK;
     if (!row_ptr || !order || !workspace || workspace_bytes < need)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_node_order: NULL pointer or workspace too small");
-    if (n_nodes <= 65536) {
+    if (n_nodes <= kOrderSmallMax) {
         CGTP_LAUNCH("k_order_small", s, k_order_small, dim3(1), dim3(1024), 0, s, row_ptr, n_nodes, order);
         return hip_check(hipGetLastError(), "cgtp_node_order launch");
     }
@@ -1384,7 +1442,7 @@ int cgtp_node_order(const int32_t *row_ptr, int64_t n_nodes, int32_t *order, voi
     // a few workgroups: each publishes at most kOrderBuckets counts
     const unsigned g = (unsigned)std::min<int64_t>(64, (n_nodes + 4095) / 4096);
     CGTP_LAUNCH("k_order_count", s, k_order_count, dim3(g), dim3(1024), 0, s, row_ptr, n_nodes, cnt);
-    CGTP_LAUNCH("k_scan", s, k_scan, dim3(1), dim3(1024), 0, s, cnt, (int64_t)kOrderBuckets, start);
+    CGTP_LAUNCH("k_scan", s, k_scan, dim3(1), dim3(1024), 0, s, cnt, (int64_t)kOrderBuckets, start, nullptr);
     CGTP_LAUNCH("k_order_scatter", s, k_order_scatter, dim3(g), dim3(1024), 0, s, row_ptr, n_nodes, start, cursor,
                 order);
     return hip_check(hipGetLastError(), "cgtp_node_order launch");

@@ -338,6 +338,16 @@ int cgtp_build_csr(const int32_t *key, const int32_t *val, int64_t n_edges, int6
                    int32_t *perm, int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val,
                    void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
 
+/* cgtp_build_csr that also writes order [n_keys], the rows' processing
+ * order of cgtp_node_order (decreasing length, rows of 1023 or more edges
+ * tie), from the row lengths the sort has already counted: with at most
+ * 65,536 keys and at least one edge it costs no extra launch.  Same
+ * arguments, workspace and errors as cgtp_build_csr; order may be NULL
+ * (then the call is cgtp_build_csr). */
+int cgtp_build_csr_order(const int32_t *key, const int32_t *val, int64_t n_edges, int64_t n_keys,
+                         int32_t *perm, int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val,
+                         int32_t *order, void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
 /* Processing order for the convolution calls: the n_nodes rows of a CSR
  * sorted by decreasing length (rows of 1023 or more edges tie), so that
  * the longest rows are started first and do not form the tail of a launch

@@ -46,7 +46,7 @@ def _replays_match_eager(torch, step, outputs, name, replays=3):
 
 
 def test_graph_uvw_step(B, torch):
-    """CSR (two-launch small path), node order and the uvw convolution with
+    """CSR with the node order (two-launch small path) and the uvw convolution with
     the SH from the edge vectors and the mixing on the matrix cores."""
     c = W.config("c5")
     g = W.molecule_batch(12, 18, cutoff=c.extra["cutoff"], seed=1)
@@ -62,12 +62,10 @@ def test_graph_uvw_step(B, torch):
     order = torch.empty(N, dtype=torch.int32, device="cuda")
     out = torch.empty(N, plan.dim_out, device="cuda")
     csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), "cuda")
-    ord_ws = B.workspace(4096 * 4, "cuda")
     f_ws = B.workspace(B.cgtp_forward_workspace_bytes(plan, N), "cuda")
 
     def step():
-        B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s))
-        B.cgtp_node_order(rp, ws=ord_ws, out=order)
+        B.cgtp_build_csr_order(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s), order=order)
         B.cgtp_conv_forward_vec(plan, x, vec, perm, w, src_s, rp, out=out, ws=f_ws, node_order=order)
 
     _replays_match_eager(torch, step, [perm, rp, src_s, out], "uvw step")
@@ -94,13 +92,11 @@ def test_graph_full_step(B, torch):
     out, g_x, g_w, F = f32(N, plan.dim_out), f32(N, plan.dim_in1), f32(E, plan.weight_numel), f32(N, 3)
     gg, d_g, d_x, d_w = f32(E, 16), f32(N, plan.dim_out), f32(N, plan.dim_in1), f32(E, plan.weight_numel)
     csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), "cuda")
-    ord_ws = B.workspace(4096 * 4, "cuda")
     ws = B.workspace(B.cgtp_conv_workspace_bytes(plan, N, E), "cuda")
 
     def step():
-        B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s))
+        B.cgtp_build_csr_order(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s), order=order)
         B.cgtp_build_csr(src_s, N, sorted_key=False, ws=csr_ws, out=(src_perm, src_rp, None, None))
-        B.cgtp_node_order(rp, ws=ord_ws, out=order)
         B.cgtp_conv_forward_backward_vec(plan, x, vec, perm, w, src_s, rp, src_rp, src_perm, g_out, ws=ws,
                                          out=(out, g_x, None, g_w, F), node_order=order)
         B.cgtp_force_loss_sh_cotangent(3, vec, perm, src_s, dst_s, F, "f32", out=gg)

@@ -353,10 +353,11 @@ def test_conv_no_edges(B, torch):
 # ---------------------------------------------------------------------------
 # CSR build, validation, spherical harmonics, forces
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("case", ["c2", "empty", "one_node", "hub", "ragged", "multi_range", "wide_keys",
-                                  "many_splits", "molecules", "small_max", "one_key_max", "past_small_edges",
-                                  "past_small_keys"])
-def test_build_csr_bit_exact(B, torch, case):
+CSR_CASES = ["c2", "empty", "one_node", "hub", "ragged", "multi_range", "wide_keys", "many_splits", "molecules",
+             "small_max", "one_key_max", "past_small_edges", "past_small_keys"]
+
+
+def _csr_case(case):
     rs = np.random.default_rng(5)
     # two-launch path: at most 65535 edges and 2048 keys
     if case == "molecules":
@@ -387,6 +388,12 @@ def test_build_csr_bit_exact(B, torch, case):
         key, n = np.where(rs.random(5000) < 0.5, 3, rs.integers(0, 40, 5000)).astype(np.int32), 40
     else:
         key, n = rs.integers(0, 1000, 777).astype(np.int32), 1000
+    return key, n
+
+
+@pytest.mark.parametrize("case", CSR_CASES)
+def test_build_csr_bit_exact(B, torch, case):
+    key, n = _csr_case(case)
     perm_ref, rp_ref = oracle.csr(key, n)
     print(f"csr {case}", flush=True)
     val = (np.arange(len(key), dtype=np.int32) * 7 + 3).astype(np.int32)
@@ -398,6 +405,33 @@ def test_build_csr_bit_exact(B, torch, case):
     np.testing.assert_array_equal(perm.cpu().numpy(), perm_ref)
     np.testing.assert_array_equal(sk.cpu().numpy(), key[perm_ref])
     np.testing.assert_array_equal(sv.cpu().numpy(), val[perm_ref])
+
+
+def _check_lpt_order(order, rp):
+    """A permutation of the rows with non-increasing lengths (1023 and more tie)."""
+    assert sorted(order.tolist()) == list(range(len(rp) - 1))
+    deg = np.minimum(np.diff(rp)[order], 1023)
+    assert np.all(deg[:-1] >= deg[1:])
+
+
+@pytest.mark.parametrize("case", CSR_CASES)
+def test_build_csr_order(B, torch, case):
+    """The node order written by the CSR's own launches (small path, the
+    scan of the large path) or, past them, by the separate order launches;
+    the CSR itself is the plain build's, bit for bit."""
+    key, n = _csr_case(case)
+    perm_ref, rp_ref = oracle.csr(key, n)
+    print(f"csr+order {case}", flush=True)
+    val = (np.arange(len(key), dtype=np.int32) * 5 + 1).astype(np.int32)
+    kd = torch.from_numpy(key).cuda() if len(key) else torch.zeros(0, dtype=torch.int32, device="cuda")
+    vd = torch.from_numpy(val).cuda() if len(key) else torch.zeros(0, dtype=torch.int32, device="cuda")
+    perm, rp, sk, sv, order = B.cgtp_build_csr_order(kd, n, val=vd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(rp.cpu().numpy(), rp_ref)
+    np.testing.assert_array_equal(perm.cpu().numpy(), perm_ref)
+    np.testing.assert_array_equal(sk.cpu().numpy(), key[perm_ref])
+    np.testing.assert_array_equal(sv.cpu().numpy(), val[perm_ref])
+    _check_lpt_order(order.cpu().numpy(), rp_ref)
 
 
 @pytest.mark.parametrize("n", [50, 20000])
