@@ -57,7 +57,8 @@ struct KernelShape {
 };
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
-// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, full, ubudget)
+// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, full, ubudget,
+// ucpl)
 // overrides
 // them for experiments.
 struct Tuning {
@@ -66,12 +67,15 @@ struct Tuning {
     bool y_vector = true;    // load the y row with vector (not scalar) loads
     bool nt_w = true;        // non-temporal loads of the per-edge weights
     bool prefetch = true;    // load edge t+1 while edge t is computed
-    int stage = 64;          // edges per LDS chunk of src and y rows (0 = off)
+    int stage = -1;          // edges per LDS chunk of src and y rows (0 = off; -1: 64, or 32 for uvw
+                             // layers without radial weights)
     int cy_path = -1;        // uniform products per path (1) or per edge (0); -1: by dtype
-    int depth = 3;           // edges of prefetch in flight (staged loop)
+    int depth = 0;           // edges of prefetch in flight (staged loop; 0: 3, or 2 for uvw layers
+                             // without radial weights)
     bool bgy = false;        // backward via B_ij = sum_k R_ijk g_k (fewer FMAs, more VGPRs)
     int full = 7;            // dispatch to the folded-flag kernels: bit 0 backward, bit 1 double backward, bit 2 fused forward+backward
     int ubudget = 0;         // uvw accumulators per lane and unit (0: 32, or 144 with radial weights)
+    int ucpl = 0;            // uvw channels per lane (0: 1)
 };
 Tuning tuning_from_env();
 

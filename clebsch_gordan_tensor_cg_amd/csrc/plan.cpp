@@ -289,6 +289,7 @@ Tuning tuning_from_env() {
             else if (k == "bgy") t.bgy = v != 0;
             else if (k == "full") t.full = v & 7;
             else if (k == "ubudget") t.ubudget = v < 1 ? 0 : v;
+            else if (k == "ucpl") t.ucpl = v < 1 ? 0 : (v > 8 ? 8 : v);
         }
         pos = comma + 1;
     }
@@ -302,11 +303,15 @@ void split_uvw(Plan &p, KernelShape &ks) {
     ks.groups.clear();
     int max_mul = 0;
     for (auto &P : p.paths) max_mul = std::max(max_mul, P.mul1);
-    ks.lanes_per_item = max_mul >= 64 ? 64 : next_pow2(std::max(1, max_mul));
+    // cpl channels per lane share each edge's uniform products
+    const int cpl = p.tune.ucpl > 0 ? p.tune.ucpl : 1;
+    const int lanes = (max_mul + cpl - 1) / cpl;
+    ks.lanes_per_item = lanes >= 64 ? 64 : next_pow2(std::max(1, lanes));
     ks.items_per_wave = 64 / ks.lanes_per_item;
-    // accumulators per lane: one per (path, v, k), times H+1 with radial weights
-    // defaults from sweeps of the 44-path l <= 6 layer (100 x 18 atoms)
-    const int budget = p.tune.ubudget > 0 ? p.tune.ubudget : (p.radial_h > 0 ? 144 : 32);
+    // accumulators per lane: one per (path, v, k) and channel slot, times H+1
+    // with radial weights; defaults from sweeps of the 44-path l <= 6 layer
+    // (100 x 18 atoms)
+    const int budget = (p.tune.ubudget > 0 ? p.tune.ubudget : (p.radial_h > 0 ? 144 : 32)) / cpl;
     for (int b = 0; b < (int)p.in1.size(); ++b) {
         Group cur;
         int acc = 0;
@@ -328,8 +333,8 @@ void split_uvw(Plan &p, KernelShape &ks) {
     }
     ks.n_units = 0;
     for (auto &g : ks.groups) {
-        g.cpl = 1;
-        g.slices = (g.max_mul + ks.lanes_per_item - 1) / ks.lanes_per_item;
+        g.cpl = cpl;
+        g.slices = (g.max_mul + ks.lanes_per_item * cpl - 1) / (ks.lanes_per_item * cpl);
         ks.n_units += g.slices;
     }
 }
@@ -364,6 +369,12 @@ void choose_shapes(Plan &p) {
     // uniform products per path where registers are tight: FP64 (two VGPRs
     // each) and the bf16 uvw layers (SH rows up to l = 6); per edge otherwise
     if (p.tune.cy_path < 0) p.tune.cy_path = (p.dtype == CGTP_F64 || p.dtype == CGTP_BF16_F32ACC) ? 1 : 0;
+    // uvw layers without radial weights: shorter chunks (a quarter of the LDS
+    // per wavefront) and two edges in flight measured faster (sweep of the
+    // 100 x 18 atom layer: 47 against 50 us); the radial form keeps 64 and 3
+    const bool uvw_plain = p.mode == CGTP_UVW && p.radial_h == 0;
+    if (p.tune.stage < 0) p.tune.stage = uvw_plain ? 32 : 64;
+    if (p.tune.depth <= 0) p.tune.depth = uvw_plain ? 2 : 3;
     if (p.mode == CGTP_UVW) {
         mix_tables(p);
         split_uvw(p, p.fwd);
