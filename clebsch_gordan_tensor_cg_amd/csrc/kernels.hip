@@ -894,7 +894,7 @@ struct CotLaunch {
 // B[4(l/16)+0..3][l%16], and receives D[4(l/16)+i][l%16], i = 0..3.
 // ---------------------------------------------------------------------------
 constexpr int kMixMaxPaths = 64;
-constexpr int kMixKC = 512;   // contraction rows staged per step (64 KiB of bf16 at 64 columns)
+constexpr int kMixKC = 256;   // contraction rows staged per step (32 KiB of bf16 at 64 columns)
 constexpr int kMixMaxBlocks = 4;   // output blocks mixed by one launch
 // one output block of a mixing launch
 struct MixBlockArgs {
@@ -940,7 +940,7 @@ __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return (
 // rows in 16-byte segments and 8-byte aligned path tensors, so loads need no
 // guards (the general variant checks every element).
 template <bool kFast>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_uvw_mix(const uint16_t *__restrict__ T0, const uint16_t *__restrict__ W,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_uvw_mix(const uint16_t *__restrict__ T0, const uint16_t *__restrict__ W,
                                                  int64_t wstride, MixArgs args, float *__restrict__ out, int64_t dim3,
                                                  int accumulate, float *__restrict__ part0) {
     __shared__ __attribute__((aligned(16))) uint16_t Ws[kMixKC * 64];
