@@ -47,11 +47,11 @@ int check_loaded(cgtp_plan_t plan) {
     return CGTP_OK;
 }
 
-int launch(hipFunction_t f, const char *name, int64_t blocks, hipStream_t s, void **args) {
+int launch(hipFunction_t f, const char *name, int64_t blocks, hipStream_t s, void **args, unsigned threads = 64) {
     if (blocks <= 0) return CGTP_OK;
     if (blocks > 0x7fffffffLL) return set_error(CGTP_ERR_INVALID_ARGUMENT, "grid too large");
     TimedLaunch tl(name, s);
-    hipError_t e = hipModuleLaunchKernel(f, (unsigned)blocks, 1, 1, 64, 1, 1, 0, s, args, nullptr);
+    hipError_t e = hipModuleLaunchKernel(f, (unsigned)blocks, 1, 1, threads, 1, 1, 0, s, args, nullptr);
     if (e != hipSuccess) return set_error(CGTP_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return CGTP_OK;
 }
@@ -380,7 +380,9 @@ static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, c
     void *args[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, (void *)&order, (void *)&vec,
                     (void *)&vperm, (void *)&radial, &ws, &n, &graph};
     const int64_t ipw = p.fwd.items_per_wave;
-    int rc = launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
+    // the matrix-core form: one workgroup of four wavefronts per item
+    int rc = p.uvw_mma ? launch(p.k_fwd, "cgtp_fwd", n_items, s, args, 256)
+                       : launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
     if (rc) return rc;
     int acc = 0;
     if (!blocks_covered(p.out, p.paths, true)) {

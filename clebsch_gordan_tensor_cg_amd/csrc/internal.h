@@ -58,7 +58,7 @@ struct KernelShape {
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
 // of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, full, ubudget,
-// ucpl)
+// ucpl, umma)
 // overrides
 // them for experiments.
 struct Tuning {
@@ -76,6 +76,8 @@ struct Tuning {
     int full = 7;            // dispatch to the folded-flag kernels: bit 0 backward, bit 1 double backward, bit 2 fused forward+backward
     int ubudget = 0;         // uvw accumulators per lane and unit (0: 32, or 144 with radial weights)
     int ucpl = 0;            // uvw channels per lane (0: 1)
+    int umma = 0;            // uvw path tensors as per-node products on the matrix cores where they fit
+                             // (measured slower on the 100 x 18 atom layer: off by default)
 };
 Tuning tuning_from_env();
 
@@ -108,6 +110,7 @@ struct Plan {
     std::vector<MixBlock> mix;     // uvw only
     std::vector<int> mix_of_path;  // uvw: index into mix for each path
     int64_t t_per_item = 0;        // uvw: T elements per item
+    bool uvw_mma = false;          // uvw: path tensors by the matrix-core kernel (256 threads per item)
     std::string source;
     std::string cache_key;
     bool cached = false;
@@ -135,6 +138,11 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 inline int bwd_full_flags(const Plan &p) { return 1 | 2 | 4 | (p.bwd.n_units > 1 ? 64 : 0); }
 inline int dbl_full_flags(const Plan &) { return 1 | 2; }
 inline int fb_full_flags(const Plan &p) { return 1 | 2 | 4 | (p.fb.n_units > 1 ? 64 : 0); }
+
+// uvw path tensors on the matrix cores: LDS bytes of one workgroup (0 when
+// the plan has no such kernel: radial weights, or no path)
+size_t uvw_mma_lds_bytes(const Plan &p);
+constexpr size_t kUvwMmaMaxLds = 96 * 1024;   // static LDS of one workgroup (two per CU)
 
 // planner
 int parse_irreps(const char *s, std::vector<Irrep> &out, std::string &err);

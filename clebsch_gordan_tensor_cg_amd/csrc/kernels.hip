@@ -1111,7 +1111,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
 }
 
 // out[item][off3 + col*d3 + k] (=|+=) sum_s part[s][item*d3 + k][col] for
-// every split block of the launch (elements enumerated block after block)
+// every split block of the launch (elements enumerated block after block).
+// I: the index type of the element arithmetic (32-bit divisions whenever
+// every block's M * mul3 fits).
+template <class I>
 __global__ void k_uvw_mix_reduce(const float *__restrict__ part0, MixArgs args, int64_t total, float *__restrict__ out,
                                  int64_t dim3, int accumulate) {
     for (int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i0 < total;
@@ -1132,11 +1135,11 @@ __global__ void k_uvw_mix_reduce(const float *__restrict__ part0, MixArgs args, 
             }
         }
         const float *__restrict__ part = part0 + part_off;
-        const int64_t r = i / mul3, col = i % mul3;
+        const I ii = (I)i, r = ii / (I)mul3, col = ii - r * (I)mul3;
         float acc = 0.f;
         for (int sp = 0; sp < n_split; ++sp) acc += part[(int64_t)sp * M * mul3 + i];
-        const int64_t item = r / d3, k = r % d3;
-        float *o = out + item * dim3 + off3 + col * d3 + k;
+        const I item = r / (I)d3, k = r - item * (I)d3;
+        float *o = out + (int64_t)item * dim3 + off3 + (int64_t)col * d3 + k;
         *o = accumulate ? *o + acc : acc;
     }
 }
@@ -1170,7 +1173,7 @@ int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items,
     for (size_t b0 = 0; b0 < p.mix.size(); b0 += kMixMaxBlocks) {
         MixArgs args{};
         args.nb = (int)std::min<size_t>(kMixMaxBlocks, p.mix.size() - b0);
-        int64_t wg = 0, red = 0;
+        int64_t wg = 0, red = 0, red_max = 0;
         // unguarded loads: 16-row contraction steps, whole 16-byte weight
         // segments, 8-byte aligned path-tensor rows
         bool fast = (((uintptr_t)T) & 7) == 0 && (((uintptr_t)w) & 15) == 0 && p.wnumel % 8 == 0;
@@ -1201,6 +1204,7 @@ int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items,
             if (a.n_split > 1) {
                 part_off += (int64_t)a.n_split * a.M * a.mul3;
                 red += a.M * a.mul3;
+                red_max = std::max<int64_t>(red_max, a.M * a.mul3);
             }
             int64_t groups = (a.M + 63) / 64;
             if (groups * a.n_split > 4096) groups = std::max<int64_t>(1, 4096 / a.n_split);
@@ -1216,8 +1220,12 @@ int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items,
         if (red > 0) {
             unsigned g = grid_for(red);
             if (g > 8192) g = 8192;
-            CGTP_LAUNCH("k_uvw_mix_reduce", s, k_uvw_mix_reduce, dim3(g), dim3(kBlock), 0, s, (const float *)part, args,
-                        red, (float *)out, p.dim3, accumulate);
+            if (red_max < (int64_t(1) << 31))
+                CGTP_LAUNCH("k_uvw_mix_reduce", s, k_uvw_mix_reduce<uint32_t>, dim3(g), dim3(kBlock), 0, s,
+                            (const float *)part, args, red, (float *)out, p.dim3, accumulate);
+            else
+                CGTP_LAUNCH("k_uvw_mix_reduce", s, k_uvw_mix_reduce<int64_t>, dim3(g), dim3(kBlock), 0, s,
+                            (const float *)part, args, red, (float *)out, p.dim3, accumulate);
         }
     }
     return hip_check(hipGetLastError(), "uvw mix launch");

@@ -290,6 +290,7 @@ Tuning tuning_from_env() {
             else if (k == "full") t.full = v & 7;
             else if (k == "ubudget") t.ubudget = v < 1 ? 0 : v;
             else if (k == "ucpl") t.ucpl = v < 1 ? 0 : (v > 8 ? 8 : v);
+            else if (k == "umma") t.umma = v != 0;
         }
         pos = comma + 1;
     }
@@ -378,6 +379,8 @@ void choose_shapes(Plan &p) {
     if (p.mode == CGTP_UVW) {
         mix_tables(p);
         split_uvw(p, p.fwd);
+        const size_t lds = uvw_mma_lds_bytes(p);
+        p.uvw_mma = p.tune.umma && lds > 0 && lds <= kUvwMmaMaxLds;
         return;
     }
     split(p, p.fwd, 0);

@@ -838,6 +838,42 @@ def test_uvw_conv_small(B, torch, k):
     assert_close(out.cpu().numpy(), ref, "bf16", f"uvw small {k}")
 
 
+@pytest.mark.parametrize("k", range(len(UVW_SMALL)))
+def test_uvw_matrix_core_path_tensors(B, torch, k, monkeypatch):
+    """The optional path-tensor kernel that contracts each node's gathered x
+    rows with its edges' coupled SH on the matrix cores (tuning switch umma=1;
+    the coupled SH enter the products rounded to bf16), conv and single TP."""
+    monkeypatch.setenv("CGTP_TUNE", "umma=1")
+    plan, prob = _uvw_case(B, k)
+    assert "cgtp_xs_place" in plan.source()
+    g = W.molecule_batch(n_graphs=5, n_atoms=9, cutoff=5.0, seed=60 + k)   # rows of up to 8 edges
+    G = GraphArrays(g.src, g.dst, g.n_nodes)
+    rng = np.random.default_rng(70 + k)
+    x = W.normal(rng, (g.n_nodes, prob.dim1), "bf16")
+    sh = W.normal(rng, (G.E, prob.dim2), "bf16")
+    w = W.normal(rng, (prob.weight_numel,), "bf16")
+    d = G.dev(torch)
+    print(f"uvw matrix-core path tensors k={k}", flush=True)
+    out = B.cgtp_conv_forward(plan, to_dev(torch, x, "bf16"), to_dev(torch, sh[G.perm], "bf16"),
+                              to_dev(torch, w, "bf16"), d["src"], d["dst_row_ptr"])
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), prob.conv_forward(x, sh, w, g.src, g.dst, g.n_nodes), "bf16", f"uvw mma {k}")
+    # plus a hub row of 40 more edges: three 16-edge chunks, the last one ragged
+    src = np.concatenate([g.src, rng.integers(0, g.n_nodes, 40)]).astype(np.int32)
+    dst = np.concatenate([g.dst, np.zeros(40)]).astype(np.int32)
+    sh2 = W.normal(rng, (len(src), prob.dim2), "bf16")
+    G2 = GraphArrays(src, dst, g.n_nodes)
+    d2 = G2.dev(torch)
+    out2 = B.cgtp_conv_forward(plan, to_dev(torch, x, "bf16"), to_dev(torch, sh2[G2.perm], "bf16"),
+                               to_dev(torch, w, "bf16"), d2["src"], d2["dst_row_ptr"])
+    torch.cuda.synchronize()
+    assert_close(out2.cpu().numpy(), prob.conv_forward(x, sh2, w, src, dst, g.n_nodes), "bf16", f"uvw mma hub {k}")
+    y = W.normal(rng, (23, prob.dim2), "bf16")
+    out3 = B.cgtp_forward(plan, to_dev(torch, x[:23], "bf16"), to_dev(torch, y, "bf16"), to_dev(torch, w, "bf16"))
+    torch.cuda.synchronize()
+    assert_close(out3.cpu().numpy(), prob.tp_forward(x[:23], y, w), "bf16", f"uvw mma single {k}")
+
+
 def test_uvw_single_tp(B, torch):
     plan, prob = _uvw_case(B, 0)
     rng = np.random.default_rng(77)
