@@ -120,11 +120,12 @@ def _check(rc: int):
 
 
 def _ptr(t):
+    # a plain int: ctypes converts it for c_void_p arguments
     if t is None:
         return None
     if not t.is_contiguous():
         raise ValueError("tensors passed to cgtp must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 def _want(plan, **tensors):
@@ -149,10 +150,12 @@ def _want(plan, **tensors):
 def _stream(stream=None, like=None):
     """Stream handle: the given stream, else torch's current stream on the
     tensors' device (host tensors: the NULL stream, for argument checks)."""
-    if stream is None and like is not None and not like.is_cuda:
-        return ctypes.c_void_p(None)
+    if stream is None and like is not None:
+        if not like.is_cuda:
+            return None
+        return torch._C._cuda_getCurrentRawStream(like.device.index)
     s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return s.cuda_stream
 
 
 # ---------------------------------------------------------------------------
@@ -231,6 +234,8 @@ def cgtp_plan(irreps_in1, irreps_in2, irreps_out, paths=None, mode="uvu", dtype=
 # execution
 # ---------------------------------------------------------------------------
 def cgtp_forward_workspace_bytes(plan: Plan, n_items: int) -> int:
+    if plan.mode == "uvu":
+        return 0   # uvu forwards take no workspace
     b = ctypes.c_size_t()
     _check(lib().cgtp_forward_workspace_bytes(plan.handle, n_items, ctypes.byref(b)))
     return b.value
