@@ -96,19 +96,16 @@ struct BwdOut {
     bool keep_parts = false;  // leave the per-unit y-gradient partials in the workspace
 };
 
-// workspace layout of the backward calls: x-messages [E][dim1] in source
-// order, SH-gradient parts [units][E][dim2], message row of each edge [E]
+// workspace layout of the backward calls: x-messages [E][dim1] in the edges'
+// (destination) order, gathered through src_perm by the segment sums;
+// SH-gradient parts [units][E][dim2]; per-edge force vectors [E][3]
 int parts_units(const Plan &p) { return std::max(1, std::max(p.bwd.n_units, p.fb.n_units)); }
 char *ws_parts(const Plan &p, char *ws, int64_t n_edges) {
     return ws + align256((size_t)n_edges * p.dim1 * out_bytes(p.dtype));
 }
-int32_t *ws_mrow(const Plan &p, char *ws, int64_t n_edges) {
-    return (int32_t *)(ws_parts(p, ws, n_edges) +
-                       align256((size_t)parts_units(p) * n_edges * p.dim2 * out_bytes(p.dtype)));
-}
 // per-edge force vectors [E][3] of the backward with forces
 char *ws_force(const Plan &p, char *ws, int64_t n_edges) {
-    return (char *)ws_mrow(p, ws, n_edges) + align256((size_t)n_edges * sizeof(int32_t));
+    return ws_parts(p, ws, n_edges) + align256((size_t)parts_units(p) * n_edges * p.dim2 * out_bytes(p.dtype));
 }
 
 int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
@@ -116,7 +113,6 @@ int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const in
             BwdOut o, char *ws, hipStream_t s, const void *vec = nullptr, const int32_t *vperm = nullptr) {
     void *m = ws;
     char *parts = ws_parts(p, ws, n_edges);
-    const int32_t *mrow = ws_mrow(p, ws, n_edges);
     const bool fused = o.fwd != nullptr && !o.fb;   // the double backward's y term
     const bool fb = o.fb;
     const KernelShape &ks = fused ? p.dbl : fb ? p.fb : p.bwd;
@@ -143,11 +139,10 @@ int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const in
     long long n = n_nodes, ne = n_edges;
     int graph = 1;
     void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&order,
-                    (void *)&vec, (void *)&vperm, (void *)&g_out, &gw, &m, &third, (void *)&mrow, &n, &ne, &graph,
-                    &flags};
+                    (void *)&vec, (void *)&vperm, (void *)&g_out, &gw, &m, &third, &n, &ne, &graph, &flags};
     void *args_fb[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&order,
-                       (void *)&vec, (void *)&vperm, (void *)&g_out, &gw, &m, &third, &fourth, (void *)&mrow, &n, &ne,
-                       &graph, &flags};
+                       (void *)&vec, (void *)&vperm, (void *)&g_out, &gw, &m, &third, &fourth, &n, &ne, &graph,
+                       &flags};
     const int64_t ipw = ks.items_per_wave;
     const bool full = fused ? ((p.tune.full & 2) && flags == dbl_full_flags(p))
                       : fb  ? ((p.tune.full & 4) && flags == fb_full_flags(p))
@@ -483,8 +478,7 @@ int cgtp_conv_workspace_bytes(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges
     const Plan &p = plan->p;
     const size_t eb = out_bytes(p.dtype);
     *bytes = align256((size_t)n_edges * p.dim1 * eb) +
-             align256((size_t)parts_units(p) * n_edges * p.dim2 * eb) +
-             align256((size_t)n_edges * sizeof(int32_t)) + align256((size_t)n_edges * 3 * eb) + 256;
+             align256((size_t)parts_units(p) * n_edges * p.dim2 * eb) + align256((size_t)n_edges * 3 * eb) + 256;
     return CGTP_OK;
 }
 
@@ -533,7 +527,6 @@ static int conv_backward_impl(cgtp_plan_t plan, const void *x, const void *sh, c
         out = nullptr;
     }
     char *ws = (char *)workspace;
-    if (g_x && (rc = launch_invert_perm(src_perm, n_edges, ws_mrow(p, ws, n_edges), s))) return rc;
     BwdOut o;
     o.fwd = out;
     o.fb = out != nullptr;
@@ -549,7 +542,7 @@ static int conv_backward_impl(cgtp_plan_t plan, const void *x, const void *sh, c
     }
     rc = run_bwd(p, x, sh, w, src, dst_row_ptr, node_order, g_out, n_nodes, n_edges, o, ws, s, vec, vperm);
     if (rc) return rc;
-    if (g_x && (rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, nullptr, n_nodes, p.dim1, g_x, 0, s)))
+    if (g_x && (rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, src_perm, n_nodes, p.dim1, g_x, 0, s)))
         return rc;
     if (F) {
         const int units = (out ? p.fb : p.bwd).n_units;
@@ -629,9 +622,6 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
     const int64_t E = n_edges;
     bool wrote_g = false, wrote_sh = false, wrote_w = false, wrote_m = false;
-    if (d_x && E > 0 && (gg_sh || gg_w) &&
-        (rc = launch_invert_perm(src_perm, E, ws_mrow(p, (char *)workspace, E), s)))
-        return rc;
     if (E > 0) {
         // y term, one pass: d_g_out += f(x, gg_sh, w), d_x += fx*(g; gg_sh, w),
         // d_w += fw*(g; x, gg_sh)
@@ -693,7 +683,7 @@ int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, c
     }
     if (d_g_out && !wrote_g && (rc = launch_zero(p.dtype, d_g_out, n_nodes * p.dim3, s))) return rc;
     if (d_x) {
-        if (wrote_m) rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, nullptr, n_nodes, p.dim1, d_x, 0, s);
+        if (wrote_m) rc = launch_segment_sum_rows(p.dtype, workspace, src_row_ptr, src_perm, n_nodes, p.dim1, d_x, 0, s);
         else rc = launch_zero(p.dtype, d_x, n_nodes * p.dim1, s);
         if (rc) return rc;
     }

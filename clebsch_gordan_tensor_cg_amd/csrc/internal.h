@@ -189,7 +189,6 @@ int launch_zero(cgtp_dtype dt, void *p, int64_t n, hipStream_t s);
 int launch_sh_forces(int lmax, cgtp_dtype dt, const void *vec, const int32_t *perm, const void *g_sh, int n_parts,
                      int64_t part_stride, const int32_t *dst_row_ptr, const int32_t *src_row_ptr,
                      const int32_t *src_perm, int64_t n_nodes, int64_t n_edges, void *F, void *v, hipStream_t s);
-int launch_invert_perm(const int32_t *perm, int64_t n, int32_t *inv, hipStream_t s);
 // out[item][off3 + w*d3 + k] (=|+=) sum_K T[(item*d3 + k)*K + kk] W_b3[kk][w]
 // channel mixing of every output block of a uvw layer (T: path tensors)
 int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items, void *out, int accumulate,

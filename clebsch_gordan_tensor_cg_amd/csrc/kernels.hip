@@ -122,12 +122,6 @@ __global__ void k_sum_parts(const T *__restrict__ parts, int n_parts, int64_t n,
     }
 }
 
-// inv[perm[k]] = k; perm is a permutation of [0, n)
-__global__ void k_invert_perm(const int32_t *__restrict__ perm, int64_t n, int32_t *__restrict__ inv) {
-    for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x)
-        inv[perm[k]] = (int32_t)k;
-}
-
 // ---------------------------------------------------------------------------
 // CSR build
 // ---------------------------------------------------------------------------
@@ -1296,13 +1290,6 @@ int launch_sh_forces(int lmax, cgtp_dtype dt, const void *vec, const int32_t *pe
     return hip_check(hipGetLastError(), "node force launch");
 }
 
-int launch_invert_perm(const int32_t *perm, int64_t n, int32_t *inv, hipStream_t s) {
-    if (n <= 0) return CGTP_OK;
-    unsigned g = grid_for(n);
-    if (g > 65536) g = 65536;
-    CGTP_LAUNCH("k_invert_perm", s, k_invert_perm, dim3(g), dim3(kBlock), 0, s, perm, n, inv);
-    return hip_check(hipGetLastError(), "invert perm launch");
-}
 
 int launch_zero(cgtp_dtype dt, void *p, int64_t n, hipStream_t s) {
     if (n <= 0) return CGTP_OK;
