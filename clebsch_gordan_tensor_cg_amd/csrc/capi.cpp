@@ -375,8 +375,8 @@ static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, c
     void *args[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, (void *)&order, (void *)&vec,
                     (void *)&vperm, (void *)&radial, &ws, &n, &graph};
     const int64_t ipw = p.fwd.items_per_wave;
-    // the matrix-core form: one workgroup of four wavefronts per item
-    int rc = p.uvw_mma ? launch(p.k_fwd, "cgtp_fwd", n_items, s, args, 256)
+    // the matrix-core form: one workgroup of four wavefronts per (item, input-1 block)
+    int rc = p.uvw_mma ? launch(p.k_fwd, "cgtp_fwd", n_items * p.uvw_mma_groups, s, args, 256)
                        : launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
     if (rc) return rc;
     int acc = 0;

@@ -110,7 +110,8 @@ struct Plan {
     std::vector<MixBlock> mix;     // uvw only
     std::vector<int> mix_of_path;  // uvw: index into mix for each path
     int64_t t_per_item = 0;        // uvw: T elements per item
-    bool uvw_mma = false;          // uvw: path tensors by the matrix-core kernel (256 threads per item)
+    bool uvw_mma = false;          // uvw: path tensors by the matrix-core kernel
+    int uvw_mma_groups = 0;        // its workgroups per item (input-1 blocks with paths), 256 threads each
     std::string source;
     std::string cache_key;
     bool cached = false;
@@ -142,7 +143,8 @@ inline int fb_full_flags(const Plan &p) { return 1 | 2 | 4 | (p.fb.n_units > 1 ?
 // uvw path tensors on the matrix cores: LDS bytes of one workgroup (0 when
 // the plan has no such kernel: radial weights, or no path)
 size_t uvw_mma_lds_bytes(const Plan &p);
-constexpr size_t kUvwMmaMaxLds = 96 * 1024;   // static LDS of one workgroup (two per CU)
+int uvw_mma_group_count(const Plan &p);
+constexpr size_t kUvwMmaMaxLds = 64 * 1024;   // static LDS of one workgroup
 
 // planner
 int parse_irreps(const char *s, std::vector<Irrep> &out, std::string &err);

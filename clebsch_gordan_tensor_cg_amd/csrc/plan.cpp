@@ -381,6 +381,7 @@ void choose_shapes(Plan &p) {
         split_uvw(p, p.fwd);
         const size_t lds = uvw_mma_lds_bytes(p);
         p.uvw_mma = p.tune.umma && lds > 0 && lds <= kUvwMmaMaxLds;
+        p.uvw_mma_groups = p.uvw_mma ? uvw_mma_group_count(p) : 0;
         return;
     }
     split(p, p.fwd, 0);

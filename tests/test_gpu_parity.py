@@ -840,12 +840,12 @@ def test_uvw_conv_small(B, torch, k):
 
 @pytest.mark.parametrize("k", range(len(UVW_SMALL)))
 def test_uvw_matrix_core_path_tensors(B, torch, k, monkeypatch):
-    """The optional path-tensor kernel that contracts each node's gathered x
-    rows with its edges' coupled SH on the matrix cores (tuning switch umma=1;
-    the coupled SH enter the products rounded to bf16), conv and single TP."""
+    """The path-tensor kernel that sums each node's outer products x_e (x) y_e
+    on the matrix cores and contracts the sum with the coupling once per node
+    (tuning switch umma), conv, a hub row and the single TP."""
     monkeypatch.setenv("CGTP_TUNE", "umma=1")
     plan, prob = _uvw_case(B, k)
-    assert "cgtp_xs_place" in plan.source()
+    assert "__builtin_amdgcn_mfma_f32_16x16x16bf16_1k" in plan.source()
     g = W.molecule_batch(n_graphs=5, n_atoms=9, cutoff=5.0, seed=60 + k)   # rows of up to 8 edges
     G = GraphArrays(g.src, g.dst, g.n_nodes)
     rng = np.random.default_rng(70 + k)
