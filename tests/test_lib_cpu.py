@@ -68,6 +68,26 @@ def test_generated_source_has_each_nonzero_once_per_channel_slot(B):
     assert len(re.findall(r"\ba0_\d+_\d+ = fma\(", fwd)) == nnz
 
 
+def test_uvw_matrix_core_source_contracts_each_nonzero_once(B, monkeypatch):
+    """The optional uvw kernel (tuning switch umma): the outer-product sums go
+    to the matrix cores, and the coupling is applied once per node with one
+    term per CG nonzero of every (path, v, k) column.  The default kernel has
+    no matrix-core code (its channel mixing is a library kernel)."""
+    a, b, c = "8x0+8x1+8x2", "1x0+1x1+1x2", "12x0+12x1+12x2"
+    plain = B.Plan(a, b, c, None, "uvw", "bf16", True, no_load=True).source()
+    assert "__builtin_amdgcn_mfma" not in plain
+    monkeypatch.setenv("CGTP_TUNE", "umma=1")
+    src = B.Plan(a, b, c, None, "uvw", "bf16", True, no_load=True).source()
+    assert "__builtin_amdgcn_mfma_f32_16x16x16bf16_1k" in src
+    nnz = 0
+    for l1 in range(3):
+        for l2 in range(3):
+            for l3 in range(abs(l1 - l2), min(l1 + l2, 2) + 1):
+                nnz += int((np.abs(oracle.real_cg(l1, l2, l3)) > 1e-14).sum())
+    # contraction terms "c * pr[j]", one per nonzero
+    assert len(re.findall(r"[-+] 0x[0-9a-fp.+-]+f \* pr\[\d+\]", src)) == nnz
+
+
 @pytest.mark.parametrize("args,code", [
     (("8x0e+", "1x0e", "8x0e"), -1),          # grammar
     (("8x0e", "1x0e", "8x1e"), -1),           # no allowed path
