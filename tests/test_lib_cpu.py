@@ -189,3 +189,16 @@ def test_sh_from_vectors_needs_sh_row_plan(B):
         B.cgtp_conv_forward_vec(p, torch.zeros(2, p.dim_in1), torch.ones(1, 3), None, torch.zeros(1, p.weight_numel),
                                 e, torch.tensor([0, 1, 1], dtype=torch.int32))
     assert ei.value.code in (-1, -2)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every call raises: there is no CPU fallback."""
+    from clebsch_gordan_tensor_cg_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "libcgtp.so"))
+    with pytest.raises(RuntimeError, match="is not built"):
+        binding.lib()
+    with pytest.raises(RuntimeError, match="is not built"):
+        binding.Plan("8x0e", "1x0e", "8x0e", no_load=True)
+    with pytest.raises(RuntimeError, match="is not built"):
+        binding.cgtp_csr_workspace_bytes(10, 10)
