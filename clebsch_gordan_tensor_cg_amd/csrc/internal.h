@@ -58,7 +58,7 @@ struct KernelShape {
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
 // of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, full, ubudget,
-// ucpl, umma)
+// ucpl, umma, depth_bwd)
 // overrides
 // them for experiments.
 struct Tuning {
@@ -72,6 +72,7 @@ struct Tuning {
     int cy_path = -1;        // uniform products per path (1) or per edge (0); -1: by dtype
     int depth = 0;           // edges of prefetch in flight (staged loop; 0: 3, or 2 for uvw layers
                              // without radial weights)
+    int depth_bwd = 0;       // the same for the backward, double backward and one-pass kernels (0: 2)
     bool bgy = false;        // backward via B_ij = sum_k R_ijk g_k (fewer FMAs, more VGPRs)
     int full = 7;            // dispatch to the folded-flag kernels: bit 0 backward, bit 1 double backward, bit 2 fused forward+backward
     int ubudget = 0;         // uvw accumulators per lane and unit (0: 32, or 144 with radial weights)

@@ -247,7 +247,7 @@ void split(Plan &p, KernelShape &ks, int kind) {
         for (int b : g.out_blocks) acc += p.out[b].dim();
         for (int b : g.in1_blocks) xin += p.in1[b].dim();
         for (int a : g.paths) wts += p.paths[a].mul2;
-        int per_ch = acc + (1 + std::max(1, p.tune.depth)) * (xin + wts);
+        int per_ch = acc + (1 + std::max(1, kind == 0 ? p.tune.depth : p.tune.depth_bwd)) * (xin + wts);
         if (kind >= 1) per_ch += xin;  // message accumulators
         if (kind >= 2) per_ch += acc;  // fused forward accumulators
         per_ch *= wide;
@@ -286,6 +286,7 @@ Tuning tuning_from_env() {
             else if (k == "stage") t.stage = v < 0 ? 0 : (v > 256 ? 256 : v);
             else if (k == "cypath") t.cy_path = v;
             else if (k == "depth") t.depth = v < 1 ? 1 : (v > 4 ? 4 : v);
+            else if (k == "depth_bwd") t.depth_bwd = v < 1 ? 1 : (v > 4 ? 4 : v);
             else if (k == "bgy") t.bgy = v != 0;
             else if (k == "full") t.full = v & 7;
             else if (k == "ubudget") t.ubudget = v < 1 ? 0 : v;
@@ -376,6 +377,9 @@ void choose_shapes(Plan &p) {
     const bool uvw_plain = p.mode == CGTP_UVW && p.radial_h == 0;
     if (p.tune.stage < 0) p.tune.stage = uvw_plain ? 32 : 64;
     if (p.tune.depth <= 0) p.tune.depth = uvw_plain ? 2 : 3;
+    // the backward kinds: two edges in flight (C4 one-pass and double backward
+    // 583.5 against 586.5 us with three; the forward is faster with three)
+    if (p.tune.depth_bwd <= 0) p.tune.depth_bwd = 2;
     if (p.mode == CGTP_UVW) {
         mix_tables(p);
         split_uvw(p, p.fwd);
