@@ -186,9 +186,9 @@ int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, 
  * row_ptr[n_nodes] = n_edges; check untrusted input with cgtp_validate_csr
  * first.  node_order [n_nodes] (may be NULL: natural order) is the order
  * in which destination rows are handed to the device, a permutation of
- * 0..n_nodes-1, normally from cgtp_node_order; it changes timing only,
- * never a result (an entry out of range leaves its slot idle, so a node
- * missing from it is not written).  workspace:
+ * 0..n_nodes-1, normally from cgtp_build_csr_order or cgtp_node_order;
+ * it changes timing only, never a result (an entry out of range leaves its
+ * slot idle, so a node missing from it is not written).  workspace:
  * cgtp_forward_workspace_bytes(n_nodes) (may be NULL for uvu plans). */
 int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
                       const int32_t *src, const int32_t *dst_row_ptr, const int32_t *node_order,
