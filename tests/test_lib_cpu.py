@@ -179,6 +179,29 @@ def test_graph_helper_sizes(B):
     assert B.lib().cgtp_sparse_attention_layout_bytes(-1, 5, ctypes.byref(b)) == -1
 
 
+def test_csr_argument_errors(B):
+    """cgtp_build_csr / cgtp_build_csr_order reject bad sizes, NULL buffers and
+    short workspaces before any launch (no GPU needed to reach the checks)."""
+    import ctypes
+    L = B.lib()
+    b = ctypes.c_size_t()
+    assert L.cgtp_csr_workspace_bytes(1000, 50, ctypes.byref(b)) == 0
+    need = b.value
+    key = (ctypes.c_int32 * 4)()
+    out = (ctypes.c_int32 * 64)()
+    ws = (ctypes.c_uint8 * max(need, 1))()
+    for fn, extra in ((L.cgtp_build_csr, ()), (L.cgtp_build_csr_order, (out,))):
+        # negative sizes
+        assert fn(key, None, -1, 50, out, out, None, None, *extra, ws, need, None) == -1
+        # keys but no perm
+        assert fn(key, None, 1000, 50, None, out, None, None, *extra, ws, need, None) == -1
+        # values wanted without a value array
+        assert fn(key, None, 1000, 50, out, out, None, out, *extra, ws, need, None) == -1
+        # workspace too small
+        assert fn(key, None, 1000, 50, out, out, None, None, *extra, ws, need - 1, None) == -1
+        assert "cgtp_build_csr" in L.cgtp_last_error().decode()
+
+
 def test_sh_from_vectors_needs_sh_row_plan(B):
     """cgtp_conv_forward_vec refuses plans whose input 2 is not one SH row
     before any device work (checked on the host)."""
