@@ -153,9 +153,14 @@ def _stream(stream=None, like=None):
     if stream is None and like is not None:
         if not like.is_cuda:
             return None
-        return torch._C._cuda_getCurrentRawStream(like.device.index)
+        if _raw_stream is not None:   # torch's cheap accessor for the current stream
+            return _raw_stream(like.device.index)
+        return torch.cuda.current_stream(like.device).cuda_stream
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 # ---------------------------------------------------------------------------
