@@ -45,7 +45,7 @@ class _Dims(ctypes.Structure):
 EXPORTS = [
     "cgtp_plan", "cgtp_plan_info", "cgtp_plan_paths", "cgtp_plan_coupling", "cgtp_plan_source",
     "cgtp_plan_destroy", "cgtp_forward_workspace_bytes", "cgtp_forward", "cgtp_conv_forward",
-    "cgtp_conv_workspace_bytes", "cgtp_conv_forward_vec", "cgtp_conv_backward_vec", "cgtp_conv_forward_radial", "cgtp_sparse_attention",
+    "cgtp_conv_workspace_bytes", "cgtp_conv_forward_vec", "cgtp_conv_backward_vec", "cgtp_conv_forward_radial", "cgtp_sparse_attention", "cgtp_sparse_attention_rows",
     "cgtp_conv_forward_backward", "cgtp_conv_forward_backward_vec",
     "cgtp_sparse_attention_layout_bytes", "cgtp_sparse_attention_prepare",
     "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_csr_workspace_bytes", "cgtp_build_csr",
@@ -82,6 +82,7 @@ def lib():
             "cgtp_node_order_workspace_bytes": [i64, vp],
             "cgtp_conv_forward_radial": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
             "cgtp_sparse_attention": [i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, i64, i64, vp, sz, vp, vp],
+            "cgtp_sparse_attention_rows": [i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp],
             "cgtp_sparse_attention_layout_bytes": [i64, i64, vp],
             "cgtp_sparse_attention_prepare": [vp, vp, i64, i64, i64, vp, sz, vp],
             "cgtp_conv_forward_vec": [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
@@ -478,6 +479,22 @@ def cgtp_sparse_attention(q, k, v, row_ptr, n_edges: int, layout, scale=None, ou
         out = torch.empty(n_rows, H, D, dtype=torch.float32, device=q.device)
     _check(lib().cgtp_sparse_attention(DTYPES["bf16"], H, D, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
                                        n_rows, n_edges, _ptr(layout), layout.numel(), _ptr(out), _stream(stream, q)))
+    return out
+
+
+def cgtp_sparse_attention_rows(q, k, v, col, row_ptr, scale=None, out=None, stream=None):
+    """The same attention in row form, straight from the CSR (col, row_ptr):
+    q [n_rows][H][D], k and v [n_cols][H][D] (bf16); returns float32
+    [n_rows][H][D]."""
+    n_rows = row_ptr.shape[0] - 1
+    H, D = q.shape[1], q.shape[2]
+    if scale is None:
+        scale = 1.0 / D ** 0.5
+    if out is None:
+        out = torch.empty(n_rows, H, D, dtype=torch.float32, device=q.device)
+    _check(lib().cgtp_sparse_attention_rows(DTYPES["bf16"], H, D, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(col),
+                                            _ptr(row_ptr), n_rows, k.shape[0], col.shape[0], _ptr(out),
+                                            _stream(stream, q)))
     return out
 
 

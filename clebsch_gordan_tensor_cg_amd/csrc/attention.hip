@@ -298,6 +298,105 @@ int hip_ok(hipError_t e, const char *what) {
     return set_error(CGTP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// Row form: one group of D/4 lanes per (row, head), four head dimensions per
+// lane (one 8-byte load of k and of v per edge), the row's edges walked in
+// order with an online softmax in FP32.  For graphs whose 16-row windows
+// share few columns (random numbering: about one row per distinct column),
+// the window kernel's 16 x 16 tiles are nearly empty; here every lane does
+// useful work, k and v rows are read once per edge from the caches, and no
+// layout is needed.  P is not rounded (FP32 throughout after the bf16 loads).
+// LPH: lanes per head (D / 4, a power of two).  A wavefront holds 64 / LPH
+// (row, head) slots: several heads of one row, or several rows when the
+// heads do not fill it.
+template <int LPH>
+__global__ void __launch_bounds__(256) k_sparse_attention_rows_bf16(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ col, const int32_t *__restrict__ row_ptr, int64_t n_rows, int64_t n_cols, int H,
+    float scale, float *__restrict__ out) {
+    constexpr int D = 4 * LPH, SLOTS = 64 / LPH;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = blockIdx.x * (int64_t)(blockDim.x / 64) + (threadIdx.x >> 6);
+    const int slot = lane / LPH, sub = lane % LPH;
+    int64_t row;
+    int head;
+    if (H >= SLOTS) {   // several wavefronts per row
+        const int64_t wpr = (H + SLOTS - 1) / SLOTS;
+        row = wave / wpr;
+        head = (int)(wave % wpr) * SLOTS + slot;
+    } else {            // several rows per wavefront
+        const int rpw = SLOTS / H;
+        const int r = slot / H;
+        row = wave * rpw + r;
+        head = slot % H;
+        if (r >= rpw) row = n_rows;   // slots past the last whole row stay idle
+    }
+    const bool active = row < n_rows && head < H;
+    int beg = 0, end = 0;
+    if (active) {
+        beg = row_ptr[row];
+        end = row_ptr[row + 1];
+    }
+    // the wavefront walks as many edges as its longest row
+    int len = end - beg;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) len = max(len, __shfl_xor(len, off, 64));
+    float qv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (active) {
+        const uint2 qq = *(const uint2 *)(q + (row * H + head) * (int64_t)D + 4 * sub);
+        qv[0] = __uint_as_float(qq.x << 16) * scale;
+        qv[1] = __uint_as_float(qq.x & 0xffff0000u) * scale;
+        qv[2] = __uint_as_float(qq.y << 16) * scale;
+        qv[3] = __uint_as_float(qq.y & 0xffff0000u) * scale;
+    }
+    float m = -INFINITY, l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    constexpr int U = 4;   // edges whose operands are loaded together
+    for (int t0 = 0; t0 < len; t0 += U) {
+        uint2 kk[U], vv[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = beg + t0 + u;
+            const int c = t < end ? col[t] : -1;
+            ok[u] = c >= 0 && c < n_cols;
+            const int64_t at = ((int64_t)(ok[u] ? c : 0) * H + (active ? head : 0)) * D + 4 * sub;
+            kk[u] = ok[u] ? *(const uint2 *)(k + at) : make_uint2(0u, 0u);
+            vv[u] = ok[u] ? *(const uint2 *)(v + at) : make_uint2(0u, 0u);
+        }
+        // the batch's scores, then one running-max update and one rescale for
+        // the whole batch (invalid edges score -inf and weigh 0)
+        float sc[U];
+        float mb = m;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float s = qv[0] * __uint_as_float(kk[u].x << 16) + qv[1] * __uint_as_float(kk[u].x & 0xffff0000u) +
+                      qv[2] * __uint_as_float(kk[u].y << 16) + qv[3] * __uint_as_float(kk[u].y & 0xffff0000u);
+#pragma unroll
+            for (int off = 1; off < LPH; off <<= 1) s += __shfl_xor(s, off, 64);
+            sc[u] = ok[u] ? s : -INFINITY;   // the whole head group agrees on ok
+            mb = fmaxf(mb, sc[u]);
+        }
+        if (mb == -INFINITY) continue;   // no valid edge yet in this head group
+        const float corr = __expf(m - mb);
+        l *= corr;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] *= corr;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float p = __expf(sc[u] - mb);   // 0 for an invalid edge
+            l += p;
+            acc[0] += p * __uint_as_float(vv[u].x << 16);
+            acc[1] += p * __uint_as_float(vv[u].x & 0xffff0000u);
+            acc[2] += p * __uint_as_float(vv[u].y << 16);
+            acc[3] += p * __uint_as_float(vv[u].y & 0xffff0000u);
+        }
+        m = mb;
+    }
+    if (!active) return;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float4 o = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    *(float4 *)(out + (row * H + head) * (int64_t)D + 4 * sub) = o;
+}
+
 }  // namespace
 }  // namespace cgtp
 
@@ -369,6 +468,48 @@ int cgtp_sparse_attention(cgtp_dtype dtype, int32_t n_heads, int32_t head_dim, f
 #undef CGTP_ATTN_CASE
     }
     return hip_ok(hipGetLastError(), "sparse attention launch");
+}
+
+
+int cgtp_sparse_attention_rows(cgtp_dtype dtype, int32_t n_heads, int32_t head_dim, float scale, const void *q,
+                               const void *k, const void *v, const int32_t *col, const int32_t *row_ptr,
+                               int64_t n_rows, int64_t n_cols, int64_t n_edges, void *out, cgtp_stream_t stream) {
+    clear_error();
+    if (dtype != CGTP_BF16_F32ACC)
+        return set_error(CGTP_ERR_UNSUPPORTED, "cgtp_sparse_attention_rows: bf16 inputs (CGTP_BF16_F32ACC) only");
+    if (n_heads < 1 || n_heads > 65535 ||
+        (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128))
+        return set_error(CGTP_ERR_INVALID_ARGUMENT,
+                         "cgtp_sparse_attention_rows: head_dim must be 16, 32, 64 or 128; n_heads 1..65535");
+    if (n_rows < 0 || n_cols < 0 || n_edges < 0 || n_rows > 0x7fffffffLL || n_edges > 0x7fffffffLL ||
+        n_cols > 0x7fffffffLL)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention_rows: sizes out of range");
+    if (n_rows == 0) return CGTP_OK;
+    if (!row_ptr || !out || (n_edges > 0 && (!q || !k || !v || !col)))
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention_rows: NULL buffer");
+    if ((((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v)) & 7 || ((uintptr_t)out) & 15)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT,
+                         "cgtp_sparse_attention_rows: q, k, v must be 8-byte and out 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const int lph = head_dim / 4, slots = 64 / lph;
+    const int64_t waves = n_heads >= slots ? n_rows * ((n_heads + slots - 1) / slots)
+                                           : (n_rows + slots / n_heads - 1) / (slots / n_heads);
+    const int64_t blocks = (waves + 3) / 4;
+    if (blocks > 0x7fffffffLL) return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sparse_attention_rows: grid too large");
+    switch (lph) {
+#define CGTP_ROWS_CASE(L)                                                                                         \
+    case L:                                                                                                        \
+        CGTP_LAUNCH("k_sparse_attention_rows_bf16", s, k_sparse_attention_rows_bf16<L>, dim3((unsigned)blocks),     \
+                    dim3(256), 0, s, (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, col, row_ptr,    \
+                    n_rows, n_cols, (int)n_heads, scale, (float *)out);                                            \
+        break;
+        CGTP_ROWS_CASE(4)
+        CGTP_ROWS_CASE(8)
+        CGTP_ROWS_CASE(16)
+        CGTP_ROWS_CASE(32)
+#undef CGTP_ROWS_CASE
+    }
+    return hip_ok(hipGetLastError(), "sparse attention (rows) launch");
 }
 
 }  // extern "C"

@@ -386,6 +386,22 @@ int cgtp_sparse_attention(cgtp_dtype dtype, int32_t n_heads, int32_t head_dim, f
                           int64_t n_rows, int64_t n_edges, const void *layout, size_t layout_bytes,
                           void *out, cgtp_stream_t stream);
 
+/* The same attention ([F3S]'s three sparse steps fused, scores on the chip)
+ * in row form, straight from the CSR (col [n_edges], row_ptr [n_rows+1]; no
+ * prepare call): each (row, head) is taken by head_dim/4 lanes, four head
+ * dimensions per lane, and the row's edges are walked with an online
+ * softmax; products, softmax and sums in FP32 (the probabilities are not
+ * rounded).  Meant for graphs whose rows share few columns within 16-row
+ * windows (random numbering), where the matrix-core tiles of
+ * cgtp_sparse_attention stay nearly empty.  dtype CGTP_BF16_F32ACC; head_dim
+ * 16, 32, 64 or 128; q, k, v 8-byte aligned, out 16-byte aligned; edges
+ * whose column lies outside [0, n_cols) are ignored; rows without edges are
+ * zero.  Asynchronous on the stream. */
+int cgtp_sparse_attention_rows(cgtp_dtype dtype, int32_t n_heads, int32_t head_dim, float scale,
+                               const void *q, const void *k, const void *v, const int32_t *col,
+                               const int32_t *row_ptr, int64_t n_rows, int64_t n_cols, int64_t n_edges,
+                               void *out, cgtp_stream_t stream);
+
 /* Checks on the device that row_ptr is a monotone CSR over n_edges and that
  * every index in idx[n_edges] (may be NULL) lies in [0, n_idx_range).
  * Synchronises the stream.  Returns CGTP_OK or CGTP_ERR_GRAPH.
