@@ -308,6 +308,29 @@ int hip_ok(hipError_t e, const char *what) {
 // LPH: lanes per head (D / 4, a power of two).  A wavefront holds 64 / LPH
 // (row, head) slots: several heads of one row, or several rows when the
 // heads do not fill it.
+// Sum over each aligned group of LPH lanes, every lane receiving the sum:
+// DPP lane moves (quad permutes, then the half-row and row mirrors) instead
+// of LDS permutes; only the step across 16-lane rows (LPH = 32) shuffles.
+__device__ __forceinline__ float dpp_add(float x, int ctrl_tag) {
+    int v = __float_as_int(x);
+    switch (ctrl_tag) {   // the control must be a constant of the instruction
+        case 0: v = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true); break;    // quad_perm [1,0,3,2]
+        case 1: v = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true); break;    // quad_perm [2,3,0,1]
+        case 2: v = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true); break;   // row_half_mirror
+        default: v = __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true); break;  // row_mirror
+    }
+    return x + __int_as_float(v);
+}
+template <int LPH>
+__device__ __forceinline__ float head_sum(float s) {
+    s = dpp_add(s, 0);
+    s = dpp_add(s, 1);
+    if constexpr (LPH >= 8) s = dpp_add(s, 2);
+    if constexpr (LPH >= 16) s = dpp_add(s, 3);
+    if constexpr (LPH >= 32) s += __shfl_xor(s, 16, 64);
+    return s;
+}
+
 template <int LPH>
 __global__ void __launch_bounds__(256) k_sparse_attention_rows_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -370,8 +393,7 @@ __global__ void __launch_bounds__(256) k_sparse_attention_rows_bf16(
         for (int u = 0; u < U; ++u) {
             float s = qv[0] * __uint_as_float(kk[u].x << 16) + qv[1] * __uint_as_float(kk[u].x & 0xffff0000u) +
                       qv[2] * __uint_as_float(kk[u].y << 16) + qv[3] * __uint_as_float(kk[u].y & 0xffff0000u);
-#pragma unroll
-            for (int off = 1; off < LPH; off <<= 1) s += __shfl_xor(s, off, 64);
+            s = head_sum<LPH>(s);
             sc[u] = ok[u] ? s : -INFINITY;   // the whole head group agrees on ok
             mb = fmaxf(mb, sc[u]);
         }
