@@ -225,3 +225,18 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         binding.Plan("8x0e", "1x0e", "8x0e", no_load=True)
     with pytest.raises(RuntimeError, match="is not built"):
         binding.cgtp_csr_workspace_bytes(10, 10)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark runs on one GPU: asked for more it exits with a message
+    and a non-zero status before it touches any device."""
+    import json
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    r = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"], cwd=root, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus_requested"] == 2 and "one GPU" in msg["error"]
