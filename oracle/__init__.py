@@ -79,6 +79,8 @@ def lib():
         L.orc_force_loss_cotangent.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
         L.orc_csr.restype = i32
         L.orc_csr.argtypes = [vp, i64, i64, vp, vp]
+        L.orc_set_threads.restype = i32
+        L.orc_set_threads.argtypes = [i32]
         L.orc_sparse_attention.restype = i32
         L.orc_sparse_attention.argtypes = [i64, i64, i64, vp, vp, i32, i32, d, vp, vp, vp, vp]
         _lib = L
@@ -283,6 +285,12 @@ class Problem:
 # --------------------------------------------------------------------------
 # Stand-alone pieces
 # --------------------------------------------------------------------------
+
+def set_threads(n: int) -> int:
+    """OpenMP threads of the oracle's loops (0 keeps the current count);
+    returns the count in effect.  Timing only: results do not change."""
+    return int(lib().orc_set_threads(int(n)))
+
 
 def cg_complex(j1, m1, j2, m2, J, M) -> float:
     return lib().orc_cg_complex(j1, m1, j2, m2, J, M)

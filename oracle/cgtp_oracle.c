@@ -34,6 +34,22 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Thread count of the loops below (timing only; results do not depend on
+ * it: every output element is summed by one thread in a fixed order).
+ * Returns the count in effect. */
+int orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
 
 #define ORC_LMAX 12
 

@@ -169,6 +169,59 @@ def test_backward_adjoint_and_autograd(k):
     np.testing.assert_allclose(gw, aw.numpy(), atol=1e-11)
 
 
+@pytest.mark.parametrize("k", range(4))
+def test_tp_backward_adjoint_and_autograd(k):
+    """The single product's adjoint (per-item weights for problems 0-2,
+    shared weights for problem 3) against torch CPU autograd of the dense
+    einsum form, the trilinearity identities, and item independence."""
+    p = small_problems()[k]
+    B = 6
+    x, y, w = _inputs(p, B)
+    g = rng.standard_normal((B, p.dim3))
+    gx, gy, gw = p.tp_backward(x, y, w, g)
+    f = p.tp_forward(x, y, w)
+    s = (g * f).sum()
+    for a, b in ((gx, x), (gy, y), (gw, w)):
+        assert abs((a * b).sum() - s) < 1e-10 * (1 + abs(s))
+    xt, yt, wt = (torch.from_numpy(a).requires_grad_() for a in (x, y, w))
+    out = DenseTP(p).forward(xt, yt, wt)
+    ax, ay, aw = torch.autograd.grad(out, (xt, yt, wt), torch.from_numpy(g))
+    np.testing.assert_allclose(gx, ax.numpy(), atol=1e-11)
+    np.testing.assert_allclose(gy, ay.numpy(), atol=1e-11)
+    np.testing.assert_allclose(gw, aw.numpy(), atol=1e-11)
+    # item b's gradients depend only on item b (per-item weights), and the
+    # shared-weight gradient is the sum of the items' own gradients
+    for b in (0, B - 1):
+        wb = w if p.shared_weights else w[b:b + 1]
+        gxb, gyb, gwb = p.tp_backward(x[b:b + 1], y[b:b + 1], wb, g[b:b + 1])
+        np.testing.assert_allclose(gxb[0], gx[b], atol=1e-12)
+        np.testing.assert_allclose(gyb[0], gy[b], atol=1e-12)
+        if not p.shared_weights:
+            np.testing.assert_allclose(gwb[0], gw[b], atol=1e-12)
+    if p.shared_weights:
+        parts = sum(p.tp_backward(x[b:b + 1], y[b:b + 1], w, g[b:b + 1])[2] for b in range(B))
+        np.testing.assert_allclose(parts, gw, atol=1e-11)
+
+
+def test_tp_backward_finite_difference():
+    """Central differences of <g, f> for the C1 single product."""
+    p = c1_problem()
+    x, y, w = _inputs(p, 3)
+    g = rng.standard_normal((3, p.dim3))
+    gx, gy, gw = p.tp_backward(x, y, w, g)
+    L = lambda x_, y_, w_: (g * p.tp_forward(x_, y_, w_)).sum()
+    h = 1e-6
+    for arr, grad, which in ((x, gx, 0), (y, gy, 1), (w, gw, 2)):
+        for _ in range(6):
+            idx = tuple(rng.integers(0, s_) for s_ in arr.shape)
+            d = np.zeros_like(arr)
+            d[idx] = h
+            a_p, a_m = [x, y, w], [x, y, w]
+            a_p[which], a_m[which] = arr + d, arr - d
+            fd = (L(*a_p) - L(*a_m)) / (2 * h)
+            assert abs(fd - grad[idx]) < 1e-6 * (1 + abs(fd))
+
+
 def test_backward_finite_difference():
     p = small_problems()[1]
     n, src, dst = _tiny_graph()
