@@ -257,6 +257,64 @@ def cpu_baseline_conv(cfg, g, x_np, w_np, full_step: bool, frac: float):
                       f"(all nodes as sources), {dt_s:.1f} s, OpenMP threads={threads}"}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_single_thread(g, x_c2, w_c2, seed: int):
+    """The oracle on one thread: the C2 forward on the edges into the first
+    2 % of the nodes, and the C1 single product (1000 samples, repeated for
+    3 s).  Thread count set through the oracle's OpenMP runtime, restored
+    afterwards."""
+    import oracle
+    from clebsch_gordan_tensor_cg_amd import workloads as W
+    c2 = W.config("c2")
+    prob = oracle.Problem(c2.irreps_in1, c2.irreps_in2, c2.irreps_out, c2.mode, c2.paths)
+    n_s = max(1, g.n_nodes // 50)
+    mask = g.dst < n_s
+    E_s = int(mask.sum())
+    src, dst = g.src[mask], g.dst[mask]
+    vec = g.vec[mask].astype(np.float32)
+    w = w_c2[mask]
+    before = oracle.set_threads(0)
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        sh = oracle.spherical_harmonics(3, vec)
+        oracle.csr(dst, g.n_nodes)
+        prob.conv_forward(x_c2, sh, w, src, dst, g.n_nodes)
+        dt2 = time.perf_counter() - t0
+        c1 = W.config("c1")
+        p1 = oracle.Problem(c1.irreps_in1, c1.irreps_in2, c1.irreps_out, c1.mode, c1.paths)
+        rng = np.random.default_rng(seed)
+        n = c1.extra["batch"]
+        x = W.normal(rng, (n, p1.dim1), "f32")
+        y = W.normal(rng, (n, p1.dim2), "f32")
+        wc = W.normal(rng, (n, p1.weight_numel), "f32")
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 3.0:
+            p1.tp_forward(x, y, wc)
+            reps += 1
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(before)
+    return {"cores": 1,
+            "c2_fwd": {"value": E_s / dt2, "unit": "edges/s",
+                       "sample": f"csr+sh+fwd over the {E_s} edges into the first {n_s} of {g.n_nodes} nodes, "
+                                 f"{dt2:.1f} s"},
+            "c1": {"value": reps * n / dt1, "unit": "samples/s",
+                   "sample": f"{reps} repetitions of the {n}-sample forward, {dt1:.1f} s"}}
+
+
 def cpu_baseline_single(cfg, x, y, w):
     import oracle
     prob = oracle.Problem(cfg.irreps_in1, cfg.irreps_in2, cfg.irreps_out, cfg.mode, cfg.paths,
@@ -335,14 +393,14 @@ def bench_conv(args, torch, B, W):
     node_order = None if natural else order
     sh = torch.empty(E, plan.dim_in2, dtype=td, device=dev)
     out = torch.empty(N, plan.dim_out, dtype=od, device=dev)
-    nb_f = B.cgtp_forward_workspace_bytes(plan, N)
+    nb_f = B.cgtp_workspace_bytes(plan, N) if plan.mode == "uvw" else 0
     f_ws = B.workspace(nb_f, dev) if nb_f else None
     timer = Timer(torch)
     if full:
         g_out = torch.zeros(N, plan.dim_out, dtype=td, device=dev)
         g_out[:, torch.from_numpy(zero_e_columns(cfg.irreps_out)).to(dev)] = 1.0
-        ws = B.workspace(B.cgtp_conv_workspace_bytes(plan, N, E), dev)
-        fo_ws = B.workspace(B.cgtp_forces_workspace_bytes(E, dtype), dev)
+        ws = B.workspace(B.cgtp_workspace_bytes(plan, N, E), dev)
+        fo_ws = B.workspace(E * 3 * (8 if dtype == "f64" else 4), dev)
         g_x = torch.empty(N, plan.dim_in1, dtype=td, device=dev)
         g_sh = torch.empty(E, plan.dim_in2, dtype=td, device=dev)
         g_w = torch.empty(E, plan.weight_numel, dtype=td, device=dev)
@@ -379,27 +437,26 @@ def bench_conv(args, torch, B, W):
                                                              g_out, ws=ws, out=(g_x, None, g_w, F),
                                                              node_order=node_order))
         elif fused:
-            run("sh", lambda: B.cgtp_spherical_harmonics(lmax, vec, perm, dtype, out=sh))
+            run("sh", lambda: B.cgtp_sh(lmax, vec, perm, dtype, out=sh))
             run("conv_fb", lambda: B.cgtp_conv_forward_backward(plan, x, sh, w, src_s, rp, src_rp, src_perm, g_out,
                                                                 ws=ws, out=(out, g_x, g_sh, g_w),
                                                                 node_order=node_order))
-            run("forces", lambda: B.cgtp_sh_forces(lmax, vec, perm, g_sh, rp, src_rp, src_perm, dtype, ws=fo_ws,
-                                                   out=F))
+            run("forces", lambda: B.cgtp_sh_vjp_forces(lmax, vec, perm, g_sh, rp, src_rp, src_perm, dtype, ws=fo_ws,
+                                                       out=(None, F)))
         else:
-            run("sh", lambda: B.cgtp_spherical_harmonics(lmax, vec, perm, dtype, out=sh))
+            run("sh", lambda: B.cgtp_sh(lmax, vec, perm, dtype, out=sh))
             run("conv_fwd", lambda: B.cgtp_conv_forward(plan, x, sh, w, src_s, rp, out=out, ws=f_ws,
                                                         node_order=node_order))
             if not full:
                 return
-            run("conv_bwd", lambda: B.cgtp_conv_backward(plan, x, sh, w, src_s, dst_s, rp, src_rp, src_perm, g_out,
-                                                         ws=ws, out=(g_x, g_sh, g_w), node_order=node_order))
-            run("forces", lambda: B.cgtp_sh_forces(lmax, vec, perm, g_sh, rp, src_rp, src_perm, dtype, ws=fo_ws,
-                                                   out=F))
+            run("conv_bwd", lambda: B.cgtp_backward(plan, x, sh, w, src_s, rp, src_rp, src_perm, g_out,
+                                                    ws=ws, out=(g_x, g_sh, g_w), node_order=node_order))
+            run("forces", lambda: B.cgtp_sh_vjp_forces(lmax, vec, perm, g_sh, rp, src_rp, src_perm, dtype, ws=fo_ws,
+                                                       out=(None, F)))
         run("force_cot", lambda: B.cgtp_force_loss_sh_cotangent(lmax, vec, perm, src_s, dst_s, F, dtype, out=gg))
-        run("double_bwd", lambda: B.cgtp_conv_double_backward(plan, x, None if sh_in_conv else sh, w, src_s,
-                                                              dst_s, rp, src_rp, src_perm,
-                                                              g_out, None, gg, None, ws=ws,
-                                                              out=(d_g, d_x, None, d_w), node_order=node_order))
+        run("double_bwd", lambda: B.cgtp_double_backward(plan, x, None if sh_in_conv else sh, w, g_out, None, gg,
+                                                         None, src_s, rp, src_rp, src_perm, ws=ws,
+                                                         out=(d_g, d_x, None, d_w), node_order=node_order))
 
     ms, per_step, launch_mode, graph = time_steps(torch, args, lambda: step(False))
     # per-call durations: an eager pass with events between the calls
@@ -514,10 +571,59 @@ def bench_conv(args, torch, B, W):
         "kernels": kern,
         "call_ms": {k: round(v, 4) for k, v in kms.items()},
     }
+    if full and fused and sh_in_conv:
+        # the forward half of the metric on the same graph, inputs and CSR:
+        # the convolution forward alone (SH computed in the kernel), timed
+        # over its own K calls, with its own roofline
+        res["fwd"] = forward_leg(args, torch, B, plan, x, vec, perm, w, src_s, rp, out, node_order, N, E,
+                                 alg_bytes_conv_fwd(N, E, d1, d3, wn, eb, ob, wb, shb),
+                                 W.config("c2").name + (", bf16 weight storage" if bf16w else "") +
+                                 (", Morton node order" if args.morton else ""))
+        res["fwd_edges_per_s"] = res["fwd"]["value"]
     if not args.no_cpu_baseline:
         frac = {"c4": 0.25, "c2": 0.5, "c3": 0.02, "c5": 0.03}[name]
         res["cpu_baseline"] = cpu_baseline_conv(cfg, g, x_np, w_np, full, frac)
+        res["cpu_baseline"]["cpu_model"] = cpu_model()
+        res["cpu_baseline"]["host_cpus"] = os.cpu_count()
+        if "fwd" in res:
+            res["fwd"]["cpu_baseline"] = cpu_baseline_conv(cfg, g, x_np, w_np, False, 0.5)
+        if name in ("c4", "c2") and not bf16w and not args.all_parity:
+            res["cpu_baseline"]["single_thread"] = cpu_single_thread(g, x_np, w_np, args.seed)
     return res
+
+
+def forward_leg(args, torch, B, plan, x, vec, perm, w, src_s, rp, out, node_order, N, E, alg_bytes, workload):
+    """K forward calls (after W untimed ones) between HIP events, then the
+    per-launch durations of the forward kernel from the library's events."""
+    call = lambda: B.cgtp_conv_forward_vec(plan, x, vec, perm, w, src_s, rp, out=out, node_order=node_order)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record()
+    for i in range(args.steps):
+        call()
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    per = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    B.cgtp_timing_enable(True)
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    B.cgtp_timing_enable(False)
+    kt = [m for k, m in B.cgtp_timing_collect() if k == "cgtp_fwd"]
+    k_ms = float(np.mean(kt))
+    gbs = alg_bytes / (k_ms * 1e-3) / 1e9
+    return {"value": E / (ms * 1e-3), "unit": "edges/s", "ms_per_call": ms, "ms_per_call_median": float(np.median(per)),
+            "ms_per_call_min": float(np.min(per)), "calls": args.steps,
+            "config": {"workload": workload, "n_atoms": N, "n_edges": E,
+                       "step": "conv forward (SH from the edge vectors inside the kernel), CSR and node order "
+                               "built beforehand"},
+            "roofline": {"bound": "hbm", "kernel": "cgtp_fwd", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": counted_traffic(workload, "cgtp_fwd", plan.source()),
+                         "alg_bytes_per_launch": int(alg_bytes), "avg_ms": round(k_ms, 4)}}
 
 
 def bench_single(args, torch, B, W):
@@ -576,7 +682,7 @@ def bench_radial(args, torch, B, W):
     order = torch.empty(N, dtype=torch.int32, device=dev)
     csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), dev)
     out = torch.empty(N, plan.dim_out, dtype=torch.float32, device=dev)
-    f_ws = B.workspace(B.cgtp_forward_workspace_bytes(plan, N), dev)
+    f_ws = B.workspace(B.cgtp_workspace_bytes(plan, N), dev)
 
     def step():
         B.cgtp_build_csr_order(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s), order=order)

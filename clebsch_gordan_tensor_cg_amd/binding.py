@@ -44,13 +44,12 @@ class _Dims(ctypes.Structure):
 
 EXPORTS = [
     "cgtp_plan", "cgtp_plan_info", "cgtp_plan_paths", "cgtp_plan_coupling", "cgtp_plan_source",
-    "cgtp_plan_destroy", "cgtp_forward_workspace_bytes", "cgtp_forward", "cgtp_conv_forward",
-    "cgtp_conv_workspace_bytes", "cgtp_conv_forward_vec", "cgtp_conv_backward_vec", "cgtp_conv_forward_radial", "cgtp_sparse_attention", "cgtp_sparse_attention_rows",
-    "cgtp_conv_forward_backward", "cgtp_conv_forward_backward_vec",
-    "cgtp_sparse_attention_layout_bytes", "cgtp_sparse_attention_prepare",
-    "cgtp_conv_backward", "cgtp_conv_double_backward", "cgtp_csr_workspace_bytes", "cgtp_build_csr",
-    "cgtp_build_csr_order",
-    "cgtp_validate_csr", "cgtp_node_order_workspace_bytes", "cgtp_node_order", "cgtp_spherical_harmonics", "cgtp_forces_workspace_bytes", "cgtp_sh_forces",
+    "cgtp_plan_destroy", "cgtp_workspace_bytes", "cgtp_forward", "cgtp_tp_backward", "cgtp_conv_forward",
+    "cgtp_conv_forward_vec", "cgtp_conv_forward_radial", "cgtp_backward", "cgtp_conv_backward_vec",
+    "cgtp_conv_forward_backward", "cgtp_conv_forward_backward_vec", "cgtp_double_backward",
+    "cgtp_sparse_attention", "cgtp_sparse_attention_rows", "cgtp_sparse_attention_layout_bytes",
+    "cgtp_sparse_attention_prepare", "cgtp_csr_workspace_bytes", "cgtp_build_csr", "cgtp_build_csr_order",
+    "cgtp_validate_csr", "cgtp_node_order_workspace_bytes", "cgtp_node_order", "cgtp_sh", "cgtp_sh_vjp_forces",
     "cgtp_force_loss_sh_cotangent", "cgtp_timing_enable", "cgtp_timing_collect", "cgtp_last_error",
     "cgtp_version",
 ]
@@ -72,13 +71,13 @@ def lib():
             "cgtp_plan_paths": [vp, vp, i32],
             "cgtp_plan_coupling": [vp, i32, vp, i64],
             "cgtp_plan_source": [vp, vp, i64, vp],
-            "cgtp_forward_workspace_bytes": [vp, i64, vp],
+            "cgtp_workspace_bytes": [vp, i64, i64, vp],
             "cgtp_forward": [vp, vp, vp, vp, i64, vp, vp, sz, vp],
+            "cgtp_tp_backward": [vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp],
             "cgtp_conv_forward": [vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
-            "cgtp_conv_workspace_bytes": [vp, i64, i64, vp],
-            "cgtp_conv_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, sz, vp],
-            "cgtp_conv_double_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
-                                          vp, vp, vp, vp, vp, sz, vp],
+            "cgtp_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, sz, vp],
+            "cgtp_double_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+                                     vp, vp, vp, vp, vp, sz, vp],
             "cgtp_node_order_workspace_bytes": [i64, vp],
             "cgtp_conv_forward_radial": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
             "cgtp_sparse_attention": [i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, i64, i64, vp, sz, vp, vp],
@@ -96,9 +95,8 @@ def lib():
             "cgtp_build_csr": [vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
             "cgtp_build_csr_order": [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp],
             "cgtp_validate_csr": [vp, i64, i64, vp, i64, vp, vp],
-            "cgtp_spherical_harmonics": [i32, i32, vp, vp, i64, vp, vp],
-            "cgtp_forces_workspace_bytes": [i64, i32, vp],
-            "cgtp_sh_forces": [i32, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, sz, vp],
+            "cgtp_sh": [i32, i32, vp, vp, i64, vp, vp],
+            "cgtp_sh_vjp_forces": [i32, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp],
             "cgtp_force_loss_sh_cotangent": [i32, i32, vp, vp, vp, vp, vp, i64, vp, vp],
             "cgtp_timing_enable": [i32],
             "cgtp_timing_collect": [vp, vp, i32, vp],
@@ -122,30 +120,103 @@ def _check(rc: int):
 
 def _ptr(t):
     # a plain int: ctypes converts it for c_void_p arguments
-    if t is None:
-        return None
-    if not t.is_contiguous():
-        raise ValueError("tensors passed to cgtp must be contiguous")
-    return t.data_ptr()
+    return None if t is None else t.data_ptr()
 
 
-def _want(plan, **tensors):
-    """Argument check of the marshalling layer: feature-like tensors in the
-    plan's storage type, weight-like tensors in its weight storage type,
-    index tensors int32 (None entries are skipped)."""
-    for name, t in tensors.items():
+_I32 = torch.int32
+
+
+class _Args:
+    """Argument checks of the marshalling layer, done before any call into
+    the library: every tensor on the same CUDA device, contiguous, with the
+    exact shape and dtype the call's contract states.  Shapes and dtypes
+    are checked first (so that host tensors can exercise them), the device
+    last.  Index values (src in range, monotone row_ptr) are not read here:
+    cgtp_validate_csr checks untrusted graphs on the device."""
+
+    def __init__(self, call: str):
+        self.call = call
+        self.seen = []
+
+    def __call__(self, name, t, shape, dtype, optional=True):
         if t is None:
-            continue
-        if name in ("w", "gg_w"):
-            want = plan.weight_dtype
-        elif name in ("src", "dst", "dst_row_ptr", "src_row_ptr", "src_perm", "vec_perm", "node_order"):
-            want = torch.int32
-        elif name == "vec":
-            want = torch.float64 if plan.dtype == "f64" else torch.float32
-        else:
-            want = plan.torch_dtype
-        if t.dtype != want:
-            raise TypeError(f"{name}: expected {want}, got {t.dtype}")
+            if not optional:
+                raise ValueError(f"{self.call}: {name} is required")
+            return None
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.call}: {name} must be a torch.Tensor")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{self.call}: {name}: expected {dtype}, got {t.dtype}")
+        if shape is not None:
+            want = tuple(int(v) for v in shape)
+            if tuple(t.shape) != want:
+                raise ValueError(f"{self.call}: {name}: expected shape {want}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.call}: {name} must be contiguous")
+        self.seen.append((name, t))
+        return t
+
+    def device(self):
+        """All checked tensors on one CUDA device; returns it."""
+        dev = None
+        for name, t in self.seen:
+            if not t.is_cuda:
+                raise ValueError(f"{self.call}: {name} is on {t.device}; cgtp runs on the GPU only")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{self.call}: {name} is on {t.device}, other tensors on {dev}")
+        return dev
+
+
+def _feat(plan):
+    return plan.torch_dtype
+
+
+def _vec_dtype(plan):
+    return torch.float64 if plan.dtype == "f64" else torch.float32
+
+
+def _wshape(plan, n):
+    return (plan.weight_numel,) if plan.shared_weights else (n, plan.weight_numel)
+
+
+def _graph_args(A, plan, N, E, src, dst_row_ptr, node_order, src_row_ptr=None, src_perm=None):
+    A("src", src, (E,), _I32, optional=False)
+    A("dst_row_ptr", dst_row_ptr, (N + 1,), _I32, optional=False)
+    A("node_order", node_order, (N,), _I32)
+    A("src_row_ptr", src_row_ptr, (N + 1,), _I32)
+    A("src_perm", src_perm, (E,), _I32)
+
+
+def _vec_args(A, plan, E, vec, vec_perm):
+    A("vec_perm", vec_perm, (E,), _I32)
+    if vec is None:
+        raise ValueError(f"{A.call}: vec is required")
+    rows = vec.shape[0] if vec.dim() == 2 else -1
+    if vec_perm is None and rows != E:
+        raise ValueError(f"{A.call}: vec: expected shape ({E}, 3) without vec_perm, got {tuple(vec.shape)}")
+    A("vec", vec, (rows, 3), _vec_dtype(plan))
+
+
+def _out(A, name, t, shape, dtype, dev_like, want: bool):
+    """Caller-given output (checked) or a new one when wanted."""
+    if t is not None:
+        return A(name, t, shape, dtype)
+    if not want:
+        return None
+    return torch.empty(*shape, dtype=dtype, device=dev_like.device)
+
+
+def _ws(plan, N, E, ws, dev_like):
+    need = cgtp_workspace_bytes(plan, N, E)
+    if ws is None:
+        return workspace(need, dev_like.device)
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    if ws.device != dev_like.device:
+        raise ValueError(f"workspace is on {ws.device}, inputs on {dev_like.device}")
+    return ws
 
 
 def _stream(stream=None, like=None):
@@ -239,54 +310,92 @@ def cgtp_plan(irreps_in1, irreps_in2, irreps_out, paths=None, mode="uvu", dtype=
 # ---------------------------------------------------------------------------
 # execution
 # ---------------------------------------------------------------------------
-def cgtp_forward_workspace_bytes(plan: Plan, n_items: int) -> int:
-    if plan.mode == "uvu":
-        return 0   # uvu forwards take no workspace
+def cgtp_workspace_bytes(plan: Plan, n_items: int, n_edges: int = 0) -> int:
+    """Workspace bytes that serve every execution call of the plan on at most
+    n_items items and n_edges edges."""
     b = ctypes.c_size_t()
-    _check(lib().cgtp_forward_workspace_bytes(plan.handle, n_items, ctypes.byref(b)))
+    _check(lib().cgtp_workspace_bytes(plan.handle, n_items, n_edges, ctypes.byref(b)))
     return b.value
 
 
+def workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 256-byte-aligned (or better) blocks
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def _fwd_ws(plan, N, ws, like):
+    # uvu forwards take no workspace (and skip the size query)
+    if plan.mode == "uvu" and ws is None:
+        return None, 0
+    ws = _ws(plan, N, 0, ws, like)
+    return ws, ws.numel()
+
+
 def cgtp_forward(plan: Plan, x, y, w, out=None, ws=None, stream=None):
-    _want(plan, x=x, y=y, w=w)
+    A = _Args("cgtp_forward")
     B = x.shape[0]
-    if out is None:
-        out = torch.empty(B, plan.dim_out, dtype=plan.out_dtype, device=x.device)
-    nb = cgtp_forward_workspace_bytes(plan, B)
-    if ws is None and nb:
-        ws = workspace(nb, x.device)
-    _check(lib().cgtp_forward(plan.handle, _ptr(x), _ptr(y), _ptr(w), B, _ptr(out), _ptr(ws),
-                              ws.numel() if ws is not None else 0, _stream(stream, x)))
+    A("x", x, (B, plan.dim_in1), _feat(plan), optional=False)
+    A("y", y, (B, plan.dim_in2), _feat(plan), optional=False)
+    A("w", w, _wshape(plan, B), plan.weight_dtype, optional=False)
+    out = _out(A, "out", out, (B, plan.dim_out), plan.out_dtype, x, True)
+    A.device()
+    ws, nws = _fwd_ws(plan, B, ws, x)
+    _check(lib().cgtp_forward(plan.handle, _ptr(x), _ptr(y), _ptr(w), B, _ptr(out), _ptr(ws), nws,
+                              _stream(stream, x)))
     return out
 
 
+def cgtp_tp_backward(plan: Plan, x, y, w, g_out, need=("x", "y", "w"), ws=None, out=None, stream=None):
+    """Backward of cgtp_forward; returns (g_x, g_y, g_w), None where not
+    requested."""
+    A = _Args("cgtp_tp_backward")
+    B = x.shape[0]
+    A("x", x, (B, plan.dim_in1), _feat(plan), optional=False)
+    A("y", y, (B, plan.dim_in2), _feat(plan), optional=False)
+    A("w", w, _wshape(plan, B), plan.weight_dtype, optional=False)
+    A("g_out", g_out, (B, plan.dim_out), plan.out_dtype, optional=False)
+    o = out if out is not None else (None, None, None)
+    od = plan.out_dtype
+    g_x = _out(A, "g_x", o[0], (B, plan.dim_in1), od, x, out is None and "x" in need)
+    g_y = _out(A, "g_y", o[1], (B, plan.dim_in2), od, x, out is None and "y" in need)
+    g_w = _out(A, "g_w", o[2], (B, plan.weight_numel), od, x, out is None and "w" in need)
+    A.device()
+    ws = _ws(plan, B, 0, ws, x)
+    _check(lib().cgtp_tp_backward(plan.handle, _ptr(x), _ptr(y), _ptr(w), B, _ptr(g_out), _ptr(g_x), _ptr(g_y),
+                                  _ptr(g_w), _ptr(ws), ws.numel(), _stream(stream, x)))
+    return g_x, g_y, g_w
+
+
 def cgtp_conv_forward(plan: Plan, x, sh, w, src, dst_row_ptr, out=None, ws=None, stream=None, node_order=None):
-    _want(plan, x=x, sh=sh, w=w, src=src, dst_row_ptr=dst_row_ptr, node_order=node_order)
+    A = _Args("cgtp_conv_forward")
     N, E = x.shape[0], src.shape[0]
-    if out is None:
-        out = torch.empty(N, plan.dim_out, dtype=plan.out_dtype, device=x.device)
-    nb = cgtp_forward_workspace_bytes(plan, N)
-    if ws is None and nb:
-        ws = workspace(nb, x.device)
+    A("x", x, (N, plan.dim_in1), _feat(plan), optional=False)
+    A("sh", sh, (E, plan.dim_in2), _feat(plan), optional=False)
+    A("w", w, _wshape(plan, E), plan.weight_dtype, optional=False)
+    _graph_args(A, plan, N, E, src, dst_row_ptr, node_order)
+    out = _out(A, "out", out, (N, plan.dim_out), plan.out_dtype, x, True)
+    A.device()
+    ws, nws = _fwd_ws(plan, N, ws, x)
     _check(lib().cgtp_conv_forward(plan.handle, _ptr(x), _ptr(sh), _ptr(w), _ptr(src), _ptr(dst_row_ptr),
-                                   _ptr(node_order), N, E, _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
-                                   _stream(stream, x)))
+                                   _ptr(node_order), N, E, _ptr(out), _ptr(ws), nws, _stream(stream, x)))
     return out
 
 
 def cgtp_conv_forward_vec(plan: Plan, x, vec, vec_perm, w, src, dst_row_ptr, out=None, ws=None, stream=None,
                           node_order=None):
     """Convolution with the SH computed in the kernel from the edge vectors."""
-    _want(plan, x=x, vec=vec, vec_perm=vec_perm, w=w, src=src, dst_row_ptr=dst_row_ptr, node_order=node_order)
+    A = _Args("cgtp_conv_forward_vec")
     N, E = x.shape[0], src.shape[0]
-    if out is None:
-        out = torch.empty(N, plan.dim_out, dtype=plan.out_dtype, device=x.device)
-    nb = cgtp_forward_workspace_bytes(plan, N)
-    if ws is None and nb:
-        ws = workspace(nb, x.device)
+    A("x", x, (N, plan.dim_in1), _feat(plan), optional=False)
+    _vec_args(A, plan, E, vec, vec_perm)
+    A("w", w, _wshape(plan, E), plan.weight_dtype, optional=False)
+    _graph_args(A, plan, N, E, src, dst_row_ptr, node_order)
+    out = _out(A, "out", out, (N, plan.dim_out), plan.out_dtype, x, True)
+    A.device()
+    ws, nws = _fwd_ws(plan, N, ws, x)
     _check(lib().cgtp_conv_forward_vec(plan.handle, _ptr(x), _ptr(vec), _ptr(vec_perm), _ptr(w), _ptr(src),
-                                       _ptr(dst_row_ptr), _ptr(node_order), N, E, _ptr(out), _ptr(ws),
-                                       ws.numel() if ws is not None else 0, _stream(stream, x)))
+                                       _ptr(dst_row_ptr), _ptr(node_order), N, E, _ptr(out), _ptr(ws), nws,
+                                       _stream(stream, x)))
     return out
 
 
@@ -294,39 +403,64 @@ def cgtp_conv_forward_radial(plan: Plan, x, vec, vec_perm, radial, w, src, dst_r
                              stream=None, node_order=None):
     """uvw convolution with per-edge weights from the radial network:
     radial float32 [2][H], w bf16 [H+1][weight_numel]."""
-    _want(plan, x=x, vec=vec, vec_perm=vec_perm, w=w, src=src, dst_row_ptr=dst_row_ptr, node_order=node_order)
-    if radial.dtype != torch.float32:
-        raise TypeError(f"radial: expected torch.float32, got {radial.dtype}")
-    N, E = x.shape[0], src.shape[0]
-    if out is None:
-        out = torch.empty(N, plan.dim_out, dtype=torch.float32, device=x.device)
-    nb = cgtp_forward_workspace_bytes(plan, N)
-    if ws is None and nb:
-        ws = workspace(nb, x.device)
+    A = _Args("cgtp_conv_forward_radial")
+    N, E, H = x.shape[0], src.shape[0], plan.radial_hidden
+    A("x", x, (N, plan.dim_in1), _feat(plan), optional=False)
+    _vec_args(A, plan, E, vec, vec_perm)
+    A("radial", radial, (2, H), torch.float32, optional=False)
+    A("w", w, (H + 1, plan.weight_numel), plan.weight_dtype, optional=False)
+    _graph_args(A, plan, N, E, src, dst_row_ptr, node_order)
+    out = _out(A, "out", out, (N, plan.dim_out), torch.float32, x, True)
+    A.device()
+    ws, nws = _fwd_ws(plan, N, ws, x)
     _check(lib().cgtp_conv_forward_radial(plan.handle, _ptr(x), _ptr(vec), _ptr(vec_perm), _ptr(radial), _ptr(w),
                                           _ptr(src), _ptr(dst_row_ptr), _ptr(node_order), N, E, _ptr(out), _ptr(ws),
-                                          ws.numel() if ws is not None else 0, _stream(stream, x)))
+                                          nws, _stream(stream, x)))
     return out
+
+
+def _bwd_outs(A, plan, N, E, out, need, like, names=("x", "sh", "w")):
+    o = out if out is not None else (None,) * len(names)
+    od = plan.out_dtype
+    shapes = {"x": (N, plan.dim_in1), "sh": (E, plan.dim_in2), "w": (E, plan.weight_numel), "F": (N, 3)}
+    return [_out(A, ("g_" + nm) if nm != "F" else "F", t, shapes[nm], od, like, out is None and nm in need)
+            for nm, t in zip(names, o)]
+
+
+def cgtp_backward(plan: Plan, x, sh, w, src, dst_row_ptr, src_row_ptr, src_perm, g_out, need=("x", "sh", "w"),
+                  ws=None, out=None, stream=None, node_order=None):
+    """Gradient of the convolution; returns (g_x, g_sh, g_w), None where not
+    requested."""
+    A = _Args("cgtp_backward")
+    N, E = x.shape[0], src.shape[0]
+    A("x", x, (N, plan.dim_in1), _feat(plan), optional=False)
+    A("sh", sh, (E, plan.dim_in2), _feat(plan), optional=False)
+    A("w", w, _wshape(plan, E), plan.weight_dtype, optional=False)
+    _graph_args(A, plan, N, E, src, dst_row_ptr, node_order, src_row_ptr, src_perm)
+    A("g_out", g_out, (N, plan.dim_out), plan.out_dtype, optional=False)
+    g_x, g_sh, g_w = _bwd_outs(A, plan, N, E, out, need, x)
+    A.device()
+    ws = _ws(plan, N, E, ws, x)
+    _check(lib().cgtp_backward(plan.handle, _ptr(x), _ptr(sh), _ptr(w), _ptr(src), _ptr(dst_row_ptr),
+                               _ptr(node_order), _ptr(src_row_ptr), _ptr(src_perm), _ptr(g_out), N, E, _ptr(g_x),
+                               _ptr(g_sh), _ptr(g_w), _ptr(ws), ws.numel(), _stream(stream, x)))
+    return g_x, g_sh, g_w
 
 
 def cgtp_conv_backward_vec(plan: Plan, x, vec, vec_perm, w, src, dst_row_ptr, src_row_ptr, src_perm, g_out,
                            need=("x", "w", "F"), ws=None, out=None, stream=None, node_order=None):
     """Backward with in-kernel SH; returns (g_x, g_sh, g_w, F), None where not
     requested."""
-    _want(plan, x=x, vec=vec, vec_perm=vec_perm, w=w, src=src, dst_row_ptr=dst_row_ptr, src_row_ptr=src_row_ptr,
-          src_perm=src_perm, g_out=g_out, node_order=node_order)
+    A = _Args("cgtp_conv_backward_vec")
     N, E = x.shape[0], src.shape[0]
-    dev = x.device
-    od = plan.out_dtype
-    if out is None:
-        g_x = torch.empty(N, plan.dim_in1, dtype=od, device=dev) if "x" in need else None
-        g_sh = torch.empty(E, plan.dim_in2, dtype=od, device=dev) if "sh" in need else None
-        g_w = torch.empty(E, plan.weight_numel, dtype=od, device=dev) if "w" in need else None
-        F = torch.empty(N, 3, dtype=od, device=dev) if "F" in need else None
-    else:
-        g_x, g_sh, g_w, F = out
-    if ws is None:
-        ws = workspace(cgtp_conv_workspace_bytes(plan, N, E), dev)
+    A("x", x, (N, plan.dim_in1), _feat(plan), optional=False)
+    _vec_args(A, plan, E, vec, vec_perm)
+    A("w", w, _wshape(plan, E), plan.weight_dtype, optional=False)
+    _graph_args(A, plan, N, E, src, dst_row_ptr, node_order, src_row_ptr, src_perm)
+    A("g_out", g_out, (N, plan.dim_out), plan.out_dtype, optional=False)
+    g_x, g_sh, g_w, F = _bwd_outs(A, plan, N, E, out, need, x, ("x", "sh", "w", "F"))
+    A.device()
+    ws = _ws(plan, N, E, ws, x)
     _check(lib().cgtp_conv_backward_vec(plan.handle, _ptr(x), _ptr(vec), _ptr(vec_perm), _ptr(w), _ptr(src),
                                         _ptr(dst_row_ptr), _ptr(node_order), _ptr(src_row_ptr), _ptr(src_perm),
                                         _ptr(g_out), N, E, _ptr(g_x), _ptr(g_sh), _ptr(g_w), _ptr(F), _ptr(ws),
@@ -338,20 +472,17 @@ def cgtp_conv_forward_backward(plan: Plan, x, sh, w, src, dst_row_ptr, src_row_p
                                need=("x", "sh", "w"), ws=None, out=None, stream=None, node_order=None):
     """Forward and backward in one pass (g_out must not depend on out);
     returns (out, g_x, g_sh, g_w), None where not requested."""
-    _want(plan, x=x, sh=sh, w=w, src=src, dst_row_ptr=dst_row_ptr, src_row_ptr=src_row_ptr, src_perm=src_perm,
-          g_out=g_out, node_order=node_order)
+    A = _Args("cgtp_conv_forward_backward")
     N, E = x.shape[0], src.shape[0]
-    dev = x.device
-    od = plan.out_dtype
-    if out is None:
-        o = torch.empty(N, plan.dim_out, dtype=od, device=dev)
-        g_x = torch.empty(N, plan.dim_in1, dtype=od, device=dev) if "x" in need else None
-        g_sh = torch.empty(E, plan.dim_in2, dtype=od, device=dev) if "sh" in need else None
-        g_w = torch.empty(E, plan.weight_numel, dtype=od, device=dev) if "w" in need else None
-    else:
-        o, g_x, g_sh, g_w = out
-    if ws is None:
-        ws = workspace(cgtp_conv_workspace_bytes(plan, N, E), dev)
+    A("x", x, (N, plan.dim_in1), _feat(plan), optional=False)
+    A("sh", sh, (E, plan.dim_in2), _feat(plan), optional=False)
+    A("w", w, _wshape(plan, E), plan.weight_dtype, optional=False)
+    _graph_args(A, plan, N, E, src, dst_row_ptr, node_order, src_row_ptr, src_perm)
+    A("g_out", g_out, (N, plan.dim_out), plan.out_dtype, optional=False)
+    o = _out(A, "out", out[0] if out is not None else None, (N, plan.dim_out), plan.out_dtype, x, True)
+    g_x, g_sh, g_w = _bwd_outs(A, plan, N, E, out[1:] if out is not None else None, need, x)
+    A.device()
+    ws = _ws(plan, N, E, ws, x)
     _check(lib().cgtp_conv_forward_backward(plan.handle, _ptr(x), _ptr(sh), _ptr(w), _ptr(src), _ptr(dst_row_ptr),
                                             _ptr(node_order), _ptr(src_row_ptr), _ptr(src_perm), _ptr(g_out), N, E,
                                             _ptr(o), _ptr(g_x), _ptr(g_sh), _ptr(g_w), _ptr(ws), ws.numel(),
@@ -363,21 +494,18 @@ def cgtp_conv_forward_backward_vec(plan: Plan, x, vec, vec_perm, w, src, dst_row
                                    need=("x", "w", "F"), ws=None, out=None, stream=None, node_order=None):
     """Forward and backward in one pass with in-kernel SH; returns
     (out, g_x, g_sh, g_w, F), None where not requested."""
-    _want(plan, x=x, vec=vec, vec_perm=vec_perm, w=w, src=src, dst_row_ptr=dst_row_ptr, src_row_ptr=src_row_ptr,
-          src_perm=src_perm, g_out=g_out, node_order=node_order)
+    A = _Args("cgtp_conv_forward_backward_vec")
     N, E = x.shape[0], src.shape[0]
-    dev = x.device
-    od = plan.out_dtype
-    if out is None:
-        o = torch.empty(N, plan.dim_out, dtype=od, device=dev)
-        g_x = torch.empty(N, plan.dim_in1, dtype=od, device=dev) if "x" in need else None
-        g_sh = torch.empty(E, plan.dim_in2, dtype=od, device=dev) if "sh" in need else None
-        g_w = torch.empty(E, plan.weight_numel, dtype=od, device=dev) if "w" in need else None
-        F = torch.empty(N, 3, dtype=od, device=dev) if "F" in need else None
-    else:
-        o, g_x, g_sh, g_w, F = out
-    if ws is None:
-        ws = workspace(cgtp_conv_workspace_bytes(plan, N, E), dev)
+    A("x", x, (N, plan.dim_in1), _feat(plan), optional=False)
+    _vec_args(A, plan, E, vec, vec_perm)
+    A("w", w, _wshape(plan, E), plan.weight_dtype, optional=False)
+    _graph_args(A, plan, N, E, src, dst_row_ptr, node_order, src_row_ptr, src_perm)
+    A("g_out", g_out, (N, plan.dim_out), plan.out_dtype, optional=False)
+    o = _out(A, "out", out[0] if out is not None else None, (N, plan.dim_out), plan.out_dtype, x, True)
+    g_x, g_sh, g_w, F = _bwd_outs(A, plan, N, E, out[1:] if out is not None else None, need, x,
+                                  ("x", "sh", "w", "F"))
+    A.device()
+    ws = _ws(plan, N, E, ws, x)
     _check(lib().cgtp_conv_forward_backward_vec(plan.handle, _ptr(x), _ptr(vec), _ptr(vec_perm), _ptr(w), _ptr(src),
                                                 _ptr(dst_row_ptr), _ptr(node_order), _ptr(src_row_ptr),
                                                 _ptr(src_perm), _ptr(g_out), N, E, _ptr(o), _ptr(g_x), _ptr(g_sh),
@@ -385,69 +513,42 @@ def cgtp_conv_forward_backward_vec(plan: Plan, x, vec, vec_perm, w, src, dst_row
     return o, g_x, g_sh, g_w, F
 
 
-def cgtp_conv_workspace_bytes(plan: Plan, n_nodes: int, n_edges: int) -> int:
-    b = ctypes.c_size_t()
-    _check(lib().cgtp_conv_workspace_bytes(plan.handle, n_nodes, n_edges, ctypes.byref(b)))
-    return b.value
-
-
-def workspace(nbytes: int, device) -> torch.Tensor:
-    # torch's caching allocator returns 256-byte-aligned (or better) blocks
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
-
-
-def cgtp_conv_backward(plan: Plan, x, sh, w, src, dst, dst_row_ptr, src_row_ptr, src_perm, g_out,
-                       need=("x", "sh", "w"), ws=None, out=None, stream=None, node_order=None):
-    _want(plan, x=x, sh=sh, w=w, src=src, dst=dst, dst_row_ptr=dst_row_ptr, src_row_ptr=src_row_ptr,
-          src_perm=src_perm, g_out=g_out, node_order=node_order)
+def cgtp_double_backward(plan: Plan, x, sh, w, g_out, gg_x, gg_sh, gg_w, src, dst_row_ptr, src_row_ptr, src_perm,
+                         need=("g_out", "x", "sh", "w"), ws=None, out=None, stream=None, node_order=None):
+    """Second derivatives for cotangents (gg_x, gg_sh, gg_w) on the backward's
+    outputs; returns (d_g_out, d_x, d_sh, d_w), None where not requested."""
+    A = _Args("cgtp_double_backward")
     N, E = x.shape[0], src.shape[0]
-    dev = x.device
+    A("x", x, (N, plan.dim_in1), _feat(plan), optional=False)
+    A("sh", sh, (E, plan.dim_in2), _feat(plan), optional=gg_x is None and gg_w is None)
+    A("w", w, _wshape(plan, E), plan.weight_dtype, optional=False)
+    A("g_out", g_out, (N, plan.dim_out), plan.out_dtype, optional=False)
+    A("gg_x", gg_x, (N, plan.dim_in1), _feat(plan))
+    A("gg_sh", gg_sh, (E, plan.dim_in2), _feat(plan))
+    A("gg_w", gg_w, _wshape(plan, E), plan.weight_dtype)
+    _graph_args(A, plan, N, E, src, dst_row_ptr, node_order, src_row_ptr, src_perm)
+    o = out if out is not None else (None,) * 4
     od = plan.out_dtype
-    g_x, g_sh, g_w = out if out is not None else (None, None, None)
-    if out is None:
-        g_x = torch.empty(N, plan.dim_in1, dtype=od, device=dev) if "x" in need else None
-        g_sh = torch.empty(E, plan.dim_in2, dtype=od, device=dev) if "sh" in need else None
-        g_w = torch.empty(E, plan.weight_numel, dtype=od, device=dev) if "w" in need else None
-    nb = cgtp_conv_workspace_bytes(plan, N, E)
-    if ws is None:
-        ws = workspace(nb, dev)
-    _check(lib().cgtp_conv_backward(plan.handle, _ptr(x), _ptr(sh), _ptr(w), _ptr(src), _ptr(dst),
-                                    _ptr(dst_row_ptr), _ptr(node_order), _ptr(src_row_ptr), _ptr(src_perm),
-                                    _ptr(g_out), N, E, _ptr(g_x), _ptr(g_sh), _ptr(g_w), _ptr(ws), ws.numel(),
-                                    _stream(stream, x)))
-    return g_x, g_sh, g_w
-
-
-def cgtp_conv_double_backward(plan: Plan, x, sh, w, src, dst, dst_row_ptr, src_row_ptr, src_perm, g_out,
-                              gg_x=None, gg_sh=None, gg_w=None, need=("g_out", "x", "sh", "w"), ws=None,
-                              out=None, stream=None, node_order=None):
-    _want(plan, x=x, sh=sh, w=w, src=src, dst=dst, dst_row_ptr=dst_row_ptr, src_row_ptr=src_row_ptr,
-          src_perm=src_perm, g_out=g_out, gg_x=gg_x, gg_sh=gg_sh, gg_w=gg_w, node_order=node_order)
-    N, E = x.shape[0], src.shape[0]
-    dev = x.device
-    od = plan.out_dtype
-    if out is None:
-        d_g = torch.empty(N, plan.dim_out, dtype=od, device=dev) if "g_out" in need else None
-        d_x = torch.empty(N, plan.dim_in1, dtype=od, device=dev) if "x" in need else None
-        d_sh = torch.empty(E, plan.dim_in2, dtype=od, device=dev) if "sh" in need else None
-        d_w = torch.empty(E, plan.weight_numel, dtype=od, device=dev) if "w" in need else None
-    else:
-        d_g, d_x, d_sh, d_w = out
-    nb = cgtp_conv_workspace_bytes(plan, N, E)
-    if ws is None:
-        ws = workspace(nb, dev)
-    _check(lib().cgtp_conv_double_backward(plan.handle, _ptr(x), _ptr(sh), _ptr(w), _ptr(src), _ptr(dst),
-                                           _ptr(dst_row_ptr), _ptr(node_order), _ptr(src_row_ptr),
-                                           _ptr(src_perm), _ptr(g_out), _ptr(gg_x), _ptr(gg_sh), _ptr(gg_w), N, E, _ptr(d_g), _ptr(d_x),
-                                           _ptr(d_sh), _ptr(d_w), _ptr(ws), ws.numel(), _stream(stream, x)))
-    return d_g, d_x, d_sh, d_w
+    shapes = [(N, plan.dim_out), (N, plan.dim_in1), (E, plan.dim_in2), (E, plan.weight_numel)]
+    d = [_out(A, "d_" + nm, t, sh_, od, x, out is None and nm in need)
+         for nm, t, sh_ in zip(("g_out", "x", "sh", "w"), o, shapes)]
+    A.device()
+    ws = _ws(plan, N, E, ws, x)
+    _check(lib().cgtp_double_backward(plan.handle, _ptr(x), _ptr(sh), _ptr(w), _ptr(g_out), _ptr(gg_x),
+                                      _ptr(gg_sh), _ptr(gg_w), _ptr(src), _ptr(dst_row_ptr), _ptr(node_order),
+                                      _ptr(src_row_ptr), _ptr(src_perm), N, E, _ptr(d[0]), _ptr(d[1]), _ptr(d[2]),
+                                      _ptr(d[3]), _ptr(ws), ws.numel(), _stream(stream, x)))
+    return tuple(d)
 
 
 def cgtp_node_order(row_ptr, ws=None, out=None, stream=None):
     """Rows of a CSR by decreasing length (processing order for the
     convolution calls)."""
+    A = _Args("cgtp_node_order")
     n = row_ptr.shape[0] - 1
-    order = torch.empty(n, dtype=torch.int32, device=row_ptr.device) if out is None else out
+    A("row_ptr", row_ptr, (n + 1,), _I32, optional=False)
+    order = _out(A, "out", out, (n,), _I32, row_ptr, True)
+    A.device()
     b = ctypes.c_size_t()
     _check(lib().cgtp_node_order_workspace_bytes(n, ctypes.byref(b)))
     if ws is None:
@@ -458,25 +559,41 @@ def cgtp_node_order(row_ptr, ws=None, out=None, stream=None):
 
 def cgtp_sparse_attention_prepare(col, row_ptr, n_cols: int, out=None, stream=None):
     """Compacted window layout of a CSR graph for cgtp_sparse_attention."""
-    n_rows = row_ptr.shape[0] - 1
+    A = _Args("cgtp_sparse_attention_prepare")
+    n_rows, E = row_ptr.shape[0] - 1, col.shape[0]
+    A("col", col, (E,), _I32, optional=False)
+    A("row_ptr", row_ptr, (n_rows + 1,), _I32, optional=False)
+    A.device()
     b = ctypes.c_size_t()
-    _check(lib().cgtp_sparse_attention_layout_bytes(n_rows, col.shape[0], ctypes.byref(b)))
+    _check(lib().cgtp_sparse_attention_layout_bytes(n_rows, E, ctypes.byref(b)))
     layout = workspace(b.value, row_ptr.device) if out is None else out
-    _check(lib().cgtp_sparse_attention_prepare(_ptr(col), _ptr(row_ptr), n_rows, n_cols, col.shape[0], _ptr(layout),
+    if layout.numel() < b.value or layout.device != row_ptr.device:
+        raise ValueError(f"cgtp_sparse_attention_prepare: layout needs {b.value} bytes on {row_ptr.device}")
+    _check(lib().cgtp_sparse_attention_prepare(_ptr(col), _ptr(row_ptr), n_rows, n_cols, E, _ptr(layout),
                                                layout.numel(), _stream(stream, row_ptr)))
     return layout
+
+
+def _attn_args(A, q, k, v, row_ptr, out):
+    n_rows = row_ptr.shape[0] - 1
+    H, D = q.shape[1], q.shape[2]
+    A("q", q, (n_rows, H, D), torch.bfloat16, optional=False)
+    A("k", k, (k.shape[0], H, D), torch.bfloat16, optional=False)
+    A("v", v, (k.shape[0], H, D), torch.bfloat16, optional=False)
+    A("row_ptr", row_ptr, (n_rows + 1,), _I32, optional=False)
+    return n_rows, H, D, _out(A, "out", out, (n_rows, H, D), torch.float32, q, True)
 
 
 def cgtp_sparse_attention(q, k, v, row_ptr, n_edges: int, layout, scale=None, out=None, stream=None):
     """Graph sparse attention per head: q [n_rows][H][D], k and v
     [n_cols][H][D] (bf16) over a graph prepared by
     cgtp_sparse_attention_prepare; returns float32 [n_rows][H][D]."""
-    n_rows = row_ptr.shape[0] - 1
-    H, D = q.shape[1], q.shape[2]
+    A = _Args("cgtp_sparse_attention")
+    n_rows, H, D, out = _attn_args(A, q, k, v, row_ptr, out)
+    A("layout", layout, (layout.shape[0],), torch.uint8, optional=False)
+    A.device()
     if scale is None:
         scale = 1.0 / D ** 0.5
-    if out is None:
-        out = torch.empty(n_rows, H, D, dtype=torch.float32, device=q.device)
     _check(lib().cgtp_sparse_attention(DTYPES["bf16"], H, D, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
                                        n_rows, n_edges, _ptr(layout), layout.numel(), _ptr(out), _stream(stream, q)))
     return out
@@ -486,12 +603,12 @@ def cgtp_sparse_attention_rows(q, k, v, col, row_ptr, scale=None, out=None, stre
     """The same attention in row form, straight from the CSR (col, row_ptr):
     q [n_rows][H][D], k and v [n_cols][H][D] (bf16); returns float32
     [n_rows][H][D]."""
-    n_rows = row_ptr.shape[0] - 1
-    H, D = q.shape[1], q.shape[2]
+    A = _Args("cgtp_sparse_attention_rows")
+    n_rows, H, D, out = _attn_args(A, q, k, v, row_ptr, out)
+    A("col", col, (col.shape[0],), _I32, optional=False)
+    A.device()
     if scale is None:
         scale = 1.0 / D ** 0.5
-    if out is None:
-        out = torch.empty(n_rows, H, D, dtype=torch.float32, device=q.device)
     _check(lib().cgtp_sparse_attention_rows(DTYPES["bf16"], H, D, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(col),
                                             _ptr(row_ptr), n_rows, k.shape[0], col.shape[0], _ptr(out),
                                             _stream(stream, q)))
@@ -504,24 +621,25 @@ def cgtp_csr_workspace_bytes(n_edges: int, n_keys: int) -> int:
     return b.value
 
 
-def _csr_outputs(key, n_keys, val, sorted_key, ws, out):
+def _csr_outputs(A, key, n_keys, val, sorted_key, ws, out):
     E = key.shape[0]
-    dev = key.device
-    if out is None:
-        perm = torch.empty(E, dtype=torch.int32, device=dev)
-        row_ptr = torch.empty(n_keys + 1, dtype=torch.int32, device=dev)
-        sk = torch.empty(E, dtype=torch.int32, device=dev) if sorted_key else None
-        sv = torch.empty(E, dtype=torch.int32, device=dev) if val is not None else None
-    else:
-        perm, row_ptr, sk, sv = out
+    A("key", key, (E,), _I32, optional=False)
+    A("val", val, (E,), _I32)
+    o = out if out is not None else (None, None, None, None)
+    perm = _out(A, "perm", o[0], (E,), _I32, key, True)
+    row_ptr = _out(A, "row_ptr", o[1], (n_keys + 1,), _I32, key, True)
+    sk = _out(A, "sorted_key", o[2], (E,), _I32, key, out is None and sorted_key)
+    sv = _out(A, "sorted_val", o[3], (E,), _I32, key, out is None and val is not None)
+    A.device()
     if ws is None:
-        ws = workspace(cgtp_csr_workspace_bytes(E, n_keys), dev)
+        ws = workspace(cgtp_csr_workspace_bytes(E, n_keys), key.device)
     return E, perm, row_ptr, sk, sv, ws
 
 
 def cgtp_build_csr(key, n_keys: int, val=None, sorted_key: bool = True, ws=None, out=None, stream=None):
     """Returns (perm, row_ptr, sorted_key or None, sorted_val or None)."""
-    E, perm, row_ptr, sk, sv, ws = _csr_outputs(key, n_keys, val, sorted_key, ws, out)
+    A = _Args("cgtp_build_csr")
+    E, perm, row_ptr, sk, sv, ws = _csr_outputs(A, key, n_keys, val, sorted_key, ws, out)
     _check(lib().cgtp_build_csr(_ptr(key), _ptr(val), E, n_keys, _ptr(perm), _ptr(row_ptr), _ptr(sk), _ptr(sv),
                                 _ptr(ws), ws.numel(), _stream(stream, key)))
     return perm, row_ptr, sk, sv
@@ -532,15 +650,19 @@ def cgtp_build_csr_order(key, n_keys: int, val=None, sorted_key: bool = True, ws
     """cgtp_build_csr plus the longest-first node order (cgtp_node_order's)
     from the same launches.  Returns (perm, row_ptr, sorted_key or None,
     sorted_val or None, order)."""
-    E, perm, row_ptr, sk, sv, ws = _csr_outputs(key, n_keys, val, sorted_key, ws, out)
-    if order is None:
-        order = torch.empty(n_keys, dtype=torch.int32, device=key.device)
+    A = _Args("cgtp_build_csr_order")
+    order = _out(A, "order", order, (n_keys,), _I32, key, True)
+    E, perm, row_ptr, sk, sv, ws = _csr_outputs(A, key, n_keys, val, sorted_key, ws, out)
     _check(lib().cgtp_build_csr_order(_ptr(key), _ptr(val), E, n_keys, _ptr(perm), _ptr(row_ptr), _ptr(sk),
                                       _ptr(sv), _ptr(order), _ptr(ws), ws.numel(), _stream(stream, key)))
     return perm, row_ptr, sk, sv, order
 
 
 def cgtp_validate_csr(row_ptr, n_edges: int, idx=None, n_idx_range: int = 0, stream=None) -> bool:
+    A = _Args("cgtp_validate_csr")
+    A("row_ptr", row_ptr, (row_ptr.shape[0],), _I32, optional=False)
+    A("idx", idx, (n_edges,), _I32)
+    A.device()
     ws = workspace(256, row_ptr.device)
     rc = lib().cgtp_validate_csr(_ptr(row_ptr), row_ptr.shape[0] - 1, n_edges, _ptr(idx), n_idx_range,
                                  _ptr(ws), _stream(stream, row_ptr))
@@ -550,39 +672,64 @@ def cgtp_validate_csr(row_ptr, n_edges: int, idx=None, n_idx_range: int = 0, str
     return True
 
 
-def cgtp_spherical_harmonics(lmax: int, vec, perm=None, dtype: str = "f32", out=None, stream=None):
+def _sh_vec(A, vec, perm, n, dtype):
+    A("perm", perm, (n,), _I32)
+    rows = vec.shape[0] if vec.dim() == 2 else -1
+    if perm is None and rows != n:
+        raise ValueError(f"{A.call}: vec: expected shape ({n}, 3) without perm, got {tuple(vec.shape)}")
+    A("vec", vec, (rows, 3), torch.float64 if dtype == "f64" else torch.float32, optional=False)
+
+
+def cgtp_sh(lmax: int, vec, perm=None, dtype: str = "f32", out=None, stream=None):
+    """Real SH rows of degrees 0..lmax of the edge vectors vec[perm[t]]."""
+    A = _Args("cgtp_sh")
     n = perm.shape[0] if perm is not None else vec.shape[0]
-    if out is None:
-        out = torch.empty(n, (lmax + 1) ** 2, dtype=TORCH_DTYPES[dtype], device=vec.device)
-    _check(lib().cgtp_spherical_harmonics(lmax, DTYPES[dtype], _ptr(vec), _ptr(perm), n, _ptr(out),
-                                          _stream(stream, vec)))
+    _sh_vec(A, vec, perm, n, dtype)
+    out = _out(A, "out", out, (n, (lmax + 1) ** 2), TORCH_DTYPES[dtype], vec, True)
+    A.device()
+    _check(lib().cgtp_sh(lmax, DTYPES[dtype], _ptr(vec), _ptr(perm), n, _ptr(out), _stream(stream, vec)))
     return out
 
 
-def cgtp_forces_workspace_bytes(n_edges: int, dtype: str) -> int:
-    b = ctypes.c_size_t()
-    _check(lib().cgtp_forces_workspace_bytes(n_edges, DTYPES[dtype], ctypes.byref(b)))
-    return b.value
-
-
-def cgtp_sh_forces(lmax: int, vec, perm, g_sh, dst_row_ptr, src_row_ptr, src_perm, dtype: str = "f32",
-                   ws=None, out=None, stream=None):
-    N, E = dst_row_ptr.shape[0] - 1, g_sh.shape[0]
-    if out is None:
-        out = torch.empty(N, 3, dtype=TORCH_DTYPES[dtype], device=g_sh.device)
-    if ws is None:
-        ws = workspace(cgtp_forces_workspace_bytes(E, dtype), g_sh.device)
-    _check(lib().cgtp_sh_forces(lmax, DTYPES[dtype], _ptr(vec), _ptr(perm), _ptr(g_sh), _ptr(dst_row_ptr),
-                                _ptr(src_row_ptr), _ptr(src_perm), N, E, _ptr(out), _ptr(ws), ws.numel(),
-                                _stream(stream, g_sh)))
-    return out
+def cgtp_sh_vjp_forces(lmax: int, vec, perm, g_sh, dst_row_ptr, src_row_ptr, src_perm, dtype: str = "f32",
+                       need=("F",), ws=None, out=None, stream=None):
+    """Per-edge SH vector-Jacobian products g_vec = J^T g_sh and the atom
+    forces they imply; returns (g_vec, F), None where not requested
+    (need: "vec", "F")."""
+    A = _Args("cgtp_sh_vjp_forces")
+    E = g_sh.shape[0]
+    N = dst_row_ptr.shape[0] - 1 if dst_row_ptr is not None else 0
+    td = TORCH_DTYPES[dtype]
+    _sh_vec(A, vec, perm, E, dtype)
+    A("g_sh", g_sh, (E, (lmax + 1) ** 2), td, optional=False)
+    want_F = (out is None and "F" in need) or (out is not None and out[1] is not None)
+    A("dst_row_ptr", dst_row_ptr, (N + 1,), _I32, optional=not want_F)
+    A("src_row_ptr", src_row_ptr, (N + 1,), _I32, optional=not want_F)
+    A("src_perm", src_perm, (E,), _I32, optional=not want_F)
+    o = out if out is not None else (None, None)
+    g_vec = _out(A, "g_vec", o[0], (E, 3), td, g_sh, out is None and "vec" in need)
+    F = _out(A, "F", o[1], (N, 3), td, g_sh, out is None and "F" in need)
+    A.device()
+    nb = 0 if g_vec is not None else E * 3 * (8 if dtype == "f64" else 4)
+    if ws is None and nb:
+        ws = workspace(nb, g_sh.device)
+    _check(lib().cgtp_sh_vjp_forces(lmax, DTYPES[dtype], _ptr(vec), _ptr(perm), _ptr(g_sh), _ptr(dst_row_ptr),
+                                    _ptr(src_row_ptr), _ptr(src_perm), N, E, _ptr(g_vec), _ptr(F), _ptr(ws),
+                                    ws.numel() if ws is not None else 0, _stream(stream, g_sh)))
+    return g_vec, F
 
 
 def cgtp_force_loss_sh_cotangent(lmax: int, vec, perm, src, dst, F, dtype: str = "f32", out=None,
                                  stream=None):
+    A = _Args("cgtp_force_loss_sh_cotangent")
     E = src.shape[0]
-    if out is None:
-        out = torch.empty(E, (lmax + 1) ** 2, dtype=TORCH_DTYPES[dtype], device=F.device)
+    td = TORCH_DTYPES[dtype]
+    _sh_vec(A, vec, perm, E, dtype)
+    A("src", src, (E,), _I32, optional=False)
+    A("dst", dst, (E,), _I32, optional=False)
+    A("F", F, (F.shape[0], 3), td, optional=False)
+    out = _out(A, "out", out, (E, (lmax + 1) ** 2), td, F, True)
+    A.device()
     _check(lib().cgtp_force_loss_sh_cotangent(lmax, DTYPES[dtype], _ptr(vec), _ptr(perm), _ptr(src), _ptr(dst),
                                               _ptr(F), E, _ptr(out), _stream(stream, F)))
     return out

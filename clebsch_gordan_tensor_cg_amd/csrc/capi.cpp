@@ -94,6 +94,9 @@ struct BwdOut {
     bool acc_fwd = false;
     bool fb = false;      // forward and backward of one operand set (fwd = f(x, y, w))
     bool keep_parts = false;  // leave the per-unit y-gradient partials in the workspace
+    void *m_out = nullptr;    // x-messages straight into this array instead of the workspace
+                              // (independent items: message t is item t's x-gradient)
+    int graph = 1;            // 0: independent items (item t is its own one-edge segment)
 };
 
 // workspace layout of the backward calls: x-messages [E][dim1] in the edges'
@@ -111,7 +114,7 @@ char *ws_force(const Plan &p, char *ws, int64_t n_edges) {
 int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
             const int32_t *row_ptr, const int32_t *order, const void *g_out, int64_t n_nodes, int64_t n_edges,
             BwdOut o, char *ws, hipStream_t s, const void *vec = nullptr, const int32_t *vperm = nullptr) {
-    void *m = ws;
+    void *m = o.m_out ? o.m_out : (void *)ws;
     char *parts = ws_parts(p, ws, n_edges);
     const bool fused = o.fwd != nullptr && !o.fb;   // the double backward's y term
     const bool fb = o.fb;
@@ -137,7 +140,7 @@ int run_bwd(const Plan &p, const void *x, const void *y, const void *w, const in
     void *fourth = o.fwd;
     void *gw = o.g_w;
     long long n = n_nodes, ne = n_edges;
-    int graph = 1;
+    int graph = o.graph;
     void *args[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&order,
                     (void *)&vec, (void *)&vperm, (void *)&g_out, &gw, &m, &third, &n, &ne, &graph, &flags};
     void *args_fb[] = {(void *)&x, (void *)&y, (void *)&w, (void *)&src, (void *)&row_ptr, (void *)&order,
@@ -363,11 +366,26 @@ void cgtp_plan_destroy(cgtp_plan_t plan) {
     delete plan;
 }
 
+// scratch of the forward calls: uvw path tensors T (bf16) and the partial
+// tiles of split mixing contractions; uvu forwards take none
+static size_t fwd_ws_bytes(const Plan &p, int64_t n_items) {
+    if (p.mode != CGTP_UVW) return 0;
+    return align256((size_t)n_items * p.t_per_item * 2) + align256(mix_part_bytes(p, n_items));
+}
+
+// scratch of the backward calls (layout above ws_parts / ws_force)
+static size_t graph_ws_bytes(const Plan &p, int64_t n_nodes, int64_t n_edges) {
+    (void)n_nodes;
+    const size_t eb = out_bytes(p.dtype);
+    return align256((size_t)n_edges * p.dim1 * eb) + align256((size_t)parts_units(p) * n_edges * p.dim2 * eb) +
+           align256((size_t)n_edges * 3 * eb) + 256;
+}
+
 static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, const int32_t *src,
                    const int32_t *row_ptr, const int32_t *order, int64_t n_items, int graph, void *out, void *ws,
                    size_t ws_bytes, hipStream_t s, const void *vec = nullptr, const int32_t *vperm = nullptr,
                    const float *radial = nullptr) {
-    size_t need = align256((size_t)n_items * p.t_per_item * 2) + align256(mix_part_bytes(p, n_items));
+    const size_t need = fwd_ws_bytes(p, n_items);
     if (ws_bytes < need || (!ws && need)) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace too small");
     void *part = (char *)ws + align256((size_t)n_items * p.t_per_item * 2);
     if (((uintptr_t)ws) & 255) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
@@ -385,15 +403,6 @@ static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, c
         acc = 1;
     }
     if ((rc = launch_uvw_mix(p, ws, w, n_items, out, acc, part, s))) return rc;
-    return CGTP_OK;
-}
-
-int cgtp_forward_workspace_bytes(cgtp_plan_t plan, int64_t n_items, size_t *bytes) {
-    clear_error();
-    if (!plan || !bytes || n_items < 0) return set_error(CGTP_ERR_INVALID_ARGUMENT, "bad argument");
-    const Plan &p = plan->p;
-    *bytes = p.mode == CGTP_UVW ? align256((size_t)n_items * p.t_per_item * 2) + align256(mix_part_bytes(p, n_items))
-                                : 0;
     return CGTP_OK;
 }
 
@@ -472,13 +481,12 @@ int cgtp_conv_forward_vec(cgtp_plan_t plan, const void *x, const void *vec, cons
                              workspace, workspace_bytes, stream);
 }
 
-int cgtp_conv_workspace_bytes(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, size_t *bytes) {
+int cgtp_workspace_bytes(cgtp_plan_t plan, int64_t n_items, int64_t n_edges, size_t *bytes) {
     clear_error();
-    if (!plan || !bytes || n_nodes < 0 || n_edges < 0) return set_error(CGTP_ERR_INVALID_ARGUMENT, "bad argument");
+    if (!plan || !bytes || n_items < 0 || n_edges < 0) return set_error(CGTP_ERR_INVALID_ARGUMENT, "bad argument");
     const Plan &p = plan->p;
-    const size_t eb = out_bytes(p.dtype);
-    *bytes = align256((size_t)n_edges * p.dim1 * eb) +
-             align256((size_t)parts_units(p) * n_edges * p.dim2 * eb) + align256((size_t)n_edges * 3 * eb) + 256;
+    // the single product's backward counts each item as a one-edge segment
+    *bytes = std::max(fwd_ws_bytes(p, n_items), graph_ws_bytes(p, n_items, std::max(n_edges, n_items)));
     return CGTP_OK;
 }
 
@@ -491,8 +499,7 @@ static int check_graph_args(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, 
         return set_error(CGTP_ERR_UNSUPPORTED, "backward with shared weights is not provided");
     if (n_nodes < 0 || n_edges < 0 || n_edges > 0x7fffffffLL || n_nodes > 0x7fffffffLL)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "sizes out of range");
-    size_t need = 0;
-    cgtp_conv_workspace_bytes(plan, n_nodes, n_edges, &need);
+    const size_t need = graph_ws_bytes(plan->p, n_nodes, n_edges);
     if (ws_bytes < need || (!ws && need)) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace too small");
     if (((uintptr_t)ws) & 255) return set_error(CGTP_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
     return CGTP_OK;
@@ -553,15 +560,34 @@ static int conv_backward_impl(cgtp_plan_t plan, const void *x, const void *sh, c
     return rc;
 }
 
-int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
-                       const int32_t *dst, const int32_t *dst_row_ptr, const int32_t *node_order,
-                       const int32_t *src_row_ptr, const int32_t *src_perm, const void *g_out, int64_t n_nodes,
-                       int64_t n_edges, void *g_x, void *g_sh, void *g_w, void *workspace, size_t workspace_bytes,
-                       cgtp_stream_t stream) {
+int cgtp_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
+                  const int32_t *dst_row_ptr, const int32_t *node_order, const int32_t *src_row_ptr,
+                  const int32_t *src_perm, const void *g_out, int64_t n_nodes, int64_t n_edges, void *g_x, void *g_sh,
+                  void *g_w, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
     clear_error();
-    (void)dst;
     return conv_backward_impl(plan, x, sh, nullptr, nullptr, w, src, dst_row_ptr, node_order, src_row_ptr, src_perm,
                               g_out, n_nodes, n_edges, g_x, g_sh, g_w, nullptr, workspace, workspace_bytes, stream);
+}
+
+int cgtp_tp_backward(cgtp_plan_t plan, const void *x, const void *y, const void *w, int64_t batch, const void *g_out,
+                     void *g_x, void *g_y, void *g_w, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
+    clear_error();
+    // each item is its own one-edge segment: the graph calls' workspace for
+    // batch nodes and batch edges, and no source reduction (message t is
+    // item t's x-gradient, written straight into g_x)
+    int rc = check_graph_args(plan, batch, batch, workspace, workspace_bytes);
+    if (rc) return rc;
+    if (batch == 0) return CGTP_OK;
+    if (!x || !y || !w || !g_out) return set_error(CGTP_ERR_INVALID_ARGUMENT, "NULL buffer");
+    const Plan &p = plan->p;
+    BwdOut o;
+    o.graph = 0;
+    o.g_w = g_w;
+    o.want_m = g_x != nullptr;
+    o.m_out = g_x;
+    o.g_y = g_y;
+    return run_bwd(p, x, y, w, nullptr, nullptr, nullptr, g_out, batch, batch, o, (char *)workspace,
+                   (hipStream_t)stream);
 }
 
 int cgtp_conv_backward_vec(cgtp_plan_t plan, const void *x, const void *vec, const int32_t *vec_perm, const void *w,
@@ -603,15 +629,12 @@ int cgtp_conv_forward_backward_vec(cgtp_plan_t plan, const void *x, const void *
                               g_out, n_nodes, n_edges, g_x, g_sh, g_w, F, workspace, workspace_bytes, stream, out);
 }
 
-int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
-                              const int32_t *dst, const int32_t *dst_row_ptr, const int32_t *node_order,
-                              const int32_t *src_row_ptr, const int32_t *src_perm, const void *g_out,
-                              const void *gg_x, const void *gg_sh,
-                              const void *gg_w, int64_t n_nodes, int64_t n_edges, void *d_g_out, void *d_x,
-                              void *d_sh, void *d_w, void *workspace, size_t workspace_bytes,
-                              cgtp_stream_t stream) {
+int cgtp_double_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const void *g_out,
+                         const void *gg_x, const void *gg_sh, const void *gg_w, const int32_t *src,
+                         const int32_t *dst_row_ptr, const int32_t *node_order, const int32_t *src_row_ptr,
+                         const int32_t *src_perm, int64_t n_nodes, int64_t n_edges, void *d_g_out, void *d_x,
+                         void *d_sh, void *d_w, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
     clear_error();
-    (void)dst;
     int rc = check_graph_args(plan, n_nodes, n_edges, workspace, workspace_bytes);
     if (rc) return rc;
     const Plan &p = plan->p;

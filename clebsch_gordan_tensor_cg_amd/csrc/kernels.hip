@@ -1279,7 +1279,7 @@ int launch_sh_forces(int lmax, cgtp_dtype dt, const void *vec, const int32_t *pe
         int rc = dispatch_l<ForceLaunch>(lmax, dt, vec, perm, g_sh, n_parts, part_stride, n_edges, v, s);
         if (rc) return rc;
     }
-    if (n_nodes == 0) return CGTP_OK;
+    if (n_nodes == 0 || !F) return CGTP_OK;
     unsigned g = (unsigned)n_nodes;
     if (dt == CGTP_F32)
         CGTP_LAUNCH("k_node_force", s, k_node_force<float>, dim3(g), dim3(64), 0, s, (const float *)v, dst_row_ptr,
@@ -1465,37 +1465,34 @@ int cgtp_validate_csr(const int32_t *row_ptr, int64_t n_rows, int64_t n_edges, c
     return CGTP_OK;
 }
 
-int cgtp_spherical_harmonics(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm, int64_t n,
-                             void *sh, cgtp_stream_t stream) {
+int cgtp_sh(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm, int64_t n, void *sh,
+            cgtp_stream_t stream) {
     clear_error();
-    if (n < 0 || (n > 0 && (!vec || !sh)))
-        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_spherical_harmonics: bad argument");
+    if (n < 0 || (n > 0 && (!vec || !sh))) return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sh: bad argument");
     if (dtype != CGTP_F32 && dtype != CGTP_F64 && dtype != CGTP_BF16_F32ACC)
-        return set_error(CGTP_ERR_UNSUPPORTED, "cgtp_spherical_harmonics: dtype");
+        return set_error(CGTP_ERR_UNSUPPORTED, "cgtp_sh: dtype");
     if (n == 0) return CGTP_OK;
     return dispatch_l<ShLaunch>(lmax, dtype, vec, perm, n, sh, (hipStream_t)stream);
 }
 
-int cgtp_forces_workspace_bytes(int64_t n_edges, cgtp_dtype dtype, size_t *bytes) {
-    clear_error();
-    if (!bytes || n_edges < 0) return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_forces_workspace_bytes");
-    *bytes = align256((size_t)n_edges * 3 * (dtype == CGTP_F64 ? 8 : 4));
-    return CGTP_OK;
-}
-
-int cgtp_sh_forces(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm, const void *g_sh,
-                   const int32_t *dst_row_ptr, const int32_t *src_row_ptr, const int32_t *src_perm, int64_t n_nodes,
-                   int64_t n_edges, void *F, void *workspace, size_t workspace_bytes, cgtp_stream_t stream) {
+int cgtp_sh_vjp_forces(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm, const void *g_sh,
+                       const int32_t *dst_row_ptr, const int32_t *src_row_ptr, const int32_t *src_perm, int64_t n_nodes,
+                       int64_t n_edges, void *g_vec, void *F, void *workspace, size_t workspace_bytes,
+                       cgtp_stream_t stream) {
     clear_error();
     hipStream_t s = (hipStream_t)stream;
-    if (dtype != CGTP_F32 && dtype != CGTP_F64) return set_error(CGTP_ERR_UNSUPPORTED, "cgtp_sh_forces: dtype");
-    size_t need = 0;
-    cgtp_forces_workspace_bytes(n_edges, dtype, &need);
-    if (n_nodes < 0 || n_edges < 0 || (n_nodes > 0 && (!F || !dst_row_ptr || !src_row_ptr)) ||
-        (n_edges > 0 && (!vec || !g_sh || !src_perm || !workspace)) || workspace_bytes < need)
-        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sh_forces: bad argument");
+    if (dtype != CGTP_F32 && dtype != CGTP_F64) return set_error(CGTP_ERR_UNSUPPORTED, "cgtp_sh_vjp_forces: dtype");
+    if (n_nodes < 0 || n_edges < 0 || n_edges > 0x7fffffffLL || n_nodes > 0x7fffffffLL)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sh_vjp_forces: sizes out of range");
+    // the per-edge vectors go to g_vec when given, else to the workspace
+    const size_t need = g_vec ? 0 : (size_t)n_edges * 3 * (dtype == CGTP_F64 ? 8 : 4);
+    if ((F && n_nodes > 0 && (!dst_row_ptr || !src_row_ptr || (n_edges > 0 && !src_perm))) ||
+        (n_edges > 0 && (!vec || !g_sh)) || ((F || g_vec) && need > 0 && (!workspace || workspace_bytes < need)))
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_sh_vjp_forces: NULL buffer or workspace too small");
+    if (!F && !g_vec) return CGTP_OK;
+    if (!F) n_nodes = 0;   // the vectors only
     return launch_sh_forces(lmax, dtype, vec, perm, g_sh, 1, 0, dst_row_ptr, src_row_ptr, src_perm, n_nodes, n_edges,
-                            F, workspace, s);
+                            F, g_vec ? g_vec : workspace, s);
 }
 
 int cgtp_force_loss_sh_cotangent(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm,

@@ -154,23 +154,31 @@ int cgtp_plan_source(cgtp_plan_t plan, char *buf, int64_t cap, int64_t *len);
 void cgtp_plan_destroy(cgtp_plan_t plan);
 
 /* ---------------------------------------------------------------------- */
-/* Scratch for the forward calls: uvw plans contract in two steps (per-item */
-/* path tensors T_p = CG_p(x, y) summed over the item's edges, rounded to   */
-/* the MFMA operand type, then T . W per output block on the matrix cores,  */
-/* [SE3]: the TFN convolution with all paths into one output degree fused, */
-/* concatenated along K).  T, and the partial tiles of long contractions,  */
-/* live in the workspace: this many bytes for n_items items (destination   */
-/* nodes or samples); 0 for uvu plans.                                      */
+/* Scratch.  Execution calls allocate nothing; the scratch they need comes   */
+/* in as `workspace` (a 256-byte-aligned device buffer the caller owns and   */
+/* does not touch while the call is in flight on its stream):                */
+/*   - uvw forwards contract in two steps (per-item path tensors T_p =        */
+/*     CG_p(x, y) summed over the item's edges and rounded to the MFMA        */
+/*     operand type, then T . W per output block on the matrix cores, [SE3]:  */
+/*     the TFN convolution with all paths into one output degree fused,       */
+/*     concatenated along K); T and the partial tiles of long contractions    */
+/*     live in the workspace (uvu forwards need none: NULL is accepted);      */
+/*   - the backward calls keep per-edge x-messages, per-unit SH-gradient     */
+/*     partials and per-edge force vectors there.                             */
+/* cgtp_workspace_bytes returns a size that suffices for every execution     */
+/* call of the plan on at most n_items items (destination nodes or samples)  */
+/* and n_edges edges (0 for the single product, whose backward counts each   */
+/* item as one edge).  Errors: INVALID_ARGUMENT (NULL, negative sizes).      */
 /* ---------------------------------------------------------------------- */
-int cgtp_forward_workspace_bytes(cgtp_plan_t plan, int64_t n_items, size_t *bytes);
+int cgtp_workspace_bytes(cgtp_plan_t plan, int64_t n_items, int64_t n_edges, size_t *bytes);
 
 /* ---------------------------------------------------------------------- */
 /* Tensor product on independent items ([KG]: the CG tensor product).      */
 /*   out[b] = sum_paths W . CG(x[b], y[b])                                 */
 /* x [batch][dim_in1], y [batch][dim_in2], w [batch][weight_numel] (or     */
 /* [weight_numel] shared), out [batch][dim_out]; element type per dtype.    */
-/* workspace: cgtp_forward_workspace_bytes(batch) bytes, 256-byte aligned   */
-/* (may be NULL for uvu plans).                                             */
+/* workspace: cgtp_workspace_bytes(plan, batch, 0) bytes (may be NULL for   */
+/* uvu plans).                                                              */
 /* ---------------------------------------------------------------------- */
 int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, int64_t batch,
                  void *out, void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
@@ -189,7 +197,7 @@ int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, 
  * 0..n_nodes-1, normally from cgtp_build_csr_order or cgtp_node_order;
  * it changes timing only, never a result (an entry out of range leaves its
  * slot idle, so a node missing from it is not written).  workspace:
- * cgtp_forward_workspace_bytes(n_nodes) (may be NULL for uvu plans). */
+ * cgtp_workspace_bytes(plan, n_nodes, n_edges) (may be NULL for uvu plans). */
 int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
                       const int32_t *src, const int32_t *dst_row_ptr, const int32_t *node_order,
                       int64_t n_nodes, int64_t n_edges, void *out, void *workspace,
@@ -198,7 +206,7 @@ int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const voi
 /* The same convolution with the SH of the edges computed inside the kernel
  * from the edge vectors ([SE3] basis computation, moved into the
  * convolution): edge t uses sh[t] = Y(vec[e] / |vec[e]|), e = vec_perm ?
- * vec_perm[t] : t, with the conventions of cgtp_spherical_harmonics; vec
+ * vec_perm[t] : t, with the conventions of cgtp_sh; vec
  * [*][3] float (double for CGTP_F64 plans).  Needs a plan whose input 2 is
  * one SH row, 1x0+1x1+...+1xL with L <= 6 (parity labels absent or
  * (-1)^l); other plans return UNSUPPORTED.  The SH never reach memory. */
@@ -218,7 +226,7 @@ int cgtp_conv_forward_vec(cgtp_plan_t plan, const void *x, const void *vec, cons
  * cgtp_conv_forward_vec).  Because the output layer is linear, the mixing
  * runs after aggregation: per node the path tensors are summed once per
  * row of w (phi-weighted), and the mixing on the matrix cores has an
- * (H+1)-fold contraction.  workspace: cgtp_forward_workspace_bytes. */
+ * (H+1)-fold contraction.  workspace: cgtp_workspace_bytes. */
 int cgtp_conv_forward_radial(cgtp_plan_t plan, const void *x, const void *vec,
                              const int32_t *vec_perm, const float *radial, const void *w,
                              const int32_t *src, const int32_t *dst_row_ptr,
@@ -226,31 +234,38 @@ int cgtp_conv_forward_radial(cgtp_plan_t plan, const void *x, const void *vec,
                              void *out, void *workspace, size_t workspace_bytes,
                              cgtp_stream_t stream);
 
-/* Workspace needed by cgtp_conv_backward / cgtp_conv_double_backward for a
- * graph with n_edges edges (bytes; 256-byte aligned pointer required).
- * The backward calls are provided for uvu plans (FP32 and FP64). */
-int cgtp_conv_workspace_bytes(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges,
-                              size_t *bytes);
-
 /* Gradient of the convolution ([KG]: gradient kernels) for the output
  * cotangent g_out [n_nodes][dim_out]:
  *   g_x[s]  = sum over edges leaving s of d<g_out, out>/dx   [n_nodes][dim_in1]
  *   g_sh[t] = d<g_out, out>/dsh[t]                            [n_edges][dim_in2]
- *   g_w[t]  = d<g_out, out>/dw[t]            [n_edges][weight_numel] (or shared sum)
- * Edge arrays in dst-sorted order as in cgtp_conv_forward; dst [n_edges] is
- * the destination of each edge in that order; src_row_ptr [n_nodes+1] and
- * src_perm [n_edges] give, for each source node s, the positions (into the
- * dst-sorted arrays) of its edges: src_perm[src_row_ptr[s] ..
- * src_row_ptr[s+1]).  g_x is reduced per source node without atomics.
- * node_order as in cgtp_conv_forward.  Any of g_x, g_sh, g_w may be NULL
- * (not computed).  Shared-weight plans are not supported here
- * (UNSUPPORTED). */
-int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
-                       const int32_t *src, const int32_t *dst, const int32_t *dst_row_ptr,
-                       const int32_t *node_order, const int32_t *src_row_ptr,
-                       const int32_t *src_perm, const void *g_out, int64_t n_nodes,
-                       int64_t n_edges, void *g_x, void *g_sh, void *g_w, void *workspace,
-                       size_t workspace_bytes, cgtp_stream_t stream);
+ *   g_w[t]  = d<g_out, out>/dw[t]                       [n_edges][weight_numel]
+ * Edge arrays in dst-sorted order as in cgtp_conv_forward (x, sh, w, src,
+ * dst_row_ptr, node_order have the meaning and layout given there);
+ * src_row_ptr [n_nodes+1] and src_perm [n_edges] give, for each source node
+ * s, the positions (into the dst-sorted arrays) of its edges:
+ * src_perm[src_row_ptr[s] .. src_row_ptr[s+1]) (cgtp_build_csr with key =
+ * the dst-sorted src array).  g_x is reduced per source node without
+ * atomics.  Any of g_x, g_sh, g_w may be NULL (not computed); src_row_ptr and
+ * src_perm may be NULL when g_x is.  The backward calls are provided for uvu
+ * plans (CGTP_F32, CGTP_F64) with per-edge weights; other plans return
+ * UNSUPPORTED.  workspace: cgtp_workspace_bytes(plan, n_nodes, n_edges).
+ * Errors: INVALID_ARGUMENT (NULL buffer, sizes, short or misaligned
+ * workspace), UNSUPPORTED, HIP. */
+int cgtp_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const int32_t *src,
+                  const int32_t *dst_row_ptr, const int32_t *node_order, const int32_t *src_row_ptr,
+                  const int32_t *src_perm, const void *g_out, int64_t n_nodes, int64_t n_edges, void *g_x,
+                  void *g_sh, void *g_w, void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+
+/* Gradient of the single product cgtp_forward ([KG]: gradient kernels) on
+ * batch independent items, for the cotangent g_out [batch][dim_out]:
+ *   g_x[b] = d<g_out, out>/dx[b]  [batch][dim_in1],
+ *   g_y[b] = d<g_out, out>/dy[b]  [batch][dim_in2],
+ *   g_w[b] = d<g_out, out>/dw[b]  [batch][weight_numel].
+ * Any of g_x, g_y, g_w may be NULL.  Same plans as cgtp_backward (uvu,
+ * per-item weights).  workspace: cgtp_workspace_bytes(plan, batch, 0). */
+int cgtp_tp_backward(cgtp_plan_t plan, const void *x, const void *y, const void *w, int64_t batch,
+                     const void *g_out, void *g_x, void *g_y, void *g_w, void *workspace, size_t workspace_bytes,
+                     cgtp_stream_t stream);
 
 /* Backward with the SH computed from the edge vectors (as in
  * cgtp_conv_forward_vec) and, when F [n_nodes][3] is given, the forces of
@@ -258,9 +273,9 @@ int cgtp_conv_backward(cgtp_plan_t plan, const void *x, const void *sh, const vo
  * vectors (vec = pos[dst] - pos[src]), without writing the SH gradient:
  *   F[a] = - sum_{t: dst=a} J_t^T g_sh[t] + sum_{t: src=a} J_t^T g_sh[t],
  * J_t = dY/dvec at vec_t, reduced per atom over dst_row_ptr and over
- * (src_row_ptr, src_perm) without atomics (as cgtp_sh_forces).  Any of g_x,
+ * (src_row_ptr, src_perm) without atomics (as cgtp_sh_vjp_forces).  Any of g_x,
  * g_sh, g_w, F may be NULL.  Other arguments and the workspace as in
- * cgtp_conv_backward. */
+ * cgtp_backward. */
 int cgtp_conv_backward_vec(cgtp_plan_t plan, const void *x, const void *vec, const int32_t *vec_perm,
                            const void *w, const int32_t *src, const int32_t *dst_row_ptr,
                            const int32_t *node_order, const int32_t *src_row_ptr,
@@ -271,10 +286,10 @@ int cgtp_conv_backward_vec(cgtp_plan_t plan, const void *x, const void *vec, con
 /* Forward and backward in one pass over the edges, for an output cotangent
  * g_out that does not depend on out (an energy linear in the outputs, as
  * the sum of the 0e channels): out = the forward of cgtp_conv_forward, and
- * g_x, g_sh, g_w as cgtp_conv_backward, each per-edge weight row read once
+ * g_x, g_sh, g_w as cgtp_backward, each per-edge weight row read once
  * for both ([KG]: the gradient kernels; the fusion of the convolution).
  * out [n_nodes][dim_out] must not be NULL; g_x, g_sh, g_w may be NULL.
- * Other arguments and the workspace as in cgtp_conv_backward.  FP64 plans
+ * Other arguments and the workspace as in cgtp_backward.  FP64 plans
  * compute the same results with the forward and the backward as two
  * launches. */
 int cgtp_conv_forward_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
@@ -303,17 +318,17 @@ int cgtp_conv_forward_backward_vec(cgtp_plan_t plan, const void *x, const void *
  *   d_x     = fx*(g_out; gg_sh, w) + fx*(g_out; sh, gg_w)
  *   d_sh    = fsh*(g_out; gg_x, w) + fsh*(g_out; x, gg_w)
  *   d_w     = fw*(g_out; gg_x, sh) + fw*(g_out; x, gg_sh)
- * NULL cotangents are zero; NULL outputs are skipped; sh is read only for
- * the gg_x and gg_w terms (may be NULL when both are NULL).  Shapes as in
- * cgtp_conv_backward (d_g_out has the shape of g_out). */
-int cgtp_conv_double_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
-                              const int32_t *src, const int32_t *dst,
-                              const int32_t *dst_row_ptr, const int32_t *node_order,
-                              const int32_t *src_row_ptr, const int32_t *src_perm,
-                              const void *g_out, const void *gg_x,
-                              const void *gg_sh, const void *gg_w, int64_t n_nodes,
-                              int64_t n_edges, void *d_g_out, void *d_x, void *d_sh, void *d_w,
-                              void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+ * (Shapes: gg_x [n_nodes][dim_in1], gg_sh
+ * [n_edges][dim_in2], gg_w [n_edges][weight_numel]; d_g_out has the shape of
+ * g_out, d_x of x, d_sh of sh, d_w of w.)  NULL cotangents are zero; NULL
+ * outputs are skipped; sh is read only for the gg_x and gg_w terms (may be
+ * NULL when both are NULL); src_row_ptr and src_perm may be NULL when d_x
+ * is.  Graph arguments, plans, workspace and errors as in cgtp_backward. */
+int cgtp_double_backward(cgtp_plan_t plan, const void *x, const void *sh, const void *w, const void *g_out,
+                         const void *gg_x, const void *gg_sh, const void *gg_w, const int32_t *src,
+                         const int32_t *dst_row_ptr, const int32_t *node_order, const int32_t *src_row_ptr,
+                         const int32_t *src_perm, int64_t n_nodes, int64_t n_edges, void *d_g_out, void *d_x,
+                         void *d_sh, void *d_w, void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
 
 /* ---------------------------------------------------------------------- */
 /* Helpers                                                                  */
@@ -414,22 +429,28 @@ int cgtp_validate_csr(const int32_t *row_ptr, int64_t n_rows, int64_t n_edges,
  * Conventions), degrees 0..lmax (lmax <= 6), [SE3] basis computation:
  *   sh[t][l*l + m + l] = Y_lm(vec[e] / |vec[e]|),  e = perm ? perm[t] : t.
  * vec [*][3] and sh [n][(lmax+1)^2] in dtype (F32 or F64; BF16_F32ACC
- * reads float vectors and writes bf16). */
-int cgtp_spherical_harmonics(int32_t lmax, cgtp_dtype dtype, const void *vec,
-                             const int32_t *perm, int64_t n, void *sh, cgtp_stream_t stream);
+ * reads float vectors and writes bf16).  A zero vector gives undefined
+ * values.  Errors: INVALID_ARGUMENT, UNSUPPORTED (dtype, lmax > 6). */
+int cgtp_sh(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm, int64_t n, void *sh,
+            cgtp_stream_t stream);
 
-/* Forces from an energy gradient on the SH of the edges (edge order t as
- * in the convolution, vector of edge t = vec[perm ? perm[t] : t] =
- * pos[dst] - pos[src]):
- *   F[a] = - sum_{t: dst=a} J_t^T g_sh[t] + sum_{t: src=a} J_t^T g_sh[t],
- * J_t = dY/dvec at vec_t.  Reduced per atom over dst_row_ptr and over
- * (src_row_ptr, src_perm); no atomics.  F [n_nodes][3]; dtype F32 or F64.
- * workspace: cgtp_forces_workspace_bytes. */
-int cgtp_forces_workspace_bytes(int64_t n_edges, cgtp_dtype dtype, size_t *bytes);
-int cgtp_sh_forces(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm,
-                   const void *g_sh, const int32_t *dst_row_ptr, const int32_t *src_row_ptr,
-                   const int32_t *src_perm, int64_t n_nodes, int64_t n_edges, void *F,
-                   void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
+/* Vector-Jacobian product of the SH and the forces it implies ([KG]: the
+ * derivatives needed for interatomic forces).  For a gradient g_sh
+ * [n_edges][(lmax+1)^2] on the SH rows of the edges (edge order t as in the
+ * convolution, vector of edge t = vec[perm ? perm[t] : t] = pos[dst] -
+ * pos[src]):
+ *   g_vec[t] = J_t^T g_sh[t]                               [n_edges][3]
+ *   F[a] = - sum_{t: dst=a} g_vec[t] + sum_{t: src=a} g_vec[t]  [n_nodes][3]
+ * with J_t = dY/dvec at vec_t (F = -dE/dpos for an energy E with
+ * dE/dsh = g_sh).  F is reduced per atom over dst_row_ptr and over
+ * (src_row_ptr, src_perm) without atomics.  Either output may be NULL.
+ * workspace: n_edges * 3 elements of dtype (256-byte aligned) when F is
+ * wanted and g_vec is NULL, else unused (may be NULL).  dtype F32 or F64.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (dtype, lmax > 6). */
+int cgtp_sh_vjp_forces(int32_t lmax, cgtp_dtype dtype, const void *vec, const int32_t *perm, const void *g_sh,
+                       const int32_t *dst_row_ptr, const int32_t *src_row_ptr, const int32_t *src_perm,
+                       int64_t n_nodes, int64_t n_edges, void *g_vec, void *F, void *workspace,
+                       size_t workspace_bytes, cgtp_stream_t stream);
 
 /* Cotangent on the SH of the force loss L = 1/2 sum_a |F[a]|^2:
  *   gg_sh[t] = -J_t (F[dst[t]] - F[src[t]]).  dtype F32 or F64. */

@@ -62,7 +62,7 @@ def test_graph_uvw_step(B, torch):
     order = torch.empty(N, dtype=torch.int32, device="cuda")
     out = torch.empty(N, plan.dim_out, device="cuda")
     csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), "cuda")
-    f_ws = B.workspace(B.cgtp_forward_workspace_bytes(plan, N), "cuda")
+    f_ws = B.workspace(B.cgtp_workspace_bytes(plan, N), "cuda")
 
     def step():
         B.cgtp_build_csr_order(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s), order=order)
@@ -92,7 +92,7 @@ def test_graph_full_step(B, torch):
     out, g_x, g_w, F = f32(N, plan.dim_out), f32(N, plan.dim_in1), f32(E, plan.weight_numel), f32(N, 3)
     gg, d_g, d_x, d_w = f32(E, 16), f32(N, plan.dim_out), f32(N, plan.dim_in1), f32(E, plan.weight_numel)
     csr_ws = B.workspace(B.cgtp_csr_workspace_bytes(E, N), "cuda")
-    ws = B.workspace(B.cgtp_conv_workspace_bytes(plan, N, E), "cuda")
+    ws = B.workspace(B.cgtp_workspace_bytes(plan, N, E), "cuda")
 
     def step():
         B.cgtp_build_csr_order(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s), order=order)
@@ -100,8 +100,8 @@ def test_graph_full_step(B, torch):
         B.cgtp_conv_forward_backward_vec(plan, x, vec, perm, w, src_s, rp, src_rp, src_perm, g_out, ws=ws,
                                          out=(out, g_x, None, g_w, F), node_order=order)
         B.cgtp_force_loss_sh_cotangent(3, vec, perm, src_s, dst_s, F, "f32", out=gg)
-        B.cgtp_conv_double_backward(plan, x, None, w, src_s, dst_s, rp, src_rp, src_perm, g_out, None, gg, None,
-                                    ws=ws, out=(d_g, d_x, None, d_w), node_order=order)
+        B.cgtp_double_backward(plan, x, None, w, g_out, None, gg, None, src_s, rp, src_rp, src_perm,
+                               ws=ws, out=(d_g, d_x, None, d_w), node_order=order)
 
     _replays_match_eager(torch, step, [perm, rp, src_perm, src_rp, out, g_x, g_w, F, gg, d_g, d_x, d_w],
                          "full step")

@@ -2,8 +2,10 @@
 seeded inputs, through the C ABI binding.
 
 Sizes: small cases span several workgroups and ragged channel/node tails;
-the workload sizes (1000 samples, 4096-atom box) are compared element by
-element; the 16384-atom FP64 box is compared on sampled destination rows.
+the workload sizes (1000 samples, the 4096-atom box forward and full step,
+the 16384-atom FP64 box) are compared element by element on every output;
+the 100 x 18 atom uvw layer, whose oracle mixes channels per edge, on 11 %
+of its rows.
 """
 import numpy as np
 import pytest
@@ -51,6 +53,53 @@ def test_single_tp_forward_c1(B, torch, batch):
     out = B.cgtp_forward(plan, to_dev(torch, x, "f32"), to_dev(torch, y, "f32"), to_dev(torch, w, "f32"))
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy(), prob.tp_forward(x, y, w), "f32", "c1 forward")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("batch", [1000, 1, 77])
+def test_single_tp_backward_c1(B, torch, batch, dtype):
+    """Backward of the single product (each item its own one-edge segment)
+    against the oracle's adjoint, every output and subsets of them."""
+    c = W.config("c1")
+    plan = B.Plan(c.irreps_in1, c.irreps_in2, c.irreps_out, c.paths, c.mode, dtype)
+    prob = oracle.Problem(c.irreps_in1, c.irreps_in2, c.irreps_out, c.mode, c.paths)
+    rng = np.random.default_rng(5)
+    x = W.normal(rng, (batch, prob.dim1), dtype)
+    y = W.normal(rng, (batch, prob.dim2), dtype)
+    w = W.normal(rng, (batch, prob.weight_numel), dtype)
+    g = W.normal(rng, (batch, prob.dim3), dtype)
+    rx, ry, rw = prob.tp_backward(x, y, w, g)
+    dv = lambda a: to_dev(torch, a, dtype)
+    print(f"c1 backward batch={batch} {dtype}", flush=True)
+    gx, gy, gw = B.cgtp_tp_backward(plan, dv(x), dv(y), dv(w), dv(g))
+    gx2, gy2, gw2 = B.cgtp_tp_backward(plan, dv(x), dv(y), dv(w), dv(g), need=("y",))
+    torch.cuda.synchronize()
+    assert gx2 is None and gw2 is None
+    assert_close(gx.cpu().numpy(), rx, dtype, "g_x")
+    assert_close(gy.cpu().numpy(), ry, dtype, "g_y")
+    assert_close(gw.cpu().numpy(), rw, dtype, "g_w")
+    assert_close(gy2.cpu().numpy(), ry, dtype, "g_y only")
+
+
+@pytest.mark.parametrize("k", range(4))
+def test_single_tp_backward_small(B, torch, k):
+    """The single product's backward on the ragged small plans (lanes per
+    item below 64, two channel slices, mul2 > 1, summed outputs)."""
+    plan, prob = _small_problem(B, k, "f64")
+    rng = np.random.default_rng(90 + k)
+    n = 45
+    x = W.normal(rng, (n, prob.dim1), "f64")
+    y = W.normal(rng, (n, prob.dim2), "f64")
+    w = W.normal(rng, (n, prob.weight_numel), "f64")
+    g = W.normal(rng, (n, prob.dim3), "f64")
+    rx, ry, rw = prob.tp_backward(x, y, w, g)
+    dv = lambda a: to_dev(torch, a, "f64")
+    print(f"single backward small k={k}", flush=True)
+    gx, gy, gw = B.cgtp_tp_backward(plan, dv(x), dv(y), dv(w), dv(g))
+    torch.cuda.synchronize()
+    assert_close(gx.cpu().numpy(), rx, "f64", "g_x")
+    assert_close(gy.cpu().numpy(), ry, "f64", "g_y")
+    assert_close(gw.cpu().numpy(), rw, "f64", "g_w")
 
 
 # ---------------------------------------------------------------------------
@@ -119,17 +168,17 @@ def test_conv_backward_small(B, torch, k, dtype):
     gx, gy, gw = prob.conv_backward(x, sh, w, src, dst, g)
     d = G.dev(torch)
     print(f"conv backward small k={k} {dtype}", flush=True)
-    ox, oy, ow = B.cgtp_conv_backward(plan, to_dev(torch, x, dtype), to_dev(torch, sh[G.perm], dtype),
-                                      to_dev(torch, w[G.perm], dtype), d["src"], d["dst"], d["dst_row_ptr"],
-                                      d["src_row_ptr"], d["src_perm"], to_dev(torch, g, dtype))
+    ox, oy, ow = B.cgtp_backward(plan, to_dev(torch, x, dtype), to_dev(torch, sh[G.perm], dtype),
+                                 to_dev(torch, w[G.perm], dtype), d["src"], d["dst_row_ptr"],
+                                 d["src_row_ptr"], d["src_perm"], to_dev(torch, g, dtype))
     torch.cuda.synchronize()
     assert_close(ox.cpu().numpy(), gx, dtype, "g_x")
     assert_close(oy.cpu().numpy(), gy[G.perm], dtype, "g_sh")
     assert_close(ow.cpu().numpy(), gw[G.perm], dtype, "g_w")
     # a subset of outputs
-    ox2, oy2, ow2 = B.cgtp_conv_backward(plan, to_dev(torch, x, dtype), to_dev(torch, sh[G.perm], dtype),
-                                         to_dev(torch, w[G.perm], dtype), d["src"], d["dst"], d["dst_row_ptr"],
-                                         d["src_row_ptr"], d["src_perm"], to_dev(torch, g, dtype), need=("sh",))
+    ox2, oy2, ow2 = B.cgtp_backward(plan, to_dev(torch, x, dtype), to_dev(torch, sh[G.perm], dtype),
+                                    to_dev(torch, w[G.perm], dtype), d["src"], d["dst_row_ptr"],
+                                    d["src_row_ptr"], d["src_perm"], to_dev(torch, g, dtype), need=("sh",))
     assert ox2 is None and ow2 is None
     assert_close(oy2.cpu().numpy(), gy[G.perm], dtype, "g_sh only")
 
@@ -152,9 +201,9 @@ def test_conv_double_backward_small(B, torch, dtype, which):
     d = G.dev(torch)
     dv = lambda a: None if a is None else to_dev(torch, a, dtype)
     print(f"double backward {which} {dtype}", flush=True)
-    og, ox, oy, ow = B.cgtp_conv_double_backward(
-        plan, dv(x), dv(sh[G.perm]), dv(w[G.perm]), d["src"], d["dst"], d["dst_row_ptr"], d["src_row_ptr"],
-        d["src_perm"], dv(g), dv(ax), dv(ay[G.perm]), None if aw is None else dv(aw[G.perm]))
+    og, ox, oy, ow = B.cgtp_double_backward(
+        plan, dv(x), dv(sh[G.perm]), dv(w[G.perm]), dv(g), dv(ax), dv(ay[G.perm]),
+        None if aw is None else dv(aw[G.perm]), d["src"], d["dst_row_ptr"], d["src_row_ptr"], d["src_perm"])
     torch.cuda.synchronize()
     assert_close(og.cpu().numpy(), dg, dtype, "d_g_out")
     assert_close(ox.cpu().numpy(), dx, dtype, "d_x")
@@ -190,11 +239,11 @@ def test_conv_bf16_weights_small(B, torch, k):
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
     print(f"bf16 weights small k={k}", flush=True)
     out = B.cgtp_conv_forward(plan, f32(x), f32(sh[G.perm]), bf(w[G.perm]), d["src"], d["dst_row_ptr"])
-    ox, oy, ow = B.cgtp_conv_backward(plan, f32(x), f32(sh[G.perm]), bf(w[G.perm]), d["src"], d["dst"],
-                                      d["dst_row_ptr"], d["src_row_ptr"], d["src_perm"], f32(g))
-    og, dx, dy, dw = B.cgtp_conv_double_backward(
-        plan, f32(x), f32(sh[G.perm]), bf(w[G.perm]), d["src"], d["dst"], d["dst_row_ptr"], d["src_row_ptr"],
-        d["src_perm"], f32(g), None, f32(ay[G.perm]), bf(aw[G.perm]))
+    ox, oy, ow = B.cgtp_backward(plan, f32(x), f32(sh[G.perm]), bf(w[G.perm]), d["src"],
+                                 d["dst_row_ptr"], d["src_row_ptr"], d["src_perm"], f32(g))
+    og, dx, dy, dw = B.cgtp_double_backward(
+        plan, f32(x), f32(sh[G.perm]), bf(w[G.perm]), f32(g), None, f32(ay[G.perm]), bf(aw[G.perm]),
+        d["src"], d["dst_row_ptr"], d["src_row_ptr"], d["src_perm"])
     torch.cuda.synchronize()
     assert ow.dtype == torch.float32 and dw.dtype == torch.float32
     assert_close(out.cpu().numpy(), prob.conv_forward(x, sh, w, src, dst, 61), "f32", "forward")
@@ -222,8 +271,9 @@ def test_conv_node_order_changes_nothing(B, torch, k):
     ay = W.normal(rng, sh.shape, "f32")
     d = G.dev(torch)
     f = lambda a: to_dev(torch, a, "f32")
-    args = (plan, f(x), f(sh[G.perm]), f(w[G.perm]), d["src"], d["dst"], d["dst_row_ptr"], d["src_row_ptr"],
+    args = (plan, f(x), f(sh[G.perm]), f(w[G.perm]), d["src"], d["dst_row_ptr"], d["src_row_ptr"],
             d["src_perm"], f(g))
+    graph = (d["src"], d["dst_row_ptr"], d["src_row_ptr"], d["src_perm"])
     lpt = B.cgtp_node_order(d["dst_row_ptr"])
     rand = torch.from_numpy(rng.permutation(61).astype(np.int32)).cuda()
     print(f"node order k={k}", flush=True)
@@ -231,8 +281,9 @@ def test_conv_node_order_changes_nothing(B, torch, k):
     for name, order in (("natural", None), ("lpt", lpt), ("random", rand)):
         out = B.cgtp_conv_forward(plan, f(x), f(sh[G.perm]), f(w[G.perm]), d["src"], d["dst_row_ptr"],
                                   node_order=order)
-        bwd = B.cgtp_conv_backward(*args, node_order=order)
-        dbl = B.cgtp_conv_double_backward(*args, None, f(ay[G.perm]), None, node_order=order, need=("g_out", "x", "w"))
+        bwd = B.cgtp_backward(*args, node_order=order)
+        dbl = B.cgtp_double_backward(plan, f(x), f(sh[G.perm]), f(w[G.perm]), f(g), None, f(ay[G.perm]), None, *graph,
+                                     node_order=order, need=("g_out", "x", "w"))
         torch.cuda.synchronize()
         res[name] = [t.cpu().numpy() for t in (out, *bwd, *[t for t in dbl if t is not None])]
     for name in ("lpt", "random"):
@@ -452,7 +503,9 @@ def test_validate_csr(B, torch):
     rp = torch.tensor([0, 2, 2, 5], dtype=torch.int32, device="cuda")
     idx = torch.tensor([0, 1, 2, 0, 1], dtype=torch.int32, device="cuda")
     assert B.cgtp_validate_csr(rp, 5, idx, 3)
-    assert not B.cgtp_validate_csr(rp, 6, idx, 3)                       # wrong end
+    assert not B.cgtp_validate_csr(rp, 6, None, 0)                      # wrong end
+    with pytest.raises(ValueError, match="idx: expected shape"):        # idx shorter than the edges
+        B.cgtp_validate_csr(rp, 6, idx, 3)
     assert not B.cgtp_validate_csr(rp, 5, idx, 2)                       # index out of range
     bad = torch.tensor([0, 3, 2, 5], dtype=torch.int32, device="cuda")  # not monotone
     assert not B.cgtp_validate_csr(bad, 5, None, 0)
@@ -467,7 +520,7 @@ def test_spherical_harmonics(B, torch, dtype, lmax):
     perm = rs.permutation(3001).astype(np.int32)
     ref = oracle.spherical_harmonics(lmax, vin.astype(np.float64))[perm]
     print(f"sh {dtype} lmax={lmax}", flush=True)
-    out = B.cgtp_spherical_harmonics(lmax, torch.from_numpy(vin).cuda(), torch.from_numpy(perm).cuda(), dtype)
+    out = B.cgtp_sh(lmax, torch.from_numpy(vin).cuda(), torch.from_numpy(perm).cuda(), dtype)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy() if dtype == "bf16" else out.cpu().numpy()
     if dtype == "bf16":
@@ -489,10 +542,18 @@ def test_forces_and_cotangent(B, torch, dtype):
     vec_d = torch.from_numpy(vec).cuda()
     perm_d = torch.from_numpy(G.perm).cuda()
     print(f"forces {dtype}", flush=True)
-    F = B.cgtp_sh_forces(3, vec_d, perm_d, to_dev(torch, g_sh[G.perm], dtype), d["dst_row_ptr"],
-                         d["src_row_ptr"], d["src_perm"], dtype)
+    gv, F = B.cgtp_sh_vjp_forces(3, vec_d, perm_d, to_dev(torch, g_sh[G.perm], dtype), d["dst_row_ptr"],
+                                 d["src_row_ptr"], d["src_perm"], dtype, need=("vec", "F"))
     torch.cuda.synchronize()
     assert_close(F.cpu().numpy(), F_ref, dtype, "forces")
+    # the per-edge vector-Jacobian products J^T g_sh in CSR order
+    J = oracle.sh_jacobian(3, vec.astype(np.float64))
+    vjp_ref = np.einsum("ekc,ek->ec", J, g_sh)[G.perm]
+    assert_close(gv.cpu().numpy(), vjp_ref, dtype, "SH vector-Jacobian products")
+    _, F2 = B.cgtp_sh_vjp_forces(3, vec_d, perm_d, to_dev(torch, g_sh[G.perm], dtype), d["dst_row_ptr"],
+                                 d["src_row_ptr"], d["src_perm"], dtype)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(F2.cpu().numpy(), F.cpu().numpy())
     Fx = W.normal(rs, (g.n_nodes, 3), dtype)
     gg_ref = oracle.force_loss_cotangent(3, g.n_nodes, g.src, g.dst, vec.astype(np.float64), Fx)
     gg = B.cgtp_force_loss_sh_cotangent(3, vec_d, perm_d, d["src"], d["dst"], to_dev(torch, Fx, dtype), dtype)
@@ -589,7 +650,7 @@ def test_conv_forward_backward_needs_out(B, torch):
     sh = torch.zeros(G.E, prob.dim2, device="cuda")
     w = torch.zeros(G.E, prob.weight_numel, device="cuda")
     g = torch.zeros(61, prob.dim3, device="cuda")
-    ws = B.workspace(B.cgtp_conv_workspace_bytes(plan, 61, G.E), "cuda")
+    ws = B.workspace(B.cgtp_workspace_bytes(plan, 61, G.E), "cuda")
     rc = B.lib().cgtp_conv_forward_backward(plan.handle, B._ptr(x), B._ptr(sh), B._ptr(w), B._ptr(d["src"]),
                                             B._ptr(d["dst_row_ptr"]), None, B._ptr(d["src_row_ptr"]),
                                             B._ptr(d["src_perm"]), B._ptr(g), 61, G.E, None, None, None, None,
@@ -606,15 +667,15 @@ def _zero_e_columns(irreps):
     return np.array(cols, dtype=np.int64)
 
 
-def test_c4_full_step_sampled(B, torch):
-    """The default bench step at full size (4096-atom box, cutoff 5 A, about
-    214k edges) with the bench's calls: CSR by destination and by source,
-    node order, forward and backward in one pass with the forces of
-    E = sum of the 0e outputs, the force-loss cotangent and the double
-    backward.  Outputs at sampled atoms and their edges against the oracle
-    on the edges they depend on: one hop for the forward, the gradients and
-    the forces, two for the double backward (its SH cotangent needs the
-    forces at both ends of an edge)."""
+def test_c4_full_step_full_size(B, torch):
+    """The default bench step at full size (4096-atom box, cutoff 5 A,
+    213,738 edges) with the bench's calls and launch configuration: CSR by
+    destination (with the longest-first order from the same launches) and by
+    source, forward and backward in one pass with the SH computed in the
+    kernel and the forces of E = sum of the 0e outputs, the force-loss
+    cotangent and the double backward.  Every output -- out, g_x, g_w, F,
+    gg_sh, d_g_out, d_x, d_w -- against the oracle's full step, element by
+    element."""
     c = W.config("c2")
     plan, prob = _plan(B, c)
     rng = np.random.default_rng(0)
@@ -626,14 +687,11 @@ def test_c4_full_step_sampled(B, torch):
     g_out = np.zeros((N, prob.dim3))
     g_out[:, _zero_e_columns(c.irreps_out)] = 1.0
     src, dst = g.src, g.dst
-    perm_ref, _ = oracle.csr(dst, N)
-    pos_of = np.empty(E, np.int64)
-    pos_of[perm_ref] = np.arange(E)          # canonical edge id -> CSR position
+    perm_ref, rp_ref = oracle.csr(dst, N)
     print(f"c4 full step E={E}", flush=True)
     src_c, dst_c = torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda()
-    perm, rp, dst_s, src_s = B.cgtp_build_csr(dst_c, N, val=src_c)
+    perm, rp, dst_s, src_s, order = B.cgtp_build_csr_order(dst_c, N, val=src_c)
     src_perm, src_rp, _, _ = B.cgtp_build_csr(src_s, N, sorted_key=False)
-    order = B.cgtp_node_order(rp)
     x_d = to_dev(torch, x, "f32")
     w_d = to_dev(torch, w[perm_ref], "f32")
     vec_d = torch.from_numpy(vec).cuda()
@@ -641,39 +699,42 @@ def test_c4_full_step_sampled(B, torch):
     out, gx, _, gw, F = B.cgtp_conv_forward_backward_vec(plan, x_d, vec_d, perm, w_d, src_s, rp, src_rp, src_perm,
                                                          g_d, need=("x", "w", "F"), node_order=order)
     gg = B.cgtp_force_loss_sh_cotangent(3, vec_d, perm, src_s, dst_s, F, "f32")
-    dg, dx, _, dw = B.cgtp_conv_double_backward(plan, x_d, None, w_d, src_s, dst_s, rp, src_rp, src_perm, g_d,
-                                                None, gg, None, need=("g_out", "x", "w"), node_order=order)
+    dg, dx, _, dw = B.cgtp_double_backward(plan, x_d, None, w_d, g_d, None, gg, None, src_s, rp, src_rp, src_perm,
+                                           need=("g_out", "x", "w"), node_order=order)
     torch.cuda.synchronize()
-    out, gx, gw, F = out.cpu().numpy(), gx.cpu().numpy(), gw.cpu().numpy(), F.cpu().numpy()
-    dg, dx, dw = dg.cpu().numpy(), dx.cpu().numpy(), dw.cpu().numpy()
-
-    deg = np.bincount(dst, minlength=N)
-    S = np.unique(np.concatenate([rng.choice(N, 3, replace=False), [int(np.argmax(deg)), int(np.argmin(deg))]]))
+    assert np.array_equal(perm.cpu().numpy(), perm_ref) and np.array_equal(rp.cpu().numpy(), rp_ref)
+    print("c4 full step: oracle", flush=True)
     v64 = vec.astype(np.float64)
-    sh_all = oracle.spherical_harmonics(3, v64)
-    # one hop: edges into S (forward, per-edge gradients), out of S (g_x), both (forces)
-    e_in = np.nonzero(np.isin(dst, S))[0]
-    e_out = np.nonzero(np.isin(src, S))[0]
-    e_inc = np.union1d(e_in, e_out)
-    ref_out = prob.conv_forward(x, sh_all[e_in], w[e_in], src[e_in], dst[e_in], N)
-    assert_close(out[S], ref_out[S], "f32", "out at sampled atoms")
-    gx1, gy1, gw1 = prob.conv_backward(x, sh_all[e_inc], w[e_inc], src[e_inc], dst[e_inc], g_out)
-    assert_close(gx[S], gx1[S], "f32", "g_x at sampled atoms")
-    into = np.isin(dst[e_inc], S)
-    assert_close(gw[pos_of[e_inc[into]]], gw1[into], "f32", "g_w of edges into sampled atoms")
-    F1 = oracle.forces(3, N, src[e_inc], dst[e_inc], v64[e_inc], gy1)
-    assert_close(F[S], F1[S], "f32", "forces at sampled atoms")
-    # two hops: forces at every end of the edges touching S, from all their edges
-    A = np.unique(np.concatenate([S, src[e_inc], dst[e_inc]]))
-    e_A = np.nonzero(np.isin(dst, A) | np.isin(src, A))[0]
-    _, gyA, _ = prob.conv_backward(x, sh_all[e_A], w[e_A], src[e_A], dst[e_A], g_out, need=("sh",))
-    FA = oracle.forces(3, N, src[e_A], dst[e_A], v64[e_A], gyA)
-    gg1 = oracle.force_loss_cotangent(3, N, src[e_inc], dst[e_inc], v64[e_inc], FA)
-    rg, rx, _, rw = prob.conv_double_backward(x, sh_all[e_inc], w[e_inc], src[e_inc], dst[e_inc], g_out,
-                                              None, gg1, None)
-    assert_close(dg[S], rg[S], "f32", "double backward d_g_out at sampled atoms")
-    assert_close(dx[S], rx[S], "f32", "double backward d_x at sampled atoms")
-    assert_close(dw[pos_of[e_inc[into]]], rw[into], "f32", "double backward d_w of edges into sampled atoms")
+    sh = oracle.spherical_harmonics(3, v64)
+    r_out = prob.conv_forward(x, sh, w, src, dst, N)
+    print("out", assert_close(out.cpu().numpy(), r_out, "f32", "out"), flush=True)
+    del r_out
+    r_gx, r_gy, r_gw = prob.conv_backward(x, sh, w, src, dst, g_out)
+    print("g_x", assert_close(gx.cpu().numpy(), r_gx, "f32", "g_x"), flush=True)
+    print("g_w", assert_close(gw.cpu().numpy(), r_gw[perm_ref], "f32", "g_w"), flush=True)
+    del r_gw
+    r_F = oracle.forces(3, N, src, dst, v64, r_gy)
+    print("F", assert_close(F.cpu().numpy(), r_F, "f32", "forces"), flush=True)
+    r_gg = oracle.force_loss_cotangent(3, N, src, dst, v64, r_F)
+    print("gg", assert_close(gg.cpu().numpy(), r_gg[perm_ref], "f32", "force-loss SH cotangent"), flush=True)
+    # the double backward driven by gg_sh alone: the x and w cotangents are
+    # zero, so by trilinearity d_g_out = f(x, gg_sh, w), d_x = fx*(g; gg_sh, w),
+    # d_w = fw*(g; x, gg_sh)
+    r_dg = prob.conv_forward(x, r_gg, w, src, dst, N)
+    print("d_g_out", assert_close(dg.cpu().numpy(), r_dg, "f32", "d_g_out"), flush=True)
+    del r_dg
+    r_dx, _, r_dw = prob.conv_backward(x, r_gg, w, src, dst, g_out, need=("x", "w"))
+    assert_close(dx.cpu().numpy(), r_dx, "f32", "d_x")
+    dw_h, r_dw = dw.cpu().numpy(), r_dw[perm_ref]
+    # diagnostics: error per path block of the weight gradient
+    for pi, row in enumerate(prob.table):
+        o, n = int(row["woff"]), int(row["mul1"]) * int(row["mul2"])
+        blk_r = r_dw[:, o:o + n]
+        rms = float(np.sqrt(np.mean(blk_r * blk_r)))
+        err = np.abs(dw_h[:, o:o + n] - blk_r)
+        print(f"d_w path {pi}: rms {rms:.3e} max abs err {err.max():.3e} rel(block) {rel_err(dw_h[:, o:o + n], blk_r):.3e}",
+              flush=True)
+    assert_close(dw_h, r_dw, "f32", "d_w")
 
 
 # ---------------------------------------------------------------------------
@@ -692,7 +753,7 @@ def test_c2_forward_full_size(B, torch):
     ref = prob.conv_forward(x, sh_ref, w, g.src, g.dst, g.n_nodes)
     d = G.dev(torch)
     print(f"c2 full forward E={g.n_edges}", flush=True)
-    sh = B.cgtp_spherical_harmonics(3, torch.from_numpy(vec32).cuda(), torch.from_numpy(G.perm).cuda(), "f32")
+    sh = B.cgtp_sh(3, torch.from_numpy(vec32).cuda(), torch.from_numpy(G.perm).cuda(), "f32")
     out = B.cgtp_conv_forward(plan, to_dev(torch, x, "f32"), sh, to_dev(torch, w[G.perm], "f32"), d["src"],
                               d["dst_row_ptr"])
     torch.cuda.synchronize()
@@ -717,7 +778,9 @@ def _sampled_rows_check(prob, x, sh, w, src, dst, n_nodes, got_rows, rows, dtype
     return assert_close(got_rows, ref, dtype, "sampled rows")
 
 
-def test_c3_forward_fp64_full_size_sampled(B, torch):
+def test_c3_forward_fp64_full_size(B, torch):
+    """16,384-atom FP64 layer (859,102 edges, 17 paths): every output row
+    against the oracle."""
     c = W.config("c3")
     plan, prob = _plan(B, c)
     rng = np.random.default_rng(0)
@@ -728,20 +791,21 @@ def test_c3_forward_fp64_full_size_sampled(B, torch):
     w = W.normal(rng, (g.n_edges, prob.weight_numel), "f64")
     d = G.dev(torch)
     w_d = torch.from_numpy(w[G.perm]).cuda()
-    sh = B.cgtp_spherical_harmonics(3, torch.from_numpy(g.vec).cuda(), torch.from_numpy(G.perm).cuda(), "f64")
+    sh = B.cgtp_sh(3, torch.from_numpy(g.vec).cuda(), torch.from_numpy(G.perm).cuda(), "f64")
     print("c3 full forward: launch", flush=True)
     out = B.cgtp_conv_forward(plan, to_dev(torch, x, "f64"), sh, w_d, d["src"], d["dst_row_ptr"])
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(1).choice(g.n_nodes, 48, replace=False))
-    sh_ref = oracle.spherical_harmonics(3, g.vec)
-    _sampled_rows_check(prob, x, sh_ref, w, g.src, g.dst, g.n_nodes, out[torch.from_numpy(rows).cuda()].cpu().numpy(),
-                        rows, "f64")
+    got = out.cpu().numpy()
+    del out, w_d
+    print("c3 full forward: oracle", flush=True)
+    ref = prob.conv_forward(x, oracle.spherical_harmonics(3, g.vec), w, g.src, g.dst, g.n_nodes)
+    assert_close(got, ref, "f64", "c3 forward, all rows")
 
 
-def test_c2a_all_parity_morton_full_size_sampled(B, torch):
+def test_c2a_all_parity_morton_full_size(B, torch):
     """All output parities (13 paths, odd paths included) on the 4096-atom
     box numbered along a Z-order curve, processed in longest-row-first
-    order: forward rows and the per-edge gradients of the edges into them."""
+    order: every forward row and every per-edge and per-node gradient."""
     c = W.config("c2a")
     plan, prob = _plan(B, c)
     assert plan.n_paths == 13 and plan.dim_out == 7040
@@ -754,35 +818,25 @@ def test_c2a_all_parity_morton_full_size_sampled(B, torch):
     d = G.dev(torch)
     vec32 = g.vec.astype(np.float32)
     print(f"c2a forward+backward E={g.n_edges}", flush=True)
-    sh = B.cgtp_spherical_harmonics(3, torch.from_numpy(vec32).cuda(), torch.from_numpy(G.perm).cuda(), "f32")
+    sh = B.cgtp_sh(3, torch.from_numpy(vec32).cuda(), torch.from_numpy(G.perm).cuda(), "f32")
     order = B.cgtp_node_order(d["dst_row_ptr"])
     args = (plan, to_dev(torch, x, "f32"), sh, to_dev(torch, w[G.perm], "f32"), d["src"])
     out = B.cgtp_conv_forward(*args, d["dst_row_ptr"], node_order=order)
-    _, ogy, ogw = B.cgtp_conv_backward(*args, d["dst"], d["dst_row_ptr"], d["src_row_ptr"], d["src_perm"],
-                                       to_dev(torch, gout, "f32"), node_order=order)
+    ogx, ogy, ogw = B.cgtp_backward(*args, d["dst_row_ptr"], d["src_row_ptr"], d["src_perm"],
+                                    to_dev(torch, gout, "f32"), node_order=order)
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(3).choice(g.n_nodes, 32, replace=False))
     sh_ref = oracle.spherical_harmonics(3, vec32.astype(np.float64))
-    _sampled_rows_check(prob, x, sh_ref, w, g.src, g.dst, g.n_nodes,
-                        out[torch.from_numpy(rows).cuda()].cpu().numpy(), rows, "f32")
-    # per-edge gradients of the edges into the sampled rows
-    mask = np.isin(g.dst, rows)
-    remap = {r: i for i, r in enumerate(rows)}
-    sub_dst = np.array([remap[v] for v in g.dst[mask]], np.int32)
-    uniq, inv = np.unique(g.src[mask], return_inverse=True)
-    n_sub = max(len(uniq), len(rows))
-    x_sub = np.zeros((n_sub, prob.dim1)); x_sub[:len(uniq)] = x[uniq]
-    g_sub = np.zeros((n_sub, prob.dim3)); g_sub[:len(rows)] = gout[rows]
-    _, rgy, rgw = prob.conv_backward(x_sub, sh_ref[mask], w[mask], inv.astype(np.int32), sub_dst, g_sub)
-    pos = np.argsort(G.perm)[np.nonzero(mask)[0]]      # dst-sorted position of each masked edge
-    pos_d = torch.from_numpy(pos).cuda()
-    assert_close(ogy[pos_d].cpu().numpy(), rgy, "f32", "c2a g_sh")
-    assert_close(ogw[pos_d].cpu().numpy(), rgw, "f32", "c2a g_w")
+    assert_close(out.cpu().numpy(), prob.conv_forward(x, sh_ref, w, g.src, g.dst, g.n_nodes), "f32", "c2a out")
+    rgx, rgy, rgw = prob.conv_backward(x, sh_ref, w, g.src, g.dst, gout)
+    assert_close(ogx.cpu().numpy(), rgx, "f32", "c2a g_x")
+    assert_close(ogy.cpu().numpy(), rgy[G.perm], "f32", "c2a g_sh")
+    assert_close(ogw.cpu().numpy(), rgw[G.perm], "f32", "c2a g_w")
 
 
-def test_c3a_all_parity_fp64_sampled(B, torch):
-    """24 paths in FP64 on a 4096-atom box (the 16384-atom box is covered by
-    the 17-path test; its 24-path weights alone would take 21 GB)."""
+def test_c3a_all_parity_fp64_full_size(B, torch):
+    """24 paths in FP64 on a 4096-atom box, every row (the 16384-atom box is
+    covered by the 17-path test; its 24-path weights alone would take
+    21 GB)."""
     c = W.config("c3a")
     plan, prob = _plan(B, c)
     assert plan.n_paths == 24
@@ -793,14 +847,14 @@ def test_c3a_all_parity_fp64_sampled(B, torch):
     print(f"c3a full forward E={g.n_edges}: drawing weights", flush=True)
     w = W.normal(rng, (g.n_edges, prob.weight_numel), "f64")
     d = G.dev(torch)
-    sh = B.cgtp_spherical_harmonics(3, torch.from_numpy(g.vec).cuda(), torch.from_numpy(G.perm).cuda(), "f64")
+    sh = B.cgtp_sh(3, torch.from_numpy(g.vec).cuda(), torch.from_numpy(G.perm).cuda(), "f64")
     print("c3a full forward: launch", flush=True)
     out = B.cgtp_conv_forward(plan, to_dev(torch, x, "f64"), sh, torch.from_numpy(w[G.perm]).cuda(), d["src"],
                               d["dst_row_ptr"], node_order=B.cgtp_node_order(d["dst_row_ptr"]))
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(4).choice(g.n_nodes, 24, replace=False))
-    _sampled_rows_check(prob, x, oracle.spherical_harmonics(3, g.vec), w, g.src, g.dst, g.n_nodes,
-                        out[torch.from_numpy(rows).cuda()].cpu().numpy(), rows, "f64")
+    got = out.cpu().numpy()
+    ref = prob.conv_forward(x, oracle.spherical_harmonics(3, g.vec), w, g.src, g.dst, g.n_nodes)
+    assert_close(got, ref, "f64", "c3a forward, all rows")
 
 
 # ---------------------------------------------------------------------------
@@ -903,6 +957,8 @@ def test_c5_uvw_full_size_sampled(B, torch):
                               to_dev(torch, w, "bf16"), d["src"], d["dst_row_ptr"])
     torch.cuda.synchronize()
     sh_canon = sh
-    rows = np.sort(np.random.default_rng(2).choice(g.n_nodes, 24, replace=False))
+    # 200 of the 1,800 rows (11 %): the uvw oracle mixes per edge (2.3 M
+    # multiply-adds per edge), so every row would take minutes on the host
+    rows = np.sort(np.random.default_rng(2).choice(g.n_nodes, 200, replace=False))
     _sampled_rows_check(prob, x, sh_canon, np.broadcast_to(w, (g.n_edges, w.size)), g.src, g.dst, g.n_nodes,
                         out[torch.from_numpy(rows).cuda()].cpu().numpy(), rows, "bf16")

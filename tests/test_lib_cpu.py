@@ -127,12 +127,19 @@ def test_compile_failure_is_reported(B, tmp_path, monkeypatch):
 
 
 def test_no_load_plan_refuses_execution(B):
-    import torch
+    """A plan made with CGTP_PLAN_NO_LOAD has no kernels on a device: every
+    execution call refuses it on the host, before any launch."""
+    import ctypes
     p = B.Plan("8x0e", "1x0e", "8x0e", no_load=True)
-    x = torch.zeros(2, 8)
-    with pytest.raises(B.CgtpError) as ei:
-        B.cgtp_forward(p, x, torch.zeros(2, 1), torch.zeros(2, 8), out=torch.zeros(2, 8))
-    assert ei.value.code == -1
+    buf = (ctypes.c_double * 64)()
+    L = B.lib()
+    assert L.cgtp_forward(p.handle, buf, buf, buf, 2, buf, None, 0, None) == -1
+    assert "NO_LOAD" in L.cgtp_last_error().decode()
+    assert L.cgtp_tp_backward(p.handle, buf, buf, buf, 2, buf, buf, None, None, buf, 512, None) == -1
+    assert L.cgtp_backward(p.handle, buf, buf, buf, buf, buf, None, buf, buf, buf, 2, 2, buf, None, None, buf, 512,
+                           None) == -1
+    assert L.cgtp_double_backward(p.handle, buf, buf, buf, buf, None, buf, None, buf, buf, None, buf, buf, 2, 2, buf,
+                                  None, None, None, buf, 512, None) == -1
 
 
 def test_cache_round_trip(B, tmp_path, monkeypatch):
@@ -165,7 +172,7 @@ def test_plan_flag_combinations(B, tmp_path, monkeypatch):
     p = B.Plan("8x0+8x1", "1x0+1x1+1x2", "8x0+8x1", None, "uvw", "bf16", True, radial_hidden=3, no_load=True)
     # radial plans: (H+1) copies of every path along the mixing contraction
     plain = B.Plan("8x0+8x1", "1x0+1x1+1x2", "8x0+8x1", None, "uvw", "bf16", True, no_load=True)
-    assert B.cgtp_forward_workspace_bytes(p, 100) >= 4 * B.cgtp_forward_workspace_bytes(plain, 100) - 1024
+    assert B.cgtp_workspace_bytes(p, 100) >= 4 * B.cgtp_workspace_bytes(plain, 100) - 1024
 
 
 def test_graph_helper_sizes(B):
@@ -205,13 +212,121 @@ def test_csr_argument_errors(B):
 def test_sh_from_vectors_needs_sh_row_plan(B):
     """cgtp_conv_forward_vec refuses plans whose input 2 is not one SH row
     before any device work (checked on the host)."""
-    import torch
+    import ctypes
     p = B.Plan("8x0e+8x1o", "2x0e+1x1o", "8x0e+8x1o", no_load=True)
-    e = torch.zeros(1, dtype=torch.int32)
-    with pytest.raises(B.CgtpError) as ei:
-        B.cgtp_conv_forward_vec(p, torch.zeros(2, p.dim_in1), torch.ones(1, 3), None, torch.zeros(1, p.weight_numel),
-                                e, torch.tensor([0, 1, 1], dtype=torch.int32))
-    assert ei.value.code in (-1, -2)
+    buf = (ctypes.c_double * 64)()
+    rc = B.lib().cgtp_conv_forward_vec(p.handle, buf, buf, None, buf, buf, buf, None, 2, 1, buf, None, 0, None)
+    assert rc == -2
+    assert "SH row" in B.lib().cgtp_last_error().decode()
+
+
+def test_workspace_query(B):
+    """cgtp_workspace_bytes: one size for every execution call of a plan;
+    argument errors before any device contact."""
+    import ctypes
+    L = B.lib()
+    b = ctypes.c_size_t()
+    c = W.config("c2")
+    p = B.Plan(c.irreps_in1, c.irreps_in2, c.irreps_out, c.paths, c.mode, c.dtype, no_load=True)
+    assert L.cgtp_workspace_bytes(None, 10, 10, ctypes.byref(b)) == -1
+    assert L.cgtp_workspace_bytes(p.handle, -1, 10, ctypes.byref(b)) == -1
+    assert L.cgtp_workspace_bytes(p.handle, 10, -1, ctypes.byref(b)) == -1
+    assert L.cgtp_workspace_bytes(p.handle, 10, 10, None) == -1
+    # uvu: the backward's per-edge x-messages (E x dim1 floats) dominate
+    E = 213738
+    n = B.cgtp_workspace_bytes(p, 4096, E)
+    assert n >= E * p.dim_in1 * 4 + E * 3 * 4
+    assert B.cgtp_workspace_bytes(p, 4096, 2 * E) > n
+    # single product: its backward counts each item as one edge
+    assert B.cgtp_workspace_bytes(p, 1000, 0) == B.cgtp_workspace_bytes(p, 1000, 1000)
+    # uvw: the path tensors of every item (bf16), at least
+    c5 = W.config("c5")
+    q = B.Plan(c5.irreps_in1, c5.irreps_in2, c5.irreps_out, c5.paths, c5.mode, c5.dtype, c5.shared_weights,
+               no_load=True)
+    assert B.cgtp_workspace_bytes(q, 1800, 0) >= 1800 * 2 * 32 * 1132 // 16
+
+
+def test_sh_helpers_argument_errors(B):
+    """cgtp_sh and cgtp_sh_vjp_forces check sizes, NULL buffers, dtype and
+    degree on the host before any launch."""
+    import ctypes
+    L = B.lib()
+    buf = (ctypes.c_double * 64)()
+    F32, F64, BF16 = 0, 1, 2
+    assert L.cgtp_sh(3, F32, buf, None, -1, buf, None) == -1
+    assert L.cgtp_sh(3, F32, None, None, 4, buf, None) == -1
+    assert L.cgtp_sh(3, 7, buf, None, 4, buf, None) == -2          # unknown dtype
+    assert L.cgtp_sh(7, F32, buf, None, 4, buf, None) == -2        # degree above 6
+    assert L.cgtp_sh(3, F32, None, None, 0, None, None) == 0       # nothing to do
+    # vjp / forces: bf16 is not provided; negative sizes; forces need both CSRs
+    assert L.cgtp_sh_vjp_forces(3, BF16, buf, None, buf, buf, buf, buf, 2, 2, buf, buf, None, 0, None) == -2
+    assert L.cgtp_sh_vjp_forces(3, F32, buf, None, buf, buf, buf, buf, -1, 2, buf, buf, None, 0, None) == -1
+    assert L.cgtp_sh_vjp_forces(3, F32, buf, None, buf, None, buf, buf, 2, 2, buf, buf, None, 0, None) == -1
+    assert L.cgtp_sh_vjp_forces(3, F32, None, None, buf, buf, buf, buf, 2, 2, buf, buf, None, 0, None) == -1
+    # forces without g_vec need 3 E elements of workspace
+    assert L.cgtp_sh_vjp_forces(3, F64, buf, None, buf, buf, buf, buf, 2, 2, None, buf, buf, 47, None) == -1
+    assert L.cgtp_sh_vjp_forces(7, F64, buf, None, buf, buf, buf, buf, 2, 2, buf, buf, None, 0, None) == -2
+    # neither output: nothing to do
+    assert L.cgtp_sh_vjp_forces(3, F32, buf, None, buf, None, None, None, 2, 2, None, None, None, 0, None) == 0
+
+
+def test_binding_rejects_bad_arguments(B):
+    """The binding checks shape, dtype, contiguity and device of every tensor
+    before it calls the library, so a short buffer, a wrong dtype or a host
+    tensor never reaches a kernel as a raw pointer."""
+    import torch
+    c = W.config("c2")
+    p = B.Plan(c.irreps_in1, c.irreps_in2, c.irreps_out, c.paths, c.mode, c.dtype, no_load=True)
+    N, E = 5, 7
+    i32 = lambda *s: torch.zeros(*s, dtype=torch.int32)
+    f32 = lambda *s: torch.zeros(*s)
+    x, sh, w, g = f32(N, p.dim_in1), f32(E, p.dim_in2), f32(E, p.weight_numel), f32(N, p.dim_out)
+    src, rp, sperm, srp = i32(E), i32(N + 1), i32(E), i32(N + 1)
+    ok = dict(x=x, sh=sh, w=w, src=src, dst_row_ptr=rp)
+
+    def fwd(**kw):
+        a = dict(ok, **kw)
+        return B.cgtp_conv_forward(p, a["x"], a["sh"], a["w"], a["src"], a["dst_row_ptr"],
+                                   node_order=a.get("node_order"), out=a.get("out"))
+
+    with pytest.raises(ValueError, match="sh: expected shape"):
+        fwd(sh=f32(E - 1, p.dim_in2))
+    with pytest.raises(ValueError, match="w: expected shape"):
+        fwd(w=f32(E, p.weight_numel - 1))
+    with pytest.raises(ValueError, match="dst_row_ptr: expected shape"):
+        fwd(dst_row_ptr=i32(N))
+    with pytest.raises(ValueError, match="node_order: expected shape"):
+        fwd(node_order=i32(N + 1))
+    with pytest.raises(ValueError, match="out: expected shape"):
+        fwd(out=f32(N, p.dim_out + 1))
+    with pytest.raises(TypeError, match="x: expected torch.float32"):
+        fwd(x=torch.zeros(N, p.dim_in1, dtype=torch.float64))
+    with pytest.raises(TypeError, match="src: expected torch.int32"):
+        fwd(src=torch.zeros(E, dtype=torch.int64))
+    with pytest.raises(ValueError, match="contiguous"):
+        fwd(w=f32(p.weight_numel, E).t())
+    with pytest.raises(ValueError, match="on cpu"):
+        fwd()
+    with pytest.raises(ValueError, match="g_out: expected shape"):
+        B.cgtp_backward(p, x, sh, w, src, rp, srp, sperm, f32(N, p.dim_out - 1))
+    with pytest.raises(ValueError, match="src_perm: expected shape"):
+        B.cgtp_backward(p, x, sh, w, src, rp, srp, i32(E + 1), g)
+    with pytest.raises(ValueError, match="gg_sh: expected shape"):
+        B.cgtp_double_backward(p, x, None, w, g, None, f32(E + 1, p.dim_in2), None, src, rp, srp, sperm)
+    with pytest.raises(ValueError, match="vec: expected shape"):
+        B.cgtp_conv_forward_vec(p, x, f32(E + 1, 3), None, w, src, rp)
+    with pytest.raises(TypeError, match="vec: expected torch.float32"):
+        B.cgtp_conv_forward_vec(p, x, torch.zeros(E, 3, dtype=torch.float64), None, w, src, rp)
+    with pytest.raises(ValueError, match="g_sh: expected shape"):
+        B.cgtp_sh_vjp_forces(3, f32(E, 3), None, f32(E, 15), rp, srp, sperm)
+    with pytest.raises(ValueError, match="dst_row_ptr is required"):
+        B.cgtp_sh_vjp_forces(3, f32(E, 3), None, f32(E, 16), None, srp, sperm)
+    with pytest.raises(ValueError, match="on cpu"):
+        B.cgtp_sh(3, f32(E, 3))
+    # FP64 plans want float64 everywhere (vectors included)
+    p64 = B.Plan(c.irreps_in1, c.irreps_in2, c.irreps_out, c.paths, c.mode, "f64", no_load=True)
+    with pytest.raises(TypeError, match="x: expected torch.float64"):
+        B.cgtp_conv_forward(p64, x, sh.double(), w.double(), src, rp)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
