@@ -116,9 +116,11 @@ __global__ void k_sum_parts(const T *__restrict__ parts, int n_parts, int64_t n,
                             int accumulate) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x) {
-        T acc = 0;
-        for (int p = 0; p < n_parts; ++p) acc += parts[p * n + i];
-        out[i] = accumulate ? out[i] + acc : acc;
+        // the unit partials of an SH-gradient row, summed in FP64 (as the
+        // lanes of each unit were)
+        double acc = 0;
+        for (int p = 0; p < n_parts; ++p) acc += (double)parts[p * n + i];
+        out[i] = (T)(accumulate ? (double)out[i] + acc : acc);
     }
 }
 
@@ -718,6 +720,13 @@ __device__ inline void sh_grad_contract(const ShPoly<T, L> &P, const T *c, T G[3
     }
 }
 
+// The force path runs in FP64 whatever the storage type.  Its last step,
+// the force-loss cotangent -J (F[dst] - F[src]), multiplies force errors by
+// the SH Jacobian, which grows as 1/|r| on the shortest edges, so FP32
+// roundoff in F (sums of about a hundred edge vectors per atom) would reach
+// the second derivatives ten to twenty times amplified.  The three kernels
+// below load and store the storage type and compute in double.
+
 // per-edge force vector v_t = J_t^T g_t = (I - u u^T) G / |r|; g_t is the
 // sum of n_parts partial rows part_stride elements apart
 template <class T, int L>
@@ -728,22 +737,22 @@ __global__ void k_edge_force(const T *__restrict__ vec, const int32_t *__restric
     for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n;
          t += (int64_t)gridDim.x * blockDim.x) {
         const int64_t e = perm ? perm[t] : t;
-        T rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
-        const T rn = sqrt(rx * rx + ry * ry + rz * rz), inv = (T)1 / rn;
-        const T u[3] = {rx * inv, ry * inv, rz * inv};
-        ShPoly<T, L> P;
+        const double rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
+        const double rn = sqrt(rx * rx + ry * ry + rz * rz), inv = 1.0 / rn;
+        const double u[3] = {rx * inv, ry * inv, rz * inv};
+        ShPoly<double, L> P;
         P.eval(u[0], u[1], u[2]);
-        T c[NS];
+        double c[NS];
 #pragma unroll
         for (int k = 0; k < NS; ++k) c[k] = g_sh[t * NS + k];
         for (int q = 1; q < n_parts; ++q)
 #pragma unroll
             for (int k = 0; k < NS; ++k) c[k] += g_sh[q * part_stride + t * NS + k];
-        T G[3];
-        sh_grad_contract<T, L>(P, c, G);
-        const T ug = u[0] * G[0] + u[1] * G[1] + u[2] * G[2];
+        double G[3];
+        sh_grad_contract<double, L>(P, c, G);
+        const double ug = u[0] * G[0] + u[1] * G[1] + u[2] * G[2];
 #pragma unroll
-        for (int a = 0; a < 3; ++a) v[3 * t + a] = (G[a] - u[a] * ug) * inv;
+        for (int a = 0; a < 3; ++a) v[3 * t + a] = (T)((G[a] - u[a] * ug) * inv);
     }
 }
 
@@ -757,7 +766,7 @@ __global__ void __launch_bounds__(64) k_node_force(const T *__restrict__ v, cons
                                                    T *__restrict__ F) {
     const int64_t a = blockIdx.x;
     const int lane = threadIdx.x;
-    T f0 = 0, f1 = 0, f2 = 0;
+    double f0 = 0, f1 = 0, f2 = 0;
     for (int t = dst_row_ptr[a] + lane; t < dst_row_ptr[a + 1]; t += 64) {
         f0 -= v[3 * (int64_t)t];
         f1 -= v[3 * (int64_t)t + 1];
@@ -775,9 +784,9 @@ __global__ void __launch_bounds__(64) k_node_force(const T *__restrict__ v, cons
         f2 += __shfl_xor(f2, off, 64);
     }
     if (lane == 0) {
-        F[3 * a] = f0;
-        F[3 * a + 1] = f1;
-        F[3 * a + 2] = f2;
+        F[3 * a] = (T)f0;
+        F[3 * a + 1] = (T)f1;
+        F[3 * a + 2] = (T)f2;
     }
 }
 
@@ -791,28 +800,29 @@ __global__ void k_force_cotangent(const T *__restrict__ vec, const int32_t *__re
     for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n;
          t += (int64_t)gridDim.x * blockDim.x) {
         const int64_t e = perm ? perm[t] : t;
-        T rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
-        const T rn = sqrt(rx * rx + ry * ry + rz * rz), inv = (T)1 / rn;
-        const T u[3] = {rx * inv, ry * inv, rz * inv};
+        const double rx = vec[3 * e], ry = vec[3 * e + 1], rz = vec[3 * e + 2];
+        const double rn = sqrt(rx * rx + ry * ry + rz * rz), inv = 1.0 / rn;
+        const double u[3] = {rx * inv, ry * inv, rz * inv};
         const int64_t a = dst[t], b = src[t];
-        T d[3] = {F[3 * a] - F[3 * b], F[3 * a + 1] - F[3 * b + 1], F[3 * a + 2] - F[3 * b + 2]};
-        const T ud = u[0] * d[0] + u[1] * d[1] + u[2] * d[2];
+        double d[3] = {(double)F[3 * a] - (double)F[3 * b], (double)F[3 * a + 1] - (double)F[3 * b + 1],
+                       (double)F[3 * a + 2] - (double)F[3 * b + 2]};
+        const double ud = u[0] * d[0] + u[1] * d[1] + u[2] * d[2];
 #pragma unroll
         for (int c = 0; c < 3; ++c) d[c] = (d[c] - u[c] * ud) * inv;
-        ShPoly<T, L> P;
+        ShPoly<double, L> P;
         P.eval(u[0], u[1], u[2]);
         T *o = gg + t * NS;
 #pragma unroll
         for (int l = 0; l <= L; ++l) {
-            o[l * l + l] = -(T)N.v[l * l + l] * P.Q[l][1] * d[2];
+            o[l * l + l] = (T)(-N.v[l * l + l] * P.Q[l][1] * d[2]);
 #pragma unroll
             for (int m = 1; m <= l; ++m) {
-                const T nm = (T)N.v[l * l + l + m];
-                const T q = P.Q[l][m], dq = P.Q[l][m + 1];
-                const T gp0 = nm * q * (T)m * P.A[m - 1], gp1 = -nm * q * (T)m * P.B[m - 1], gp2 = nm * dq * P.A[m];
-                const T gn0 = nm * q * (T)m * P.B[m - 1], gn1 = nm * q * (T)m * P.A[m - 1], gn2 = nm * dq * P.B[m];
-                o[l * l + l + m] = -(gp0 * d[0] + gp1 * d[1] + gp2 * d[2]);
-                o[l * l + l - m] = -(gn0 * d[0] + gn1 * d[1] + gn2 * d[2]);
+                const double nm = N.v[l * l + l + m];
+                const double q = P.Q[l][m], dq = P.Q[l][m + 1];
+                const double gp0 = nm * q * m * P.A[m - 1], gp1 = -nm * q * m * P.B[m - 1], gp2 = nm * dq * P.A[m];
+                const double gn0 = nm * q * m * P.B[m - 1], gn1 = nm * q * m * P.A[m - 1], gn2 = nm * dq * P.B[m];
+                o[l * l + l + m] = (T)(-(gp0 * d[0] + gp1 * d[1] + gp2 * d[2]));
+                o[l * l + l - m] = (T)(-(gn0 * d[0] + gn1 * d[1] + gn2 * d[2]));
             }
         }
     }
