@@ -49,6 +49,7 @@ EXPORTS = [
     "cgtp_conv_forward_backward", "cgtp_conv_forward_backward_vec", "cgtp_double_backward",
     "cgtp_sparse_attention", "cgtp_sparse_attention_rows", "cgtp_sparse_attention_layout_bytes",
     "cgtp_sparse_attention_prepare", "cgtp_csr_workspace_bytes", "cgtp_build_csr", "cgtp_build_csr_order",
+    "cgtp_build_csr_order_noalloc",
     "cgtp_validate_csr", "cgtp_node_order_workspace_bytes", "cgtp_node_order", "cgtp_sh", "cgtp_sh_vjp_forces",
     "cgtp_force_loss_sh_cotangent", "cgtp_timing_enable", "cgtp_timing_collect", "cgtp_last_error",
     "cgtp_version",
@@ -94,6 +95,7 @@ def lib():
             "cgtp_csr_workspace_bytes": [i64, i64, vp],
             "cgtp_build_csr": [vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
             "cgtp_build_csr_order": [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp],
+            "cgtp_build_csr_order_noalloc": [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp],
             "cgtp_validate_csr": [vp, i64, i64, vp, i64, vp, vp],
             "cgtp_sh": [i32, i32, vp, vp, i64, vp, vp],
             "cgtp_sh_vjp_forces": [i32, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp],
@@ -655,6 +657,28 @@ def cgtp_build_csr_order(key, n_keys: int, val=None, sorted_key: bool = True, ws
     E, perm, row_ptr, sk, sv, ws = _csr_outputs(A, key, n_keys, val, sorted_key, ws, out)
     _check(lib().cgtp_build_csr_order(_ptr(key), _ptr(val), E, n_keys, _ptr(perm), _ptr(row_ptr), _ptr(sk),
                                       _ptr(sv), _ptr(order), _ptr(ws), ws.numel(), _stream(stream, key)))
+    return perm, row_ptr, sk, sv, order
+
+
+def cgtp_build_csr_order_noalloc(key, n_keys: int, val=None, sorted_key: bool = True, out=None, order=None,
+                                 stream=None):
+    """cgtp_build_csr_order with the library's fixed device scratch instead
+    of a workspace (for callers that cannot allocate; calls on one GPU must
+    not overlap).  Returns (perm, row_ptr, sorted_key or None, sorted_val or
+    None, order or None); order is written only when given."""
+    A = _Args("cgtp_build_csr_order_noalloc")
+    E = key.shape[0]
+    A("key", key, (E,), _I32, optional=False)
+    A("val", val, (E,), _I32)
+    o = out if out is not None else (None, None, None, None)
+    perm = _out(A, "perm", o[0], (E,), _I32, key, True)
+    row_ptr = _out(A, "row_ptr", o[1], (n_keys + 1,), _I32, key, True)
+    sk = _out(A, "sorted_key", o[2], (E,), _I32, key, out is None and sorted_key)
+    sv = _out(A, "sorted_val", o[3], (E,), _I32, key, out is None and val is not None)
+    A("order", order, (n_keys,), _I32)
+    A.device()
+    _check(lib().cgtp_build_csr_order_noalloc(_ptr(key), _ptr(val), E, n_keys, _ptr(perm), _ptr(row_ptr), _ptr(sk),
+                                              _ptr(sv), _ptr(order), _stream(stream, key)))
     return perm, row_ptr, sk, sv, order
 
 

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -1417,6 +1418,62 @@ int cgtp_build_csr_order(const int32_t *key, const int32_t *val, int64_t n_edges
         return hip_check(hipGetLastError(), "cgtp_build_csr order launch");
     }
     return cgtp_node_order(row_ptr, n_keys, order, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// Scratch of cgtp_build_csr_order_noalloc: a fixed array in the library's
+// device code, one copy per device, held until the process ends.  Host code
+// uses it only through the address hipGetSymbolAddress returns on each
+// device (the array's name in host code is not a device address).
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// the scratch array's address on the current device, looked up once per device
+int noalloc_scratch(void **ptr) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_check(e, "cgtp_build_csr_order_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return set_error(CGTP_ERR_UNSUPPORTED, "cgtp_build_csr_order_noalloc: device id");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (r != hipSuccess || !p) return hip_check(r != hipSuccess ? r : hipErrorInvalidSymbol,
+                                                    "cgtp_build_csr_order_noalloc: scratch address");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return CGTP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int cgtp_build_csr_order_noalloc(const int32_t *key, const int32_t *val, int64_t n_edges, int64_t n_keys,
+                                 int32_t *perm, int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val,
+                                 int32_t *order, cgtp_stream_t stream) {
+    clear_error();
+    if (n_edges < 0 || n_keys < 0 || n_edges > 0x7fffffff || n_keys > 0x7ffffffe)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_build_csr_order_noalloc: sizes out of range");
+    size_t need = 0, need_order = 0;
+    cgtp_csr_workspace_bytes(n_edges, n_keys, &need);
+    cgtp_node_order_workspace_bytes(n_keys, &need_order);
+    if (std::max(need, need_order) > kNoallocScratchBytes)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT,
+                         "cgtp_build_csr_order_noalloc: the graph needs " + std::to_string(std::max(need, need_order)) +
+                             " bytes of scratch, more than the library's fixed " +
+                             std::to_string(kNoallocScratchBytes) + "; use cgtp_build_csr_order with a workspace");
+    void *ws = nullptr;
+    const int rc = noalloc_scratch(&ws);
+    if (rc) return rc;
+    return cgtp_build_csr_order(key, val, n_edges, n_keys, perm, row_ptr, sorted_key, sorted_val, order, ws,
+                                kNoallocScratchBytes, stream);
 }
 
 int cgtp_node_order_workspace_bytes(int64_t n_nodes, size_t *bytes) {

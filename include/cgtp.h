@@ -363,6 +363,21 @@ int cgtp_build_csr_order(const int32_t *key, const int32_t *val, int64_t n_edges
                          int32_t *perm, int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val,
                          int32_t *order, void *workspace, size_t workspace_bytes, cgtp_stream_t stream);
 
+/* cgtp_build_csr_order for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same results, with the scratch taken from a fixed array
+ * of 32 MiB that the library holds on each device it runs on until the
+ * process ends, instead of a caller workspace.  Nothing is allocated.  A
+ * graph whose scratch (cgtp_csr_workspace_bytes, or the node order's when
+ * it runs separately) exceeds 32 MiB -- about 8 million edges plus keys --
+ * is refused with INVALID_ARGUMENT before any launch.  Every call on one
+ * device shares that device's array: calls that overlap on one device (on
+ * different streams or threads) race and give wrong results; serialise
+ * them.  Other arguments and errors as cgtp_build_csr_order. */
+int cgtp_build_csr_order_noalloc(const int32_t *key, const int32_t *val, int64_t n_edges, int64_t n_keys,
+                                 int32_t *perm, int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val,
+                                 int32_t *order, cgtp_stream_t stream);
+
 /* Processing order for the convolution calls: the n_nodes rows of a CSR
  * sorted by decreasing length (rows of 1023 or more edges tie), so that
  * the longest rows are started first and do not form the tail of a launch
