@@ -58,7 +58,7 @@ struct KernelShape {
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
 // of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, gy64, full,
-// ubudget, ucpl, umma, depth_bwd)
+// ubudget, ucpl, umma, cstage, depth_bwd)
 // overrides
 // them for experiments.
 struct Tuning {
@@ -78,6 +78,8 @@ struct Tuning {
     int full = 7;            // dispatch to the folded-flag kernels: bit 0 backward, bit 1 double backward, bit 2 fused forward+backward
     int ubudget = 0;         // uvw accumulators per lane and unit (0: 32, or 144 with radial weights)
     int ucpl = 0;            // uvw channels per lane (0: 1)
+    int cstage = -1;         // uvw: each chunk's uniform CG x SH products computed once per edge into LDS
+                             // (1) or by every lane of the wavefront (0); -1: 0 (measured slower)
     int umma = 0;            // uvw path tensors as per-node products on the matrix cores where they fit
                              // (measured slower on the 100 x 18 atom layer: off by default)
 };

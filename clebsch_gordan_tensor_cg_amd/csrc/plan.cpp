@@ -293,6 +293,7 @@ Tuning tuning_from_env() {
             else if (k == "ubudget") t.ubudget = v < 1 ? 0 : v;
             else if (k == "ucpl") t.ucpl = v < 1 ? 0 : (v > 8 ? 8 : v);
             else if (k == "umma") t.umma = v != 0;
+            else if (k == "cstage") t.cstage = v != 0;
         }
         pos = comma + 1;
     }
@@ -381,6 +382,11 @@ void choose_shapes(Plan &p) {
     // the backward kinds: two edges in flight (C4 one-pass and double backward
     // 583.5 against 586.5 us with three; the forward is faster with three)
     if (p.tune.depth_bwd <= 0) p.tune.depth_bwd = 2;
+    // the uniform products of an edge made once into LDS (one lane per edge)
+    // instead of by every lane: measured slower on the 100 x 18 atom layer
+    // (66 against 49 us; radial 211 against 148 us: 174 VGPRs, half the
+    // occupancy), so off unless asked for
+    if (p.tune.cstage < 0) p.tune.cstage = 0;
     if (p.mode == CGTP_UVW) {
         mix_tables(p);
         split_uvw(p, p.fwd);
