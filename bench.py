@@ -190,16 +190,18 @@ def tp_flops(cfg, plan):
 
 
 def counted_traffic(workload, kernel, source):
-    """HBM bytes per launch measured with rocprofv3 counters for exactly this
-    workload (its full description) and generated source
-    (profiles/hbm_traffic__*.json), else None."""
+    """Bytes per launch leaving L2 toward memory (reads + writes, from the
+    per-size request counters; Infinity-Cache hits included, so an upper
+    bound on HBM bytes), measured with rocprofv3 for exactly this workload
+    (its full description) and generated source (profiles/hbm_traffic__*.json),
+    else None."""
     import glob
     import hashlib
     sha = hashlib.sha1(source.encode()).hexdigest()
     for path in glob.glob(os.path.join(ROOT, "profiles", "hbm_traffic__*.json")):
         for r in json.load(open(path))["records"]:
             if r["workload"] == workload and r["kernel"] == kernel and r["source_sha1"] == sha:
-                return int((r["fetch_kib"] * r["fetch_scale"] + r["write_kib"] * r["write_scale"]) * 1024)
+                return int(r["read_bytes"] + r["write_bytes"])
     return None
 
 
