@@ -710,7 +710,8 @@ def bench_radial(args, torch, B, W):
     tf = flop / (t_ms * 1e-3) / 1e12
     mix_flop = sum(2 * N * (2 * c_ir[b][1] + 1) * c_ir[b][0] * (H + 1) *
                    sum(a_ir[i1][0] for (i1, _, i3) in plan.paths() if i3 == b) for b in range(len(c_ir)))
-    mix_ms = kern["k_uvw_mix"]["ms_per_step"]
+    mix_k = "k_uvw_mix2" if "k_uvw_mix2" in kern else "k_uvw_mix"
+    mix_ms = kern[mix_k]["ms_per_step"]
     res = {"metric": METRIC, "value": E / (ms * 1e-3), "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_median": float(np.median(per_step)),
            "ms_per_step_min": float(np.min(per_step)), "higher_is_better": True, "scaling": "weak",
@@ -723,7 +724,7 @@ def bench_radial(args, torch, B, W):
                         "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
                         "alg_flop_per_launch": int(flop), "avg_ms": round(t_ms, 4)},
-           "mixing": {"kernel": "k_uvw_mix", "ms_per_step": round(mix_ms, 4),
+           "mixing": {"kernel": mix_k, "ms_per_step": round(mix_ms, 4),
                       "TFLOP_per_s": round(mix_flop / (mix_ms * 1e-3) / 1e12, 3), "peak_bf16_mfma": 2500.0},
            "kernels": kern}
     if not args.no_cpu_baseline:

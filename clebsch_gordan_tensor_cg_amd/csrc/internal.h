@@ -58,7 +58,7 @@ struct KernelShape {
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
 // of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, gy64, full,
-// ubudget, ucpl, umma, cstage, depth_bwd)
+// ubudget, ucpl, umma, cstage, mix2, depth_bwd)
 // overrides
 // them for experiments.
 struct Tuning {
@@ -80,6 +80,9 @@ struct Tuning {
     int ucpl = 0;            // uvw channels per lane (0: 1)
     int cstage = -1;         // uvw: each chunk's uniform CG x SH products computed once per edge into LDS
                              // (1) or by every lane of the wavefront (0); -1: 0 (measured slower)
+    int mix2 = -1;           // uvw mixing: the whole contraction span staged at once, 16x16x32 MFMA (1), or
+                             // 256-row steps with 16x16x16 MFMA (0); -1: the first where every block's
+                             // contraction fits one span of 512 rows (C5 mixing 20.3 -> 18.1 us)
     int umma = 0;            // uvw path tensors as per-node products on the matrix cores where they fit
                              // (measured slower on the 100 x 18 atom layer: off by default)
 };

@@ -904,6 +904,7 @@ constexpr int kMixMaxBlocks = 4;   // output blocks mixed by one launch
 // one output block of a mixing launch
 struct MixBlockArgs {
     int32_t np, d3, mul3, n_split;
+    int32_t rows_uniform;          // rows of every path (mul1 * mul2) when equal, else 0
     int64_t M, K, Kb, off3, t_off, part_off, kspan, wg_start;
     int32_t kstart[kMixMaxPaths + 1];
     int32_t woff[kMixMaxPaths];
@@ -1115,6 +1116,141 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     }
 }
 
+// Second form of the mixing, for blocks whose contraction rows come in whole
+// 32-row steps, whose paths hold whole 8-row groups and whose columns come in
+// 64-column tiles with 16-byte aligned weights and path tensors (the TFN
+// layers).  A workgroup of four wavefronts still owns 64 rows of T (16 per
+// wavefront) and 64 output columns, but stages its whole contraction span
+// (at most kMix2MaxK rows, 64 KiB) at once and issues every A fragment
+// together with the weight loads: one global round trip, one barrier, then
+// the products on v_mfma_f32_16x16x32_bf16.  The weight rows of a 32-row step
+// are stored interleaved in groups of eight: element (r, c) of the span at
+// ((r/8)*64 + c)*8 + r%8, so a lane's B fragment (eight consecutive rows of
+// one column) is one 16-byte read.  Lane l supplies A[l%16][8(l/16)+j] and
+// B[8(l/16)+j][l%16], j = 0..7, and receives D[4(l/16)+i][l%16], i = 0..3.
+// The row of path p's weight block for contraction row r = h*Kb + kk is
+// found once per 8-row group: p = kk / rows when every path has the same
+// number of rows, else by a search of the path table.
+constexpr int kMix2MaxK = 512;
+typedef __bf16 cgtp_bf16x8 __attribute__((ext_vector_type(8)));
+
+__global__ void __launch_bounds__(256) k_uvw_mix2(const uint16_t *__restrict__ T0, const uint16_t *__restrict__ W,
+                                                  int64_t wstride, MixArgs args, float *__restrict__ out,
+                                                  int64_t dim3, int accumulate, float *__restrict__ part0) {
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[kMix2MaxK * 64];
+    __shared__ int32_t s_kstart[kMixMaxPaths + 1];
+    __shared__ int64_t s_woff[kMixMaxPaths];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int bsel = 0;
+#pragma unroll
+    for (int i = 1; i < kMixMaxBlocks; ++i)
+        if (i < args.nb && (int64_t)blockIdx.x >= args.b[i].wg_start) bsel = i;
+    int np = 0, d3 = 1, mul3 = 0, n_split = 1, rows_u = 0;
+    int64_t M = 0, K = 0, Kb = 1, off3 = 0, t_off = 0, part_off = 0, kspan = 0, wg_start = 0;
+#pragma unroll
+    for (int i = 0; i < kMixMaxBlocks; ++i)
+        if (i == bsel) {
+            np = args.b[i].np, d3 = args.b[i].d3, mul3 = args.b[i].mul3, n_split = args.b[i].n_split;
+            rows_u = args.b[i].rows_uniform;
+            M = args.b[i].M, K = args.b[i].K, Kb = args.b[i].Kb, off3 = args.b[i].off3, t_off = args.b[i].t_off;
+            part_off = args.b[i].part_off, kspan = args.b[i].kspan, wg_start = args.b[i].wg_start;
+            if (tid <= np) s_kstart[tid] = args.b[i].kstart[tid];
+            if (tid < np) s_woff[tid] = args.b[i].woff[tid];
+        }
+    __syncthreads();
+    const uint16_t *__restrict__ T = T0 + t_off;
+    float *__restrict__ part = part0 + part_off;
+    const int64_t wg = blockIdx.x - wg_start;
+    const int64_t wg_count = (bsel + 1 < args.nb ? args.b[bsel + 1 < kMixMaxBlocks ? bsel + 1 : 0].wg_start
+                                                  : (int64_t)gridDim.x) - wg_start;
+    const int r_a = lane & 15, g = lane >> 4;
+    const int64_t n_groups = (M + 63) / 64;
+    const int split = (int)(wg % n_split);
+    const int64_t k_begin = split * kspan, k_end = std::min<int64_t>(K, k_begin + kspan);
+    const int kc = (int)(k_end - k_begin);   // a multiple of 32, at most kMix2MaxK
+    const int ns = kc / 32;
+    for (int cb = 0; cb < mul3; cb += 64) {
+        for (int64_t grp = wg / n_split; grp < n_groups; grp += wg_count / n_split) {
+            const int64_t row0 = grp * 64 + wv * 16;
+            const int64_t arow = row0 + r_a < M ? row0 + r_a : M - 1;
+            const cgtp_bf16x8 *__restrict__ Ta = (const cgtp_bf16x8 *)(T + arow * K + k_begin) + g;
+            __syncthreads();   // the previous group's weights are no longer read
+            // every A fragment of the span, in flight with the weight loads
+            cgtp_bf16x8 af[kMix2MaxK / 32];
+#pragma unroll
+            for (int st = 0; st < kMix2MaxK / 32; ++st)
+                af[st] = Ta[4 * (st < ns ? st : 0)];   // clamped: every fragment is a register
+            // weight tiles of 8 rows x 8 columns: tile t covers rows 8(t/8)..+7
+            // and columns 8(t%8)..+7 of the span
+#pragma unroll
+            for (int j = 0; j < kMix2MaxK * 64 / 64 / 256; ++j) {
+                const int ti = tid + 256 * j, q = ti >> 3, c8 = (ti & 7) * 8;
+                if (8 * q >= kc) continue;
+                const int64_t r = k_begin + 8 * q;
+                const int h = (int)(r / Kb), kk = (int)(r - h * Kb);
+                int p;
+                if (rows_u > 0) {
+                    p = kk / rows_u;
+                } else {
+                    p = 0;
+                    while (p + 1 < np && kk >= s_kstart[p + 1]) ++p;
+                }
+                const uint16_t *__restrict__ src =
+                    W + h * wstride + s_woff[p] + (int64_t)(kk - s_kstart[p]) * mul3 + cb + c8;
+                uint4 v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = *(const uint4 *)(src + (int64_t)i * mul3);
+                const uint32_t w[8][4] = {{v[0].x, v[0].y, v[0].z, v[0].w}, {v[1].x, v[1].y, v[1].z, v[1].w},
+                                          {v[2].x, v[2].y, v[2].z, v[2].w}, {v[3].x, v[3].y, v[3].z, v[3].w},
+                                          {v[4].x, v[4].y, v[4].z, v[4].w}, {v[5].x, v[5].y, v[5].z, v[5].w},
+                                          {v[6].x, v[6].y, v[6].z, v[6].w}, {v[7].x, v[7].y, v[7].z, v[7].w}};
+                uint4 *dst = (uint4 *)Ws + q * 64 + c8;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {   // columns c8+2d (low halves) and c8+2d+1 (high halves)
+                    dst[2 * d] = make_uint4(lo_halves(w[0][d], w[1][d]), lo_halves(w[2][d], w[3][d]),
+                                            lo_halves(w[4][d], w[5][d]), lo_halves(w[6][d], w[7][d]));
+                    dst[2 * d + 1] = make_uint4(hi_halves(w[0][d], w[1][d]), hi_halves(w[2][d], w[3][d]),
+                                                hi_halves(w[4][d], w[5][d]), hi_halves(w[6][d], w[7][d]));
+                }
+            }
+            __syncthreads();
+            if (row0 >= M) continue;   // no rows for this wavefront (it still joined the barriers)
+            cgtp_f4 acc[4];
+            for (int ct = 0; ct < 4; ++ct) acc[ct] = (cgtp_f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < kMix2MaxK / 32; ++st) {
+                if (st < ns) {   // uniform
+                    const cgtp_bf16x8 *bq = (const cgtp_bf16x8 *)Ws + (4 * st + g) * 64 + r_a;
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st], bq[16 * ct], acc[ct], 0, 0, 0);
+                }
+            }
+            const int64_t rq = row0 + 4 * g;
+            const int64_t item_q = rq / d3;
+            const int k_q = (int)(rq - item_q * d3);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const int col = cb + ct * 16 + r_a;
+                int64_t item = item_q;
+                int k = k_q;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (rq + i < M) {
+                        if (n_split > 1) {
+                            part[((int64_t)split * M + rq + i) * mul3 + col] = acc[ct][i];
+                        } else {
+                            float *o = out + item * dim3 + off3 + (int64_t)col * d3 + k;
+                            *o = accumulate ? *o + acc[ct][i] : acc[ct][i];
+                        }
+                    }
+                    if (++k == d3) k = 0, ++item;
+                }
+            }
+        }
+    }
+}
+
 // out[item][off3 + col*d3 + k] (=|+=) sum_s part[s][item*d3 + k][col] for
 // every split block of the launch (elements enumerated block after block).
 // I: the index type of the element arithmetic (32-bit divisions whenever
@@ -1162,10 +1298,16 @@ int mix_splits(const MixBlock &mb, int64_t n_items) {
     return (int)std::max<int64_t>(1, std::min<int64_t>(sp, steps));
 }
 
+// splits of the second mixing form: each span at most kMix2MaxK rows
+int mix2_splits(const MixBlock &mb, int64_t n_items) {
+    return std::max<int>(mix_splits(mb, n_items), (int)((mb.Kr + kMix2MaxK - 1) / kMix2MaxK));
+}
+
 size_t mix_part_bytes(const Plan &p, int64_t n_items) {
     size_t b = 0;   // every split block has its own partial tiles (blocks run together)
     for (const MixBlock &mb : p.mix) {
-        const int sp = mix_splits(mb, n_items);
+        // enough for either mixing form
+        const int sp = std::max(mix_splits(mb, n_items), mix2_splits(mb, n_items));
         if (sp > 1) b += (size_t)sp * n_items * mb.d3 * mb.mul3;
     }
     return b * sizeof(float);
@@ -1182,6 +1324,19 @@ int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items,
         // unguarded loads: 16-row contraction steps, whole 16-byte weight
         // segments, 8-byte aligned path-tensor rows
         bool fast = (((uintptr_t)T) & 7) == 0 && (((uintptr_t)w) & 15) == 0 && p.wnumel % 8 == 0;
+        // the second form: whole 32-row steps, paths of whole 8-row groups,
+        // 16-byte aligned path-tensor rows
+        // (by default only where every block's contraction fits one span:
+        // more spans than the first form's splits grow the partial sums and
+        // their reduction, which measured no net gain on the radial layer)
+        bool v2 = p.tune.mix2 != 0 && (((uintptr_t)T) & 15) == 0 && (((uintptr_t)w) & 15) == 0 && p.wnumel % 8 == 0;
+        for (int i = 0; i < args.nb; ++i) {
+            const MixBlock &mb = p.mix[b0 + i];
+            v2 = v2 && mb.K % 32 == 0 && mb.mul3 % 64 == 0 && (n_items * mb.t_off_per_item) % 8 == 0 &&
+                 (int)mb.paths.size() <= kMixMaxPaths && (p.tune.mix2 > 0 || mb.Kr <= kMix2MaxK);
+            for (int pi : mb.paths)
+                v2 = v2 && p.paths[pi].woff % 8 == 0 && ((int64_t)p.paths[pi].mul1 * p.paths[pi].mul2) % 8 == 0;
+        }
         for (int i = 0; i < args.nb; ++i) {
             const MixBlock &mb = p.mix[b0 + i];
             fast = fast && mb.Kr % 16 == 0 && mb.mul3 % 64 == 0 && (n_items * mb.t_off_per_item) % 4 == 0;
@@ -1202,9 +1357,18 @@ int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items,
             a.Kb = mb.K;
             a.off3 = p.off3[mb.b3];
             a.t_off = n_items * mb.t_off_per_item;
-            a.n_split = mix_splits(mb, n_items);
-            const int64_t steps = (mb.Kr + kMixKC - 1) / kMixKC;
-            a.kspan = (steps + a.n_split - 1) / a.n_split * kMixKC;
+            a.rows_uniform = (int32_t)((int64_t)p.paths[mb.paths[0]].mul1 * p.paths[mb.paths[0]].mul2);
+            for (int pi : mb.paths)
+                if ((int64_t)p.paths[pi].mul1 * p.paths[pi].mul2 != a.rows_uniform) a.rows_uniform = 0;
+            if (v2) {
+                a.n_split = mix2_splits(mb, n_items);
+                const int64_t steps = mb.Kr / 32;
+                a.kspan = (steps + a.n_split - 1) / a.n_split * 32;
+            } else {
+                a.n_split = mix_splits(mb, n_items);
+                const int64_t steps = (mb.Kr + kMixKC - 1) / kMixKC;
+                a.kspan = (steps + a.n_split - 1) / a.n_split * kMixKC;
+            }
             a.part_off = part_off;
             if (a.n_split > 1) {
                 part_off += (int64_t)a.n_split * a.M * a.mul3;
@@ -1216,7 +1380,10 @@ int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items,
             a.wg_start = wg;
             wg += groups * a.n_split;
         }
-        if (fast)
+        if (v2)
+            CGTP_LAUNCH("k_uvw_mix2", s, k_uvw_mix2, dim3((unsigned)wg), dim3(256), 0, s, (const uint16_t *)T,
+                        (const uint16_t *)w, p.wnumel, args, (float *)out, p.dim3, accumulate, (float *)part);
+        else if (fast)
             CGTP_LAUNCH("k_uvw_mix", s, k_uvw_mix<true>, dim3((unsigned)wg), dim3(256), 0, s, (const uint16_t *)T,
                         (const uint16_t *)w, p.wnumel, args, (float *)out, p.dim3, accumulate, (float *)part);
         else
