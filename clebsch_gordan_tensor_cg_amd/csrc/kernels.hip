@@ -513,17 +513,21 @@ __global__ void __launch_bounds__(1024) k_order_scatter(const int32_t *__restric
 // consecutive counts per thread, wavefront scans by shuffles.
 // With order non-NULL (n at most 65536 rows) it then writes the longest-first
 // node order of the rows whose lengths cnt holds, as k_order_small does.
+// With max_out non-NULL it also stores the largest count there.
 __global__ void __launch_bounds__(1024) k_scan(const int32_t *__restrict__ cnt, int64_t n,
-                                                int32_t *__restrict__ row_ptr, int32_t *__restrict__ order) {
+                                                int32_t *__restrict__ row_ptr, int32_t *__restrict__ order,
+                                                int32_t *__restrict__ max_out) {
     __shared__ int32_t wsum[16];
     __shared__ int32_t hb[kOrderBuckets];
+    __shared__ int32_t wmax[16];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int32_t carry = 0;
+    int32_t carry = 0, vmax = 0;
     for (int64_t base = 0; base < n; base += 4096) {
         const int64_t i0 = base + 4 * (int64_t)threadIdx.x;
         int32_t v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = i0 + q < n ? cnt[i0 + q] : 0;
+        vmax = max(vmax, max(max(v[0], v[1]), max(v[2], v[3])));
         const int32_t own = v[0] + v[1] + v[2] + v[3];
         int32_t incl = own;
 #pragma unroll
@@ -553,6 +557,17 @@ __global__ void __launch_bounds__(1024) k_scan(const int32_t *__restrict__ cnt, 
         __syncthreads();
     }
     if (threadIdx.x == 0) row_ptr[n] = carry;
+    if (max_out) {   // uniform across the workgroup
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) vmax = max(vmax, __shfl_xor(vmax, off, 64));
+        if (lane == 0) wmax[wid] = vmax;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int32_t m = 0;
+            for (int w = 0; w < 16; ++w) m = max(m, wmax[w]);
+            *max_out = m;
+        }
+    }
     if (order) {   // uniform across the workgroup
         const int t = threadIdx.x;
         hb[t] = 0;
@@ -566,35 +581,86 @@ __global__ void __launch_bounds__(1024) k_scan(const int32_t *__restrict__ cnt, 
 
 // One wavefront per segment: each element's final slot is the number of
 // smaller edge ids in its segment, which reproduces the stable order no
-// matter in which order the scatter's atomics landed.  Segments of up to
-// kRankLds edges are staged in LDS.
+// matter in which order the scatter's atomics landed.  The segment is staged
+// in LDS.  Segments longer than kRankLds (hubs) are left to the trailing
+// workgroups of the same launch (blockIdx.x >= n_keys), which do nothing
+// unless *max_deg exceeds kRankLds.  They take the CSR slots 64 at a time;
+// each lane finds its slot's segment by binary search in row_ptr, and the
+// lanes of one hub rank their elements together against the whole segment,
+// staged through LDS kRankLds ids at a time: O(deg^2 / 64) LDS reads per hub
+// spread over the trailing workgroups instead of one wavefront's global loads.
 constexpr int kRankLds = 2048;
+constexpr int kRankHubGroups = 1024;   // trailing workgroups of k_rank_segments (fewer for small edge counts)
+
+__device__ __forceinline__ void rank_emit(int32_t me, int slot, const int32_t *__restrict__ key,
+                                          const int32_t *__restrict__ val, int32_t *__restrict__ perm,
+                                          int32_t *__restrict__ sorted_key, int32_t *__restrict__ sorted_val) {
+    perm[slot] = me;
+    if (sorted_key) sorted_key[slot] = key[me];
+    if (sorted_val) sorted_val[slot] = val[me];
+}
+
 __global__ void __launch_bounds__(64) k_rank_segments(const int32_t *__restrict__ row_ptr, int64_t n_keys,
                                                       const int32_t *__restrict__ tmp,
                                                       const int32_t *__restrict__ key,
                                                       const int32_t *__restrict__ val,
+                                                      const int32_t *__restrict__ max_deg,
                                                       int32_t *__restrict__ perm,
                                                       int32_t *__restrict__ sorted_key,
                                                       int32_t *__restrict__ sorted_val) {
     __shared__ int32_t seg[kRankLds];
-    const int64_t s = blockIdx.x;
-    if (s >= n_keys) return;
-    const int beg = row_ptr[s], end = row_ptr[s + 1];
-    const int deg = end - beg;
-    const bool staged = deg <= kRankLds;
-    if (staged)
-        for (int i = threadIdx.x; i < deg; i += 64) seg[i] = tmp[beg + i];
-    __syncthreads();
-    for (int i = threadIdx.x; i < deg; i += 64) {
-        const int32_t me = staged ? seg[i] : tmp[beg + i];
-        int rank = 0;
-        if (staged)
+    const int lane = threadIdx.x;
+    if ((int64_t)blockIdx.x < n_keys) {
+        const int64_t s = blockIdx.x;
+        const int beg = row_ptr[s], end = row_ptr[s + 1];
+        const int deg = end - beg;
+        if (deg > kRankLds) return;   // a hub: the trailing workgroups rank it
+        for (int i = lane; i < deg; i += 64) seg[i] = tmp[beg + i];
+        __syncthreads();
+        for (int i = lane; i < deg; i += 64) {
+            const int32_t me = seg[i];
+            int rank = 0;
             for (int j = 0; j < deg; ++j) rank += seg[j] < me;
-        else
-            for (int j = beg; j < end; ++j) rank += tmp[j] < me;
-        perm[beg + rank] = me;
-        if (sorted_key) sorted_key[beg + rank] = key[me];
-        if (sorted_val) sorted_val[beg + rank] = val[me];
+            rank_emit(me, beg + rank, key, val, perm, sorted_key, sorted_val);
+        }
+        return;
+    }
+    if (*max_deg <= kRankLds) return;   // no hub: the common case ends here
+    const int64_t g = (int64_t)blockIdx.x - n_keys, n_groups = (int64_t)gridDim.x - n_keys;
+    const int64_t n_slots = row_ptr[n_keys];
+    for (int64_t c = g; c * 64 < n_slots; c += n_groups) {   // uniform across the workgroup
+        const int64_t p = c * 64 + lane;
+        // segment of slot p: the last s with row_ptr[s] <= p (a slot lies in
+        // a nonempty segment, so the search ends on it)
+        int64_t lo = 0, hi = n_keys;   // row_ptr[lo] <= p < row_ptr[hi]
+        if (p < n_slots)
+            while (hi - lo > 1) {
+                const int64_t mid = (lo + hi) >> 1;
+                if (row_ptr[mid] <= p) lo = mid;
+                else hi = mid;
+            }
+        const int beg = p < n_slots ? row_ptr[lo] : 0;
+        const int end = p < n_slots ? row_ptr[lo + 1] : 0;
+        bool todo = p < n_slots && end - beg > kRankLds;
+        const int32_t me = todo ? tmp[p] : 0;
+        // the hubs among these 64 slots, one at a time (at most two: each
+        // is longer than the chunk)
+        while (__any(todo)) {
+            const int lead = __builtin_ctzll(__ballot(todo));
+            const int hb = __shfl(beg, lead, 64), he = __shfl(end, lead, 64);
+            const bool mine = todo && beg == hb;
+            int rank = 0;
+            for (int t0 = hb; t0 < he; t0 += kRankLds) {
+                const int len = min(kRankLds, he - t0);
+                for (int i = lane; i < len; i += 64) seg[i] = tmp[t0 + i];
+                __syncthreads();
+                if (mine)
+                    for (int j = 0; j < len; ++j) rank += seg[j] < me;
+                __syncthreads();
+            }
+            if (mine) rank_emit(me, hb + rank, key, val, perm, sorted_key, sorted_val);
+            todo = todo && !mine;
+        }
     }
 }
 
@@ -1561,7 +1627,7 @@ int cgtp_build_csr_order(const int32_t *key, const int32_t *val, int64_t n_edges
         else
             CGTP_LAUNCH("k_count_global", s, k_count_global, dim3(ge), dim3(kBlock), 0, s, key, n_edges, n_keys, cnt);
         int32_t *fold = n_keys <= kOrderSmallMax ? order : nullptr;   // order from the counts, same launch
-        CGTP_LAUNCH("k_scan", s, k_scan, dim3(1), dim3(1024), 0, s, cnt, n_keys, row_ptr, fold);
+        CGTP_LAUNCH("k_scan", s, k_scan, dim3(1), dim3(1024), 0, s, cnt, n_keys, row_ptr, fold, cnt + n_keys);
         if (fold) order = nullptr;
         if (lds_path)
             CGTP_LAUNCH("k_scatter", s, k_scatter, grid, dim3(kCsrThreads), lds, s, key, n_edges, n_keys, per, row_ptr,
@@ -1569,8 +1635,12 @@ int cgtp_build_csr_order(const int32_t *key, const int32_t *val, int64_t n_edges
         else
             CGTP_LAUNCH("k_scatter_global", s, k_scatter_global, dim3(ge), dim3(kBlock), 0, s, key, n_edges, n_keys,
                         row_ptr, cursor, tmp);
-        CGTP_LAUNCH("k_rank_segments", s, k_rank_segments, dim3((unsigned)n_keys), dim3(64), 0, s, row_ptr, n_keys, tmp,
-                    key, val, perm, sorted_key, sorted_val);
+        // trailing workgroups for hub segments: one per 64 edges, at most
+        // kRankHubGroups, within the grid's 2^31 - 1 limit
+        const int64_t hub_groups =
+            std::max<int64_t>(1, std::min<int64_t>({(n_edges + 63) / 64, kRankHubGroups, 0x7fffffff - n_keys}));
+        CGTP_LAUNCH("k_rank_segments", s, k_rank_segments, dim3((unsigned)(n_keys + hub_groups)), dim3(64), 0, s,
+                    row_ptr, n_keys, tmp, key, val, cnt + n_keys, perm, sorted_key, sorted_val);
     } else {
         CGTP_LAUNCH("k_fill", s, k_fill<int32_t>, dim3(grid_for(n_keys + 1)), dim3(kBlock), 0, s, row_ptr, n_keys + 1, 0);
     }
@@ -1673,7 +1743,7 @@ int cgtp_node_order(const int32_t *row_ptr, int64_t n_nodes, int32_t *order, voi
     // a few workgroups: each publishes at most kOrderBuckets counts
     const unsigned g = (unsigned)std::min<int64_t>(64, (n_nodes + 4095) / 4096);
     CGTP_LAUNCH("k_order_count", s, k_order_count, dim3(g), dim3(1024), 0, s, row_ptr, n_nodes, cnt);
-    CGTP_LAUNCH("k_scan", s, k_scan, dim3(1), dim3(1024), 0, s, cnt, (int64_t)kOrderBuckets, start, nullptr);
+    CGTP_LAUNCH("k_scan", s, k_scan, dim3(1), dim3(1024), 0, s, cnt, (int64_t)kOrderBuckets, start, nullptr, nullptr);
     CGTP_LAUNCH("k_order_scatter", s, k_order_scatter, dim3(g), dim3(1024), 0, s, row_ptr, n_nodes, start, cursor,
                 order);
     return hip_check(hipGetLastError(), "cgtp_node_order launch");

@@ -405,7 +405,8 @@ def test_conv_no_edges(B, torch):
 # CSR build, validation, spherical harmonics, forces
 # ---------------------------------------------------------------------------
 CSR_CASES = ["c2", "empty", "one_node", "hub", "ragged", "multi_range", "wide_keys", "many_splits", "molecules",
-             "small_max", "one_key_max", "past_small_edges", "past_small_keys"]
+             "small_max", "one_key_max", "past_small_edges", "past_small_keys", "hub_big", "one_key_big",
+             "two_hubs"]
 
 
 def _csr_case(case):
@@ -437,6 +438,15 @@ def _csr_case(case):
         key, n = np.zeros(300, np.int32), 1
     elif case == "hub":
         key, n = np.where(rs.random(5000) < 0.5, 3, rs.integers(0, 40, 5000)).astype(np.int32), 40
+    # segments longer than one LDS stage (2048 edges) on the multi-launch path
+    elif case == "hub_big":         # one hub of about 100,000 in-edges among 5000 keys
+        key, n = np.where(rs.random(200000) < 0.5, 7, rs.integers(0, 5000, 200000)).astype(np.int32), 5000
+    elif case == "one_key_big":     # a single segment of 70,000 edges
+        key, n = np.zeros(70000, np.int32), 1
+    elif case == "two_hubs":        # two adjacent hubs: one 64-slot chunk holds the end of one and the start of the next
+        key = np.concatenate([np.zeros(5, np.int32), np.full(3000, 1, np.int32), np.full(3000, 2, np.int32),
+                              rs.integers(3, 100, 60000).astype(np.int32)])
+        key, n = key[rs.permutation(len(key))], 100
     else:
         key, n = rs.integers(0, 1000, 777).astype(np.int32), 1000
     return key, n
