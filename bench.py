@@ -490,8 +490,10 @@ def bench_conv(args, torch, B, W):
     alg = {}
     vb = 8 if dtype == "f64" else 4
     shb = 3 * vb + 4 if sh_in_conv else d2 * eb
+    # the uvw path tensors: the per-pair matrix-core kernel where the plan has it
+    pt = "cgtp_uvw_pf" if "cgtp_uvw_pf" in launches else "cgtp_fwd"
     if name == "c5":
-        alg["cgtp_fwd"] = N * d1 * eb + E * shb + E * 4 + (N + 1) * 4   # path tensors (bf16) stay in cache
+        alg[pt] = N * d1 * eb + E * shb + E * 4 + (N + 1) * 4   # path tensors (bf16) stay in cache
     else:
         alg["cgtp_fwd"] = alg_bytes_conv_fwd(N, E, d1, d3, wn, eb, ob, wb, shb)
     if full:
@@ -538,9 +540,9 @@ def bench_conv(args, torch, B, W):
     if name == "c5":
         # the path tensors on the vector ALUs dominate: FP32 vector peak
         flop = tp_flops(cfg, plan) * E
-        t_ms = kern["cgtp_fwd"]["avg_ms"]
+        t_ms = kern[pt]["avg_ms"]
         tf = flop / (t_ms * 1e-3) / 1e12
-        roof = {"bound": "alu", "kernel": "cgtp_fwd", "achieved": round(tf, 3),
+        roof = {"bound": "alu", "kernel": pt, "achieved": round(tf, 3),
                 "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
                 "traffic": None, "alg_flop_per_launch": int(flop), "avg_ms": round(t_ms, 4)}
     res = {

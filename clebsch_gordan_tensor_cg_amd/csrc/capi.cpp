@@ -393,9 +393,15 @@ static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, c
     void *args[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, (void *)&order, (void *)&vec,
                     (void *)&vperm, (void *)&radial, &ws, &n, &graph};
     const int64_t ipw = p.fwd.items_per_wave;
-    // the matrix-core form: one workgroup of four wavefronts per (item, input-1 block)
-    int rc = p.uvw_mma ? launch(p.k_fwd, "cgtp_fwd", n_items * p.uvw_mma_groups, s, args, 256)
-                       : launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
+    // graph calls: the per-pair matrix-core form where the plan has it (one
+    // workgroup per pair of nodes); else the per-edge kernel, or the
+    // per-node matrix-core form (one workgroup of four wavefronts per item and
+    // input-1 block)
+    // (its x segments are read in 16-byte groups: x must be 16-byte aligned)
+    const bool pf = graph && p.uvw_pf && ((uintptr_t)x & 15) == 0;
+    int rc = pf                  ? launch(p.k_uvw_pf, "cgtp_uvw_pf", (n_items + 1) / 2, s, args, 64 * p.uvw_pf_waves)
+             : p.uvw_mma         ? launch(p.k_fwd, "cgtp_fwd", n_items * p.uvw_mma_groups, s, args, 256)
+                                 : launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
     if (rc) return rc;
     int acc = 0;
     if (!blocks_covered(p.out, p.paths, true)) {

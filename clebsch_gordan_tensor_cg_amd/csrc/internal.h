@@ -58,7 +58,7 @@ struct KernelShape {
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
 // of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, gy64, full,
-// ubudget, ucpl, umma, cstage, mix2, depth_bwd)
+// ubudget, ucpl, umma, cstage, mix2, depth_bwd, pform)
 // overrides
 // them for experiments.
 struct Tuning {
@@ -85,6 +85,9 @@ struct Tuning {
                              // contraction fits one span of 512 rows (C5 mixing 20.3 -> 18.1 us)
     int umma = 0;            // uvw path tensors as per-node products on the matrix cores where they fit
                              // (measured slower on the 100 x 18 atom layer: off by default)
+    int pform = -1;          // uvw path tensors of graph calls from per-chunk products P_i = sum_e y_e x_e,i
+                             // on the matrix cores, two nodes per wavefront (1), or the per-edge kernel
+                             // (0); -1: the first wherever the plan allows it
 };
 Tuning tuning_from_env();
 
@@ -119,6 +122,8 @@ struct Plan {
     int64_t t_per_item = 0;        // uvw: T elements per item
     bool uvw_mma = false;          // uvw: path tensors by the matrix-core kernel
     int uvw_mma_groups = 0;        // its workgroups per item (input-1 blocks with paths), 256 threads each
+    bool uvw_pf = false;           // uvw: graph calls take the path tensors from cgtp_uvw_pf
+    int uvw_pf_waves = 0;          // its wavefronts per workgroup (one workgroup per pair of nodes)
     std::string source;
     std::string cache_key;
     bool cached = false;
@@ -133,6 +138,7 @@ struct Plan {
     hipFunction_t k_dbl_full = nullptr;  // k_dbl with dbl_full_flags folded in
     hipFunction_t k_fb = nullptr;        // forward + backward of the same edges in one pass
     hipFunction_t k_fb_full = nullptr;   // k_fb with fb_full_flags folded in
+    hipFunction_t k_uvw_pf = nullptr;    // uvw path tensors of graph calls, per pair of nodes
     int device = -1;
 };
 
@@ -151,6 +157,10 @@ inline int fb_full_flags(const Plan &p) { return 1 | 2 | 4 | (p.fb.n_units > 1 ?
 // the plan has no such kernel: radial weights, or no path)
 size_t uvw_mma_lds_bytes(const Plan &p);
 int uvw_mma_group_count(const Plan &p);
+// uvw path tensors per pair of nodes on the matrix cores: whether the plan
+// allows them, and the wavefronts of each pair's workgroup
+bool uvw_pf_eligible(const Plan &p);
+int uvw_pf_wave_count(const Plan &p);
 constexpr size_t kUvwMmaMaxLds = 64 * 1024;   // static LDS of one workgroup
 
 // planner

@@ -293,6 +293,7 @@ Tuning tuning_from_env() {
             else if (k == "ubudget") t.ubudget = v < 1 ? 0 : v;
             else if (k == "ucpl") t.ucpl = v < 1 ? 0 : (v > 8 ? 8 : v);
             else if (k == "umma") t.umma = v != 0;
+            else if (k == "pform") t.pform = v;
             else if (k == "cstage") t.cstage = v != 0;
             else if (k == "mix2") t.mix2 = v < 0 ? -1 : (v != 0);
         }
@@ -394,6 +395,10 @@ void choose_shapes(Plan &p) {
         const size_t lds = uvw_mma_lds_bytes(p);
         p.uvw_mma = p.tune.umma && lds > 0 && lds <= kUvwMmaMaxLds;
         p.uvw_mma_groups = p.uvw_mma ? uvw_mma_group_count(p) : 0;
+        // the per-pair matrix-core form unless switched off, or the per-node
+        // one asked for instead
+        p.uvw_pf = (p.tune.pform > 0 || (p.tune.pform < 0 && !p.uvw_mma)) && uvw_pf_eligible(p);
+        p.uvw_pf_waves = p.uvw_pf ? uvw_pf_wave_count(p) : 0;
         return;
     }
     split(p, p.fwd, 0);

@@ -174,6 +174,7 @@ int compile_and_load(Plan &p, bool load, std::string &err) {
     if (e == hipSuccess && p.n_kernels > 4) e = hipModuleGetFunction(&p.k_dbl_full, p.module, "cgtp_dbl_full");
     if (e == hipSuccess && p.n_kernels > 5) e = hipModuleGetFunction(&p.k_fb, p.module, "cgtp_fb");
     if (e == hipSuccess && p.n_kernels > 6) e = hipModuleGetFunction(&p.k_fb_full, p.module, "cgtp_fb_full");
+    if (e == hipSuccess && p.uvw_pf) e = hipModuleGetFunction(&p.k_uvw_pf, p.module, "cgtp_uvw_pf");
     if (e != hipSuccess) {
         err = std::string("loading generated code object: ") + hipGetErrorString(e);
         return CGTP_ERR_HIP;

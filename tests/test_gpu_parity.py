@@ -884,9 +884,14 @@ def _uvw_case(B, k):
     return plan, prob
 
 
+@pytest.mark.parametrize("tune", ["", "pform=0"])
 @pytest.mark.parametrize("k", range(len(UVW_SMALL)))
-def test_uvw_conv_small(B, torch, k):
+def test_uvw_conv_small(B, torch, k, tune, monkeypatch):
+    """Graph calls through the per-pair matrix-core path tensors (default)
+    and through the per-edge kernel (pform=0)."""
+    monkeypatch.setenv("CGTP_TUNE", tune)
     plan, prob = _uvw_case(B, k)
+    assert ("cgtp_uvw_pf" in plan.source()) == (tune == "")
     g = W.molecule_batch(n_graphs=6, n_atoms=7, cutoff=5.0, seed=k)
     G = GraphArrays(g.src, g.dst, g.n_nodes)
     rng = np.random.default_rng(40 + k)
@@ -936,6 +941,45 @@ def test_uvw_matrix_core_path_tensors(B, torch, k, monkeypatch):
     out3 = B.cgtp_forward(plan, to_dev(torch, x[:23], "bf16"), to_dev(torch, y, "bf16"), to_dev(torch, w, "bf16"))
     torch.cuda.synchronize()
     assert_close(out3.cpu().numpy(), prob.tp_forward(x[:23], y, w), "bf16", f"uvw mma single {k}")
+
+
+@pytest.mark.parametrize("k", range(len(UVW_SMALL)))
+def test_uvw_pair_path_tensors_chunks(B, torch, k, monkeypatch):
+    """The per-pair matrix-core path tensors on rows of several 16-edge
+    chunks: a 53-edge hub row (four chunks, the last ragged) paired with a
+    short row, a row without edges, an odd node count (the last pair has one
+    node) and the longest-first node order; SH from the edge vectors where the
+    plan has one SH row."""
+    monkeypatch.setenv("CGTP_TUNE", "pform=1")
+    plan, prob = _uvw_case(B, k)
+    assert "cgtp_uvw_pf" in plan.source()
+    rng = np.random.default_rng(90 + k)
+    n = 31
+    src, dst = _small_graph(n, 260, 91 + k)
+    keep = dst != 5   # node 5 receives no edge
+    src, dst = src[keep], dst[keep]
+    src = np.concatenate([src, rng.integers(0, n, 53)]).astype(np.int32)
+    dst = np.concatenate([dst, np.full(53, 2)]).astype(np.int32)
+    G = GraphArrays(src, dst, n)
+    assert np.diff(G.row_ptr).max() > 48 and np.diff(G.row_ptr)[5] == 0
+    x = W.normal(rng, (n, prob.dim1), "bf16")
+    w = W.normal(rng, (prob.weight_numel,), "bf16")
+    d = G.dev(torch)
+    order = B.cgtp_node_order(d["dst_row_ptr"])
+    print(f"uvw pair path tensors k={k} E={G.E}", flush=True)
+    sh = W.normal(rng, (G.E, prob.dim2), "bf16")
+    out = B.cgtp_conv_forward(plan, to_dev(torch, x, "bf16"), to_dev(torch, sh[G.perm], "bf16"),
+                              to_dev(torch, w, "bf16"), d["src"], d["dst_row_ptr"], node_order=order)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), prob.conv_forward(x, sh, w, src, dst, n), "bf16", f"uvw pair {k}")
+    if k == 2:   # one SH row of degrees 0..6: the kernel evaluates it from the vectors
+        vec = _edge_vectors(rng, G.E, "f32")
+        out_v = B.cgtp_conv_forward_vec(plan, to_dev(torch, x, "bf16"), torch.from_numpy(vec).cuda(),
+                                        torch.from_numpy(G.perm).cuda(), to_dev(torch, w, "bf16"), d["src"],
+                                        d["dst_row_ptr"], node_order=order)
+        torch.cuda.synchronize()
+        ref_v = prob.conv_forward(x, oracle.spherical_harmonics(6, vec.astype(np.float64)), w, src, dst, n)
+        assert_close(out_v.cpu().numpy(), ref_v, "bf16", "uvw pair, SH from vectors")
 
 
 def test_uvw_single_tp(B, torch):

@@ -69,21 +69,29 @@ def test_generated_source_has_each_nonzero_once_per_channel_slot(B):
 
 
 def test_uvw_matrix_core_source_contracts_each_nonzero_once(B, monkeypatch):
-    """The optional uvw kernel (tuning switch umma): the outer-product sums go
-    to the matrix cores, and the coupling is applied once per node with one
-    term per CG nonzero of every (path, v, k) column.  The default kernel has
-    no matrix-core code (its channel mixing is a library kernel)."""
+    """The uvw path-tensor kernels apply the coupling with one term per CG
+    nonzero of every (path, v, k) column: the default per-pair kernel after
+    its products P_i = sum_e y_e x_e,i on the matrix cores, the optional
+    per-node kernel (tuning switch umma) likewise.  The per-edge kernel
+    (pform=0) has no matrix-core code (its channel mixing is a library
+    kernel)."""
     a, b, c = "8x0+8x1+8x2", "1x0+1x1+1x2", "12x0+12x1+12x2"
-    plain = B.Plan(a, b, c, None, "uvw", "bf16", True, no_load=True).source()
-    assert "__builtin_amdgcn_mfma" not in plain
-    monkeypatch.setenv("CGTP_TUNE", "umma=1")
-    src = B.Plan(a, b, c, None, "uvw", "bf16", True, no_load=True).source()
-    assert "__builtin_amdgcn_mfma_f32_16x16x16bf16_1k" in src
     nnz = 0
     for l1 in range(3):
         for l2 in range(3):
             for l3 in range(abs(l1 - l2), min(l1 + l2, 2) + 1):
                 nnz += int((np.abs(oracle.real_cg(l1, l2, l3)) > 1e-14).sum())
+    monkeypatch.setenv("CGTP_TUNE", "pform=0")
+    plain = B.Plan(a, b, c, None, "uvw", "bf16", True, no_load=True).source()
+    assert "__builtin_amdgcn_mfma" not in plain
+    monkeypatch.setenv("CGTP_TUNE", "")
+    pf = B.Plan(a, b, c, None, "uvw", "bf16", True, no_load=True).source()
+    assert "__builtin_amdgcn_mfma_f32_32x32x16_bf16" in pf and "__builtin_amdgcn_permlane32_swap" in pf
+    # contraction terms "c * c<half>_<tile>[<register>]", one per nonzero
+    assert len(re.findall(r"[-+] 0x[0-9a-fp.+-]+f \* c[01]_\d+\[\d+\]", pf)) == nnz
+    monkeypatch.setenv("CGTP_TUNE", "umma=1")
+    src = B.Plan(a, b, c, None, "uvw", "bf16", True, no_load=True).source()
+    assert "__builtin_amdgcn_mfma_f32_16x16x16bf16_1k" in src and "cgtp_uvw_pf" not in src
     # contraction terms "c * pr[j]", one per nonzero
     assert len(re.findall(r"[-+] 0x[0-9a-fp.+-]+f \* pr\[\d+\]", src)) == nnz
 
