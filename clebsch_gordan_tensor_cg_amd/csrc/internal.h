@@ -58,7 +58,7 @@ struct KernelShape {
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
 // of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, gy64, full,
-// ubudget, ucpl, umma, cstage, mix2, depth_bwd, pform)
+// ubudget, ucpl, umma, cstage, mix2, depth_bwd, pform, pfw)
 // overrides
 // them for experiments.
 struct Tuning {
@@ -88,6 +88,7 @@ struct Tuning {
     int pform = -1;          // uvw path tensors of graph calls from per-chunk products P_i = sum_e y_e x_e,i
                              // on the matrix cores, two nodes per wavefront (1), or the per-edge kernel
                              // (0); -1: the first wherever the plan allows it
+    int pfw = 0;             // wavefronts per node pair in that kernel (0: 4)
 };
 Tuning tuning_from_env();
 

@@ -294,6 +294,7 @@ Tuning tuning_from_env() {
             else if (k == "ucpl") t.ucpl = v < 1 ? 0 : (v > 8 ? 8 : v);
             else if (k == "umma") t.umma = v != 0;
             else if (k == "pform") t.pform = v;
+            else if (k == "pfw") t.pfw = v;
             else if (k == "cstage") t.cstage = v != 0;
             else if (k == "mix2") t.mix2 = v < 0 ? -1 : (v != 0);
         }
