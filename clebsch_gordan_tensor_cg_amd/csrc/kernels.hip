@@ -1191,14 +1191,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
 // together with the weight loads: one global round trip, one barrier, then
 // the products on v_mfma_f32_16x16x32_bf16.  The weight rows of a 32-row step
 // are stored interleaved in groups of eight: element (r, c) of the span at
-// ((r/8)*64 + c)*8 + r%8, so a lane's B fragment (eight consecutive rows of
-// one column) is one 16-byte read.  Lane l supplies A[l%16][8(l/16)+j] and
+// mix2_slot(r/8, c)*8 + r%8, so a lane's B fragment (eight consecutive rows
+// of one column) is one 16-byte read.  Lane l supplies A[l%16][8(l/16)+j] and
 // B[8(l/16)+j][l%16], j = 0..7, and receives D[4(l/16)+i][l%16], i = 0..3.
 // The row of path p's weight block for contraction row r = h*Kb + kk is
 // found once per 8-row group: p = kk / rows when every path has the same
 // number of rows, else by a search of the path table.
 constexpr int kMix2MaxK = 512;
 typedef __bf16 cgtp_bf16x8 __attribute__((ext_vector_type(8)));
+// 16-byte slot of column c in 8-row group q: the low three bits of c are
+// XORed with ((c >> 3) + q) mod 8, so the staging writes (eight column
+// groups of two row groups per 16 lanes) and the fragment reads (16
+// consecutive columns) of 16 lanes fall in 16 distinct slots modulo 256 bytes
+__device__ __forceinline__ int mix2_slot(int q, int c) { return q * 64 + (c ^ (((c >> 3) + q) & 7)); }
 
 __global__ void __launch_bounds__(256) k_uvw_mix2(const uint16_t *__restrict__ T0, const uint16_t *__restrict__ W,
                                                   int64_t wstride, MixArgs args, float *__restrict__ out,
@@ -1270,13 +1275,14 @@ __global__ void __launch_bounds__(256) k_uvw_mix2(const uint16_t *__restrict__ T
                                           {v[2].x, v[2].y, v[2].z, v[2].w}, {v[3].x, v[3].y, v[3].z, v[3].w},
                                           {v[4].x, v[4].y, v[4].z, v[4].w}, {v[5].x, v[5].y, v[5].z, v[5].w},
                                           {v[6].x, v[6].y, v[6].z, v[6].w}, {v[7].x, v[7].y, v[7].z, v[7].w}};
-                uint4 *dst = (uint4 *)Ws + q * 64 + c8;
+                uint4 *ws4 = (uint4 *)Ws;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {   // columns c8+2d (low halves) and c8+2d+1 (high halves)
-                    dst[2 * d] = make_uint4(lo_halves(w[0][d], w[1][d]), lo_halves(w[2][d], w[3][d]),
-                                            lo_halves(w[4][d], w[5][d]), lo_halves(w[6][d], w[7][d]));
-                    dst[2 * d + 1] = make_uint4(hi_halves(w[0][d], w[1][d]), hi_halves(w[2][d], w[3][d]),
-                                                hi_halves(w[4][d], w[5][d]), hi_halves(w[6][d], w[7][d]));
+                    ws4[mix2_slot(q, c8 + 2 * d)] = make_uint4(lo_halves(w[0][d], w[1][d]), lo_halves(w[2][d], w[3][d]),
+                                                               lo_halves(w[4][d], w[5][d]), lo_halves(w[6][d], w[7][d]));
+                    ws4[mix2_slot(q, c8 + 2 * d + 1)] =
+                        make_uint4(hi_halves(w[0][d], w[1][d]), hi_halves(w[2][d], w[3][d]), hi_halves(w[4][d], w[5][d]),
+                                   hi_halves(w[6][d], w[7][d]));
                 }
             }
             __syncthreads();
@@ -1286,10 +1292,11 @@ __global__ void __launch_bounds__(256) k_uvw_mix2(const uint16_t *__restrict__ T
 #pragma unroll
             for (int st = 0; st < kMix2MaxK / 32; ++st) {
                 if (st < ns) {   // uniform
-                    const cgtp_bf16x8 *bq = (const cgtp_bf16x8 *)Ws + (4 * st + g) * 64 + r_a;
+                    const cgtp_bf16x8 *bq = (const cgtp_bf16x8 *)Ws;
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct)
-                        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st], bq[16 * ct], acc[ct], 0, 0, 0);
+                        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st], bq[mix2_slot(4 * st + g, r_a + 16 * ct)],
+                                                                          acc[ct], 0, 0, 0);
                 }
             }
             const int64_t rq = row0 + 4 * g;
