@@ -545,6 +545,10 @@ def bench_conv(args, torch, B, W):
         roof = {"bound": "alu", "kernel": pt, "achieved": round(tf, 3),
                 "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
                 "traffic": None, "alg_flop_per_launch": int(flop), "avg_ms": round(t_ms, 4)}
+        if pt == "cgtp_uvw_pf":
+            roof["flop_count"] = ("the per-edge form's CG flops; this kernel forms each 16-edge chunk's products "
+                                  "on the matrix cores and applies the CG terms once per chunk, and is bound by "
+                                  "the latency of each node pair's loads, not by the VALU")
     res = {
         "metric": METRIC,
         "value": E / (ms * 1e-3),
