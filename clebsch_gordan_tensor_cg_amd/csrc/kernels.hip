@@ -269,126 +269,40 @@ __global__ void k_scatter_global(const int32_t *__restrict__ key, int64_t n, int
     }
 }
 
-// Small key arrays in two launches and without device atomics.
-// k_csr_small_count (one workgroup) counts the keys of each of kSmallCsrRuns
-// contiguous edge runs in LDS, scans the key totals into row_ptr and writes,
-// per (run, key), the slot of the run's first edge with that key (16 bits:
-// every slot is below 65536).  k_csr_small_place (one wavefront per run)
-// walks its run in edge order, 64 edges at a time: one ballot per key bit
-// finds the lanes holding the same key, which ranks each edge among the
-// chunk's equal keys and elects the highest such lane to advance the run's
-// slot for that key.  The placement is therefore stable (edge order inside
-// every segment) without a sort.
-constexpr int kSmallCsrRuns = 32;
+// Small key arrays (at most 65,535 edges and 2,048 keys) in one launch, with
+// no device atomics and no communication between workgroups.  The edges are
+// cut into runs of a power-of-two length (at least 64, at most
+// kSmallCsrMaxRuns runs).  Workgroup r counts the keys of the whole array in
+// LDS -- each key's total in the low half of a word, its count in the runs
+// before r in the high half (a run or the array holds at most 65,535 edges,
+// so no carry) -- scans the totals into each key's first slot and so knows
+// where its own run's edges of each key go.  Its first wavefront then walks
+// the run in edge order, 64 edges at a time: one ballot per key bit finds
+// the lanes holding the same key, which ranks each edge among the chunk's
+// equal keys and elects the highest such lane to advance the key's next
+// slot.  The placement is therefore stable (edge order inside every segment)
+// without a sort.  Workgroup 0 also writes row_ptr and, with order non-NULL,
+// the longest-first node order (as k_order_small) from the totals.  Each
+// workgroup rereads the key array (at most 256 KiB) from L2.
+constexpr int kSmallCsrMaxRuns = 128;
 constexpr int64_t kSmallCsrMaxKeys = 2048;
 constexpr int64_t kSmallCsrMaxEdges = 65535;
-constexpr int kSmallCsrChunks = 32;          // 64-edge chunks of one run (a run holds at most 2048 edges)
+constexpr int kSmallCsrChunks = 8;           // 64-edge chunks of one run (a run holds at most 512 edges)
 static_assert(kSmallCsrMaxKeys == 2048, "the key-match ballots cover 11 bits");
-constexpr int kSmallCsrKeysPerThread = 32;   // keys per thread and round of the counting workgroup
+static_assert(kSmallCsrMaxEdges <= (int64_t)kSmallCsrMaxRuns * 64 * kSmallCsrChunks, "runs of at most 512 edges");
+constexpr int kSmallCsrKeysPerThread = 32;   // keys per thread and round of the counting
 __host__ __device__ constexpr bool small_csr(int64_t n_edges, int64_t n_keys) {
     return n_edges > 0 && n_keys > 0 && n_edges <= kSmallCsrMaxEdges && n_keys <= kSmallCsrMaxKeys;
 }
-
-__host__ __device__ constexpr int64_t small_csr_stride(int64_t n_keys) { return (n_keys + 1) & ~int64_t(1); }
-// runs of 2^s edges, the smallest power of two with kSmallCsrRuns runs covering n
+// runs of 2^s edges: the smallest power of two, at least 64, with at most
+// kSmallCsrMaxRuns runs covering n
 __host__ __device__ constexpr int small_csr_run_shift(int64_t n) {
-    int sh = 0;
-    while ((int64_t(kSmallCsrRuns) << sh) < n) ++sh;
+    int sh = 6;
+    while ((int64_t(kSmallCsrMaxRuns) << sh) < n) ++sh;
     return sh;
 }
-// bytes of the per-(run, key) slot table in the workspace
-__host__ __device__ constexpr size_t small_csr_table_bytes(int64_t n_keys) {
-    return sizeof(uint16_t) * kSmallCsrRuns * (size_t)small_csr_stride(n_keys);
-}
-
-// counters: word [j][k] holds run 2j's count of key k in its low half and
-// run 2j+1's in its high half (a run holds at most 2048 edges, so no carry)
-// With order non-NULL the same workgroup also writes the longest-first node
-// order (as k_order_small) from the key totals it already holds.
-__global__ void __launch_bounds__(1024) k_csr_small_count(const int32_t *__restrict__ key, int64_t n, int64_t n_keys,
-                                                          int32_t *__restrict__ row_ptr,
-                                                          uint32_t *__restrict__ table,
-                                                          int32_t *__restrict__ order) {
-    extern __shared__ uint32_t cpair[];   // [kSmallCsrRuns / 2][n_keys]
-    __shared__ int32_t wsum[16];
-    __shared__ int32_t hb[kOrderBuckets];
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    const int nk = (int)n_keys;
-    const int rsh = small_csr_run_shift(n);
-    for (int i = t; i < (kSmallCsrRuns / 2) * nk; i += blockDim.x) cpair[i] = 0;
-    if (order) hb[t] = 0;
-    __syncthreads();
-    // 32 keys of a thread in flight at once: one round for up to 32768 edges
-    for (int h = 0; h * 32 * 1024 < n; ++h) {
-        int32_t kr[kSmallCsrKeysPerThread];
-#pragma unroll
-        for (int u = 0; u < kSmallCsrKeysPerThread; ++u) {
-            const int e = t + (h * kSmallCsrKeysPerThread + u) * 1024;
-            const int32_t kv = key[e < n ? e : n - 1];   // clamped: no branch around the load
-            kr[u] = e < n ? kv : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < kSmallCsrKeysPerThread; ++u) {
-            const int k = kr[u];
-            if (k >= 0 && k < nk) {
-                const int r = (t + (h * kSmallCsrKeysPerThread + u) * 1024) >> rsh;
-                atomicAdd(&cpair[(r >> 1) * nk + k], (r & 1) ? 65536u : 1u);
-            }
-        }
-    }
-    __syncthreads();
-    // two consecutive keys per thread: totals, scan, row_ptr and run slots
-    int tot[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int k = 2 * t + q;
-        tot[q] = 0;
-        if (k < nk)
-            for (int j = 0; j < kSmallCsrRuns / 2; ++j) {
-                const uint32_t c = cpair[j * nk + k];
-                tot[q] += (int)(c & 0xffffu) + (int)(c >> 16);
-            }
-    }
-    const int own = tot[0] + tot[1];
-    int incl = own;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += v;
-    }
-    if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wv; ++w) before += wsum[w];
-    const int first = before + incl - own;
-    if (2 * t < nk) {
-        int acc[2] = {first, first + tot[0]};
-        row_ptr[2 * t] = acc[0];
-        if (2 * t + 1 < nk) row_ptr[2 * t + 1] = acc[1];
-        const int64_t words = small_csr_stride(nk) / 2;
-        for (int j = 0; j < kSmallCsrRuns / 2; ++j) {
-            const uint32_t c0 = cpair[j * nk + 2 * t];
-            const uint32_t c1 = 2 * t + 1 < nk ? cpair[j * nk + 2 * t + 1] : 0u;
-            // run 2j, then run 2j+1: keys 2t (low half) and 2t+1 (high half)
-            table[(2 * j) * words + t] = (uint32_t)acc[0] | ((uint32_t)acc[1] << 16);
-            acc[0] += (int)(c0 & 0xffffu);
-            acc[1] += (int)(c1 & 0xffffu);
-            table[(2 * j + 1) * words + t] = (uint32_t)acc[0] | ((uint32_t)acc[1] << 16);
-            acc[0] += (int)(c0 >> 16);
-            acc[1] += (int)(c1 >> 16);
-        }
-    }
-    if (t == (int)blockDim.x - 1) row_ptr[nk] = before + incl;   // every valid key counted
-    if (order) {   // uniform: the whole workgroup takes this branch or none of it
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            if (2 * t + q < nk) atomicAdd(&hb[lpt_bucket(tot[q])], 1);
-        __syncthreads();   // also orders the reads of wsum above before its reuse
-        lpt_bucket_starts(hb, wsum);
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            if (2 * t + q < nk) order[atomicAdd(&hb[lpt_bucket(tot[q])], 1)] = 2 * t + q;
-    }
+__host__ __device__ constexpr int64_t small_csr_runs(int64_t n) {
+    return (n + (int64_t(1) << small_csr_run_shift(n)) - 1) >> small_csr_run_shift(n);
 }
 
 // lanes of this wavefront whose key equals this lane's key (valid lanes
@@ -409,57 +323,106 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__global__ void __launch_bounds__(64) k_csr_small_place(const int32_t *__restrict__ key,
-                                                        const int32_t *__restrict__ val, int64_t n, int64_t n_keys,
-                                                        int nbits, const uint16_t *__restrict__ table,
-                                                        int32_t *__restrict__ perm, int32_t *__restrict__ sorted_key,
-                                                        int32_t *__restrict__ sorted_val) {
-    extern __shared__ uint16_t slot_of[];   // [n_keys]: this run's next slot per key
-    const int lane = threadIdx.x;
+__global__ void __launch_bounds__(1024) k_csr_small(const int32_t *__restrict__ key, const int32_t *__restrict__ val,
+                                                    int64_t n, int64_t n_keys, int nbits, int32_t *__restrict__ row_ptr,
+                                                    int32_t *__restrict__ perm, int32_t *__restrict__ sorted_key,
+                                                    int32_t *__restrict__ sorted_val, int32_t *__restrict__ order) {
+    __shared__ uint32_t cnt[kSmallCsrMaxKeys];   // counts (total | before << 16), then each key's next slot
+    __shared__ int32_t wsum[16];
+    __shared__ int32_t hb[kOrderBuckets];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int nk = (int)n_keys;
-    const int64_t run = int64_t(1) << small_csr_run_shift(n);
-    const int64_t e0 = blockIdx.x * run, e1 = e0 + run < n ? e0 + run : n;
-    const uint16_t *__restrict__ row = table + blockIdx.x * small_csr_stride(nk);
-    // the whole run's keys and values in flight at once, one per lane and chunk
+    const int rsh = small_csr_run_shift(n);
+    const int64_t r0 = (int64_t)blockIdx.x << rsh;
+    const int64_t r1 = r0 + (int64_t(1) << rsh) < n ? r0 + (int64_t(1) << rsh) : n;
+    const bool lead = blockIdx.x == 0;
+    for (int i = t; i < nk; i += blockDim.x) cnt[i] = 0u;
+    if (order && lead) hb[t] = 0;
+    __syncthreads();
+    // 32 keys of a thread in flight at once: one round for up to 32,768 edges
+    for (int h = 0; h * kSmallCsrKeysPerThread * 1024 < n; ++h) {
+        int32_t kr[kSmallCsrKeysPerThread];
+#pragma unroll
+        for (int u = 0; u < kSmallCsrKeysPerThread; ++u) {
+            const int64_t e = t + (int64_t)(h * kSmallCsrKeysPerThread + u) * 1024;
+            const int32_t kv = key[e < n ? e : n - 1];   // clamped: no branch around the load
+            kr[u] = e < n ? kv : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kSmallCsrKeysPerThread; ++u) {
+            const int k = kr[u];
+            const int64_t e = t + (int64_t)(h * kSmallCsrKeysPerThread + u) * 1024;
+            if (k >= 0 && k < nk) atomicAdd(&cnt[k], e < r0 ? 0x10001u : 1u);
+        }
+    }
+    __syncthreads();
+    // two consecutive keys per thread: totals, scan, row_ptr, this run's first slots
+    int tot[2], bef[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int k = 2 * t + q;
+        const uint32_t c = k < nk ? cnt[k] : 0u;
+        tot[q] = (int)(c & 0xffffu);
+        bef[q] = (int)(c >> 16);
+    }
+    const int own = tot[0] + tot[1];
+    int incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();   // also: every count is read before any is overwritten below
+    int before = 0;
+    for (int w = 0; w < wv; ++w) before += wsum[w];
+    const int first = before + incl - own;
+    if (2 * t < nk) {
+        if (lead) {
+            row_ptr[2 * t] = first;
+            if (2 * t + 1 < nk) row_ptr[2 * t + 1] = first + tot[0];
+        }
+        cnt[2 * t] = (uint32_t)(first + bef[0]);
+        if (2 * t + 1 < nk) cnt[2 * t + 1] = (uint32_t)(first + tot[0] + bef[1]);
+    }
+    if (lead && t == (int)blockDim.x - 1) row_ptr[nk] = before + incl;   // every valid key counted
+    if (order && lead) {   // uniform: the whole workgroup takes this branch or none of it
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            if (2 * t + q < nk) atomicAdd(&hb[lpt_bucket(tot[q])], 1);
+        __syncthreads();   // also orders the reads of wsum above before its reuse
+        lpt_bucket_starts(hb, wsum);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            if (2 * t + q < nk) order[atomicAdd(&hb[lpt_bucket(tot[q])], 1)] = 2 * t + q;
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    // the first wavefront walks the run; every chunk's keys and values in flight at once
     int32_t kb[kSmallCsrChunks], vb[kSmallCsrChunks] = {};
 #pragma unroll
     for (int u = 0; u < kSmallCsrChunks; ++u) {
-        const int64_t e = e0 + 64 * u + lane;
-        const int64_t ec = e < e1 ? e : (e0 < e1 ? e1 - 1 : 0);   // clamped: no branch around the loads
+        const int64_t e = r0 + 64 * u + lane;
+        const int64_t ec = e < r1 ? e : r1 - 1;   // clamped: no branch around the loads
         const int32_t kv = key[ec];
-        kb[u] = e < e1 ? kv : -1;
+        kb[u] = e < r1 ? kv : -1;
         if (sorted_val) vb[u] = val[ec];
     }
-    // the run's slot row, as 32-bit words, all in flight together
-    constexpr int kRowWords = (int)(kSmallCsrMaxKeys / 2 / 64);
-    const int words = (int)(small_csr_stride(nk) / 2);
-    uint32_t rw[kRowWords];
-#pragma unroll
-    for (int u = 0; u < kRowWords; ++u) {
-        const int i = lane + 64 * u;
-        rw[u] = i < words ? ((const uint32_t *)row)[i] : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < kRowWords; ++u) {
-        const int i = lane + 64 * u;
-        if (i < words) ((uint32_t *)slot_of)[i] = rw[u];
-    }
-    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kSmallCsrChunks; ++u) {
-        if (e0 + 64 * u >= e1) break;   // uniform across the wavefront
-        const int64_t e = e0 + 64 * u + lane;
+        if (r0 + 64 * u >= r1) break;   // uniform across the wavefront
+        const int64_t e = r0 + 64 * u + lane;
         const int32_t k = kb[u];
         const bool valid = k >= 0 && k < nk;
         const uint64_t m = same_key_lanes(k, valid, nbits);
-        const int base = valid ? (int)slot_of[k] : 0;   // read by every lane before the update
+        const int base = valid ? (int)cnt[k] : 0;   // read by every lane before the update
         if (valid) {
             const int slot = base + lanes_below(m);
             perm[slot] = (int32_t)e;
             if (sorted_key) sorted_key[slot] = k;
             if (sorted_val) sorted_val[slot] = vb[u];
         }
-        if (valid && ((m >> lane) >> 1) == 0) slot_of[k] = (uint16_t)(base + __popcll(m));
+        if (valid && ((m >> lane) >> 1) == 0) cnt[k] = (uint32_t)(base + __popcll(m));
     }
 }
 
@@ -1564,7 +1527,6 @@ int cgtp_csr_workspace_bytes(int64_t n_edges, int64_t n_keys, size_t *bytes) {
     if (!bytes || n_edges < 0 || n_keys < 0)
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_csr_workspace_bytes: bad argument");
     *bytes = align256(sizeof(int32_t) * (size_t)(n_keys + 1)) * 2 + align256(sizeof(int32_t) * (size_t)(n_edges + 1));
-    if (small_csr(n_edges, n_keys)) *bytes = std::max(*bytes, align256(small_csr_table_bytes(n_keys)));
     return CGTP_OK;
 }
 
@@ -1591,17 +1553,8 @@ int cgtp_build_csr_order(const int32_t *key, const int32_t *val, int64_t n_edges
     if (small_csr(n_edges, n_keys)) {
         int nbits = 0;
         while ((int64_t(1) << nbits) < n_keys) ++nbits;
-        const size_t lds = sizeof(uint32_t) * (kSmallCsrRuns / 2) * (size_t)n_keys;   // up to 128 KiB
-        static const hipError_t lds_ok = hipFuncSetAttribute(
-            (const void *)k_csr_small_count, hipFuncAttributeMaxDynamicSharedMemorySize,
-            (int)(sizeof(uint32_t) * (kSmallCsrRuns / 2) * kSmallCsrMaxKeys));
-        if (lds_ok != hipSuccess) return hip_check(lds_ok, "cgtp_build_csr: LDS size attribute");
-        uint32_t *table = (uint32_t *)workspace;
-        CGTP_LAUNCH("k_csr_small_count", s, k_csr_small_count, dim3(1), dim3(1024), lds, s, key, n_edges, n_keys,
-                    row_ptr, table, order);
-        CGTP_LAUNCH("k_csr_small_place", s, k_csr_small_place, dim3(kSmallCsrRuns), dim3(64),
-                    sizeof(uint16_t) * (size_t)small_csr_stride(n_keys), s, key, val, n_edges, n_keys, nbits,
-                    (const uint16_t *)table, perm, sorted_key, sorted_val);
+        CGTP_LAUNCH("k_csr_small", s, k_csr_small, dim3((unsigned)small_csr_runs(n_edges)), dim3(1024), 0, s, key, val,
+                    n_edges, n_keys, nbits, row_ptr, perm, sorted_key, sorted_val, order);
         return hip_check(hipGetLastError(), "cgtp_build_csr launch");
     }
     char *ws = (char *)workspace;
