@@ -540,13 +540,19 @@ def bench_conv(args, torch, B, W):
     if name == "c5":
         # the path tensors on the vector ALUs dominate: FP32 vector peak
         flop = tp_flops(cfg, plan) * E
+        mixes = pt == "cgtp_uvw_pf" and not any(k.startswith("k_uvw_mix") for k in kern)
+        if mixes:   # the channel mixing runs inside the same kernel: its flops too
+            a_ir, c_ir = parse_irreps(cfg.irreps_in1), parse_irreps(cfg.irreps_out)
+            flop += sum(2 * N * (2 * c_ir[b][1] + 1) * c_ir[b][0] *
+                        sum(a_ir[i1][0] for (i1, _, i3) in plan.paths() if i3 == b) for b in range(len(c_ir)))
         t_ms = kern[pt]["avg_ms"]
         tf = flop / (t_ms * 1e-3) / 1e12
         roof = {"bound": "alu", "kernel": pt, "achieved": round(tf, 3),
                 "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
                 "traffic": None, "alg_flop_per_launch": int(flop), "avg_ms": round(t_ms, 4)}
         if pt == "cgtp_uvw_pf":
-            roof["flop_count"] = ("the per-edge form's CG flops; this kernel forms each 16-edge chunk's products "
+            roof["flop_count"] = ("the per-edge form's CG flops" + (" plus the channel mixing's (done in the same "
+                                  "kernel)" if mixes else "") + "; this kernel forms each 16-edge chunk's products "
                                   "on the matrix cores and applies the CG terms once per chunk, and is bound by "
                                   "the latency of each node pair's loads, not by the VALU")
     res = {

@@ -399,9 +399,16 @@ static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, c
     // input-1 block)
     // (its x segments are read in 16-byte groups: x must be 16-byte aligned)
     const bool pf = graph && p.uvw_pf && ((uintptr_t)x & 15) == 0;
-    int rc = pf                  ? launch(p.k_uvw_pf, "cgtp_uvw_pf", (n_items + 1) / 2, s, args, 64 * p.uvw_pf_waves)
-             : p.uvw_mma         ? launch(p.k_fwd, "cgtp_fwd", n_items * p.uvw_mma_groups, s, args, 256)
-                                 : launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
+    if (pf) {
+        // the pair kernel; with the mixing inside it writes out directly
+        void *pargs[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, (void *)&order, (void *)&vec,
+                         (void *)&vperm, (void *)&radial, &ws, &n, &graph, (void *)&w, &out};
+        int rc = launch(p.k_uvw_pf, "cgtp_uvw_pf", (n_items + 1) / 2, s, pargs, 64 * p.uvw_pf_waves);
+        if (rc || p.uvw_pf_mix) return rc;
+    }
+    int rc = pf          ? CGTP_OK
+             : p.uvw_mma ? launch(p.k_fwd, "cgtp_fwd", n_items * p.uvw_mma_groups, s, args, 256)
+                         : launch(p.k_fwd, "cgtp_fwd", (n_items + ipw - 1) / ipw * p.fwd.n_units, s, args);
     if (rc) return rc;
     int acc = 0;
     if (!blocks_covered(p.out, p.paths, true)) {

@@ -58,7 +58,7 @@ struct KernelShape {
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
 // of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, gy64, full,
-// ubudget, ucpl, umma, cstage, mix2, depth_bwd, pform, pfw)
+// ubudget, ucpl, umma, cstage, mix2, depth_bwd, pform, pfw, pfuse)
 // overrides
 // them for experiments.
 struct Tuning {
@@ -89,6 +89,7 @@ struct Tuning {
                              // on the matrix cores, two nodes per wavefront (1), or the per-edge kernel
                              // (0); -1: the first wherever the plan allows it
     int pfw = 0;             // wavefronts per node pair in that kernel (0: 4)
+    int pfuse = 1;           // that kernel also does the channel mixing where the plan allows it
 };
 Tuning tuning_from_env();
 
@@ -125,6 +126,7 @@ struct Plan {
     int uvw_mma_groups = 0;        // its workgroups per item (input-1 blocks with paths), 256 threads each
     bool uvw_pf = false;           // uvw: graph calls take the path tensors from cgtp_uvw_pf
     int uvw_pf_waves = 0;          // its wavefronts per workgroup (one workgroup per pair of nodes)
+    bool uvw_pf_mix = false;       // and it does the channel mixing too (writes out, not T)
     std::string source;
     std::string cache_key;
     bool cached = false;
@@ -162,6 +164,7 @@ int uvw_mma_group_count(const Plan &p);
 // allows them, and the wavefronts of each pair's workgroup
 bool uvw_pf_eligible(const Plan &p);
 int uvw_pf_wave_count(const Plan &p);
+bool uvw_pf_mixes(const Plan &p);   // that kernel also does the channel mixing (no T in memory)
 constexpr size_t kUvwMmaMaxLds = 64 * 1024;   // static LDS of one workgroup
 
 // planner

@@ -295,6 +295,7 @@ Tuning tuning_from_env() {
             else if (k == "umma") t.umma = v != 0;
             else if (k == "pform") t.pform = v;
             else if (k == "pfw") t.pfw = v;
+            else if (k == "pfuse") t.pfuse = v;
             else if (k == "cstage") t.cstage = v != 0;
             else if (k == "mix2") t.mix2 = v < 0 ? -1 : (v != 0);
         }
@@ -400,6 +401,7 @@ void choose_shapes(Plan &p) {
         // one asked for instead
         p.uvw_pf = (p.tune.pform > 0 || (p.tune.pform < 0 && !p.uvw_mma)) && uvw_pf_eligible(p);
         p.uvw_pf_waves = p.uvw_pf ? uvw_pf_wave_count(p) : 0;
+        p.uvw_pf_mix = p.uvw_pf && uvw_pf_mixes(p);
         return;
     }
     split(p, p.fwd, 0);

@@ -884,14 +884,15 @@ def _uvw_case(B, k):
     return plan, prob
 
 
-@pytest.mark.parametrize("tune", ["", "pform=0"])
+@pytest.mark.parametrize("tune", ["", "pfuse=0", "pform=0"])
 @pytest.mark.parametrize("k", range(len(UVW_SMALL)))
 def test_uvw_conv_small(B, torch, k, tune, monkeypatch):
-    """Graph calls through the per-pair matrix-core path tensors (default)
-    and through the per-edge kernel (pform=0)."""
+    """Graph calls through the per-pair matrix-core path tensors with the
+    channel mixing inside (default), with the mixing as its own launch
+    (pfuse=0), and through the per-edge kernel (pform=0)."""
     monkeypatch.setenv("CGTP_TUNE", tune)
     plan, prob = _uvw_case(B, k)
-    assert ("cgtp_uvw_pf" in plan.source()) == (tune == "")
+    assert ("cgtp_uvw_pf" in plan.source()) == (tune != "pform=0")
     g = W.molecule_batch(n_graphs=6, n_atoms=7, cutoff=5.0, seed=k)
     G = GraphArrays(g.src, g.dst, g.n_nodes)
     rng = np.random.default_rng(40 + k)
