@@ -296,6 +296,7 @@ Tuning tuning_from_env() {
             else if (k == "pform") t.pform = v;
             else if (k == "pfw") t.pfw = v;
             else if (k == "pfuse") t.pfuse = v;
+            else if (k == "pfocc") t.pfocc = v;
             else if (k == "cstage") t.cstage = v != 0;
             else if (k == "mix2") t.mix2 = v < 0 ? -1 : (v != 0);
         }
