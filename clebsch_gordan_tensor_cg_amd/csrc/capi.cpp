@@ -397,8 +397,9 @@ static int run_uvw(const Plan &p, const void *x, const void *y, const void *w, c
     // workgroup per pair of nodes); else the per-edge kernel, or the
     // per-node matrix-core form (one workgroup of four wavefronts per item and
     // input-1 block)
-    // (its x segments are read in 16-byte groups: x must be 16-byte aligned)
-    const bool pf = graph && p.uvw_pf && ((uintptr_t)x & 15) == 0;
+    // (its x segments, and with the mixing inside the weight rows, are read
+    // in 16-byte groups: they must be 16-byte aligned)
+    const bool pf = graph && p.uvw_pf && ((uintptr_t)x & 15) == 0 && (!p.uvw_pf_mix || ((uintptr_t)w & 15) == 0);
     if (pf) {
         // the pair kernel; with the mixing inside it writes out directly
         void *pargs[] = {(void *)&x, (void *)&y, (void *)&src, (void *)&row_ptr, (void *)&order, (void *)&vec,

@@ -58,7 +58,7 @@ struct KernelShape {
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
 // of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, gy64, full,
-// ubudget, ucpl, umma, cstage, mix2, depth_bwd, pform, pfw, pfuse, pfocc)
+// ubudget, ucpl, umma, cstage, mix2, depth_bwd, pform, pfw, pfuse, pfocc, pfma, pfml)
 // overrides
 // them for experiments.
 struct Tuning {
@@ -91,6 +91,8 @@ struct Tuning {
     int pfw = 0;             // wavefronts per node pair in that kernel (0: 4)
     int pfuse = 1;           // that kernel also does the channel mixing where the plan allows it
     int pfocc = 0;           // its wavefronts per SIMD asked of the compiler (0: 4)
+    int pfma = 0;            // its mixing: products whose weight rows are loaded ahead (0: 6)
+    int pfml = 0;            // and whose fragments are read from LDS ahead (0: 2)
 };
 Tuning tuning_from_env();
 
