@@ -728,8 +728,12 @@ def bench_radial(args, torch, B, W):
     tf = flop / (t_ms * 1e-3) / 1e12
     mix_flop = sum(2 * N * (2 * c_ir[b][1] + 1) * c_ir[b][0] * (H + 1) *
                    sum(a_ir[i1][0] for (i1, _, i3) in plan.paths() if i3 == b) for b in range(len(c_ir)))
-    mix_k = "k_uvw_mix2" if "k_uvw_mix2" in kern else "k_uvw_mix"
-    mix_ms = kern[mix_k]["ms_per_step"]
+    mix_k = next(k for k in ("k_uvw_mix3", "k_uvw_mix2", "k_uvw_mix") if k in kern)
+    # the mixing with its partial-tile reduction, if the form has one
+    mix_ms = kern[mix_k]["ms_per_step"] + kern.get("k_uvw_mix_reduce", {"ms_per_step": 0.0})["ms_per_step"]
+    # the (H+1)-fold path tensors the mixing reads (bf16), every output block
+    t_bytes = sum(2 * N * (2 * c_ir[b][1] + 1) * (H + 1) *
+                  sum(a_ir[i1][0] for (i1, _, i3) in plan.paths() if i3 == b) for b in range(len(c_ir)))
     res = {"metric": METRIC, "value": E / (ms * 1e-3), "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_median": float(np.median(per_step)),
            "ms_per_step_min": float(np.min(per_step)), "higher_is_better": True, "scaling": "weak",
@@ -743,7 +747,8 @@ def bench_radial(args, torch, B, W):
                         "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
                         "alg_flop_per_launch": int(flop), "avg_ms": round(t_ms, 4)},
            "mixing": {"kernel": mix_k, "ms_per_step": round(mix_ms, 4),
-                      "TFLOP_per_s": round(mix_flop / (mix_ms * 1e-3) / 1e12, 3), "peak_bf16_mfma": 2500.0},
+                      "TFLOP_per_s": round(mix_flop / (mix_ms * 1e-3) / 1e12, 3), "peak_bf16_mfma": 2500.0,
+                      "path_tensor_bytes": int(t_bytes), "GB_per_s": round(t_bytes / (mix_ms * 1e-3) / 1e9, 1)},
            "kernels": kern}
     if not args.no_cpu_baseline:
         import oracle

@@ -58,7 +58,7 @@ struct KernelShape {
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
 // of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, gy64, full,
-// ubudget, ucpl, umma, cstage, mix2, depth_bwd, pform, pfw, pfuse, pfocc, pfma, pfml)
+// ubudget, ucpl, umma, cstage, mix2, mix3, depth_bwd, pform, pfw, pfuse, pfocc, pfma, pfml)
 // overrides
 // them for experiments.
 struct Tuning {
@@ -83,6 +83,8 @@ struct Tuning {
     int mix2 = -1;           // uvw mixing: the whole contraction span staged at once, 16x16x32 MFMA (1), or
                              // 256-row steps with 16x16x16 MFMA (0); -1: the first where every block's
                              // contraction fits one span of 512 rows (C5 mixing 20.3 -> 18.1 us)
+    int mix3 = -1;           // uvw mixing: the streaming form over the whole contraction (1, or -1: wherever a
+                             // block's contraction is longer than one span of the second form), or never (0)
     int umma = 0;            // uvw path tensors as per-node products on the matrix cores where they fit
                              // (measured slower on the 100 x 18 atom layer: off by default)
     int pform = -1;          // uvw path tensors of graph calls from per-chunk products P_i = sum_e y_e x_e,i

@@ -1287,6 +1287,168 @@ __global__ void __launch_bounds__(256) k_uvw_mix2(const uint16_t *__restrict__ T
     }
 }
 
+// The streaming form, for contractions longer than one span (a radial
+// network's (H+1)-fold rows): a workgroup owns 64 rows of T (16 per
+// wavefront) and 64 output columns and walks the whole contraction in
+// stages of kMix3Stage 32-row steps, so no partial tiles and no reduction.
+// Each stage's A fragments (16 bytes per lane and step, straight from T) and
+// weight rows (16 bytes per thread and step: row tid/8, columns
+// 8 (tid%8) .. + 7) are loaded kMix3Ahead stages before the stage is
+// multiplied; the weight rows go to one of two LDS buffers, one barrier per
+// stage, and the B fragments come back by two transposed reads (in each
+// 16-lane quarter, lane 4 q + r receives element r of the 8-byte reads of
+// lanes q, q + 4, q + 8 and q + 12: lane 4 j + q reads row 8 kg + 4 h + j,
+// columns 16 ct + 4 q .. + 3, and lane n receives rows 8 kg + 4 h .. + 3 of
+// column 16 ct + n).  The weight offset of every 8-row group of the
+// contraction is computed once per workgroup into an LDS table.
+// 16-byte chunk j of a stored weight row r sits at chunk j ^ mix3_swz(r): the
+// 8 rows x 2 chunks of a 32-lane transposed read then fill all 16 bank groups.
+constexpr int kMix3Stage = 4;
+constexpr int kMix3Ahead = 3;
+constexpr int kMix3MaxSteps = 512;   // contraction rows of one block at most 32 x this
+__device__ __forceinline__ int mix3_swz(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
+typedef __attribute__((address_space(3))) cgtp_s4 cgtp_lds_s4;
+typedef __bf16 cgtp_bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t cgtp_u32x4 __attribute__((ext_vector_type(4)));   // (a plain vector: kept in registers)
+
+__global__ void __launch_bounds__(256) k_uvw_mix3(const uint16_t *__restrict__ T0, const uint16_t *__restrict__ W,
+                                                  int64_t wstride, MixArgs args, float *__restrict__ out,
+                                                  int64_t dim3, int accumulate) {
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kMix3Stage * 32 * 64];
+    __shared__ int64_t wtab[kMix3MaxSteps * 4];
+    __shared__ int32_t s_kstart[kMixMaxPaths + 1];
+    __shared__ int64_t s_woff[kMixMaxPaths];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int bsel = 0;
+#pragma unroll
+    for (int i = 1; i < kMixMaxBlocks; ++i)
+        if (i < args.nb && (int64_t)blockIdx.x >= args.b[i].wg_start) bsel = i;
+    int np = 0, d3 = 1, mul3 = 0, rows_u = 0;
+    int64_t M = 0, K = 0, Kb = 1, off3 = 0, t_off = 0, wg_start = 0;
+#pragma unroll
+    for (int i = 0; i < kMixMaxBlocks; ++i)
+        if (i == bsel) {
+            np = args.b[i].np, d3 = args.b[i].d3, mul3 = args.b[i].mul3, rows_u = args.b[i].rows_uniform;
+            M = args.b[i].M, K = args.b[i].K, Kb = args.b[i].Kb, off3 = args.b[i].off3, t_off = args.b[i].t_off;
+            wg_start = args.b[i].wg_start;
+            if (tid <= np) s_kstart[tid] = args.b[i].kstart[tid];
+            if (tid < np) s_woff[tid] = args.b[i].woff[tid];
+        }
+    __syncthreads();
+    const int nsteps = (int)(K / 32);   // K a multiple of 32, at most 32 kMix3MaxSteps
+    // weight offset of contraction row 8 i (its 8-row group inside one path)
+    for (int i = tid; i < 4 * nsteps; i += 256) {
+        const int r = 8 * i, kbi = (int)Kb;
+        const int h = r / kbi, kk = r - h * kbi;
+        int p = 0;
+        if (rows_u > 0)
+            p = kk / rows_u;
+        else
+            while (p + 1 < np && kk >= s_kstart[p + 1]) ++p;
+        wtab[i] = h * wstride + s_woff[p] + (int64_t)(kk - s_kstart[p]) * mul3;
+    }
+    __syncthreads();
+    const uint16_t *__restrict__ T = T0 + t_off;
+    const int64_t wg = blockIdx.x - wg_start;
+    const int64_t wg_count = (bsel + 1 < args.nb ? args.b[bsel + 1 < kMixMaxBlocks ? bsel + 1 : 0].wg_start
+                                                  : (int64_t)gridDim.x) - wg_start;
+    const int r_a = lane & 15, g = lane >> 4;
+    const int64_t n_groups = (M + 63) / 64;
+    const int nst = (nsteps + kMix3Stage - 1) / kMix3Stage;
+    const int wr = tid >> 3, wc = tid & 7;   // this thread's weight row in a step and its 16-byte chunk
+    const int wrow = (wr & 7) * mul3 + 8 * wc;   // its offset inside the row's 8-row group
+    const int wsw = 8 * (wc ^ mix3_swz(wr));     // its chunk's place in a stored row
+    for (int cb = 0; cb < mul3; cb += 64) {
+        for (int64_t grp = wg; grp < n_groups; grp += wg_count) {
+            const int64_t row0 = grp * 64 + wv * 16;
+            const int64_t arow = row0 + r_a < M ? row0 + r_a : M - 1;
+            const cgtp_bf16x8 *__restrict__ Ta = (const cgtp_bf16x8 *)(T + arow * K) + g;
+            const uint16_t *__restrict__ Wc = W + cb + wrow;
+            // ring slot u holds stage st = u (mod 4) in registers: fragments
+            // a<u>[q] and weight rows w<u>[q], q < kMix3Stage
+            static_assert(kMix3Ahead == 3, "the ring below is written out for 4 slots");
+            cgtp_bf16x8 a0[kMix3Stage], a1[kMix3Stage], a2[kMix3Stage], a3[kMix3Stage];
+            cgtp_u32x4 w0[kMix3Stage], w1[kMix3Stage], w2[kMix3Stage], w3[kMix3Stage];
+            // loads of stage st; a step past the end reads the last step again
+            // (an L2 hit) and its products are skipped.  No load sits in a
+            // branch: at a join the compiler would wait for every load in flight.
+#define CGTP_MIX3_LOAD(u, st)                                                            \
+    {                                                                                    \
+        _Pragma("unroll") for (int q = 0; q < kMix3Stage; ++q) {                         \
+            const int step_ = (st) * kMix3Stage + q;                                     \
+            const int sc_ = step_ < nsteps ? step_ : nsteps - 1;                         \
+            a##u[q] = Ta[4 * sc_];                                                       \
+            w##u[q] = *(const cgtp_u32x4 *)(Wc + wtab[4 * sc_ + (wr >> 3)]);             \
+        }                                                                                \
+    }
+            // stage st from slot u (loading stage st + 3 into slot un first):
+            // weight rows to LDS, barrier, products
+#define CGTP_MIX3_STAGE(u, un, st)                                                                            \
+    {                                                                                                         \
+        CGTP_MIX3_LOAD(un, (st) + kMix3Ahead)                                                                 \
+        uint16_t *__restrict__ buf = Ws[(st) & 1];                                                            \
+        {                                                                                                     \
+            _Pragma("unroll") for (int q = 0; q < kMix3Stage; ++q)                                            \
+                *(cgtp_u32x4 *)(buf + (q * 32 + wr) * 64 + wsw) = w##u[q];                                    \
+        }                                                                                                     \
+        __syncthreads();                                                                                      \
+        _Pragma("unroll") for (int q = 0; q < kMix3Stage; ++q) {                                              \
+            if ((st) * kMix3Stage + q >= nsteps) break; /* uniform; no load in this branch */                 \
+            _Pragma("unroll") for (int ct = 0; ct < 4; ++ct) {                                                \
+                cgtp_s4 t2_[2];                                                                               \
+                _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                               \
+                    const int r = 8 * g + 4 * h + ((lane >> 2) & 3);                                          \
+                    const int chunk = (2 * ct + ((lane & 3) >> 1)) ^ mix3_swz(r);                             \
+                    t2_[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                                         \
+                        (cgtp_lds_s4 *)(buf + (q * 32 + r) * 64 + 8 * chunk + 4 * (lane & 1)));               \
+                }                                                                                             \
+                const cgtp_bf16x8 b_ = __builtin_shufflevector(__builtin_bit_cast(cgtp_bf16x4, t2_[0]),       \
+                                                               __builtin_bit_cast(cgtp_bf16x4, t2_[1]), 0, 1, \
+                                                               2, 3, 4, 5, 6, 7);                             \
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a##u[q], b_, acc[ct], 0, 0, 0);             \
+            }                                                                                                 \
+        }                                                                                                     \
+    }
+            CGTP_MIX3_LOAD(0, 0)
+            CGTP_MIX3_LOAD(1, 1)
+            CGTP_MIX3_LOAD(2, 2)
+#pragma unroll
+            for (int q = 0; q < kMix3Stage; ++q) a3[q] = a0[q], w3[q] = w0[q];   // defined before slot 3's first use
+            cgtp_f4 acc[4];
+            for (int ct = 0; ct < 4; ++ct) acc[ct] = (cgtp_f4){0.f, 0.f, 0.f, 0.f};
+            // four stages per iteration, the last ones past the end without
+            // products; every wavefront runs the same stages (the barriers match)
+            for (int st0 = 0; st0 < nst; st0 += 4) {
+                CGTP_MIX3_STAGE(0, 3, st0)
+                CGTP_MIX3_STAGE(1, 0, st0 + 1)
+                CGTP_MIX3_STAGE(2, 1, st0 + 2)
+                CGTP_MIX3_STAGE(3, 2, st0 + 3)
+            }
+#undef CGTP_MIX3_STAGE
+#undef CGTP_MIX3_LOAD
+            __syncthreads();   // every wavefront is done with both buffers before the next group writes them
+            if (row0 >= M) continue;
+            const int64_t rq = row0 + 4 * g;
+            const int64_t item_q = rq / d3;
+            const int k_q = (int)(rq - item_q * d3);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const int col = cb + ct * 16 + r_a;
+                int64_t item = item_q;
+                int k = k_q;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (rq + i < M) {
+                        float *o = out + item * dim3 + off3 + (int64_t)col * d3 + k;
+                        *o = accumulate ? *o + acc[ct][i] : acc[ct][i];
+                    }
+                    if (++k == d3) k = 0, ++item;
+                }
+            }
+        }
+    }
+}
+
 // out[item][off3 + col*d3 + k] (=|+=) sum_s part[s][item*d3 + k][col] for
 // every split block of the launch (elements enumerated block after block).
 // I: the index type of the element arithmetic (32-bit divisions whenever
@@ -1366,13 +1528,25 @@ int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items,
         // more spans than the first form's splits grow the partial sums and
         // their reduction, which measured no net gain on the radial layer)
         bool v2 = p.tune.mix2 != 0 && (((uintptr_t)T) & 15) == 0 && (((uintptr_t)w) & 15) == 0 && p.wnumel % 8 == 0;
+        // the streaming form (by default wherever a block's contraction is
+        // longer than one span of the second form): the same alignment, whole
+        // 32-row steps and 64-column tiles
+        bool v3 = p.tune.mix3 != 0 && (((uintptr_t)T) & 15) == 0 && (((uintptr_t)w) & 15) == 0 && p.wnumel % 8 == 0;
+        bool v3_wanted = p.tune.mix3 > 0;
         for (int i = 0; i < args.nb; ++i) {
             const MixBlock &mb = p.mix[b0 + i];
             v2 = v2 && mb.K % 32 == 0 && mb.mul3 % 64 == 0 && (n_items * mb.t_off_per_item) % 8 == 0 &&
                  (int)mb.paths.size() <= kMixMaxPaths && (p.tune.mix2 > 0 || mb.Kr <= kMix2MaxK);
             for (int pi : mb.paths)
                 v2 = v2 && p.paths[pi].woff % 8 == 0 && ((int64_t)p.paths[pi].mul1 * p.paths[pi].mul2) % 8 == 0;
+            v3 = v3 && mb.Kr % 32 == 0 && mb.Kr <= 32 * kMix3MaxSteps && mb.mul3 % 64 == 0 &&
+                 (n_items * mb.t_off_per_item) % 8 == 0 && (int)mb.paths.size() <= kMixMaxPaths;
+            for (int pi : mb.paths)
+                v3 = v3 && p.paths[pi].woff % 8 == 0 && ((int64_t)p.paths[pi].mul1 * p.paths[pi].mul2) % 8 == 0;
+            v3_wanted = v3_wanted || mb.Kr > kMix2MaxK;
         }
+        v3 = v3 && v3_wanted;
+        if (v3) v2 = false;
         for (int i = 0; i < args.nb; ++i) {
             const MixBlock &mb = p.mix[b0 + i];
             fast = fast && mb.Kr % 16 == 0 && mb.mul3 % 64 == 0 && (n_items * mb.t_off_per_item) % 4 == 0;
@@ -1396,7 +1570,10 @@ int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items,
             a.rows_uniform = (int32_t)((int64_t)p.paths[mb.paths[0]].mul1 * p.paths[mb.paths[0]].mul2);
             for (int pi : mb.paths)
                 if ((int64_t)p.paths[pi].mul1 * p.paths[pi].mul2 != a.rows_uniform) a.rows_uniform = 0;
-            if (v2) {
+            if (v3) {
+                a.n_split = 1;
+                a.kspan = mb.Kr;
+            } else if (v2) {
                 a.n_split = mix2_splits(mb, n_items);
                 const int64_t steps = mb.Kr / 32;
                 a.kspan = (steps + a.n_split - 1) / a.n_split * 32;
@@ -1416,7 +1593,10 @@ int launch_uvw_mix(const Plan &p, const void *T, const void *w, int64_t n_items,
             a.wg_start = wg;
             wg += groups * a.n_split;
         }
-        if (v2)
+        if (v3)
+            CGTP_LAUNCH("k_uvw_mix3", s, k_uvw_mix3, dim3((unsigned)wg), dim3(256), 0, s, (const uint16_t *)T,
+                        (const uint16_t *)w, p.wnumel, args, (float *)out, p.dim3, accumulate);
+        else if (v2)
             CGTP_LAUNCH("k_uvw_mix2", s, k_uvw_mix2, dim3((unsigned)wg), dim3(256), 0, s, (const uint16_t *)T,
                         (const uint16_t *)w, p.wnumel, args, (float *)out, p.dim3, accumulate, (float *)part);
         else if (fast)

@@ -298,6 +298,7 @@ Tuning tuning_from_env() {
             else if (k == "pfuse") t.pfuse = v;
             else if (k == "pfocc") t.pfocc = v;
             else if (k == "pfma") t.pfma = v;
+            else if (k == "mix3") t.mix3 = v;
             else if (k == "pfml") t.pfml = v;
             else if (k == "cstage") t.cstage = v != 0;
             else if (k == "mix2") t.mix2 = v < 0 ? -1 : (v != 0);

@@ -884,12 +884,13 @@ def _uvw_case(B, k):
     return plan, prob
 
 
-@pytest.mark.parametrize("tune", ["", "pfuse=0", "pform=0"])
+@pytest.mark.parametrize("tune", ["", "pfuse=0", "pform=0", "pfuse=0,mix3=1"])
 @pytest.mark.parametrize("k", range(len(UVW_SMALL)))
 def test_uvw_conv_small(B, torch, k, tune, monkeypatch):
     """Graph calls through the per-pair matrix-core path tensors with the
     channel mixing inside (default), with the mixing as its own launch
-    (pfuse=0), and through the per-edge kernel (pform=0)."""
+    (pfuse=0; with mix3=1 in the streaming form where the plan allows it),
+    and through the per-edge kernel (pform=0)."""
     monkeypatch.setenv("CGTP_TUNE", tune)
     plan, prob = _uvw_case(B, k)
     assert ("cgtp_uvw_pf" in plan.source()) == (tune != "pform=0")
@@ -906,6 +907,36 @@ def test_uvw_conv_small(B, torch, k, tune, monkeypatch):
                               to_dev(torch, w, "bf16"), d["src"], d["dst_row_ptr"])
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy(), ref, "bf16", f"uvw small {k}")
+
+
+@pytest.mark.parametrize("shift", ["w", "x"])
+@pytest.mark.parametrize("k", range(len(UVW_SMALL)))
+def test_uvw_conv_unaligned_operands(B, torch, k, shift):
+    """The pair kernel reads x segments, and with the mixing inside weight
+    rows, in 16-byte groups: an operand that starts 2 bytes past such a
+    boundary takes the per-edge kernel and gives the same result."""
+    plan, prob = _uvw_case(B, k)
+    g = W.molecule_batch(n_graphs=4, n_atoms=11, cutoff=5.0, seed=90 + k)
+    G = GraphArrays(g.src, g.dst, g.n_nodes)
+    rng = np.random.default_rng(95 + k)
+    x = W.normal(rng, (g.n_nodes, prob.dim1), "bf16")
+    sh = W.normal(rng, (G.E, prob.dim2), "bf16")
+    w = W.normal(rng, (prob.weight_numel,), "bf16")
+    d = G.dev(torch)
+
+    def shifted(a):   # a bf16 device copy whose data starts one element into its allocation
+        flat = to_dev(torch, np.concatenate([np.zeros(1, np.float32), a.reshape(-1)]), "bf16")
+        v = flat[1:].view(a.shape)
+        assert v.data_ptr() % 16 == 2
+        return v
+
+    print(f"uvw conv unaligned {shift} k={k}", flush=True)
+    xd = shifted(x) if shift == "x" else to_dev(torch, x, "bf16")
+    wd = shifted(w) if shift == "w" else to_dev(torch, w, "bf16")
+    out = B.cgtp_conv_forward(plan, xd, to_dev(torch, sh[G.perm], "bf16"), wd, d["src"], d["dst_row_ptr"])
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), prob.conv_forward(x, sh, w, g.src, g.dst, g.n_nodes), "bf16",
+                 f"uvw unaligned {shift} {k}")
 
 
 @pytest.mark.parametrize("k", range(len(UVW_SMALL)))

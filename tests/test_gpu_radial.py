@@ -53,8 +53,12 @@ def _run(B, torch, plan, g, x, w, radial, order=None):
     return out.cpu().numpy(), vec
 
 
-@pytest.mark.parametrize("k,H", [(0, 1), (0, 4), (1, 3), (2, 2)])
-def test_radial_conv_small(B, torch, k, H):
+@pytest.mark.parametrize("k,H,tune", [(0, 1, ""), (0, 4, ""), (1, 3, ""), (2, 2, ""), (2, 2, "mix3=0"), (2, 5, "")])
+def test_radial_conv_small(B, torch, k, H, tune, monkeypatch):
+    """Ragged molecule batches; on the C5 irreps the (H+1)-fold contraction
+    exceeds one span of 512 rows, so the mixing takes the streaming form by
+    default and the split form with mix3=0."""
+    monkeypatch.setenv("CGTP_TUNE", tune)
     plan, prob = _case(B, k, H)
     g = W.molecule_batch(n_graphs=6, n_atoms=7, cutoff=5.0, seed=k)
     rng = np.random.default_rng(60 + k)
