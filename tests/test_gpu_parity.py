@@ -909,6 +909,36 @@ def test_uvw_conv_small(B, torch, k, tune, monkeypatch):
     assert_close(out.cpu().numpy(), ref, "bf16", f"uvw small {k}")
 
 
+# paths of 16 and 32 contraction rows (so no uniform row count) and 128
+# output channels (two 64-column tiles of the streaming mixing)
+WIDE_UVW = ("16x0+16x1+32x2", "1x0+1x1+1x2", "128x0+128x1")
+
+
+@pytest.mark.parametrize("tune", ["pform=0,mix3=1", "pform=0,mix3=0", "pfuse=0,mix3=1", ""])
+def test_uvw_mix_forms_wide_layer(B, torch, tune, monkeypatch):
+    """Every channel-mixing form on a layer whose blocks mix paths of
+    different row counts into 128 output channels: the streaming form
+    (mix3=1, behind the per-edge or the pair kernel's path tensors), the
+    whole-span form (mix3=0) and the default."""
+    monkeypatch.setenv("CGTP_TUNE", tune)
+    a, b, c = WIDE_UVW
+    plan = B.Plan(a, b, c, None, "uvw", "bf16", shared_weights=True)
+    prob = oracle.Problem(a, b, c, "uvw", None, shared_weights=True)
+    g = W.molecule_batch(n_graphs=5, n_atoms=9, cutoff=5.0, seed=77)
+    G = GraphArrays(g.src, g.dst, g.n_nodes)
+    rng = np.random.default_rng(78)
+    x = W.normal(rng, (g.n_nodes, prob.dim1), "bf16")
+    sh = W.normal(rng, (G.E, prob.dim2), "bf16")
+    w = W.normal(rng, (prob.weight_numel,), "bf16")
+    d = G.dev(torch)
+    print(f"uvw wide layer tune={tune}", flush=True)
+    out = B.cgtp_conv_forward(plan, to_dev(torch, x, "bf16"), to_dev(torch, sh[G.perm], "bf16"),
+                              to_dev(torch, w, "bf16"), d["src"], d["dst_row_ptr"])
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), prob.conv_forward(x, sh, w, g.src, g.dst, g.n_nodes), "bf16",
+                 f"uvw wide {tune}")
+
+
 @pytest.mark.parametrize("shift", ["w", "x"])
 @pytest.mark.parametrize("k", range(len(UVW_SMALL)))
 def test_uvw_conv_unaligned_operands(B, torch, k, shift):

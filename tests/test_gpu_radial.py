@@ -14,6 +14,8 @@ CASES = [
     ("8x0+8x1+8x2", "1x0+1x1+1x2", "12x0+12x1+12x2"),
     ("5x0+5x1", "1x0+1x1+1x2+1x3", "16x0+16x1+16x2"),
     ("32x0+32x1+32x2+32x3", W.sh_irreps(6, parity=False), "64x0+64x1+64x2+64x3"),
+    # paths of 16 and 32 rows into 128 output channels
+    ("16x0+16x1+32x2", "1x0+1x1+1x2", "128x0+128x1"),
 ]
 
 
@@ -53,7 +55,8 @@ def _run(B, torch, plan, g, x, w, radial, order=None):
     return out.cpu().numpy(), vec
 
 
-@pytest.mark.parametrize("k,H,tune", [(0, 1, ""), (0, 4, ""), (1, 3, ""), (2, 2, ""), (2, 2, "mix3=0"), (2, 5, "")])
+@pytest.mark.parametrize("k,H,tune", [(0, 1, ""), (0, 4, ""), (1, 3, ""), (2, 2, ""), (2, 2, "mix3=0"), (2, 5, ""),
+                                      (3, 2, "mix3=1"), (3, 2, "")])
 def test_radial_conv_small(B, torch, k, H, tune, monkeypatch):
     """Ragged molecule batches; on the C5 irreps the (H+1)-fold contraction
     exceeds one span of 512 rows, so the mixing takes the streaming form by
