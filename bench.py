@@ -27,6 +27,7 @@ line.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -104,11 +105,19 @@ def time_steps(torch, args, step):
         run()
         torch.cuda.synchronize()
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    marks[0].record()
-    for i in range(args.steps):
-        run()
-        marks[i + 1].record()
-    torch.cuda.synchronize()
+    # Python's garbage collector stays off while the steps are issued (as in
+    # timeit): a collection pause on the host would leave the GPU idle
+    gc_on = gc.isenabled()
+    gc.disable()
+    try:
+        marks[0].record()
+        for i in range(args.steps):
+            run()
+            marks[i + 1].record()
+        torch.cuda.synchronize()
+    finally:
+        if gc_on:
+            gc.enable()
     per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     mode = "eager" if graph is None else "hip graph of the step (captured once, replayed)"
     return marks[0].elapsed_time(marks[-1]) / args.steps, per_step, mode, graph

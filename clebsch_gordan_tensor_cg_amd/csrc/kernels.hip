@@ -283,13 +283,16 @@ __global__ void k_scatter_global(const int32_t *__restrict__ key, int64_t n, int
 // slot.  The placement is therefore stable (edge order inside every segment)
 // without a sort.  Workgroup 0 also writes row_ptr and, with order non-NULL,
 // the longest-first node order (as k_order_small) from the totals.  Each
-// workgroup rereads the key array (at most 256 KiB) from L2.
-constexpr int kSmallCsrMaxRuns = 128;
+// workgroup rereads the key array (at most 256 KiB) from L2.  The run count
+// trades that redundant counting against the length of the one-wavefront
+// walk: on 100 molecules of 18 atoms (25,710 edges) 51 runs of 512 edges took
+// 14.7 us, 101 of 256 12.8 us, 201 of 128 11.7 us and 402 of 64 15.9 us.
+constexpr int kSmallCsrMaxRuns = 256;
 constexpr int64_t kSmallCsrMaxKeys = 2048;
 constexpr int64_t kSmallCsrMaxEdges = 65535;
-constexpr int kSmallCsrChunks = 8;           // 64-edge chunks of one run (a run holds at most 512 edges)
+constexpr int kSmallCsrChunks = 4;           // 64-edge chunks of one run (a run holds at most 256 edges)
 static_assert(kSmallCsrMaxKeys == 2048, "the key-match ballots cover 11 bits");
-static_assert(kSmallCsrMaxEdges <= (int64_t)kSmallCsrMaxRuns * 64 * kSmallCsrChunks, "runs of at most 512 edges");
+static_assert(kSmallCsrMaxEdges <= (int64_t)kSmallCsrMaxRuns * 64 * kSmallCsrChunks, "runs of at most 256 edges");
 constexpr int kSmallCsrKeysPerThread = 32;   // keys per thread and round of the counting
 __host__ __device__ constexpr bool small_csr(int64_t n_edges, int64_t n_keys) {
     return n_edges > 0 && n_keys > 0 && n_edges <= kSmallCsrMaxEdges && n_keys <= kSmallCsrMaxKeys;
