@@ -197,7 +197,10 @@ int cgtp_forward(cgtp_plan_t plan, const void *x, const void *y, const void *w, 
  * 0..n_nodes-1, normally from cgtp_build_csr_order or cgtp_node_order;
  * it changes timing only, never a result (an entry out of range leaves its
  * slot idle, so a node missing from it is not written).  workspace:
- * cgtp_workspace_bytes(plan, n_nodes, n_edges) (may be NULL for uvu plans). */
+ * cgtp_workspace_bytes(plan, n_nodes, n_edges) (may be NULL for uvu plans).
+ * uvw bf16 plans run the per-pair matrix-core kernel when x is 16-byte
+ * aligned (and w too, where that kernel also does the channel mixing), else
+ * the per-edge kernel: the same results, only the speed differs. */
 int cgtp_conv_forward(cgtp_plan_t plan, const void *x, const void *sh, const void *w,
                       const int32_t *src, const int32_t *dst_row_ptr, const int32_t *node_order,
                       int64_t n_nodes, int64_t n_edges, void *out, void *workspace,
