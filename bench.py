@@ -199,8 +199,8 @@ def tp_flops(cfg, plan):
     return tot
 
 
-def counted_traffic(workload, kernel, source):
-    """Bytes per launch leaving L2 toward memory (reads + writes, from the
+def counted_traffic_rw(workload, kernel, source):
+    """(read, written) bytes per launch leaving L2 toward memory (from the
     per-size request counters; Infinity-Cache hits included, so an upper
     bound on HBM bytes), measured with rocprofv3 for exactly this workload
     (its full description) and generated source (profiles/hbm_traffic__*.json),
@@ -211,8 +211,14 @@ def counted_traffic(workload, kernel, source):
     for path in glob.glob(os.path.join(ROOT, "profiles", "hbm_traffic__*.json")):
         for r in json.load(open(path))["records"]:
             if r["workload"] == workload and r["kernel"] == kernel and r["source_sha1"] == sha:
-                return int(r["read_bytes"] + r["write_bytes"])
+                return int(r["read_bytes"]), int(r["write_bytes"])
     return None
+
+
+def counted_traffic(workload, kernel, source):
+    """Counted bytes per launch (reads + writes, see counted_traffic_rw), else None."""
+    rw = counted_traffic_rw(workload, kernel, source)
+    return None if rw is None else rw[0] + rw[1]
 
 
 def copy_probe(torch):
@@ -229,6 +235,51 @@ def copy_probe(torch):
     torch.cuda.synchronize()
     ms = s.elapsed_time(e)
     return {"bytes_read": 4 * n, "bytes_written": 4 * n, "ms": ms, "GB_per_s": 8 * n / (ms * 1e-3) / 1e9}
+
+
+def stream_probe(torch, B, nbytes=1 << 30, reps=5):
+    """Plain streams on this device through the library's probe kernel
+    (16-byte non-temporal loads and stores): 1 GiB read, 1 GiB written,
+    1 GiB copied (read + written), each the best of `reps` launches after
+    one warm-up.  Buffers four times the Infinity Cache, so the bytes are
+    HBM bytes."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    res = {"bytes": nbytes}
+    for kind in ("read", "write", "copy"):
+        B.cgtp_stream_probe(kind, a, b)
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            B.cgtp_stream_probe(kind, a, b)
+            e.record()
+            torch.cuda.synchronize()
+            ms = s.elapsed_time(e)
+            best = ms if best is None else min(best, ms)
+        moved = nbytes * (2 if kind == "copy" else 1)
+        res[f"{kind}_GB_per_s"] = round(moved / (best * 1e-3) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
+def against_streams(roof, sp):
+    """The kernel's rate next to the measured plain streams; with counted
+    (read, written) bytes, the time those bytes take at the measured read
+    and write rates (a serial model that the copy stream follows) and the
+    fraction of it the kernel reaches."""
+    rw = roof.pop("_rw", None)
+    if roof.get("unit") != "GB/s":
+        return
+    roof["frac_of_measured_read"] = round(roof["achieved"] / sp["read_GB_per_s"], 4)
+    if rw is not None:
+        model_ms = (rw[0] / (sp["read_GB_per_s"] * 1e9) + rw[1] / (sp["write_GB_per_s"] * 1e9)) * 1e3
+        roof["traffic_rw"] = [rw[0], rw[1]]
+        roof["traffic_model_ms"] = round(model_ms, 4)
+        roof["frac_of_traffic_model"] = round(model_ms / roof["avg_ms"], 4)
 
 
 # ---------------------------------------------------------------------------
@@ -546,6 +597,7 @@ def bench_conv(args, torch, B, W):
     roof = {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GB_per_s"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
             "traffic": counted_traffic(workload, dom, plan.source()),
+            "_rw": counted_traffic_rw(workload, dom, plan.source()),
             "alg_bytes_per_launch": kern[dom]["alg_bytes"], "avg_ms": round(kern[dom]["avg_ms"], 4)}
     if name == "c5":
         # the path tensors (and, where they run in the same kernel, the channel
@@ -652,6 +704,7 @@ def forward_leg(args, torch, B, plan, x, vec, perm, w, src_s, rp, out, node_orde
             "roofline": {"bound": "hbm", "kernel": "cgtp_fwd", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": counted_traffic(workload, "cgtp_fwd", plan.source()),
+                         "_rw": counted_traffic_rw(workload, "cgtp_fwd", plan.source()),
                          "alg_bytes_per_launch": int(alg_bytes), "avg_ms": round(k_ms, 4)}}
 
 
@@ -880,6 +933,7 @@ def main():
         b.build(verbose=False)
     torch.cuda.set_device(0)
     probe = copy_probe(torch)
+    sprobe = stream_probe(torch, B)
     if args.workload == "c1":
         res = bench_single(args, torch, B, W)
     elif args.workload == "c5r":
@@ -891,9 +945,13 @@ def main():
     # context: the dominant kernel against a measured device-copy stream
     # (512 MiB read + 512 MiB written), next to the datasheet peak
     res["copy_probe"] = probe
+    res["stream_probe"] = sprobe
     roof = res["roofline"]
     if roof["unit"] == "GB/s":
         roof["frac_of_measured_copy"] = round(roof["achieved"] / probe["GB_per_s"], 4)
+    against_streams(roof, sprobe)
+    if "fwd" in res:
+        against_streams(res["fwd"]["roofline"], sprobe)
     print(json.dumps(res))
 
 

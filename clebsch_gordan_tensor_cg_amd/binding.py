@@ -51,8 +51,8 @@ EXPORTS = [
     "cgtp_sparse_attention_prepare", "cgtp_csr_workspace_bytes", "cgtp_build_csr", "cgtp_build_csr_order",
     "cgtp_build_csr_order_noalloc",
     "cgtp_validate_csr", "cgtp_node_order_workspace_bytes", "cgtp_node_order", "cgtp_sh", "cgtp_sh_vjp_forces",
-    "cgtp_force_loss_sh_cotangent", "cgtp_timing_enable", "cgtp_timing_collect", "cgtp_last_error",
-    "cgtp_version",
+    "cgtp_force_loss_sh_cotangent", "cgtp_timing_enable", "cgtp_timing_collect", "cgtp_stream_probe",
+    "cgtp_last_error", "cgtp_version",
 ]
 
 _lib = None
@@ -102,6 +102,7 @@ def lib():
             "cgtp_force_loss_sh_cotangent": [i32, i32, vp, vp, vp, vp, vp, i64, vp, vp],
             "cgtp_timing_enable": [i32],
             "cgtp_timing_collect": [vp, vp, i32, vp],
+            "cgtp_stream_probe": [i32, vp, vp, sz, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -772,6 +773,28 @@ def cgtp_timing_collect(cap: int = 1 << 16):
                                      ctypes.byref(n)))
     raw = names.raw
     return [(raw[64 * i:64 * i + 64].split(b"\0", 1)[0].decode(), float(ms[i])) for i in range(n.value)]
+
+
+STREAM_PROBE_KINDS = {"read": 0, "write": 1, "copy": 2}
+
+
+def cgtp_stream_probe(kind: str, src, dst, stream=None):
+    """One streaming launch over dst (and src): kind "read" reads src (dst
+    receives at most 4 bytes), "write" writes dst, "copy" copies src into
+    dst.  Both CUDA tensors of one device, byte sizes equal (read: src's
+    size) and a multiple of 16."""
+    if kind not in STREAM_PROBE_KINDS:
+        raise ValueError(f"kind must be one of {sorted(STREAM_PROBE_KINDS)}")
+    ts = [t for t in (src, dst) if t is not None]
+    if dst is None or (kind != "write" and src is None):
+        raise ValueError("stream probe needs dst (and src unless kind is 'write')")
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous() or t.device != dst.device:
+            raise ValueError("stream probe buffers must be contiguous CUDA tensors on one device")
+    nbytes = (src if kind != "write" else dst).numel() * (src if kind != "write" else dst).element_size()
+    if kind == "copy" and dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("copy: src and dst sizes differ")
+    _check(lib().cgtp_stream_probe(STREAM_PROBE_KINDS[kind], _ptr(src), _ptr(dst), nbytes, _stream(stream, dst)))
 
 
 def version() -> str:

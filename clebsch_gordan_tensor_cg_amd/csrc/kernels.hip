@@ -1955,3 +1955,48 @@ int cgtp_force_loss_sh_cotangent(int32_t lmax, cgtp_dtype dtype, const void *vec
 }
 
 }  // extern "C"
+
+// Streaming bandwidth probe (a measurement aid, not part of the hot path):
+// every lane moves 16-byte vectors with non-temporal loads and stores over a
+// grid-stride loop.  KIND 0 reads src and folds it into one value that is
+// stored only if it equals a value no finite input sum reaches (so the loads
+// cannot be removed), 1 writes dst, 2 copies src to dst.
+template <int KIND>
+__global__ void __launch_bounds__(256) k_stream_probe(const float *__restrict__ src, float *__restrict__ dst,
+                                                      int64_t n_vec) {
+    typedef float V __attribute__((ext_vector_type(4)));
+    const V *a = (const V *)src;
+    V *b = (V *)dst;
+    const int64_t st = (int64_t)gridDim.x * blockDim.x;
+    V acc = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_vec; i += st) {
+        if (KIND == 1) {
+            const V v = {1.f, 2.f, 3.f, (float)(i & 1023)};
+            __builtin_nontemporal_store(v, b + i);
+        } else {
+            const V v = __builtin_nontemporal_load(a + i);
+            if (KIND == 2) __builtin_nontemporal_store(v, b + i);
+            else acc += v;
+        }
+    }
+    if (KIND == 0 && acc.x + acc.y + acc.z + acc.w == __builtin_inff()) dst[0] = acc.x;
+}
+
+extern "C" int cgtp_stream_probe(int32_t kind, const void *src, void *dst, size_t bytes, cgtp_stream_t stream) {
+    clear_error();
+    if (kind < 0 || kind > 2 || bytes % 16 || (kind != 1 && !src) || !dst ||
+        (((uintptr_t)src | (uintptr_t)dst) & 15))
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_stream_probe: bad argument");
+    const int64_t n = (int64_t)(bytes / 16);
+    if (n == 0) return CGTP_OK;
+    hipStream_t s = (hipStream_t)stream;
+    // grids measured best on MI355X for each stream kind (1 GiB buffers):
+    // reads 2048 workgroups, writes and copies 1024
+    const unsigned g = (unsigned)std::min<int64_t>(kind == 0 ? 2048 : 1024, (n + 255) / 256);
+    const float *a = (const float *)src;
+    float *b = (float *)dst;
+    if (kind == 0) CGTP_LAUNCH("k_stream_probe_read", s, k_stream_probe<0>, dim3(g), dim3(256), 0, s, a, b, n);
+    else if (kind == 1) CGTP_LAUNCH("k_stream_probe_write", s, k_stream_probe<1>, dim3(g), dim3(256), 0, s, a, b, n);
+    else CGTP_LAUNCH("k_stream_probe_copy", s, k_stream_probe<2>, dim3(g), dim3(256), 0, s, a, b, n);
+    return hip_check(hipGetLastError(), "stream probe launch");
+}

@@ -486,6 +486,16 @@ int cgtp_force_loss_sh_cotangent(int32_t lmax, cgtp_dtype dtype, const void *vec
 int cgtp_timing_enable(int enable);
 int cgtp_timing_collect(char (*names)[64], float *ms, int32_t cap, int32_t *n);
 
+/* Streaming bandwidth probe, a measurement aid beside the kernels'
+ * roofline (the ceiling the hardware reaches for plain streams, reported
+ * next to the datasheet peak).  kind 0 reads `bytes` of src, 1 writes
+ * `bytes` of dst (a fixed pattern), 2 copies src to dst; 16-byte
+ * non-temporal loads and stores over a grid-stride loop.  bytes must be a
+ * multiple of 16 and src, dst 16-byte aligned (kind 0 may store at most
+ * 4 bytes at dst, which must be writable; src is unused for kind 1).  One
+ * launch on stream, nothing allocated.  Errors: INVALID_ARGUMENT. */
+int cgtp_stream_probe(int32_t kind, const void *src, void *dst, size_t bytes, cgtp_stream_t stream);
+
 /* Description of the last error on this thread ("" if none). */
 const char *cgtp_last_error(void);
 

@@ -90,6 +90,77 @@ inline unsigned __float_as_uint(float f) {
     return u;
 }
 inline float __expf(float v) { return std::exp(v); }
+inline float __int_as_float(int u) {
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+inline int __float_as_int(float f) {
+    int u;
+    std::memcpy(&u, &f, 4);
+    return u;
+}
+inline long long __double_as_longlong(double d) {
+    long long u;
+    std::memcpy(&u, &d, 8);
+    return u;
+}
+inline double __longlong_as_double(long long u) {
+    double d;
+    std::memcpy(&d, &u, 8);
+    return d;
+}
+
+// Cross-lane moves of the gfx950 instruction set, as documented: the pair
+// returned by a swap is (new first operand, new second operand).
+struct emu_u2 {
+    unsigned v[2];
+    unsigned operator[](int i) const { return v[i]; }
+};
+// lanes 32-63 of a trade places with lanes 0-31 of b
+inline emu_u2 __builtin_amdgcn_permlane32_swap(unsigned a, unsigned b, bool, bool) {
+    static unsigned ba[64], bb[64];
+    const int lane = (int)threadIdx.x;
+    ba[lane] = a;
+    bb[lane] = b;
+    emu_barrier();
+    emu_u2 r;
+    r.v[0] = lane < 32 ? ba[lane] : bb[lane - 32];
+    r.v[1] = lane < 32 ? ba[lane + 32] : bb[lane];
+    emu_barrier();
+    return r;
+}
+// odd rows (16 lanes) of a trade places with the even rows of b below them
+inline emu_u2 __builtin_amdgcn_permlane16_swap(unsigned a, unsigned b, bool, bool) {
+    static unsigned ba[64], bb[64];
+    const int lane = (int)threadIdx.x;
+    const bool odd = (lane >> 4) & 1;
+    ba[lane] = a;
+    bb[lane] = b;
+    emu_barrier();
+    emu_u2 r;
+    r.v[0] = odd ? bb[lane - 16] : ba[lane];
+    r.v[1] = odd ? bb[lane] : ba[lane + 16];
+    emu_barrier();
+    return r;
+}
+// data-parallel-primitive moves within rows of 16 lanes: row mirror, half-row
+// mirror and quad permutations (the controls the kernels use)
+inline int __builtin_amdgcn_mov_dpp(int v, int ctrl, int, int, bool) {
+    static int buf[64];
+    const int lane = (int)threadIdx.x;
+    buf[lane] = v;
+    emu_barrier();
+    const int base = lane & ~15, l = lane & 15;
+    int src;
+    if (ctrl == 0x140) src = base + (15 - l);
+    else if (ctrl == 0x141) src = base + (l & 8) + (7 - (l & 7));
+    else if (ctrl >= 0 && ctrl < 0x100) src = (lane & ~3) + ((ctrl >> (2 * (lane & 3))) & 3);
+    else std::abort();
+    const int r = buf[src];
+    emu_barrier();
+    return r;
+}
 
 // Runs one workgroup of 64 lanes: lane l runs body() with threadIdx.x == l.
 template <class F>

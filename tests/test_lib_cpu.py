@@ -278,6 +278,26 @@ def test_sh_helpers_argument_errors(B):
     assert L.cgtp_sh_vjp_forces(3, F32, buf, None, buf, None, None, None, 2, 2, None, None, None, 0, None) == 0
 
 
+def test_stream_probe_argument_errors(B):
+    """The bandwidth probe checks its kind, size and alignment on the host
+    before any launch; an empty size does nothing."""
+    import ctypes
+    L = B.lib()
+    buf = (ctypes.c_double * 8)()
+    base = ctypes.addressof(buf)
+    a = base + (-base % 16)        # a 16-byte aligned address inside buf
+    assert L.cgtp_stream_probe(3, a, a, 16, None) == -1              # unknown kind
+    assert L.cgtp_stream_probe(-1, a, a, 16, None) == -1
+    assert L.cgtp_stream_probe(2, a, a, 24, None) == -1              # not a multiple of 16
+    assert L.cgtp_stream_probe(2, a + 4, a, 16, None) == -1          # misaligned source
+    assert L.cgtp_stream_probe(1, None, a + 8, 16, None) == -1       # misaligned destination
+    assert L.cgtp_stream_probe(0, None, a, 16, None) == -1           # a read needs a source
+    assert L.cgtp_stream_probe(1, None, None, 16, None) == -1        # every kind needs dst
+    assert L.cgtp_stream_probe(2, a, a, 0, None) == 0                # nothing to move
+    with pytest.raises(ValueError):
+        B.cgtp_stream_probe("scan", None, None)
+
+
 def test_binding_rejects_bad_arguments(B):
     """The binding checks shape, dtype, contiguity and device of every tensor
     before it calls the library, so a short buffer, a wrong dtype or a host
