@@ -475,14 +475,16 @@ def bench_conv(args, torch, B, W):
 
     def step(timed: bool):
         run = timer.run if timed else (lambda name_, fn: fn())
-        # the transpose CSR (by source) serves only the backward passes
-        # the node order comes out of the destination CSR's own launches
+        # the transpose CSR (by source) serves only the backward passes; the
+        # edge list is canonical (sorted by source, then destination), so it
+        # follows from the destination CSR's perm in one launch.  The node
+        # order comes out of the destination CSR's own launches
         run("csr", lambda: (B.cgtp_build_csr(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s))
                             if natural else
                             B.cgtp_build_csr_order(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s),
                                                    order=order),
-                            B.cgtp_build_csr(src_s, N, sorted_key=False, ws=csr_ws,
-                                             out=(src_perm, src_rp, None, None)) if full else None))
+                            B.cgtp_build_csr_transpose_canonical(src_c, perm, N, out=(src_perm, src_rp))
+                            if full else None))
         if sh_in_conv and fused:
             # one pass: out, g_x, g_w and the forces (from the per-unit
             # SH-gradient partials), SH computed inside the kernel

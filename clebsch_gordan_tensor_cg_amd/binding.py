@@ -49,7 +49,7 @@ EXPORTS = [
     "cgtp_conv_forward_backward", "cgtp_conv_forward_backward_vec", "cgtp_double_backward",
     "cgtp_sparse_attention", "cgtp_sparse_attention_rows", "cgtp_sparse_attention_layout_bytes",
     "cgtp_sparse_attention_prepare", "cgtp_csr_workspace_bytes", "cgtp_build_csr", "cgtp_build_csr_order",
-    "cgtp_build_csr_order_noalloc",
+    "cgtp_build_csr_order_noalloc", "cgtp_build_csr_transpose_canonical",
     "cgtp_validate_csr", "cgtp_node_order_workspace_bytes", "cgtp_node_order", "cgtp_sh", "cgtp_sh_vjp_forces",
     "cgtp_force_loss_sh_cotangent", "cgtp_timing_enable", "cgtp_timing_collect", "cgtp_stream_probe",
     "cgtp_last_error", "cgtp_version",
@@ -96,6 +96,7 @@ def lib():
             "cgtp_build_csr": [vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
             "cgtp_build_csr_order": [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp],
             "cgtp_build_csr_order_noalloc": [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp],
+            "cgtp_build_csr_transpose_canonical": [vp, vp, i64, i64, vp, vp, vp],
             "cgtp_validate_csr": [vp, i64, i64, vp, i64, vp, vp],
             "cgtp_sh": [i32, i32, vp, vp, i64, vp, vp],
             "cgtp_sh_vjp_forces": [i32, i32, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp],
@@ -659,6 +660,24 @@ def cgtp_build_csr_order(key, n_keys: int, val=None, sorted_key: bool = True, ws
     _check(lib().cgtp_build_csr_order(_ptr(key), _ptr(val), E, n_keys, _ptr(perm), _ptr(row_ptr), _ptr(sk),
                                       _ptr(sv), _ptr(order), _ptr(ws), ws.numel(), _stream(stream, key)))
     return perm, row_ptr, sk, sv, order
+
+
+def cgtp_build_csr_transpose_canonical(src, perm, n_keys: int, out=None, stream=None):
+    """Transpose CSR (by source) of a canonical edge list (sorted by source,
+    ties by destination) from its destination CSR's perm; the same arrays
+    cgtp_build_csr gives for the destination-sorted sources.  Returns
+    (src_perm, src_row_ptr)."""
+    A = _Args("cgtp_build_csr_transpose_canonical")
+    E = src.shape[0]
+    A("src", src, (E,), _I32, optional=False)
+    A("perm", perm, (E,), _I32, optional=False)
+    o = out if out is not None else (None, None)
+    src_perm = _out(A, "src_perm", o[0], (E,), _I32, src, True)
+    src_row_ptr = _out(A, "src_row_ptr", o[1], (n_keys + 1,), _I32, src, True)
+    A.device()
+    _check(lib().cgtp_build_csr_transpose_canonical(_ptr(src), _ptr(perm), E, n_keys, _ptr(src_perm),
+                                                    _ptr(src_row_ptr), _stream(stream, src)))
+    return src_perm, src_row_ptr
 
 
 def cgtp_build_csr_order_noalloc(key, n_keys: int, val=None, sorted_key: bool = True, out=None, order=None,

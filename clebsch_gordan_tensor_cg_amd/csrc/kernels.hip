@@ -75,22 +75,19 @@ __global__ void __launch_bounds__(256) k_segment_sum_rows(const T *__restrict__ 
     for (int64_t c = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * VT::N; c < width; c += step) {
         if (vec_ok) {
             V acc = VT::zero();
-            int k = beg;
-            // eight source rows in flight per thread
-            for (; k + 8 <= end; k += 8) {
-                V a[8];
+            // sixteen source rows in flight per thread; the segment's last
+            // rows in the same batch, masked (rows still summed in order)
+            for (int k = beg; k < end; k += 16) {
+                V a[16];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int64_t r = kPerm ? perm[k + u] : k + u;
+                for (int u = 0; u < 16; ++u) {
+                    const bool ok = k + u < end;
+                    const int64_t r = ok ? (kPerm ? perm[k + u] : k + u) : 0;
                     // each row is read once: stream it past the caches
-                    a[u] = __builtin_nontemporal_load((const V *)(rows + r * width + c));
+                    a[u] = ok ? __builtin_nontemporal_load((const V *)(rows + r * width + c)) : VT::zero();
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) VT::add(acc, a[u]);
-            }
-            for (; k < end; ++k) {
-                const int64_t r = kPerm ? perm[k] : k;
-                VT::add(acc, *(const V *)(rows + r * width + c));
+                for (int u = 0; u < 16; ++u) VT::add(acc, a[u]);
             }
             V *o = (V *)(out + s * width + c);
             if (accumulate) {
@@ -640,6 +637,35 @@ __global__ void k_validate(const int32_t *__restrict__ row_ptr, int64_t n_rows, 
     if (idx)
         for (int64_t e = t0; e < n_edges; e += stride)
             if (idx[e] < 0 || idx[e] >= range) bad[0] = 1;
+}
+
+// Transpose CSR of a canonical edge list (sorted by source, ties by
+// destination) from its destination CSR.  perm[t] is the canonical id of the
+// edge at destination-sorted position t.  The edges of source s are the
+// canonical run [first index with src >= s, first index with src >= s+1),
+// ordered by destination and therefore by destination-sorted position, which
+// is the stable order by source of the destination-sorted edges: the
+// transpose's entry for canonical edge e is the position t with perm[t] = e,
+// and its row pointers are those run boundaries (found by binary search).
+__global__ void k_csr_transpose_canonical(const int32_t *__restrict__ src, const int32_t *__restrict__ perm,
+                                          int64_t n_edges, int64_t n_keys, int32_t *__restrict__ src_perm,
+                                          int32_t *__restrict__ src_row_ptr) {
+    const int64_t n = n_edges > n_keys + 1 ? n_edges : n_keys + 1;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+        if (t < n_edges) {
+            const int32_t e = perm[t];
+            if (e >= 0 && e < n_edges) src_perm[e] = (int32_t)t;   // in bounds whatever perm holds
+        }
+        if (t <= n_keys) {
+            int64_t lo = 0, hi = n_edges;   // first index with src >= t
+            while (lo < hi) {
+                const int64_t mid = (lo + hi) >> 1;
+                if (src[mid] < t) lo = mid + 1;
+                else hi = mid;
+            }
+            src_row_ptr[t] = (int32_t)lo;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1634,8 +1660,9 @@ int launch_segment_sum_rows(cgtp_dtype dt, const void *rows, const int32_t *row_
     int threads = (int)std::min<int64_t>(kBlock, (chunks + 63) / 64 * 64);
     int64_t gy = (chunks + threads - 1) / threads;
     if (gy > 65535) gy = 65535;
-    // about eight workgroups per compute unit, each walking over segments
-    const int64_t gx = std::min<int64_t>(n_seg, 2048);
+    // about sixteen workgroups per compute unit, each walking over segments
+    // (4096 measured 3 % faster than 2048 on 4096 rows of 512 floats)
+    const int64_t gx = std::min<int64_t>(n_seg, 4096);
     dim3 grid((unsigned)gx, (unsigned)gy);
     if (dt == CGTP_F64) {
         if (perm)
@@ -1798,6 +1825,21 @@ int cgtp_build_csr_order(const int32_t *key, const int32_t *val, int64_t n_edges
         return hip_check(hipGetLastError(), "cgtp_build_csr order launch");
     }
     return cgtp_node_order(row_ptr, n_keys, order, workspace, workspace_bytes, stream);
+}
+
+int cgtp_build_csr_transpose_canonical(const int32_t *src, const int32_t *perm, int64_t n_edges, int64_t n_keys,
+                                       int32_t *src_perm, int32_t *src_row_ptr, cgtp_stream_t stream) {
+    clear_error();
+    if (n_edges < 0 || n_keys < 0 || n_edges > 0x7fffffff || n_keys > 0x7ffffffe)
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_build_csr_transpose_canonical: sizes out of range");
+    if (!src_row_ptr || (n_edges > 0 && (!src || !perm || !src_perm)))
+        return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_build_csr_transpose_canonical: NULL pointer");
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t n = std::max<int64_t>(n_edges, n_keys + 1);
+    const unsigned g = (unsigned)std::min<int64_t>(grid_for(n), 65536);
+    CGTP_LAUNCH("k_csr_transpose_canonical", s, k_csr_transpose_canonical, dim3(g), dim3(kBlock), 0, s, src, perm,
+                n_edges, n_keys, src_perm, src_row_ptr);
+    return hip_check(hipGetLastError(), "cgtp_build_csr_transpose_canonical launch");
 }
 
 }  // extern "C"

@@ -381,6 +381,24 @@ int cgtp_build_csr_order_noalloc(const int32_t *key, const int32_t *val, int64_t
                                  int32_t *perm, int32_t *row_ptr, int32_t *sorted_key, int32_t *sorted_val,
                                  int32_t *order, cgtp_stream_t stream);
 
+/* The transpose CSR (by source) that the backward calls take, for a
+ * canonical edge list: edges sorted by source, ties by destination, every
+ * source in [0, n_keys) and no repeated (source, destination) pair ([KG]'s
+ * gradient needs the sum over each node's out-edges).  perm is the
+ * destination CSR's permutation of that list (cgtp_build_csr with the
+ * destinations as keys, all of them in range, so that perm is a
+ * permutation of 0..n_edges-1; entries outside it are skipped).  Writes
+ * src_row_ptr [n_keys+1] and src_perm
+ * [n_edges], bit for bit what cgtp_build_csr gives when it sorts the
+ * destination-sorted sources (its perm and row_ptr): the edges of source s
+ * are the canonical run of s, in order of destination.  One launch, no
+ * workspace, nothing allocated.  An edge list that is not canonical gives
+ * undefined (in-range) results; check with cgtp_validate_csr where unsure.
+ * Errors: INVALID_ARGUMENT (sizes, NULL). */
+int cgtp_build_csr_transpose_canonical(const int32_t *src, const int32_t *perm, int64_t n_edges,
+                                       int64_t n_keys, int32_t *src_perm, int32_t *src_row_ptr,
+                                       cgtp_stream_t stream);
+
 /* Processing order for the convolution calls: the n_nodes rows of a CSR
  * sorted by decreasing length (rows of 1023 or more edges tie), so that
  * the longest rows are started first and do not form the tail of a launch

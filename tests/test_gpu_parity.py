@@ -495,6 +495,52 @@ def test_build_csr_order(B, torch, case):
     _check_lpt_order(order.cpu().numpy(), rp_ref)
 
 
+def _canonical_graph(case):
+    """(src, dst, n_nodes) of a canonical edge list: sorted by source, ties
+    by destination, no repeated pair."""
+    if case == "box4096":
+        g = W.periodic_graph(4096, cutoff=5.0, seed=0)
+        return g.src, g.dst, g.n_nodes
+    if case == "molecules":
+        g = W.molecule_batch(100, 18, seed=0)
+        return g.src, g.dst, g.n_nodes
+    if case == "empty":
+        return np.zeros(0, np.int32), np.zeros(0, np.int32), 5
+    if case == "one_edge":
+        return np.array([3], np.int32), np.array([0], np.int32), 4
+    # random pairs with isolated nodes (no in- or out-edges) at both ends
+    rs = np.random.default_rng(23)
+    n = 3000
+    s_, d_ = rs.integers(7, n - 9, 40000), rs.integers(7, n - 9, 40000)
+    pairs = np.unique(np.stack([s_, d_], 1), axis=0)
+    pairs = pairs[pairs[:, 0] != pairs[:, 1]]
+    return pairs[:, 0].astype(np.int32), pairs[:, 1].astype(np.int32), n
+
+
+@pytest.mark.parametrize("case", ["box4096", "molecules", "random_isolated", "empty", "one_edge"])
+def test_csr_transpose_canonical(B, torch, case):
+    """The transpose CSR of a canonical edge list from the destination CSR's
+    perm equals, bit for bit, the stable sort by source of the
+    destination-sorted sources (the oracle's, and the library's general
+    build)."""
+    src, dst, n = _canonical_graph(case)
+    src, dst = src.astype(np.int32), dst.astype(np.int32)
+    assert np.all(np.lexsort((dst, src)) == np.arange(len(src)))
+    perm_ref, _ = oracle.csr(dst, n)
+    sp_ref, srp_ref = oracle.csr(src[perm_ref], n)
+    print(f"csr transpose canonical {case}: E={len(src)} N={n}", flush=True)
+    dev = lambda a: torch.from_numpy(a).cuda() if len(a) else torch.zeros(0, dtype=torch.int32, device="cuda")
+    perm, rp, _, src_s = B.cgtp_build_csr(dev(dst), n, val=dev(src))
+    sp, srp = B.cgtp_build_csr_transpose_canonical(dev(src), perm, n)
+    sp_gen, srp_gen, _, _ = B.cgtp_build_csr(src_s, n, sorted_key=False)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(perm.cpu().numpy(), perm_ref)
+    np.testing.assert_array_equal(srp.cpu().numpy(), srp_ref)
+    np.testing.assert_array_equal(sp.cpu().numpy(), sp_ref)
+    np.testing.assert_array_equal(sp.cpu().numpy(), sp_gen.cpu().numpy())
+    np.testing.assert_array_equal(srp.cpu().numpy(), srp_gen.cpu().numpy())
+
+
 @pytest.mark.parametrize("n", [50, 20000])
 def test_build_csr_skips_out_of_range_keys(B, torch, n):
     rs = np.random.default_rng(11)

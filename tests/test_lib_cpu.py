@@ -278,6 +278,20 @@ def test_sh_helpers_argument_errors(B):
     assert L.cgtp_sh_vjp_forces(3, F32, buf, None, buf, None, None, None, 2, 2, None, None, None, 0, None) == 0
 
 
+def test_csr_transpose_canonical_argument_errors(B):
+    """Sizes and NULL buffers are checked on the host before any launch."""
+    import ctypes
+    L = B.lib()
+    buf = (ctypes.c_int32 * 16)()
+    assert L.cgtp_build_csr_transpose_canonical(buf, buf, -1, 3, buf, buf, None) == -1
+    assert L.cgtp_build_csr_transpose_canonical(buf, buf, 4, -1, buf, buf, None) == -1
+    assert L.cgtp_build_csr_transpose_canonical(buf, buf, 1 << 31, 3, buf, buf, None) == -1
+    assert L.cgtp_build_csr_transpose_canonical(None, buf, 4, 3, buf, buf, None) == -1
+    assert L.cgtp_build_csr_transpose_canonical(buf, None, 4, 3, buf, buf, None) == -1
+    assert L.cgtp_build_csr_transpose_canonical(buf, buf, 4, 3, None, buf, None) == -1
+    assert L.cgtp_build_csr_transpose_canonical(buf, buf, 4, 3, buf, None, None) == -1
+
+
 def test_stream_probe_argument_errors(B):
     """The bandwidth probe checks its kind, size and alignment on the host
     before any launch; an empty size does nothing."""
