@@ -57,7 +57,7 @@ struct KernelShape {
 };
 
 // Generator options.  Defaults are the tuned values; CGTP_TUNE (comma list
-// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, gy64, redx, full,
+// of key=value: cpl_fwd, cpl_bwd, cpl_dbl, cpl_fb, yvec, ntw, pf, budget, stage, cypath, depth, bgy, gy64, redx, stnt, full,
 // ubudget, ucpl, umma, cstage, mix2, mix3, depth_bwd, pform, pfw, pfuse, pfocc, pfma, pfml)
 // overrides
 // them for experiments.
@@ -75,6 +75,9 @@ struct Tuning {
     int depth_bwd = 0;       // the same for the backward, double backward and one-pass kernels (0: 2)
     bool bgy = false;        // backward via B_ij = sum_k R_ijk g_k (fewer FMAs, more VGPRs)
     bool gy64 = true;        // SH-gradient rows summed across lanes in FP64 (float plans)
+    int stnt = 4;            // rows written by non-temporal stores, by kind (bit set): 1 the forward's output
+                             // rows, 2 the output rows of the one-pass and double-backward kernels, 4 weight
+                             // gradients, 8 x-messages; the rest by plain stores
     bool redx = true;        // cross-lane sums by VALU lane exchanges (permlane swaps, DPP) instead of
                              // shuffles through the LDS crossbar
     int full = 7;            // dispatch to the folded-flag kernels: bit 0 backward, bit 1 double backward, bit 2 fused forward+backward

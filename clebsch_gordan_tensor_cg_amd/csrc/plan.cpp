@@ -290,6 +290,7 @@ Tuning tuning_from_env() {
             else if (k == "bgy") t.bgy = v != 0;
             else if (k == "gy64") t.gy64 = v != 0;
             else if (k == "redx") t.redx = v != 0;
+            else if (k == "stnt") t.stnt = v & 15;
             else if (k == "full") t.full = v & 7;
             else if (k == "ubudget") t.ubudget = v < 1 ? 0 : v;
             else if (k == "ucpl") t.ucpl = v < 1 ? 0 : (v > 8 ? 8 : v);
