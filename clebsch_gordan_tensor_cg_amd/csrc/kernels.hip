@@ -81,8 +81,11 @@ __global__ void __launch_bounds__(256) k_segment_sum_rows(const T *__restrict__ 
                 V a[16];
 #pragma unroll
                 for (int u = 0; u < 16; ++u) {
+                    // past the segment's end (the same for the whole
+                    // workgroup): no row load, the index read clamped in range
                     const bool ok = k + u < end;
-                    const int64_t r = ok ? (kPerm ? perm[k + u] : k + u) : 0;
+                    const int kk = ok ? k + u : beg;
+                    const int64_t r = kPerm ? perm[kk] : kk;
                     // each row is read once: stream it past the caches
                     a[u] = ok ? __builtin_nontemporal_load((const V *)(rows + r * width + c)) : VT::zero();
                 }
