@@ -96,7 +96,7 @@ def test_graph_full_step(B, torch):
 
     def step():
         B.cgtp_build_csr_order(dst_c, N, val=src_c, ws=csr_ws, out=(perm, rp, dst_s, src_s), order=order)
-        B.cgtp_build_csr(src_s, N, sorted_key=False, ws=csr_ws, out=(src_perm, src_rp, None, None))
+        B.cgtp_build_csr_transpose_canonical(src_c, perm, N, out=(src_perm, src_rp))
         B.cgtp_conv_forward_backward_vec(plan, x, vec, perm, w, src_s, rp, src_rp, src_perm, g_out, ws=ws,
                                          out=(out, g_x, None, g_w, F), node_order=order)
         B.cgtp_force_loss_sh_cotangent(3, vec, perm, src_s, dst_s, F, "f32", out=gg)

@@ -746,8 +746,14 @@ def test_c4_full_step_full_size(B, torch):
     perm_ref, rp_ref = oracle.csr(dst, N)
     print(f"c4 full step E={E}", flush=True)
     src_c, dst_c = torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda()
+    # the bench's step: the destination CSR with the node order, then the
+    # transpose from the canonical edge order (checked against the general
+    # build of the transpose)
     perm, rp, dst_s, src_s, order = B.cgtp_build_csr_order(dst_c, N, val=src_c)
-    src_perm, src_rp, _, _ = B.cgtp_build_csr(src_s, N, sorted_key=False)
+    src_perm, src_rp = B.cgtp_build_csr_transpose_canonical(src_c, perm, N)
+    sp_gen, srp_gen, _, _ = B.cgtp_build_csr(src_s, N, sorted_key=False)
+    torch.cuda.synchronize()
+    assert torch.equal(src_perm, sp_gen) and torch.equal(src_rp, srp_gen)
     x_d = to_dev(torch, x, "f32")
     w_d = to_dev(torch, w[perm_ref], "f32")
     vec_d = torch.from_numpy(vec).cuda()
