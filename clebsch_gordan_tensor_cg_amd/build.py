@@ -28,27 +28,30 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Wno-unused-command-line-argument", "-Wno-format-security"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     subprocess.check_call(cmd)
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, out: str = OUT, build_dir: str = BUILD, extra=()) -> str:
+    """Compile every source and link the shared library at `out`; `extra`
+    flags go to every compile and the link (e.g. host-only sanitizers for a
+    test build: each -fsanitize= after -Xarch_host)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".cpp", ".hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + f".tmp{os.getpid()}"
-    subprocess.check_call([HIPCC, *COMMON, "-shared", *objs, "-o", tmp, "-ldl"])
-    os.replace(tmp, OUT)
+        objs = list(ex.map(lambda f: _compile(f, build_dir, extra), srcs))
+    tmp = out + f".tmp{os.getpid()}"
+    subprocess.check_call([HIPCC, *COMMON, *extra, "-shared", *objs, "-o", tmp, "-ldl"])
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
 
 
 def aot_standard_plans(verbose: bool = True) -> None:

@@ -2,6 +2,7 @@
 // generated kernels.  See include/cgtp.h for the contract of every call.
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <exception>
 #include <functional>
@@ -303,6 +304,7 @@ int cgtp_plan(const char *irreps_in1, const char *irreps_in2, const char *irreps
         choose_shapes(p);
         p.source = generate_source(p);
         if ((rc = compile_and_load(p, !(flags & CGTP_PLAN_NO_LOAD), err))) return fail(rc, err);
+        if (std::getenv("CGTP_DEBUG")) dump_plan(p);
         *out = h;
         return CGTP_OK;
     } catch (const std::bad_alloc &) {

@@ -181,6 +181,8 @@ constexpr size_t kUvwMmaMaxLds = 64 * 1024;   // static LDS of one workgroup
 int parse_irreps(const char *s, std::vector<Irrep> &out, std::string &err);
 int real_coupling(int l1, int l2, int l3, std::vector<double> &R, std::string &err);
 void choose_shapes(Plan &p);
+// the plan's paths, work split and tuning on stderr (CGTP_DEBUG)
+void dump_plan(const Plan &p);
 
 // code generation
 std::string generate_source(const Plan &p);

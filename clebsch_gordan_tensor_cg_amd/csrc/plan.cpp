@@ -416,4 +416,61 @@ void choose_shapes(Plan &p) {
     split(p, p.fb, 3);
 }
 
+
+// Plan dump (CGTP_DEBUG set in the environment): the paths with their
+// nonzero counts, each kernel kind's work split and the tuning in force,
+// one plan per block on stderr.
+void dump_plan(const Plan &p) {
+    auto irs = [](const std::vector<Irrep> &v) {
+        std::string o;
+        for (const Irrep &ir : v) {
+            if (!o.empty()) o += "+";
+            o += std::to_string(ir.mul) + "x" + std::to_string(ir.l) +
+                 (ir.parity > 0 ? "e" : ir.parity < 0 ? "o" : "");
+        }
+        return o;
+    };
+    auto list = [](const std::vector<int> &v) {
+        std::string o;
+        for (int x : v) o += (o.empty() ? "" : " ") + std::to_string(x);
+        return o;
+    };
+    const char *dt = p.dtype == CGTP_F64 ? "f64" : p.dtype == CGTP_F32 ? "f32" : "bf16-f32acc";
+    std::fprintf(stderr, "cgtp plan: %s (dim %lld) x %s (dim %lld) -> %s (dim %lld), %s, %s, flags 0x%x\n",
+                 irs(p.in1).c_str(), (long long)p.dim1, irs(p.in2).c_str(), (long long)p.dim2, irs(p.out).c_str(),
+                 (long long)p.dim3, p.mode == CGTP_UVW ? "uvw" : "uvu", dt, p.flags);
+    size_t nnz = 0;
+    for (size_t a = 0; a < p.paths.size(); ++a) {
+        const Path &P = p.paths[a];
+        nnz += P.nz.size();
+        std::fprintf(stderr, "  path %zu: blocks (%d, %d, %d), l (%d x %d -> %d), mul %d x %d -> %d, %zu nonzeros, "
+                             "weights at %lld\n",
+                     a, P.i1, P.i2, P.i3, P.l1, P.l2, P.l3, P.mul1, P.mul2, P.mul3, P.nz.size(), (long long)P.woff);
+    }
+    std::fprintf(stderr, "  %zu paths, %zu nonzeros, %lld weights per item, SH degree in the kernels %d\n",
+                 p.paths.size(), nnz, (long long)p.wnumel, p.sh_lmax);
+    const char *names[] = {"forward", "backward", "double backward", "forward+backward"};
+    const KernelShape *shapes[] = {&p.fwd, &p.bwd, &p.dbl, &p.fb};
+    for (int k = 0; k < 4; ++k) {
+        const KernelShape &ks = *shapes[k];
+        if (ks.groups.empty()) continue;
+        std::fprintf(stderr, "  %s: %d lanes per item, %d items per wavefront, %d units\n", names[k],
+                     ks.lanes_per_item, ks.items_per_wave, ks.n_units);
+        for (size_t gi = 0; gi < ks.groups.size(); ++gi) {
+            const Group &g = ks.groups[gi];
+            std::fprintf(stderr, "    group %zu: paths [%s], input-1 blocks [%s], output blocks [%s], %d channels, "
+                                 "%d per lane, %d slices\n",
+                         gi, list(g.paths).c_str(), list(g.in1_blocks).c_str(), list(g.out_blocks).c_str(), g.max_mul,
+                         g.cpl, g.slices);
+        }
+    }
+    const Tuning &t = p.tune;
+    std::fprintf(stderr, "  tuning: depth %d, depth_bwd %d, stage %d, budget %d, gy64 %d, redx %d, stnt %d, full %d, "
+                         "bgy %d, pform %d, pfuse %d\n",
+                 t.depth, t.depth_bwd, t.stage, t.budget, (int)t.gy64, (int)t.redx, t.stnt, t.full, (int)t.bgy,
+                 t.pform, t.pfuse);
+    std::fprintf(stderr, "  generated source: %zu bytes, %d kernels, code object %s\n", p.source.size(), p.n_kernels,
+                 p.cached ? "from the cache" : "compiled");
+}
+
 }  // namespace cgtp

@@ -31,11 +31,15 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "cgtp_oracle.c")
-_LIB = os.path.join(_HERE, "libcgtp_oracle.so")
+# CGTP_ORACLE_LIB: another build of the same source to load instead (the
+# sanitizer test's); it is never rebuilt here
+_LIB = os.environ.get("CGTP_ORACLE_LIB") or os.path.join(_HERE, "libcgtp_oracle.so")
 
 
 def build_oracle(force: bool = False) -> str:
     """Compile the C oracle with gcc (host only)."""
+    if os.environ.get("CGTP_ORACLE_LIB"):
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + f".tmp{os.getpid()}"
         subprocess.check_call(

@@ -56,6 +56,47 @@ def test_plan_dims_and_paths_match_oracle(B, name):
                                                                  op.weight_numel)
 
 
+@pytest.mark.parametrize("name,n_paths,nnz", [("c1", 7, 37), ("c2", 10, 86), ("c3", 17, 215), ("c5", 44, 1132)])
+def test_plan_dump(name, n_paths, nnz):
+    """CGTP_DEBUG prints the plan: its path and CG-nonzero counts (the
+    workloads' counts, and the oracle's own nonzeros of each path's real
+    coupling tensor) and every kernel kind's work split, whose units cover
+    every path exactly once."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from clebsch_gordan_tensor_cg_amd import binding as B, workloads as W\n"
+            "c = W.config(%r)\n"
+            "B.Plan(c.irreps_in1, c.irreps_in2, c.irreps_out, c.paths, c.mode, c.dtype, c.shared_weights, "
+            "no_load=True)\n" % (ROOT, name))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600,
+                       env=dict(os.environ, CGTP_DEBUG="1"))
+    assert r.returncode == 0, r.stderr[-2000:]
+    err = r.stderr
+    assert f"  {n_paths} paths, {nnz} nonzeros," in err, err[-3000:]
+    c = W.config(name)
+    op = oracle.Problem(c.irreps_in1, c.irreps_in2, c.irreps_out, c.mode, c.paths, c.shared_weights)
+    irr = lambda s: oracle.parse_irreps(s)
+    a, b, o = irr(c.irreps_in1), irr(c.irreps_in2), irr(c.irreps_out)
+    onz = sum(int((np.abs(oracle.real_cg(a[i].l, b[j].l, o[k].l)) > 1e-14).sum()) for i, j, k in op.paths)
+    assert onz == nnz
+    for line in err.splitlines():
+        m = re.match(r"  path (\d+): .* (\d+) nonzeros,", line)
+        if m:
+            i, j, k = op.paths[int(m.group(1))]
+            assert int(m.group(2)) == int((np.abs(oracle.real_cg(a[i].l, b[j].l, o[k].l)) > 1e-14).sum())
+    # every kernel kind's groups cover the paths once
+    kinds = re.split(r"\n  (?:forward\+backward|double backward|backward|forward): ", err)
+    seen = 0
+    for blk in kinds[1:]:
+        paths = []
+        for m in re.finditer(r"group \d+: paths \[([0-9 ]*)\]", blk):
+            paths += [int(v) for v in m.group(1).split()]
+        assert sorted(paths) == list(range(n_paths)), blk
+        seen += 1
+    assert seen >= 1
+
+
 def test_generated_source_has_each_nonzero_once_per_channel_slot(B):
     c = W.config("c1")
     p = B.Plan(c.irreps_in1, c.irreps_in2, c.irreps_out, c.paths, c.mode, c.dtype, no_load=True)
