@@ -65,7 +65,8 @@ struct Tuning {
     int cpl[4] = {0, 0, 0, 0};  // channels per lane per kernel kind (0 = by budget)
     int budget = 112;        // VGPR estimate allowed for two channels per lane
     bool y_vector = true;    // load the y row with vector (not scalar) loads
-    bool nt_w = true;        // non-temporal loads of the per-edge weights
+    int nt_w = -1;           // non-temporal loads of the per-edge weights: -1 where one item fills a
+                             // wavefront (plain where items share one), 0 never, 1 always
     bool prefetch = true;    // load edge t+1 while edge t is computed
     int stage = -1;          // edges per LDS chunk of src and y rows (0 = off; -1: 64, or 32 for uvw
                              // layers without radial weights)

@@ -281,7 +281,7 @@ Tuning tuning_from_env() {
             else if (k == "cpl_fb") t.cpl[3] = v;
             else if (k == "budget") t.budget = v;
             else if (k == "yvec") t.y_vector = v != 0;
-            else if (k == "ntw") t.nt_w = v != 0;
+            else if (k == "ntw") t.nt_w = v < 0 ? -1 : (v != 0);
             else if (k == "pf") t.prefetch = v != 0;
             else if (k == "stage") t.stage = v < 0 ? 0 : (v > 256 ? 256 : v);
             else if (k == "cypath") t.cy_path = v;
