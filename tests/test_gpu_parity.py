@@ -41,8 +41,10 @@ def _plan(B, cfg_or_args, **kw):
 # ---------------------------------------------------------------------------
 # single tensor product
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("batch", [1000, 1, 77])
+@pytest.mark.parametrize("batch", [1000, 1, 77, 1000000])
 def test_single_tp_forward_c1(B, torch, batch):
+    """The single product against the oracle, every output; a million items
+    is the launch the bench times for its bandwidth figure."""
     c = W.config("c1")
     plan, prob = _plan(B, c)
     rng = np.random.default_rng(0)
