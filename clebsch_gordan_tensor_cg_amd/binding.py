@@ -151,7 +151,9 @@ class _Args:
             raise TypeError(f"{self.call}: {name} must be a torch.Tensor")
         if dtype is not None and t.dtype != dtype:
             raise TypeError(f"{self.call}: {name}: expected {dtype}, got {t.dtype}")
-        if shape is not None:
+        # (torch.Size compares equal to a tuple of ints: the common case costs
+        # one comparison; the slow path normalises numpy integers)
+        if shape is not None and t.shape != shape:
             want = tuple(int(v) for v in shape)
             if tuple(t.shape) != want:
                 raise ValueError(f"{self.call}: {name}: expected shape {want}, got {tuple(t.shape)}")
@@ -161,15 +163,18 @@ class _Args:
         return t
 
     def device(self):
-        """All checked tensors on one CUDA device; returns it."""
+        """All checked tensors on one CUDA device; returns its index.
+        (get_device() is an int, -1 on the host: cheaper than building a
+        torch.device per tensor, which matters for launch-bound calls.)"""
         dev = None
         for name, t in self.seen:
-            if not t.is_cuda:
+            d = t.get_device()
+            if d < 0:
                 raise ValueError(f"{self.call}: {name} is on {t.device}; cgtp runs on the GPU only")
             if dev is None:
-                dev = t.device
-            elif t.device != dev:
-                raise ValueError(f"{self.call}: {name} is on {t.device}, other tensors on {dev}")
+                dev = d
+            elif d != dev:
+                raise ValueError(f"{self.call}: {name} is on {t.device}, other tensors on cuda:{dev}")
         return dev
 
 
@@ -227,11 +232,12 @@ def _stream(stream=None, like=None):
     """Stream handle: the given stream, else torch's current stream on the
     tensors' device (host tensors: the NULL stream, for argument checks)."""
     if stream is None and like is not None:
-        if not like.is_cuda:
+        d = like.get_device()
+        if d < 0:
             return None
         if _raw_stream is not None:   # torch's cheap accessor for the current stream
-            return _raw_stream(like.device.index)
-        return torch.cuda.current_stream(like.device).cuda_stream
+            return _raw_stream(d)
+        return torch.cuda.current_stream(d).cuda_stream
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
 
