@@ -2,10 +2,11 @@
 
 The HIP source a plan generates is compiled for the host with a thin shim
 (tests/emu/shim.h: one thread per lane, LDS as shared statics, shuffles and
-wavefront syncs through a barrier) and AddressSanitizer, every buffer
-allocated at its exact size, and launched over the same grid the library
-uses.  Checked: no access outside any buffer, and the outputs against the
-oracle.  The case is the one whose FP64 form took a device memory fault on
+wavefront syncs through a barrier), AddressSanitizer and
+UndefinedBehaviorSanitizer, every buffer allocated at its exact size, and
+launched over the same grid the library uses.  Checked: no access outside
+any buffer, no undefined behaviour (shifts, signed overflow, misaligned or
+null accesses, invalid loads), and the outputs against the oracle.  The case is the one whose FP64 form took a device memory fault on
 the GPU (128-channel plan, SH computed from edge vectors, forces from the
 per-unit SH-gradient partials): the FP64 one-pass kernel stays switched off
 on the device; this shows that the code generated now stays in bounds for
@@ -79,7 +80,8 @@ def test_one_pass_kernel_emulated(B, tmp_path, dtype):
     wr("src.bin", G.src_d, np.int32); wr("rp.bin", G.row_ptr, np.int32); wr("vperm.bin", G.perm, np.int32)
     (tmp_path / "kernel.inc").write_text(src_text)
     exe = tmp_path / "run_fb"
-    cmd = [CLANG, "-std=c++20", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
+    cmd = [CLANG, "-std=c++20", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer",
            "-D__HIPCC_RTC__", f"-DREAL={'double' if dtype == 'f64' else 'float'}", "-I", str(tmp_path),
            "-I", os.path.join(HERE, "emu"), os.path.join(HERE, "emu", "run_fb.cpp"), "-o", str(exe)]
     subprocess.run(cmd, check=True, capture_output=True, timeout=600)
@@ -99,7 +101,8 @@ def test_one_pass_kernel_emulated(B, tmp_path, dtype):
                             str(prob.weight_numel), str(units), str(ipw), str(flags), "1"],
                            cwd=tmp_path, capture_output=True, text=True, timeout=600,
                            env=dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1"))
-        assert r.returncode == 0 and "AddressSanitizer" not in r.stderr, r.stderr[-3000:]
+        assert r.returncode == 0 and "AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr, \
+            r.stderr[-3000:]
         rd = lambda name, cnt: np.fromfile(str(tmp_path / name), dtype=f, count=cnt)
         out = rd("out_emu.bin", n * prob.dim3).reshape(n, prob.dim3)
         assert rel_err(out, ref) <= tol
