@@ -649,25 +649,24 @@ __global__ void k_validate(const int32_t *__restrict__ row_ptr, int64_t n_rows, 
 // ordered by destination and therefore by destination-sorted position, which
 // is the stable order by source of the destination-sorted edges: the
 // transpose's entry for canonical edge e is the position t with perm[t] = e,
-// and its row pointers are those run boundaries (found by binary search).
+// and its row pointers are those run boundaries.  Row pointer s is the first
+// canonical index whose source is at least s: position t (0..E) opens rows
+// (src[t-1], src[t]], with src[-1] = -1 and src[E] = n_keys, sources clamped
+// to [-1, n_keys] (every write in bounds whatever src holds; for a sorted
+// list this equals a binary search for each s).
 __global__ void k_csr_transpose_canonical(const int32_t *__restrict__ src, const int32_t *__restrict__ perm,
                                           int64_t n_edges, int64_t n_keys, int32_t *__restrict__ src_perm,
                                           int32_t *__restrict__ src_row_ptr) {
-    const int64_t n = n_edges > n_keys + 1 ? n_edges : n_keys + 1;
-    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+    auto clamp_key = [n_keys](int64_t v) { return v < -1 ? (int64_t)-1 : (v > n_keys ? n_keys : v); };
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t <= n_edges;
+         t += (int64_t)gridDim.x * blockDim.x) {
         if (t < n_edges) {
             const int32_t e = perm[t];
             if (e >= 0 && e < n_edges) src_perm[e] = (int32_t)t;   // in bounds whatever perm holds
         }
-        if (t <= n_keys) {
-            int64_t lo = 0, hi = n_edges;   // first index with src >= t
-            while (lo < hi) {
-                const int64_t mid = (lo + hi) >> 1;
-                if (src[mid] < t) lo = mid + 1;
-                else hi = mid;
-            }
-            src_row_ptr[t] = (int32_t)lo;
-        }
+        const int64_t prev = t == 0 ? -1 : clamp_key(src[t - 1]);
+        const int64_t cur = t == n_edges ? n_keys : clamp_key(src[t]);
+        for (int64_t k = prev + 1; k <= cur; ++k) src_row_ptr[k] = (int32_t)t;
     }
 }
 
@@ -1838,8 +1837,7 @@ int cgtp_build_csr_transpose_canonical(const int32_t *src, const int32_t *perm, 
     if (!src_row_ptr || (n_edges > 0 && (!src || !perm || !src_perm)))
         return set_error(CGTP_ERR_INVALID_ARGUMENT, "cgtp_build_csr_transpose_canonical: NULL pointer");
     hipStream_t s = (hipStream_t)stream;
-    const int64_t n = std::max<int64_t>(n_edges, n_keys + 1);
-    const unsigned g = (unsigned)std::min<int64_t>(grid_for(n), 65536);
+    const unsigned g = (unsigned)std::min<int64_t>(grid_for(n_edges + 1), 65536);   // positions 0..E
     CGTP_LAUNCH("k_csr_transpose_canonical", s, k_csr_transpose_canonical, dim3(g), dim3(kBlock), 0, s, src, perm,
                 n_edges, n_keys, src_perm, src_row_ptr);
     return hip_check(hipGetLastError(), "cgtp_build_csr_transpose_canonical launch");

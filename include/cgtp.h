@@ -393,7 +393,8 @@ int cgtp_build_csr_order_noalloc(const int32_t *key, const int32_t *val, int64_t
  * destination-sorted sources (its perm and row_ptr): the edges of source s
  * are the canonical run of s, in order of destination.  One launch, no
  * workspace, nothing allocated.  An edge list that is not canonical gives
- * undefined (in-range) results; check with cgtp_validate_csr where unsure.
+ * undefined (in-range) results, in up to n_edges * n_keys steps; check with
+ * cgtp_validate_csr where unsure.
  * Errors: INVALID_ARGUMENT (sizes, NULL). */
 int cgtp_build_csr_transpose_canonical(const int32_t *src, const int32_t *perm, int64_t n_edges,
                                        int64_t n_keys, int32_t *src_perm, int32_t *src_row_ptr,
